@@ -1,0 +1,194 @@
+"""CPU oracle for the affine Q4 group-32 quantized linear layer.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only code allowed to import this package. It shares no
+code with the HIP library (``bit_group_quantized_amd``) and neither imports the
+other.
+
+The arithmetic lives in plain C (``q4_oracle.c``); this module only builds and
+loads it and marshals numpy arrays. Every function cites the passage of the
+pages it follows in the C source. Summary of what is computed:
+
+* ``quantize(w)``: per 32-weight group along the input dimension, scale =
+  (max - min)/15 and bias = min, both rounded to bf16; codes are
+  ``clamp(rint((w - bias')/scale'), 0, 15)`` against the stored bf16 values;
+  8 codes per uint32, low nibble first ("personaplex-edge-q4" model card,
+  Release details table: affine Q4, group size 32, BF16 activations).
+* ``unpack``: codes and ``w_hat = scale'*q + bias'``.
+* ``matmul(x, ...)``: ``y = x . W_hat^T`` summed in float64 (the blog
+  translation's MultiLinear figure: quantized product with transpose).
+* ``multilinear_step``: the same product on rows ``[s*out, (s+1)*out)``.
+
+Parity status of each function is recorded in the design notes; every function
+here is pinned by ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "q4_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle_q4.so")
+_lib = None
+
+GROUP = 32
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc into ``oracle/liboracle_q4.so``."""
+    if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+           "-fopenmp", "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I = ctypes.c_int64
+    lib.oracle_quantize.argtypes = [P, I, I, P, P, P]
+    lib.oracle_unpack.argtypes = [P, P, P, I, I, P, P]
+    lib.oracle_matmul.argtypes = [P, I, P, P, P, I, I, P]
+    lib.oracle_multilinear_step.argtypes = [P, I, P, P, P, I, I, I, I, P]
+    lib.oracle_bf16_round.argtypes = [P, I, P]
+    lib.oracle_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    for f in ("oracle_quantize", "oracle_unpack", "oracle_matmul", "oracle_multilinear_step",
+              "oracle_bf16_round"):
+        getattr(lib, f).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str) -> None:
+    if rc == 1:
+        raise ValueError(f"{what}: invalid argument (shape or pointer)")
+    if rc == 2:
+        raise ValueError(f"{what}: non-finite input")
+    if rc != 0:
+        raise RuntimeError(f"{what}: oracle error {rc}")
+
+
+def threads() -> int:
+    return int(_load().oracle_threads())
+
+
+def set_threads(t: int) -> None:
+    _load().oracle_set_threads(int(t))
+
+
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) of fp32 values, round to nearest even."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.empty(a.shape, dtype=np.uint16)
+    _check(_load().oracle_bf16_round(_ptr(a), a.size, _ptr(out)), "bf16_round")
+    return out
+
+
+def bf16_value(h: np.ndarray) -> np.ndarray:
+    """fp32 values of bf16 bit patterns (exact widening)."""
+    return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def quantize(w: np.ndarray):
+    """Quantize fp32 W [n, k] -> (packed uint32 [n, k/8], scales uint16 [n, k/32],
+    biases uint16 [n, k/32])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w.shape
+    packed = np.empty((n, k // 8), dtype=np.uint32)
+    scales = np.empty((n, k // GROUP), dtype=np.uint16)
+    biases = np.empty((n, k // GROUP), dtype=np.uint16)
+    _check(_load().oracle_quantize(_ptr(w), n, k, _ptr(packed), _ptr(scales), _ptr(biases)), "quantize")
+    return packed, scales, biases
+
+
+def unpack(packed: np.ndarray, scales: np.ndarray, biases: np.ndarray, k: int):
+    """Return (q uint8 [n, k], w_hat fp32 [n, k])."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint32)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    biases = np.ascontiguousarray(biases, dtype=np.uint16)
+    n = packed.shape[0]
+    q = np.empty((n, k), dtype=np.uint8)
+    w_hat = np.empty((n, k), dtype=np.float32)
+    _check(_load().oracle_unpack(_ptr(packed), _ptr(scales), _ptr(biases), n, k, _ptr(q), _ptr(w_hat)),
+           "unpack")
+    return q, w_hat
+
+
+def matmul(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray, biases: np.ndarray, k: int) -> np.ndarray:
+    """y = x . W_hat^T in float64. x_bits: bf16 bit patterns [m, k] (or [k])."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    squeeze = x_bits.ndim == 1
+    if squeeze:
+        x_bits = x_bits[None, :]
+    m = x_bits.shape[0]
+    packed = np.ascontiguousarray(packed, dtype=np.uint32)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    biases = np.ascontiguousarray(biases, dtype=np.uint16)
+    n = packed.shape[0]
+    if x_bits.shape[1] != k or packed.shape[1] * 8 != k:
+        raise ValueError("shape mismatch")
+    y = np.empty((m, n), dtype=np.float64)
+    _check(_load().oracle_matmul(_ptr(x_bits), m, _ptr(packed), _ptr(scales), _ptr(biases), n, k, _ptr(y)),
+           "matmul")
+    return y[0] if squeeze else y
+
+
+def multilinear_step(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray, biases: np.ndarray,
+                     num_steps: int, out: int, k: int, step: int) -> np.ndarray:
+    """Product with the row block of codebook step ``step`` ([num_steps*out, k] weights)."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    squeeze = x_bits.ndim == 1
+    if squeeze:
+        x_bits = x_bits[None, :]
+    m = x_bits.shape[0]
+    packed = np.ascontiguousarray(packed, dtype=np.uint32)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    biases = np.ascontiguousarray(biases, dtype=np.uint16)
+    if packed.shape[0] != num_steps * out:
+        raise ValueError("packed rows must equal num_steps*out")
+    y = np.empty((m, out), dtype=np.float64)
+    _check(_load().oracle_multilinear_step(_ptr(x_bits), m, _ptr(packed), _ptr(scales), _ptr(biases),
+                                           num_steps, out, k, step, _ptr(y)), "multilinear_step")
+    return y[0] if squeeze else y
+
+
+def output_bits_bf16(y: np.ndarray) -> np.ndarray:
+    """What a bf16 output tensor holds for the exact result y: bf16_rne(fl32(y))."""
+    return bf16_round(np.asarray(y, dtype=np.float64).astype(np.float32))
+
+
+def floored_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """Max over outputs of |got - ref| / max(|ref|, 1e-3 * rms(ref)), per output row.
+
+    "Max relative error" is ill-posed where the exact output is near zero; the
+    floor of 1e-3 of the row's RMS is the reading used for the tolerances."""
+    got = np.atleast_2d(np.asarray(got, dtype=np.float64))
+    ref = np.atleast_2d(np.asarray(ref, dtype=np.float64))
+    worst = 0.0
+    for g, r in zip(got, ref):
+        if r.size == 0:
+            continue
+        rms = float(np.sqrt(np.mean(r * r)))
+        floor = max(1e-3 * rms, np.finfo(np.float64).tiny)
+        e = np.abs(g - r) / np.maximum(np.abs(r), floor)
+        worst = max(worst, float(e.max()))
+    return worst

@@ -1,0 +1,230 @@
+/*
+ * Reference CPU oracle for the affine 4-bit group-32 quantized linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the plain, slow, obviously-correct
+ * statement of what the GPU path must compute. Only the test suite, the
+ * smoke check and the CPU-baseline leg of the benchmark may load it. It
+ * shares no code, header, table or constant with the HIP library.
+ *
+ * What it follows (sources are the web pages the method is taken from):
+ *  - "personaplex-edge-q4" model card, Release details table: the format is
+ *    affine Q4 with group size 32 and BF16 activations; the parameter count
+ *    and the source/packed sizes in that table fix 5 bits per weight, i.e. a
+ *    4-bit code plus a 16-bit scale and a 16-bit bias per 32 weights.
+ *  - same card, introduction: weights stay packed at inference and feed a
+ *    quantized matmul; they are not expanded back to BF16.
+ *  - "NVIDIA PersonaPlex 7B on Apple Silicon" (blog translation), section on
+ *    the Depformer's per-step weight switching (MultiLinear code figure): the
+ *    quantized product takes (x, w, scales, biases) with transpose, i.e.
+ *    y = x . W^T with W stored [out, in], groups running along `in`, and a
+ *    codebook step s slicing rows [s*out, (s+1)*out) of weight, scales and
+ *    biases together.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *  - quantizer: per group, mn = min, mx = max, scale = fl32(fl32(mx-mn)/15)
+ *    with a correctly rounded divide, bias = mn; both stored as bf16 by
+ *    round-to-nearest-even; codes are computed against the STORED bf16
+ *    scale/bias: q = clamp(rint_half_even(fl32(fl32(w-b')/s')), 0, 15), and
+ *    q = 0 for every element when the stored scale is zero;
+ *  - min/max scan the group in index order with strict comparisons;
+ *  - packing: 8 codes per uint32 along the input dimension, code t of a word
+ *    in bits [4t, 4t+4) (low nibble first); scales and biases are two
+ *    separate [n][k/32] arrays of bf16 bit patterns;
+ *  - dequantized weight w_hat = fl32(s' * q + b') (s'*q is exact, so this is
+ *    a single rounding);
+ *  - product: y[m][n] = sum_k w_hat[n][k] * x[m][k], summed in double in
+ *    natural k order (each product is exact in double).
+ *
+ * Non-finite inputs are outside the method's domain: every entry point
+ * rejects them with a nonzero return code.
+ *
+ * Built with gcc -O2 -ffp-contract=off -fopenmp (no intrinsics); OpenMP is
+ * used only to split output rows across host threads.
+ */
+#include <stdint.h>
+#include <string.h>
+#include <math.h>
+#include <stddef.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG 1
+#define ORACLE_ERR_NONFINITE 2
+
+/* --- bf16 helpers: a bf16 is the upper 16 bits of an IEEE binary32 --- */
+
+static float bits_to_f32(uint32_t u) {
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+static uint32_t f32_to_bits(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return u;
+}
+
+/* Value of a bf16 bit pattern: exact widening to binary32. */
+static float bf16_value(uint16_t h) { return bits_to_f32((uint32_t)h << 16); }
+
+/* Round a finite binary32 to bf16, to nearest, ties to even. Dropping the
+ * low 16 bits is truncation; adding 0x7FFF plus the kept LSB first turns it
+ * into round-half-even (a carry out of the mantissa correctly bumps the
+ * exponent). */
+static uint16_t bf16_round_nearest_even(float f) {
+  uint32_t u = f32_to_bits(f);
+  uint32_t kept_lsb = (u >> 16) & 1u;
+  u += 0x7FFFu + kept_lsb;
+  return (uint16_t)(u >> 16);
+}
+
+/* --- quantize + pack --- */
+
+int oracle_version(void) { return 1; }
+
+int oracle_bf16_round(const float* in, int64_t count, uint16_t* out) {
+  if (!in || !out || count < 0) return ORACLE_ERR_ARG;
+  for (int64_t i = 0; i < count; ++i) {
+    if (!isfinite(in[i])) return ORACLE_ERR_NONFINITE;
+    out[i] = bf16_round_nearest_even(in[i]);
+  }
+  return ORACLE_OK;
+}
+
+/* Quantize one group of 32 weights; write 32 codes, the stored scale and bias. */
+static void quantize_group(const float* w, uint8_t* q, uint16_t* scale_bits, uint16_t* bias_bits) {
+  float mn = w[0], mx = w[0];
+  for (int i = 1; i < 32; ++i) {
+    if (w[i] < mn) mn = w[i];
+    if (w[i] > mx) mx = w[i];
+  }
+  float range = mx - mn;
+  float scale = range / 15.0f;
+  uint16_t sb = bf16_round_nearest_even(scale);
+  uint16_t bb = bf16_round_nearest_even(mn);
+  float s_stored = bf16_value(sb);
+  float b_stored = bf16_value(bb);
+  for (int i = 0; i < 32; ++i) {
+    if (s_stored == 0.0f) {
+      q[i] = 0;
+      continue;
+    }
+    float t = (w[i] - b_stored) / s_stored;
+    float r = rintf(t); /* default rounding mode: nearest, ties to even */
+    if (r < 0.0f) r = 0.0f;
+    if (r > 15.0f) r = 15.0f;
+    q[i] = (uint8_t)r;
+  }
+  *scale_bits = sb;
+  *bias_bits = bb;
+}
+
+/* w: fp32 [n][k] row-major, k % 32 == 0.
+ * packed: uint32 [n][k/8]; scales, biases: bf16 bits [n][k/32]. */
+int oracle_quantize(const float* w, int64_t n, int64_t k, uint32_t* packed, uint16_t* scales,
+                    uint16_t* biases) {
+  if (!w || !packed || !scales || !biases || n < 0 || k < 0 || k % 32 != 0) return ORACLE_ERR_ARG;
+  for (int64_t i = 0; i < n * k; ++i)
+    if (!isfinite(w[i])) return ORACLE_ERR_NONFINITE;
+  const int64_t groups = k / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t g = 0; g < groups; ++g) {
+      uint8_t q[32];
+      quantize_group(w + r * k + g * 32, q, &scales[r * groups + g], &biases[r * groups + g]);
+      for (int j = 0; j < 4; ++j) {
+        uint32_t word = 0;
+        for (int t = 0; t < 8; ++t) word |= (uint32_t)q[8 * j + t] << (4 * t);
+        packed[r * (k / 8) + g * 4 + j] = word;
+      }
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* --- unpack / dequantize --- */
+
+/* q_out (nullable): uint8 [n][k]; w_out (nullable): fp32 [n][k]. */
+int oracle_unpack(const uint32_t* packed, const uint16_t* scales, const uint16_t* biases, int64_t n,
+                  int64_t k, uint8_t* q_out, float* w_out) {
+  if (!packed || !scales || !biases || n < 0 || k < 0 || k % 32 != 0) return ORACLE_ERR_ARG;
+  const int64_t groups = k / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t c = 0; c < k; ++c) {
+      uint32_t word = packed[r * (k / 8) + c / 8];
+      uint8_t q = (uint8_t)((word >> (4 * (c % 8))) & 0xFu);
+      if (q_out) q_out[r * k + c] = q;
+      if (w_out) {
+        float s = bf16_value(scales[r * groups + c / 32]);
+        float b = bf16_value(biases[r * groups + c / 32]);
+        w_out[r * k + c] = s * (float)q + b;
+      }
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* --- quantized product y = x . W_hat^T --- */
+
+/* x: bf16 bits [m][k]; y: double [m][n] (exact-sum reference, before any
+ * output rounding). Dequantizes each weight to fp32 and takes a plain dot
+ * product accumulated in double. */
+int oracle_matmul(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                  const uint16_t* biases, int64_t n, int64_t k, double* y) {
+  if (!x || !packed || !scales || !biases || !y || m < 0 || n < 0 || k < 0 || k % 32 != 0)
+    return ORACLE_ERR_ARG;
+  for (int64_t i = 0; i < m * k; ++i)
+    if (!isfinite(bf16_value(x[i]))) return ORACLE_ERR_NONFINITE;
+  const int64_t groups = k / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t row = 0; row < m; ++row) {
+      double acc = 0.0;
+      for (int64_t c = 0; c < k; ++c) {
+        uint32_t word = packed[r * (k / 8) + c / 8];
+        uint32_t q = (word >> (4 * (c % 8))) & 0xFu;
+        float s = bf16_value(scales[r * groups + c / 32]);
+        float b = bf16_value(biases[r * groups + c / 32]);
+        float w_hat = s * (float)q + b;
+        acc += (double)w_hat * (double)bf16_value(x[row * k + c]);
+      }
+      y[row * n + r] = acc;
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* Depformer per-step product: weights hold num_steps blocks of `out` rows
+ * ([num_steps*out][k]); step s uses rows [s*out, (s+1)*out) of the packed
+ * codes, scales and biases together, then the same product. */
+int oracle_multilinear_step(const uint16_t* x, int64_t m, const uint32_t* packed,
+                            const uint16_t* scales, const uint16_t* biases, int64_t num_steps,
+                            int64_t out, int64_t k, int64_t step, double* y) {
+  if (num_steps <= 0 || step < 0 || step >= num_steps || out < 0 || k < 0 || k % 32 != 0)
+    return ORACLE_ERR_ARG;
+  if (!packed || !scales || !biases) return ORACLE_ERR_ARG;
+  const int64_t start = step * out;
+  return oracle_matmul(x, m, packed + start * (k / 8), scales + start * (k / 32),
+                       biases + start * (k / 32), out, k, y);
+}
+
+/* Threads the OpenMP runtime will use (1 when built without OpenMP). */
+int oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+void oracle_set_threads(int t) {
+#ifdef _OPENMP
+  if (t > 0) omp_set_num_threads(t);
+#else
+  (void)t;
+#endif
+}
