@@ -1,0 +1,251 @@
+// C ABI of libq4 (declared in include/q4.h): argument validation, launch
+// configuration and kernel launches. No allocation, no synchronisation.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "q4.h"
+#include "q4_kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+inline q4_status launch_status() {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return Q4_ERR_HIP;
+  }
+  return Q4_OK;
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int kNumCU = 256;
+
+int grid_for_groups(int64_t n_groups) {
+  const int64_t blocks = ceil_div(n_groups, 256);
+  return static_cast<int>(blocks < 8 * kNumCU * 4 ? (blocks < 1 ? 1 : blocks) : 8 * kNumCU * 4);
+}
+
+// ---- GEMV launch: pick the lane split C so that S = ceil(G/C) waves cover
+// the input groups with the least idle lanes (ties: wider rows per load).
+struct GemvPlan {
+  int c;
+  int waves;
+  int rows_per_block;
+  int blocks;
+};
+
+constexpr int kGemvU = 8;
+
+bool plan_gemv(int64_t n, int64_t G, GemvPlan* p) {
+  int best_c = 0, best_s = 0;
+  int64_t best_waste = -1;
+  const int cs[4] = {64, 32, 16, 8};
+  for (int i = 0; i < 4; ++i) {
+    const int c = cs[i];
+    const int64_t s = ceil_div(G, c);
+    if (s > 16) continue;
+    const int64_t waste = s * c - G;
+    if (best_waste < 0 || waste < best_waste) {
+      best_waste = waste;
+      best_c = c;
+      best_s = static_cast<int>(s);
+    }
+  }
+  if (best_waste < 0) return false;
+  const int rows_iter = (64 / best_c) * kGemvU;
+  // Aim for >= 2 blocks per CU; each block covers at least one iteration.
+  const int64_t target_blocks = 2 * kNumCU;
+  int64_t rpb = ceil_div(n, target_blocks);
+  rpb = ceil_div(rpb, rows_iter) * rows_iter;
+  if (rpb < rows_iter) rpb = rows_iter;
+  p->c = best_c;
+  p->waves = best_s;
+  p->rows_per_block = static_cast<int>(rpb);
+  p->blocks = static_cast<int>(ceil_div(n, rpb));
+  return true;
+}
+
+template <int C>
+void launch_gemv_c(const GemvPlan& p, bool f32, const uint16_t* x, const uint32_t* packed,
+                   const uint16_t* scales, const uint16_t* biases, int n, int G, void* y,
+                   hipStream_t st) {
+  const dim3 grid(p.blocks), block(64 * p.waves);
+  if (f32)
+    hipLaunchKernelGGL((q4k::gemv_kernel<C, kGemvU, true>), grid, block, 0, st, x, packed, scales,
+                       biases, n, G, p.rows_per_block, y);
+  else
+    hipLaunchKernelGGL((q4k::gemv_kernel<C, kGemvU, false>), grid, block, 0, st, x, packed, scales,
+                       biases, n, G, p.rows_per_block, y);
+}
+
+q4_status run_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                   const uint16_t* biases, int64_t n, int64_t k, void* y, q4_out_dtype dt,
+                   hipStream_t st) {
+  const int64_t G = k / 32;
+  GemvPlan p;
+  if (!plan_gemv(n, G, &p)) return Q4_ERR_UNSUPPORTED;
+  const bool f32 = dt == Q4_OUT_F32;
+  switch (p.c) {
+    case 64: launch_gemv_c<64>(p, f32, x, packed, scales, biases, (int)n, (int)G, y, st); break;
+    case 32: launch_gemv_c<32>(p, f32, x, packed, scales, biases, (int)n, (int)G, y, st); break;
+    case 16: launch_gemv_c<16>(p, f32, x, packed, scales, biases, (int)n, (int)G, y, st); break;
+    default: launch_gemv_c<8>(p, f32, x, packed, scales, biases, (int)n, (int)G, y, st); break;
+  }
+  return launch_status();
+}
+
+// ---- small GEMM launch (MFMA): S waves of GS groups each, T row tiles of 16.
+template <int GS, int T>
+void launch_gemm_gs(int waves, bool f32, const uint16_t* x, int m, const uint32_t* packed,
+                    const uint16_t* scales, const uint16_t* biases, int n, int G, void* y,
+                    hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(ceil_div(n, 16 * T))), block(64 * waves);
+  const size_t shmem = static_cast<size_t>(waves) * T * 256 * sizeof(float);
+  if (f32)
+    hipLaunchKernelGGL((q4k::gemm_mfma_kernel<GS, T, true>), grid, block, shmem, st, x, m, packed,
+                       scales, biases, n, G, y);
+  else
+    hipLaunchKernelGGL((q4k::gemm_mfma_kernel<GS, T, false>), grid, block, shmem, st, x, m, packed,
+                       scales, biases, n, G, y);
+}
+
+q4_status run_gemm_small(const uint16_t* x, int64_t m, const uint32_t* packed,
+                         const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
+                         void* y, q4_out_dtype dt, hipStream_t st) {
+  if (m == 1) return run_gemv(x, packed, scales, biases, n, k, y, dt, st);
+  const int64_t G = k / 32;
+  const bool f32 = dt == Q4_OUT_F32;
+  constexpr int T = 1;
+  const int gss[4] = {8, 16, 24, 32};
+  for (int i = 0; i < 4; ++i) {
+    const int64_t waves = ceil_div(G, gss[i]);
+    if (waves > 16) continue;
+    switch (gss[i]) {
+      case 8: launch_gemm_gs<8, T>((int)waves, f32, x, (int)m, packed, scales, biases, (int)n, (int)G, y, st); break;
+      case 16: launch_gemm_gs<16, T>((int)waves, f32, x, (int)m, packed, scales, biases, (int)n, (int)G, y, st); break;
+      case 24: launch_gemm_gs<24, T>((int)waves, f32, x, (int)m, packed, scales, biases, (int)n, (int)G, y, st); break;
+      default: launch_gemm_gs<32, T>((int)waves, f32, x, (int)m, packed, scales, biases, (int)n, (int)G, y, st); break;
+    }
+    return launch_status();
+  }
+  return Q4_ERR_UNSUPPORTED;
+}
+
+q4_status check_matrix(const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+                       int64_t n, int64_t k) {
+  if (!packed || !scales || !biases) return Q4_ERR_NULL;
+  if (n < 0 || k <= 0 || k % 32 != 0 || n > INT32_MAX / 2) return Q4_ERR_SHAPE;
+  return Q4_OK;
+}
+
+q4_status check_align_matrix(const uint32_t* packed, const uint16_t* scales, const uint16_t* biases) {
+  if (!aligned(packed, 16) || !aligned(scales, 2) || !aligned(biases, 2)) return Q4_ERR_ALIGN;
+  return Q4_OK;
+}
+
+q4_status check_product(const uint16_t* x, int64_t m, const uint32_t* packed,
+                        const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
+                        void* y, q4_out_dtype dt) {
+  if (!x || !y) return Q4_ERR_NULL;
+  q4_status s = check_matrix(packed, scales, biases, n, k);
+  if (s != Q4_OK) return s;
+  if (m < 1 || m > Q4_MAX_M) return Q4_ERR_SHAPE;
+  if (dt != Q4_OUT_BF16 && dt != Q4_OUT_F32) return Q4_ERR_SHAPE;
+  s = check_align_matrix(packed, scales, biases);
+  if (s != Q4_OK) return s;
+  if (!aligned(x, 16) || !aligned(y, dt == Q4_OUT_F32 ? 4 : 2)) return Q4_ERR_ALIGN;
+  if (k > Q4_MAX_K) return Q4_ERR_UNSUPPORTED;
+  return Q4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int q4_layout_version(void) { return 1; }
+
+const char* q4_status_str(int status) {
+  switch (status) {
+    case Q4_OK: return "ok";
+    case Q4_ERR_NULL: return "null pointer";
+    case Q4_ERR_SHAPE: return "invalid shape or argument";
+    case Q4_ERR_ALIGN: return "misaligned pointer";
+    case Q4_ERR_UNSUPPORTED: return "unsupported size";
+    case Q4_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int q4_last_hip_error(void) { return g_last_hip_error; }
+
+q4_status q4_pack(const float* w, int64_t n, int64_t k, uint32_t* packed, uint16_t* scales,
+                  uint16_t* biases, void* stream) {
+  if (!w) return Q4_ERR_NULL;
+  q4_status s = check_matrix(packed, scales, biases, n, k);
+  if (s != Q4_OK) return s;
+  s = check_align_matrix(packed, scales, biases);
+  if (s != Q4_OK) return s;
+  if (!aligned(w, 16)) return Q4_ERR_ALIGN;
+  if (n == 0) return Q4_OK;
+  const int64_t ng = n * (k / 32);
+  hipLaunchKernelGGL(q4k::pack_kernel, dim3(grid_for_groups(ng)), dim3(256), 0, as_stream(stream), w,
+                     ng, packed, scales, biases);
+  return launch_status();
+}
+
+q4_status q4_unpack(const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+                    int64_t n, int64_t k, uint8_t* q_out, float* w_out, void* stream) {
+  q4_status s = check_matrix(packed, scales, biases, n, k);
+  if (s != Q4_OK) return s;
+  if (!q_out && !w_out) return Q4_ERR_NULL;
+  s = check_align_matrix(packed, scales, biases);
+  if (s != Q4_OK) return s;
+  if ((q_out && !aligned(q_out, 16)) || (w_out && !aligned(w_out, 16))) return Q4_ERR_ALIGN;
+  if (n == 0) return Q4_OK;
+  const int64_t ng = n * (k / 32);
+  hipLaunchKernelGGL(q4k::unpack_kernel, dim3(grid_for_groups(ng)), dim3(256), 0, as_stream(stream),
+                     packed, scales, biases, ng, q_out, w_out);
+  return launch_status();
+}
+
+q4_status q4_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                  const uint16_t* biases, int64_t n, int64_t k, void* y, q4_out_dtype y_dtype,
+                  void* stream) {
+  const q4_status s = check_product(x, 1, packed, scales, biases, n, k, y, y_dtype);
+  if (s != Q4_OK) return s;
+  if (n == 0) return Q4_OK;
+  return run_gemv(x, packed, scales, biases, n, k, y, y_dtype, as_stream(stream));
+}
+
+q4_status q4_gemm_small(const uint16_t* x, int64_t m, const uint32_t* packed,
+                        const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
+                        void* y, q4_out_dtype y_dtype, void* stream) {
+  const q4_status s = check_product(x, m, packed, scales, biases, n, k, y, y_dtype);
+  if (s != Q4_OK) return s;
+  if (n == 0) return Q4_OK;
+  return run_gemm_small(x, m, packed, scales, biases, n, k, y, y_dtype, as_stream(stream));
+}
+
+q4_status q4_multilinear_step(const uint16_t* x, int64_t m, const uint32_t* packed,
+                              const uint16_t* scales, const uint16_t* biases, int64_t num_steps,
+                              int64_t out, int64_t k, int64_t step, void* y,
+                              q4_out_dtype y_dtype, void* stream) {
+  if (!x || !y || !packed || !scales || !biases) return Q4_ERR_NULL;
+  if (num_steps <= 0 || out < 0 || step < 0 || step >= num_steps) return Q4_ERR_SHAPE;
+  if (out > 0 && num_steps > (INT32_MAX / 2) / out) return Q4_ERR_SHAPE;
+  const q4_status s = check_product(x, m, packed, scales, biases, out, k, y, y_dtype);
+  if (s != Q4_OK) return s;
+  if (out == 0) return Q4_OK;
+  const int64_t row0 = step * out;
+  return run_gemm_small(x, m, packed + row0 * (k / 8), scales + row0 * (k / 32),
+                        biases + row0 * (k / 32), out, k, y, y_dtype, as_stream(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,363 @@
+// Device code of libq4: gfx950 (CDNA4) kernels for the affine 4-bit group-32
+// quantized linear layer. Included by q4_api.hip only.
+//
+// Format (model card "personaplex-edge-q4", Release details table: affine Q4,
+// group size 32, BF16 activations): a group of 32 inputs is one 16-byte run of
+// four uint32 words, code of input 8j+t in bits [4t, 4t+4) of word j; one bf16
+// scale and one bf16 bias per group in two separate [n][k/32] arrays.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4k {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// Code unpacking. A byte holding c in 0..15 read as OCP e4m3 is exactly
+// c * 2^-9 (c < 8: subnormal c/8 * 2^-6; c >= 8: (1 + (c-8)/8) * 2^-6), so the
+// gfx950 scaled fp8->bf16 conversion with scale 2^9 yields the integer c as an
+// exact bf16. Masking the word with 0x0F0F0F0F puts codes 0,2,4,6 of the word
+// in bytes 0..3; shifting by 4 first gives codes 1,3,5,7.
+// Output pairs (low half first): (c0,c2) (c4,c6) (c1,c3) (c5,c7).
+__device__ __forceinline__ void word_to_bf16_pairs(uint32_t w, uint32_t& p02, uint32_t& p46,
+                                                   uint32_t& p13, uint32_t& p57) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+  p02 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, false));
+  p46 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, true));
+  p13 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, false));
+  p57 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, true));
+}
+
+// Eight bf16 activations x0..x7 (as loaded: four uint32 (x0,x1) (x2,x3)
+// (x4,x5) (x6,x7)) re-paired to match word_to_bf16_pairs.
+__device__ __forceinline__ void x_to_pairs(uint4 e, uint32_t& p02, uint32_t& p46, uint32_t& p13,
+                                           uint32_t& p57) {
+  p02 = (e.x & 0xFFFFu) | (e.y << 16);
+  p46 = (e.z & 0xFFFFu) | (e.w << 16);
+  p13 = (e.x >> 16) | (e.y & 0xFFFF0000u);
+  p57 = (e.z >> 16) | (e.w & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ float x_sum8(uint4 e) {
+  return ((bf16_to_f32(e.x & 0xFFFFu) + bf16_to_f32(e.x >> 16)) +
+          (bf16_to_f32(e.y & 0xFFFFu) + bf16_to_f32(e.y >> 16))) +
+         ((bf16_to_f32(e.z & 0xFFFFu) + bf16_to_f32(e.z >> 16)) +
+          (bf16_to_f32(e.w & 0xFFFFu) + bf16_to_f32(e.w >> 16)));
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// sum_{t<32} c_t * x_t for one group: 16 packed bf16 dot products, fp32 sum.
+__device__ __forceinline__ float group_dot(uint4 w, const uint32_t (&xp)[16]) {
+  float acc = 0.f;
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t q02, q46, q13, q57;
+    word_to_bf16_pairs(ws[j], q02, q46, q13, q57);
+    acc = dot2(q02, xp[4 * j + 0], acc);
+    acc = dot2(q46, xp[4 * j + 1], acc);
+    acc = dot2(q13, xp[4 * j + 2], acc);
+    acc = dot2(q57, xp[4 * j + 3], acc);
+  }
+  return acc;
+}
+
+template <bool OUT_F32>
+__device__ __forceinline__ void store_out(void* y, int64_t idx, float v) {
+  if constexpr (OUT_F32) {
+    static_cast<float*>(y)[idx] = v;
+  } else {
+    static_cast<uint16_t*>(y)[idx] = f32_to_bf16_rne(v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Quantize + pack: one thread per group of 32.
+__global__ void __launch_bounds__(256) pack_kernel(const float* __restrict__ w, int64_t n_groups,
+                                                    uint32_t* __restrict__ packed,
+                                                    uint16_t* __restrict__ scales,
+                                                    uint16_t* __restrict__ biases) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n_groups; idx += stride) {
+    const float4* src = reinterpret_cast<const float4*>(w + idx * 32);
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 t = src[i];
+      v[4 * i + 0] = t.x;
+      v[4 * i + 1] = t.y;
+      v[4 * i + 2] = t.z;
+      v[4 * i + 3] = t.w;
+    }
+    float mn = v[0], mx = v[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) {
+      if (v[i] < mn) mn = v[i];
+      if (v[i] > mx) mx = v[i];
+    }
+    const float scale = (mx - mn) / 15.0f;  // IEEE division (correctly rounded)
+    const uint16_t sb = f32_to_bf16_rne(scale);
+    const uint16_t bb = f32_to_bf16_rne(mn);
+    const float s = bf16_to_f32(sb);
+    const float b = bf16_to_f32(bb);
+    uint32_t words[4] = {0u, 0u, 0u, 0u};
+    if (s != 0.0f) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        float r = rintf((v[i] - b) / s);
+        r = fminf(fmaxf(r, 0.0f), 15.0f);
+        words[i >> 3] |= (uint32_t)r << (4 * (i & 7));
+      }
+    }
+    reinterpret_cast<uint4*>(packed)[idx] = make_uint4(words[0], words[1], words[2], words[3]);
+    scales[idx] = sb;
+    biases[idx] = bb;
+  }
+}
+
+// Unpack: one thread per group; codes as bytes and/or w_hat = s*q + b.
+__global__ void __launch_bounds__(256) unpack_kernel(const uint32_t* __restrict__ packed,
+                                                      const uint16_t* __restrict__ scales,
+                                                      const uint16_t* __restrict__ biases,
+                                                      int64_t n_groups, uint8_t* __restrict__ q_out,
+                                                      float* __restrict__ w_out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n_groups; idx += stride) {
+    const uint4 wd = reinterpret_cast<const uint4*>(packed)[idx];
+    const uint32_t ws[4] = {wd.x, wd.y, wd.z, wd.w};
+    if (q_out) {
+      uint32_t bytes[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = ws[j] & 0x0F0F0F0Fu;         // codes 0,2,4,6
+        const uint32_t hi = (ws[j] >> 4) & 0x0F0F0F0Fu;  // codes 1,3,5,7
+        // interleave to input order c0 c1 c2 c3 | c4 c5 c6 c7
+        bytes[2 * j] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+        bytes[2 * j + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(q_out + idx * 32);
+      dst[0] = make_uint4(bytes[0], bytes[1], bytes[2], bytes[3]);
+      dst[1] = make_uint4(bytes[4], bytes[5], bytes[6], bytes[7]);
+    }
+    if (w_out) {
+      const float s = bf16_to_f32(scales[idx]);
+      const float b = bf16_to_f32(biases[idx]);
+      float4* dst = reinterpret_cast<float4*>(w_out + idx * 32);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float4 t;
+        const uint32_t word = ws[i >> 1];
+        const int sh = (i & 1) * 16;
+        t.x = fmaf(s, (float)((word >> (sh + 0)) & 0xFu), b);
+        t.y = fmaf(s, (float)((word >> (sh + 4)) & 0xFu), b);
+        t.z = fmaf(s, (float)((word >> (sh + 8)) & 0xFu), b);
+        t.w = fmaf(s, (float)((word >> (sh + 12)) & 0xFu), b);
+        dst[i] = t;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// GEMV, one activation row.
+//
+// Mapping: a wave is split into 64/C row slots of C lanes; lane (slot, c) of
+// wave w owns group g = w*C + c of the input dimension for every row it
+// visits, so its 32 activations live in 16 registers (re-paired bf16) for the
+// whole kernel and the weight stream needs no shared memory. A block has
+// S = ceil(G/C) waves covering all groups; each load instruction of a wave
+// reads C consecutive 16-byte groups of one row per slot (C*16 contiguous
+// bytes). Each lane handles U rows per iteration (U independent loads in
+// flight), reduces each row's partial over its C lanes with butterfly
+// shuffles, and the S waves' partials are added in fixed order through LDS.
+template <int C, int U, bool OUT_F32>
+__global__ void __launch_bounds__(1024) gemv_kernel(const uint16_t* __restrict__ x,
+                                                     const uint32_t* __restrict__ packed,
+                                                     const uint16_t* __restrict__ scales,
+                                                     const uint16_t* __restrict__ biases, int n,
+                                                     int G, int rows_per_block,
+                                                     void* __restrict__ y) {
+  constexpr int RPI = 64 / C;   // row slots per wave
+  constexpr int ROWS = RPI * U; // rows per iteration
+  __shared__ float red[16][ROWS];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const int c = lane % C;
+  const int slot = lane / C;
+  const int g = wave * C + c;
+  const bool gv = g < G;
+
+  uint32_t xp[16];
+  float xsum = 0.f;
+  if (gv) {
+    const uint4* xs = reinterpret_cast<const uint4*>(x + (int64_t)g * 32);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 e = xs[j];
+      x_to_pairs(e, xp[4 * j + 0], xp[4 * j + 1], xp[4 * j + 2], xp[4 * j + 3]);
+      xsum += x_sum8(e);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) xp[j] = 0u;
+  }
+
+  const int row_begin = blockIdx.x * rows_per_block;
+  const int row_end = min(n, row_begin + rows_per_block);
+  const int64_t wpr = (int64_t)G * 4;  // words per row
+  for (int r0 = row_begin; r0 < row_end; r0 += ROWS) {
+    uint4 wv[U];
+    uint32_t sv[U], bv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = r0 + u * RPI + slot;
+      if (gv && row < row_end) {
+        wv[u] = *reinterpret_cast<const uint4*>(packed + (int64_t)row * wpr + 4 * g);
+        sv[u] = scales[(int64_t)row * G + g];
+        bv[u] = biases[(int64_t)row * G + g];
+      } else {
+        wv[u] = make_uint4(0u, 0u, 0u, 0u);
+        sv[u] = 0u;
+        bv[u] = 0u;
+      }
+    }
+    float part[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float acc = group_dot(wv[u], xp);
+      part[u] = fmaf(bf16_to_f32(sv[u]), acc, bf16_to_f32(bv[u]) * xsum);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int off = C / 2; off > 0; off >>= 1) part[u] += __shfl_xor(part[u], off, 64);
+    }
+    if (c == 0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) red[wave][u * RPI + slot] = part[u];
+    }
+    __syncthreads();
+    if (threadIdx.x < ROWS) {
+      const int rr = threadIdx.x;
+      float s = 0.f;
+      for (int w2 = 0; w2 < nwaves; ++w2) s += red[w2][rr];
+      const int row = r0 + rr;
+      if (row < row_end) store_out<OUT_F32>(y, row, s);
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Small GEMM, M in [2, 16] activation rows, on MFMA.
+//
+// One v_mfma_f32_16x16x32_bf16 covers exactly one group (32 inputs) for 16
+// activation rows (A operand, zero-padded past m) and 16 weight rows (B
+// operand = the 32 codes as exact bf16 integers). The group's scale and bias
+// are applied to the fp32 tile afterwards, D*s + b*X_g, where the group sums
+// X_g come from a second MFMA against a B of ones. Lane l of the MFMA holds
+// A/B k-block l/16 (8 inputs = one packed word) for row l%16 and receives the
+// outputs D[4*(l/16)+i][l%16], i < 4. The 8 inputs of a k-block use the same
+// re-pairing on both operands, so the contraction is unchanged.
+//
+// A block has S waves; wave w owns groups [w*GS, (w+1)*GS) and keeps its
+// activation tile in registers; the block walks T tiles of 16 weight rows and
+// the S waves' tiles are summed in fixed order through LDS.
+template <int GS, int T, bool OUT_F32>
+__global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restrict__ x, int m,
+                                                          const uint32_t* __restrict__ packed,
+                                                          const uint16_t* __restrict__ scales,
+                                                          const uint16_t* __restrict__ biases,
+                                                          int n, int G, void* __restrict__ y) {
+  extern __shared__ float red_dyn[];  // [nwaves][T][4][64]
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const int r16 = lane & 15;
+  const int kb = lane >> 4;
+  const int g0 = wave * GS;
+  const int gcount = max(0, min(G - g0, GS));
+  const int64_t K = (int64_t)G * 32;
+
+  u32x4_t a[GS];
+#pragma unroll
+  for (int i = 0; i < GS; ++i) {
+    a[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if (i < gcount && r16 < m) {
+      const uint4 e = *reinterpret_cast<const uint4*>(x + (int64_t)r16 * K + (int64_t)(g0 + i) * 32 + 8 * kb);
+      uint32_t p02, p46, p13, p57;
+      x_to_pairs(e, p02, p46, p13, p57);
+      a[i] = u32x4_t{p02, p46, p13, p57};
+    }
+  }
+  const u32x4_t ones = u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const f32x4_t zero = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = zero;
+
+  const int nbase = blockIdx.x * 16 * T;
+  const int64_t wpr = (int64_t)G * 4;
+#pragma unroll
+  for (int i = 0; i < GS; ++i) {
+    if (i < gcount) {
+      const int g = g0 + i;
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a[i]);
+      const f32x4_t xg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, ones), zero, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const int row = nbase + 16 * t + r16;
+        uint32_t wd = 0u, sb = 0u, bb = 0u;
+        if (row < n) {
+          wd = packed[(int64_t)row * wpr + 4 * g + kb];
+          sb = scales[(int64_t)row * G + g];
+          bb = biases[(int64_t)row * G + g];
+        }
+        uint32_t q02, q46, q13, q57;
+        word_to_bf16_pairs(wd, q02, q46, q13, q57);
+        const u32x4_t bq = u32x4_t{q02, q46, q13, q57};
+        const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bq), zero, 0, 0, 0);
+        const float s = bf16_to_f32(sb);
+        const float b = bf16_to_f32(bb);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[t][j] = fmaf(s, d[j], fmaf(b, xg[j], acc[t][j]));
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) red_dyn[((wave * T + t) * 4 + j) * 64 + lane] = acc[t][j];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < T * 256; idx += blockDim.x) {
+    float s = 0.f;
+    for (int w2 = 0; w2 < nwaves; ++w2) s += red_dyn[w2 * T * 256 + idx];
+    const int l = idx & 63;
+    const int j = (idx >> 6) & 3;
+    const int t = idx >> 8;
+    const int mi = 4 * (l >> 4) + j;
+    const int row = nbase + 16 * t + (l & 15);
+    if (mi < m && row < n) store_out<OUT_F32>(y, (int64_t)mi * n + row, s);
+  }
+}
+
+}  // namespace q4k

@@ -1,0 +1,136 @@
+/*
+ * q4.h — C ABI of the MI355X (gfx950) affine 4-bit group-32 quantized linear
+ * library (libq4.so).
+ *
+ * The operation: a weight matrix W [out = n][in = k] is stored quantized in
+ * groups of 32 consecutive input elements; each group has a bf16 scale s and
+ * a bf16 bias b, and each weight a 4-bit code q in 0..15, with
+ * w_hat = s*q + b. Activations are bf16. The product is y = x . W_hat^T
+ * ("personaplex-edge-q4" model card, introduction and Release details table:
+ * affine Q4, group size 32, BF16 activations, weights kept packed at
+ * inference; "NVIDIA PersonaPlex 7B on Apple Silicon", Depformer MultiLinear
+ * code figure: quantized product with transpose, scales and biases sliced by
+ * output rows).
+ *
+ * STORED LAYOUT, version 1 (q4_layout_version() == 1):
+ *   packed : uint32 [n][k/8], row-major. Word j of row r holds the codes of
+ *            inputs 8j..8j+7; the code of input 8j+t sits in bits [4t, 4t+4)
+ *            (low nibble first). One 16-byte run of 4 words is one group.
+ *   scales : uint16 [n][k/32], bf16 bit patterns, row-major.
+ *   biases : uint16 [n][k/32], bf16 bit patterns, row-major.
+ *   Stored bytes per weight: 1/2 + 2/32 + 2/32 = 5/8.
+ * A MultiLinear weight for S codebook steps is one such tensor with
+ * n = S*out rows; step s owns rows [s*out, (s+1)*out).
+ *
+ * CONVENTIONS FOR EVERY ENTRY POINT
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or retains them.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call is asynchronous on that stream and performs no host/device
+ *     synchronisation and no allocation, so it may be captured into a HIP
+ *     graph.
+ *   - Arguments are validated on the host before any HIP call; the first
+ *     failing check decides the status, and on any error nothing is launched.
+ *     Checks, in order: a required pointer is NULL -> Q4_ERR_NULL; a size is
+ *     out of range -> Q4_ERR_SHAPE; a pointer is misaligned -> Q4_ERR_ALIGN;
+ *     a valid size the kernels do not cover -> Q4_ERR_UNSUPPORTED.
+ *   - n == 0 is a valid empty call: nothing is launched and Q4_OK returned.
+ *   - k must be a positive multiple of 32.
+ *   - Alignment: `w` (fp32 input of q4_pack), `packed`, `x`, and the unpack
+ *     outputs must be 16-byte aligned; scales, biases and y need their natural
+ *     element alignment.
+ *   - A launch failure returns Q4_ERR_HIP; q4_last_hip_error() then gives the
+ *     hipError_t value (per calling thread).
+ *   - Non-finite weights or activations are outside the method's domain; they
+ *     are not checked on the device and give unspecified results.
+ *   - Accumulation is fp32; outputs are rounded once (round to nearest even)
+ *     when y is bf16. Results are deterministic: no atomics are used in any
+ *     reduction.
+ *   - No C++ exception crosses this interface. The library is thread-safe.
+ */
+#ifndef Q4_H
+#define Q4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4_GROUP 32
+#define Q4_MAX_M 16
+#define Q4_MAX_K 16384
+
+typedef enum q4_status {
+  Q4_OK = 0,
+  Q4_ERR_NULL = 1,
+  Q4_ERR_SHAPE = 2,
+  Q4_ERR_ALIGN = 3,
+  Q4_ERR_UNSUPPORTED = 4,
+  Q4_ERR_HIP = 5
+} q4_status;
+
+typedef enum q4_out_dtype { Q4_OUT_BF16 = 0, Q4_OUT_F32 = 1 } q4_out_dtype;
+
+/* Version of the stored layout described above. Returns 1. */
+int q4_layout_version(void);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char* q4_status_str(int status);
+
+/* hipError_t of the most recent Q4_ERR_HIP returned on the calling thread
+ * (0 if none). */
+int q4_last_hip_error(void);
+
+/* Quantize and pack (model card, Release details table: affine Q4, group 32).
+ * For each row and each group of 32 inputs: mn/mx = min/max of the group,
+ * scale = (mx - mn)/15 in fp32 (correctly rounded), stored scale s' and bias
+ * b' = the bf16 (nearest-even) roundings of scale and mn; each code is
+ * clamp(rint_half_even((w - b')/s'), 0, 15), or 0 for the whole group when
+ * s' == 0. min/max scan the group in index order with strict comparisons.
+ *   w      : fp32 [n][k] (input)
+ *   packed : uint32 [n][k/8], scales/biases: uint16 [n][k/32] (outputs)
+ * Bit-exact with the CPU oracle. */
+q4_status q4_pack(const float* w, int64_t n, int64_t k, uint32_t* packed, uint16_t* scales,
+                  uint16_t* biases, void* stream);
+
+/* Unpack: recover codes and/or dequantized weights w_hat = s'*q + b' (one
+ * rounding to fp32; the product s'*q is exact). Bit-exact with the oracle.
+ *   q_out : uint8 [n][k] or NULL;  w_out : fp32 [n][k] or NULL (at least one
+ *   must be non-NULL). */
+q4_status q4_unpack(const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+                    int64_t n, int64_t k, uint8_t* q_out, float* w_out, void* stream);
+
+/* Quantized matrix-vector product, one activation row (M = 1):
+ *   y[r] = sum_k w_hat[r][k] * x[k]   for r in [0, n)
+ * computed per group as s'*(sum q*x) + b'*(sum x) with fp32 accumulation.
+ *   x : bf16 [k] (uint16 bit patterns), y : [n] of y_dtype. */
+q4_status q4_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                  const uint16_t* biases, int64_t n, int64_t k, void* y, q4_out_dtype y_dtype,
+                  void* stream);
+
+/* Small quantized GEMM for M concurrent activation rows (1 <= m <= 16), all
+ * sharing one pass over the weights:
+ *   y[i][r] = sum_k w_hat[r][k] * x[i][k]
+ *   x : bf16 [m][k] row-major, y : [m][n] row-major of y_dtype.
+ * m == 1 is the same computation as q4_gemv. Supports k <= Q4_MAX_K. */
+q4_status q4_gemm_small(const uint16_t* x, int64_t m, const uint32_t* packed,
+                        const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
+                        void* y, q4_out_dtype y_dtype, void* stream);
+
+/* Depformer MultiLinear step ("NVIDIA PersonaPlex 7B on Apple Silicon",
+ * Depformer section, MultiLinear code figure): the weight holds num_steps
+ * blocks of `out` rows ([num_steps*out][k]); step `step` multiplies by rows
+ * [step*out, (step+1)*out) of packed, scales and biases together (a pointer
+ * offset, no copy), then the same product as q4_gemm_small.
+ *   x : bf16 [m][k], y : [m][out]. step must lie in [0, num_steps). */
+q4_status q4_multilinear_step(const uint16_t* x, int64_t m, const uint32_t* packed,
+                              const uint16_t* scales, const uint16_t* biases, int64_t num_steps,
+                              int64_t out, int64_t k, int64_t step, void* y,
+                              q4_out_dtype y_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4_H */

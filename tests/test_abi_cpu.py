@@ -1,0 +1,107 @@
+"""Host-side checks of the C ABI: the library loads, exports every function the
+header declares, and rejects invalid arguments before touching the GPU (every
+call here fails validation, so no HIP call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_group_quantized_amd as q4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:q4_status|int|const char\*)\s+(q4_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    assert names == sorted(q4.exported_symbols())
+    for want in ("q4_pack", "q4_unpack", "q4_gemv", "q4_gemm_small", "q4_multilinear_step"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(q4.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_layout_version_and_status_strings():
+    assert q4.q4_layout_version() == 1
+    assert q4.q4_status_str(0) == "ok"
+    assert q4.q4_status_str(q4.Q4_ERR_ALIGN) == "misaligned pointer"
+    assert q4.q4_status_str(99) == "unknown status"
+
+
+A16 = 0x10000   # a 16-byte aligned fake address: validation fails before any use
+ODD = 0x10001
+
+
+def _p(v):
+    return ctypes.c_void_p(v)
+
+
+@pytest.mark.parametrize("case,want", [
+    (dict(x=0), q4.Q4_ERR_NULL),
+    (dict(packed=0), q4.Q4_ERR_NULL),
+    (dict(scales=0), q4.Q4_ERR_NULL),
+    (dict(biases=0), q4.Q4_ERR_NULL),
+    (dict(y=0), q4.Q4_ERR_NULL),
+    (dict(k=0), q4.Q4_ERR_SHAPE),
+    (dict(k=48), q4.Q4_ERR_SHAPE),
+    (dict(n=-1), q4.Q4_ERR_SHAPE),
+    (dict(dtype=7), q4.Q4_ERR_SHAPE),
+    (dict(x=ODD), q4.Q4_ERR_ALIGN),
+    (dict(packed=A16 + 4), q4.Q4_ERR_ALIGN),
+    (dict(scales=ODD), q4.Q4_ERR_ALIGN),
+    (dict(y=ODD), q4.Q4_ERR_ALIGN),
+    (dict(k=32 * 1024), q4.Q4_ERR_UNSUPPORTED),
+])
+def test_gemv_validation(case, want):
+    a = dict(x=A16, packed=A16, scales=A16, biases=A16, n=16, k=64, y=A16, dtype=0)
+    a.update(case)
+    st = q4.load().q4_gemv(_p(a["x"]), _p(a["packed"]), _p(a["scales"]), _p(a["biases"]), a["n"], a["k"],
+                           _p(a["y"]), a["dtype"], None)
+    assert st == want
+
+
+@pytest.mark.parametrize("m,want", [(0, q4.Q4_ERR_SHAPE), (17, q4.Q4_ERR_SHAPE), (-3, q4.Q4_ERR_SHAPE)])
+def test_gemm_small_rejects_m(m, want):
+    st = q4.load().q4_gemm_small(_p(A16), m, _p(A16), _p(A16), _p(A16), 16, 64, _p(A16), 0, None)
+    assert st == want
+
+
+@pytest.mark.parametrize("steps,step,want", [
+    (16, 16, q4.Q4_ERR_SHAPE), (16, -1, q4.Q4_ERR_SHAPE), (0, 0, q4.Q4_ERR_SHAPE)])
+def test_multilinear_rejects_step(steps, step, want):
+    st = q4.load().q4_multilinear_step(_p(A16), 1, _p(A16), _p(A16), _p(A16), steps, 8, 64, step, _p(A16), 0,
+                                       None)
+    assert st == want
+
+
+def test_pack_and_unpack_validation():
+    lib = q4.load()
+    assert lib.q4_pack(None, 4, 64, _p(A16), _p(A16), _p(A16), None) == q4.Q4_ERR_NULL
+    assert lib.q4_pack(_p(ODD), 4, 64, _p(A16), _p(A16), _p(A16), None) == q4.Q4_ERR_ALIGN
+    assert lib.q4_pack(_p(A16), 4, 40, _p(A16), _p(A16), _p(A16), None) == q4.Q4_ERR_SHAPE
+    assert lib.q4_unpack(_p(A16), _p(A16), _p(A16), 4, 64, None, None, None) == q4.Q4_ERR_NULL
+    assert lib.q4_unpack(_p(A16), _p(A16), _p(A16), 4, 64, _p(ODD), None, None) == q4.Q4_ERR_ALIGN
+
+
+def test_empty_calls_are_noops():
+    lib = q4.load()
+    assert lib.q4_gemv(_p(A16), _p(A16), _p(A16), _p(A16), 0, 64, _p(A16), 0, None) == q4.Q4_OK
+    assert lib.q4_pack(_p(A16), 0, 64, _p(A16), _p(A16), _p(A16), None) == q4.Q4_OK
+    assert lib.q4_multilinear_step(_p(A16), 2, _p(A16), _p(A16), _p(A16), 16, 0, 64, 3, _p(A16), 1, None) == q4.Q4_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    w = torch.zeros(4, 64)
+    with pytest.raises(ValueError):
+        q4.q4_pack(w)

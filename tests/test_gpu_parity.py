@@ -1,0 +1,212 @@
+"""GPU parity: the HIP library against the CPU oracle on seeded inputs.
+
+Pack and unpack must be bit-exact; products must meet the floored relative
+tolerance (1e-2 for bf16 outputs, 2e-3 for fp32 outputs). Inputs to each
+product are the ORACLE's packed arrays, so product parity does not depend on
+the GPU quantizer; expected values come only from ``oracle``.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_group_quantized_amd as q4
+import oracle
+import workloads
+from helpers import (TOL_BF16, TOL_F32, bf16_bits_np, dev, out_np, packed_np, to_gpu_bf16_bits, to_gpu_f32,
+                     upload_quantized)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    q4.load()
+
+
+def _w(n, k, seed=0, item=0):
+    return workloads.weights(seed, 9, 0, item, n, k)
+
+
+def _x(m, k, seed=0, item=0):
+    return workloads.activations(seed, 9, 0, item, m, k)
+
+
+# shapes: (n, k) — several tiles plus ragged tails, and the pages' layer shapes
+SMALL_SHAPES = [(1, 32), (5, 64), (37, 96), (100, 160), (257, 256), (300, 1056), (1000, 2048), (129, 4096)]
+MODEL_SHAPES = [(4096, 4096), (11264, 4096), (4096, 11264), (1024, 1024), (2816, 1024), (1024, 2816)]
+
+
+# ------------------------------------------------------------------ pack / unpack
+
+@pytest.mark.parametrize("n,k", SMALL_SHAPES + MODEL_SHAPES)
+def test_pack_bit_exact(n, k):
+    w = _w(n, k, seed=n + k)
+    P, S, B = oracle.quantize(w)
+    gp, gs, gb = q4.q4_pack(to_gpu_f32(w))
+    torch.cuda.synchronize()
+    assert np.array_equal(packed_np(gp), P)
+    assert np.array_equal(bf16_bits_np(gs), S)
+    assert np.array_equal(bf16_bits_np(gb), B)
+
+
+def _edge_weights():
+    """Degenerate groups, exact-affine groups, exact ties of the code rounding,
+    signed zeros, huge and tiny magnitudes."""
+    r = np.random.default_rng(5)
+    rows = []
+    rows.append(np.full(64, 0.7, dtype=np.float32))                      # constant groups
+    z = np.zeros(64, dtype=np.float32); z[3] = -0.0; z[40] = 1e-40; rows.append(z)
+    a, s0 = -1.5, 0.25
+    codes = np.concatenate([np.arange(16), np.arange(16)[::-1], r.integers(0, 16, 32)])
+    codes[32] = 0; codes[33] = 15
+    rows.append((a + s0 * codes).astype(np.float32))                        # exact affine
+    t = np.zeros(64, dtype=np.float32)
+    t[0] = 0.0; t[1] = 15 * 0.125                                           # scale 0.125, bias 0
+    t[2:32] = (np.arange(30) % 15 + 0.5) * 0.125                            # exact half-way ties
+    t[32:] = (r.integers(-1000, 1000, 32) * 0.5).astype(np.float32)
+    rows.append(t)
+    rows.append((r.standard_normal(64) * 1e30).astype(np.float32))
+    rows.append((r.standard_normal(64) * 1e-30).astype(np.float32))
+    big = r.standard_normal(64).astype(np.float32); big[5] = 300.0; rows.append(big)
+    return np.stack(rows)
+
+
+def test_pack_edge_cases_bit_exact():
+    w = _edge_weights()
+    P, S, B = oracle.quantize(w)
+    gp, gs, gb = q4.q4_pack(to_gpu_f32(w))
+    torch.cuda.synchronize()
+    assert np.array_equal(packed_np(gp), P)
+    assert np.array_equal(bf16_bits_np(gs), S)
+    assert np.array_equal(bf16_bits_np(gb), B)
+
+
+@pytest.mark.parametrize("n,k", [(37, 96), (4096, 4096), (7, 64)])
+def test_unpack_bit_exact(n, k):
+    w = _edge_weights() if n == 7 else _w(n, k, seed=3)
+    P, S, B = oracle.quantize(w)
+    q_ref, w_ref = oracle.unpack(P, S, B, w.shape[1])
+    q, wh = q4.q4_unpack(*upload_quantized(P, S, B))
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(wh.cpu().numpy().view(np.uint32), w_ref.view(np.uint32))
+
+
+# ------------------------------------------------------------------ products
+
+def _check(y_gpu: torch.Tensor, y_ref: np.ndarray, out_dtype):
+    got = out_np(y_gpu).reshape(y_ref.shape)
+    err = oracle.floored_rel_err(got, y_ref)
+    tol = TOL_F32 if out_dtype == torch.float32 else TOL_BF16
+    assert err <= tol, f"floored rel err {err:.3e} > {tol}"
+    if out_dtype == torch.bfloat16:
+        # a bf16 output is at most one rounding away from the exact value plus
+        # the fp32 accumulation error
+        assert err <= 2 ** -8 + TOL_F32
+    return err
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("n,k", SMALL_SHAPES + MODEL_SHAPES)
+def test_gemv_matches_oracle(n, k, out_dtype):
+    w = _w(n, k, seed=7 * n + k)
+    P, S, B = oracle.quantize(w)
+    x = _x(1, k, seed=k)
+    y_ref = oracle.matmul(x, P, S, B, k)
+    y = q4.q4_gemv(to_gpu_bf16_bits(x[0]), *upload_quantized(P, S, B), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    _check(y, y_ref[0], out_dtype)
+
+
+@pytest.mark.parametrize("m", [2, 3, 4, 7, 16])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("n,k", [(37, 96), (300, 1056), (1000, 2048)] + MODEL_SHAPES)
+def test_gemm_small_matches_oracle(n, k, m, out_dtype):
+    w = _w(n, k, seed=n + 3 * k)
+    P, S, B = oracle.quantize(w)
+    x = _x(m, k, seed=m + k)
+    y_ref = oracle.matmul(x, P, S, B, k)
+    y = q4.q4_gemm_small(to_gpu_bf16_bits(x), *upload_quantized(P, S, B), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    _check(y, y_ref, out_dtype)
+
+
+@pytest.mark.parametrize("m", [1, 2, 16])
+def test_one_hot_input_gives_exact_dequantized_column(m):
+    """x = e_j in one activation row: y = w_hat[:, j] exactly in fp32 (pins the
+    code, group, scale and bias indexing through the kernels)."""
+    n, k = 160, 4096
+    w = _w(n, k, seed=99)
+    P, S, B = oracle.quantize(w)
+    _, w_hat = oracle.unpack(P, S, B, k)
+    gP, gS, gB = upload_quantized(P, S, B)
+    for j in (0, 1, 7, 8, 31, 32, 33, 1000, 4095):
+        x = np.zeros((m, k), dtype=np.uint16)
+        x[m - 1, j] = 0x3F80
+        gx = to_gpu_bf16_bits(x)
+        y = q4.q4_gemm_small(gx, gP, gS, gB, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+        assert np.array_equal(got[m - 1], w_hat[:, j]), j
+        if m > 1:
+            assert not got[: m - 1].any()
+
+
+def test_gemm_rows_equal_gemv():
+    """Each row of the small GEMM agrees with a GEMV of that row within tolerance."""
+    n, k, m = 4096, 4096, 4
+    w = _w(n, k, seed=17)
+    P, S, B = oracle.quantize(w)
+    gP, gS, gB = upload_quantized(P, S, B)
+    x = _x(m, k, seed=5)
+    Y = q4.q4_gemm_small(to_gpu_bf16_bits(x), gP, gS, gB, out_dtype=torch.float32)
+    for i in range(m):
+        y = q4.q4_gemv(to_gpu_bf16_bits(x[i]), gP, gS, gB, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert oracle.floored_rel_err(out_np(Y[i]), out_np(y)) <= 2 * TOL_F32
+
+
+def test_deterministic():
+    n, k = 11264, 4096
+    w = _w(n, k, seed=23)
+    P, S, B = oracle.quantize(w)
+    gP, gS, gB = upload_quantized(P, S, B)
+    x = to_gpu_bf16_bits(_x(1, k, seed=1)[0])
+    X = to_gpu_bf16_bits(_x(16, k, seed=2))
+    a = q4.q4_gemv(x, gP, gS, gB, out_dtype=torch.float32)
+    b = q4.q4_gemv(x, gP, gS, gB, out_dtype=torch.float32)
+    c = q4.q4_gemm_small(X, gP, gS, gB, out_dtype=torch.float32)
+    d = q4.q4_gemm_small(X, gP, gS, gB, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(c.view(torch.int32), d.view(torch.int32))
+
+
+# ------------------------------------------------------------------ MultiLinear
+
+@pytest.mark.parametrize("m", [1, 4])
+@pytest.mark.parametrize("out,k", [(1024, 1024), (2816, 1024), (1024, 2816), (40, 96)])
+def test_multilinear_steps(out, k, m):
+    steps = workloads.DEP_STEPS if out * k <= 2816 * 1024 else 4
+    W = np.concatenate([_w(out, k, seed=200 + s, item=s) for s in range(steps)])
+    P, S, B = oracle.quantize(W)
+    gP, gS, gB = upload_quantized(P, S, B)
+    x = _x(m, k, seed=out)
+    gx = to_gpu_bf16_bits(x)
+    for s in range(steps):
+        y_ref = oracle.multilinear_step(x, P, S, B, steps, out, k, s)
+        y = q4.q4_multilinear_step(gx, gP, gS, gB, steps, s, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        _check(y, y_ref, torch.float32)
+        # the step is the product on that row block: bit-identical to a direct call
+        blk = slice(s * out, (s + 1) * out)
+        direct = q4.q4_gemm_small(gx, gP[blk].contiguous(), gS[blk].contiguous(), gB[blk].contiguous(),
+                                  out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), direct.view(torch.int32))
+
+
+def test_multilinear_out_of_range_step_raises():
+    P, S, B = oracle.quantize(_w(64, 64))
+    gP, gS, gB = upload_quantized(P, S, B)
+    x = to_gpu_bf16_bits(_x(1, 64))
+    with pytest.raises(q4.Q4Error):
+        q4.q4_multilinear_step(x, gP, gS, gB, 4, 4)
