@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark: affine Q4 group-32 weight stream of the 32-layer temporal step, M=1.
+
+One "step" is one pass of the whole hot path over one synthetic frame: the 32
+temporal layers' 224 quantized GEMVs (per layer q, k, v, o 4096x4096; gate, up
+11264x4096; down 4096x11264), run as 128 ordered stages (q/k/v share the
+attention input, gate/up share the FFN input). Weights and activations are
+seeded synthetic stand-ins for the model's (``workloads``), packed on the GPU
+before timing; the timed region starts with everything resident in HBM.
+
+Prints ONE JSON line (rank 0, N=1):
+  value        packed-weight GB/s over the step (algorithmic bytes: 4-bit codes
+               + bf16 scale + bf16 bias per 32 weights = 0.625 B/weight)
+  ms_per_step  wall time per step (HIP events on the launch stream)
+  roofline     the dominant kernel (the persistent chain kernel: one launch
+               per step) against the 8 TB/s HBM peak
+  cpu_baseline the CPU oracle on a bounded sample of the same workload
+
+Executors: ``--mode chain`` (default: one persistent launch per step) or
+``--mode launches`` (224 q4_gemv launches per step, replayed as a HIP graph).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "packed-weight GB/s (% HBM peak) + us per 32-layer Q4 temporal step, M=1"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def packed_bytes(n: int, k: int) -> int:
+    """Stored bytes of an [n, k] Q4 matrix: k/2 code bytes + 2 bf16 per 32 per row."""
+    return n * k // 2 + 2 * 2 * n * (k // 32)
+
+
+def make_temporal_chain(seed: int = 0, layers: int = workloads.TEMPORAL_LAYERS,
+                        config: int = workloads.CFG_STEP, out_dtype=None, device=None):
+    """Build the temporal-step chain on the GPU: weights drawn on the host (seeded),
+    quantized and packed by q4_pack on the GPU; activations drawn per layer and stage."""
+    import torch
+
+    import bit_group_quantized_amd as q4
+    from bit_group_quantized_amd.step import Chain, Q4Matrix, Stage
+
+    device = device or torch.device("cuda:0")
+    out_dtype = out_dtype or torch.bfloat16
+    lin = workloads.temporal_layer()
+    stages = []
+    t0 = time.time()
+    for layer in range(layers):
+        ws = workloads.weights_many([(seed, config, layer, li.item, li.n, li.k) for li in lin])
+        mats = []
+        for w in ws:
+            wt = torch.from_numpy(w).to(device)
+            mats.append(Q4Matrix(*q4.q4_pack(wt)))
+            del wt
+        del ws
+        by_stage = {}
+        for li, m in zip(lin, mats):
+            by_stage.setdefault(li.stage, []).append((li, m))
+        for st in sorted(by_stage):
+            k = by_stage[st][0][0].k
+            x = workloads.activations(seed, config, layer, 100 + st, 1, k)[0]
+            xt = torch.from_numpy(x.view(np.int16)).to(device).view(torch.bfloat16)
+            stages.append(Stage(xt, [m for _, m in by_stage[st]]))
+        if layer % 8 == 7:
+            log(f"[bench] built {layer + 1}/{layers} layers ({time.time() - t0:.1f}s)")
+    torch.cuda.synchronize()
+    return Chain(stages, out_dtype)
+
+
+def cpu_baseline(seed: int, budget_s: float):
+    """The oracle (plain C, OpenMP over rows) on whole temporal layers until the
+    time budget is spent; reported as packed-weight GB/s and us per 32-layer step."""
+    import oracle
+
+    lin = workloads.temporal_layer()
+    elapsed, bytes_done, layers = 0.0, 0, 0
+    while elapsed < budget_s and layers < workloads.TEMPORAL_LAYERS:
+        ws = workloads.weights_many([(seed, workloads.CFG_STEP, layers, li.item, li.n, li.k) for li in lin])
+        qs = [oracle.quantize(w) for w in ws]      # not timed: offline conversion
+        del ws
+        xs = {st: workloads.activations(seed, workloads.CFG_STEP, layers, 100 + st, 1, k)
+              for st, k in {(li.stage, li.k) for li in lin}}
+        t0 = time.perf_counter()
+        for li, (P, S, B) in zip(lin, qs):
+            oracle.matmul(xs[li.stage], P, S, B, li.k)
+        elapsed += time.perf_counter() - t0
+        bytes_done += sum(packed_bytes(li.n, li.k) for li in lin)
+        layers += 1
+    gbs = bytes_done / elapsed / 1e9
+    us_step = elapsed / layers * workloads.TEMPORAL_LAYERS * 1e6
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{layers} of 32 temporal layers (7 GEMVs each, M=1), oracle product timed "
+                      f"({elapsed:.1f} s); quantization not timed",
+            "us_per_step": round(us_step, 1)}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--mode", choices=("chain", "launches"), default="chain")
+    ap.add_argument("--layers", type=int, default=workloads.TEMPORAL_LAYERS,
+                    help="temporal layers (32 = the full step; fewer only for profiling runs)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the step "
+              "shards as described in the design notes but no multi-GPU path is built.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import bit_group_quantized_amd as q4
+
+    q4.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    chain = make_temporal_chain(args.seed, args.layers, device=dev)
+    wbytes = chain.weight_bytes()
+    launches_per_step = 1 if args.mode == "chain" else chain.num_matrices()
+
+    if args.mode == "chain":
+        chain.prepare_chain()
+        run = chain.run_chain
+    else:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            chain.run_launches()  # warm the kernels outside capture
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            chain.run_launches()
+        run = g.replay
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    if args.mode == "chain" and chain.chain_status() != 0:
+        print(f"chain executor reported status {chain.chain_status()}", file=sys.stderr)
+        return 1
+
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        run()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]  # ms
+    total_ms = ev[0].elapsed_time(ev[-1])
+    if args.mode == "chain" and chain.chain_status() != 0:
+        print(f"chain executor reported status {chain.chain_status()}", file=sys.stderr)
+        return 1
+
+    ms_per_step = total_ms / args.steps
+    gbs = wbytes / (ms_per_step * 1e-3) / 1e9
+    # dominant kernel: in chain mode the single launch per step; its duration is
+    # the per-step event interval on the launch stream
+    kernel_ms = ms_per_step / launches_per_step
+    achieved = (wbytes / launches_per_step) / (kernel_ms * 1e-3) / 1e9
+    full = args.layers == workloads.TEMPORAL_LAYERS
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "us_per_step": round(ms_per_step * 1e3, 1),
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "temporal_step_m1" if full else f"temporal_{args.layers}_layers_m1",
+                   "layers": args.layers, "hidden": workloads.HIDDEN, "ffn": workloads.FFN, "m": 1,
+                   "group": 32, "weights_per_step": sum(li.n * li.k for li in workloads.temporal_layer()) * args.layers,
+                   "packed_bytes_per_step": wbytes, "executor": args.mode,
+                   "launches_per_step": launches_per_step, "stages_per_step": len(chain.stages)},
+        "step_ms_p10_p50_p90": [round(float(np.percentile(per, q)), 4) for q in (10, 50, 90)],
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "chain_kernel" if args.mode == "chain" else "gemv_kernel",
+                     "bytes_per_launch": wbytes // launches_per_step},
+    }
+    if not args.no_cpu:
+        log("[bench] cpu baseline ...")
+        result["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

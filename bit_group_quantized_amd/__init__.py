@@ -35,8 +35,19 @@ _lib = None
 
 _EXPORTS = (
     "q4_layout_version", "q4_status_str", "q4_last_hip_error", "q4_pack", "q4_unpack", "q4_gemv",
-    "q4_gemm_small", "q4_multilinear_step",
+    "q4_gemm_small", "q4_multilinear_step", "q4_chain_plan_bytes", "q4_chain_encode", "q4_chain_run",
 )
+CHAIN_WORKSPACE_BYTES = 131328
+
+
+class _ChainMatrix(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("n", ctypes.c_int64)]
+
+
+class _ChainStage(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("k", ctypes.c_int64), ("first_matrix", ctypes.c_int32),
+                ("num_matrices", ctypes.c_int32)]
 
 
 class Q4Error(RuntimeError):
@@ -67,7 +78,12 @@ def load():
     lib.q4_gemv.argtypes = [P, P, P, P, I, I, P, V, P]
     lib.q4_gemm_small.argtypes = [P, I, P, P, P, I, I, P, V, P]
     lib.q4_multilinear_step.argtypes = [P, I, P, P, P, I, I, I, I, P, V, P]
-    for f in ("q4_pack", "q4_unpack", "q4_gemv", "q4_gemm_small", "q4_multilinear_step"):
+    lib.q4_chain_plan_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.q4_chain_plan_bytes.restype = ctypes.c_int64
+    lib.q4_chain_encode.argtypes = [P, ctypes.c_int32, P, ctypes.c_int32, V, P, I]
+    lib.q4_chain_run.argtypes = [P, V, P, P]
+    for f in ("q4_pack", "q4_unpack", "q4_gemv", "q4_gemm_small", "q4_multilinear_step", "q4_chain_encode",
+              "q4_chain_run"):
         getattr(lib, f).restype = V
     _lib = lib
     return lib
@@ -226,3 +242,69 @@ def q4_multilinear_step(x: torch.Tensor, packed: torch.Tensor, scales: torch.Ten
            load().q4_multilinear_step(_ptr(x2), m, _ptr(packed), _ptr(scales), _ptr(biases), num_steps, out_rows,
                                       k, int(step), _ptr(out), code, _ptr_stream(x)))
     return out
+
+
+# ---------------------------------------------------------------- chain executor
+
+class ChainPlan:
+    """An encoded chain: the device copy of the plan plus what it references
+    (kept alive here so the device pointers in the plan stay valid)."""
+
+    def __init__(self, device_plan: torch.Tensor, out_dtype: torch.dtype, keep: list):
+        self.device_plan = device_plan
+        self.out_dtype = out_dtype
+        self._keep = keep
+
+
+def q4_chain_workspace_bytes() -> int:
+    return CHAIN_WORKSPACE_BYTES
+
+
+def q4_chain_build(stages, out_dtype: Optional[torch.dtype] = None) -> ChainPlan:
+    """Encode stages (objects with .x, .mats (each .packed/.scales/.biases) and
+    .outs) and upload the plan. All outputs must share one dtype."""
+    lib = load()
+    mats = []
+    descs = []
+    keep = []
+    for st in stages:
+        _need(st.x, "x", torch.bfloat16)
+        first = len(mats)
+        k = st.x.numel()
+        for m, y in zip(st.mats, st.outs):
+            n, km = _check_matrix(m.packed, m.scales, m.biases)
+            if km != k:
+                raise ValueError("every matrix of a stage must have the stage's k")
+            if out_dtype is None:
+                out_dtype = y.dtype
+            _need(y, "y", out_dtype)
+            if y.numel() != n:
+                raise ValueError("output must hold n elements")
+            mats.append(_ChainMatrix(m.packed.data_ptr(), m.scales.data_ptr(), m.biases.data_ptr(), y.data_ptr(), n))
+            keep += [m.packed, m.scales, m.biases, y]
+        descs.append(_ChainStage(st.x.data_ptr(), k, first, len(mats) - first))
+        keep.append(st.x)
+    code = _out_code(out_dtype)
+    ns, nm = len(descs), len(mats)
+    nbytes = int(lib.q4_chain_plan_bytes(ns, nm))
+    if nbytes <= 0:
+        raise ValueError("empty chain")
+    host = (ctypes.c_uint8 * nbytes)()
+    sarr = (_ChainStage * ns)(*descs)
+    marr = (_ChainMatrix * nm)(*mats)
+    _check("q4_chain_encode", lib.q4_chain_encode(ctypes.byref(sarr), ns, ctypes.byref(marr), nm, code,
+                                                  ctypes.byref(host), nbytes))
+    dev = stages[0].x.device
+    host_t = torch.frombuffer(bytearray(host), dtype=torch.uint8)
+    plan = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    plan.copy_(host_t)
+    return ChainPlan(plan, out_dtype, keep)
+
+
+def q4_chain_run(plan: ChainPlan, workspace: torch.Tensor) -> None:
+    """Run the chain on the current stream. workspace: zero-filled device tensor
+    of at least CHAIN_WORKSPACE_BYTES (its word 0 reports barrier timeouts)."""
+    if workspace.numel() * workspace.element_size() < CHAIN_WORKSPACE_BYTES or not workspace.is_cuda:
+        raise ValueError("workspace must be a device tensor of >= %d bytes" % CHAIN_WORKSPACE_BYTES)
+    _check("q4_chain_run", load().q4_chain_run(_ptr(plan.device_plan), _out_code(plan.out_dtype), _ptr(workspace),
+                                               _ptr_stream(workspace)))

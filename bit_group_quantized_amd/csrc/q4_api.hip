@@ -5,6 +5,7 @@
 
 #include "q4.h"
 #include "q4_kernels.h"
+#include "q4_chain.h"
 
 namespace {
 
@@ -246,6 +247,179 @@ q4_status q4_multilinear_step(const uint16_t* x, int64_t m, const uint32_t* pack
   const int64_t row0 = step * out;
   return run_gemm_small(x, m, packed + row0 * (k / 8), scales + row0 * (k / 32),
                         biases + row0 * (k / 32), out, k, y, y_dtype, as_stream(stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Chain executor host side.
+namespace {
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return kNumCU;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return kNumCU;
+  return cus;
+}
+
+constexpr size_t kChainLdsBytes = sizeof(q4k::ChainLds);
+
+// Per device: raise the dynamic-LDS limit of the chain kernels once and check
+// that one 1024-thread block fits per compute unit.
+bool chain_ready_on_device() {
+  static int state[64] = {0};  // 0 unknown, 1 ready, -1 not possible
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  if (state[dev] == 0) {
+    bool ok = hipFuncSetAttribute(reinterpret_cast<const void*>(&q4k::chain_kernel<true>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kChainLdsBytes) == hipSuccess &&
+              hipFuncSetAttribute(reinterpret_cast<const void*>(&q4k::chain_kernel<false>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kChainLdsBytes) == hipSuccess;
+    int a = 0, b = 0;
+    ok = ok &&
+         hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, q4k::chain_kernel<true>, 64 * q4k::kChainWaves,
+                                                      kChainLdsBytes) == hipSuccess &&
+         hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, q4k::chain_kernel<false>, 64 * q4k::kChainWaves,
+                                                      kChainLdsBytes) == hipSuccess &&
+         a >= 1 && b >= 1;
+    (void)hipGetLastError();
+    state[dev] = ok ? 1 : -1;
+  }
+  return state[dev] == 1;
+}
+
+// Lanes per row for a stage of G groups: among 64/32/16/8 lanes, the split
+// with the fewest idle lanes whose chunk count CH = ceil(G/C) fits one round
+// and whose rows per unit (64/C) divide every matrix's row count.
+bool plan_stage(int64_t G, int* c_log2, int* CH, const q4_chain_matrix* mats = nullptr, int32_t nm = 0) {
+  int best_c = 0;
+  int64_t best_waste = -1, best_ch = 0;
+  const int cs[4] = {64, 32, 16, 8};
+  for (int i = 0; i < 4; ++i) {
+    const int64_t ch = ceil_div(G, cs[i]);
+    if (ch > q4k::kSlots || ch * cs[i] > q4k::kMaxGroups) continue;
+    bool whole_units = true;
+    for (int32_t j = 0; j < nm; ++j) whole_units = whole_units && mats[j].n % (64 / cs[i]) == 0;
+    if (!whole_units) continue;
+    const int64_t waste = ch * cs[i] - G;
+    if (best_waste < 0 || waste < best_waste) {
+      best_waste = waste;
+      best_c = cs[i];
+      best_ch = ch;
+    }
+  }
+  if (best_waste < 0) return false;
+  int lg = 0;
+  while ((1 << lg) < best_c) ++lg;
+  *c_log2 = lg;
+  *CH = static_cast<int>(best_ch);
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t q4_chain_plan_bytes(int32_t num_stages, int32_t num_matrices) {
+  if (num_stages <= 0 || num_matrices <= 0) return -1;
+  return static_cast<int64_t>(sizeof(q4k::ChainHeader)) +
+         static_cast<int64_t>(num_stages) * sizeof(q4k::ChainStageDesc) +
+         static_cast<int64_t>(num_matrices) * sizeof(q4k::ChainMatDesc);
+}
+
+q4_status q4_chain_encode(const q4_chain_stage* stages, int32_t num_stages,
+                          const q4_chain_matrix* matrices, int32_t num_matrices,
+                          q4_out_dtype y_dtype, void* host_plan, int64_t plan_bytes) {
+  if (!stages || !matrices || !host_plan) return Q4_ERR_NULL;
+  if (num_stages <= 0 || num_matrices <= 0) return Q4_ERR_SHAPE;
+  if (y_dtype != Q4_OUT_BF16 && y_dtype != Q4_OUT_F32) return Q4_ERR_SHAPE;
+  const int64_t need = q4_chain_plan_bytes(num_stages, num_matrices);
+  if (plan_bytes < need) return Q4_ERR_SHAPE;
+  int32_t next_matrix = 0;
+  for (int32_t s = 0; s < num_stages; ++s) {
+    const q4_chain_stage& st = stages[s];
+    if (st.num_matrices <= 0 || st.first_matrix != next_matrix ||
+        st.first_matrix + (int64_t)st.num_matrices > num_matrices)
+      return Q4_ERR_SHAPE;
+    next_matrix += st.num_matrices;
+    int64_t rows = 0;
+    for (int32_t i = 0; i < st.num_matrices; ++i) {
+      const q4_chain_matrix& m = matrices[st.first_matrix + i];
+      const q4_status c = check_product(st.x, 1, m.packed, m.scales, m.biases, m.n, st.k, m.y, y_dtype);
+      if (c != Q4_OK) return c;
+      if (m.n >= (1 << 22)) return Q4_ERR_UNSUPPORTED;
+      rows += m.n;
+    }
+    int lg, ch;
+    if (st.num_matrices > q4k::kMaxMatsPerStage || rows > (1 << 24) || num_matrices > 1024 ||
+        !plan_stage(st.k / 32, &lg, &ch, matrices + st.first_matrix, st.num_matrices))
+      return Q4_ERR_UNSUPPORTED;
+  }
+  if (next_matrix != num_matrices) return Q4_ERR_SHAPE;
+  if (need > q4k::kPlanLdsBytes) return Q4_ERR_UNSUPPORTED;
+
+  unsigned char* out = static_cast<unsigned char*>(host_plan);
+  auto* hdr = reinterpret_cast<q4k::ChainHeader*>(out);
+  *hdr = q4k::ChainHeader{};
+  hdr->magic = q4k::kChainMagic;
+  hdr->num_stages = num_stages;
+  hdr->num_mats = num_matrices;
+  hdr->out_f32 = y_dtype == Q4_OUT_F32 ? 1 : 0;
+  hdr->plan_bytes = static_cast<int32_t>(need);
+  auto* sd = reinterpret_cast<q4k::ChainStageDesc*>(hdr + 1);
+  int32_t max_rows = 0;
+  for (int32_t s = 0; s < num_stages; ++s) {
+    const q4_chain_stage& st = stages[s];
+    q4k::ChainStageDesc d{};
+    d.x = st.x;
+    d.G = static_cast<int32_t>(st.k / 32);
+    plan_stage(d.G, &d.c_log2, &d.CH, matrices + st.first_matrix, st.num_matrices);
+    d.UPR = q4k::kSlots / d.CH;
+    d.num_mats = st.num_matrices;
+    d.mat_begin = st.first_matrix;
+    int32_t off = 0;
+    for (int32_t i = 0; i < st.num_matrices; ++i) {
+      d.row_off[i] = off;
+      off += static_cast<int32_t>(matrices[st.first_matrix + i].n);
+    }
+    for (int32_t i = st.num_matrices; i <= q4k::kMaxMatsPerStage; ++i) d.row_off[i] = off;
+    d.nrows = off;
+    if (off > max_rows) max_rows = off;
+    sd[s] = d;
+  }
+  hdr->max_rows = max_rows;
+  auto* md = reinterpret_cast<q4k::ChainMatDesc*>(sd + num_stages);
+  for (int32_t i = 0; i < num_matrices; ++i) {
+    q4k::ChainMatDesc d{};
+    d.packed = matrices[i].packed;
+    d.scales = matrices[i].scales;
+    d.biases = matrices[i].biases;
+    d.y = matrices[i].y;
+    d.n = static_cast<int32_t>(matrices[i].n);
+    md[i] = d;
+  }
+  return Q4_OK;
+}
+
+q4_status q4_chain_run(const void* device_plan, q4_out_dtype y_dtype, void* workspace, void* stream) {
+  if (!device_plan || !workspace) return Q4_ERR_NULL;
+  if (y_dtype != Q4_OUT_BF16 && y_dtype != Q4_OUT_F32) return Q4_ERR_SHAPE;
+  if (!aligned(device_plan, 64) || !aligned(workspace, 128)) return Q4_ERR_ALIGN;
+  // One block of 16 waves per compute unit, all resident at once (the stage
+  // barrier needs that); bounded waits turn a violation into a status.
+  const int cus = device_cu_count();
+  if (cus > q4k::kChainMaxBlocks) return Q4_ERR_UNSUPPORTED;
+  if (!chain_ready_on_device()) return Q4_ERR_UNSUPPORTED;
+  const dim3 grid(cus), block(64 * q4k::kChainWaves);
+  const q4k::ChainHeader* plan = static_cast<const q4k::ChainHeader*>(device_plan);
+  uint32_t* ws = static_cast<uint32_t*>(workspace);
+  if (y_dtype == Q4_OUT_F32)
+    hipLaunchKernelGGL(q4k::chain_kernel<true>, grid, block, kChainLdsBytes, as_stream(stream), plan, ws);
+  else
+    hipLaunchKernelGGL(q4k::chain_kernel<false>, grid, block, kChainLdsBytes, as_stream(stream), plan, ws);
+  return launch_status();
 }
 
 }  // extern "C"

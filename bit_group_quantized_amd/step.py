@@ -1,0 +1,88 @@
+"""Step driver: runs an ordered chain of quantized GEMV stages on one GPU.
+
+A stage is one activation vector x (bf16 [k]) multiplied by one or more packed
+Q4 matrices that share it (q, k, v share the attention input; gate and up share
+the FFN input). Stages run in order: a stage may consume the previous stage's
+outputs, so no stage starts its products before the previous one has finished.
+This is the per-frame temporal step's weight stream (blog translation,
+pipeline diagram: 32 layers of width 4096) and the Depformer's per-codebook
+step (same page, MultiLinear figure).
+
+Two executors:
+* ``launches``: one q4_gemv call per matrix, in order, on the current stream
+  (capturable into a HIP graph with ``torch.cuda.graph``);
+* ``chain``: the whole chain in one persistent launch (q4_chain_run).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import torch
+
+from . import q4_chain_build, q4_chain_run, q4_chain_workspace_bytes, q4_gemv
+
+
+@dataclass
+class Q4Matrix:
+    packed: torch.Tensor   # int32 [n, k/8]
+    scales: torch.Tensor   # bf16 [n, k/32]
+    biases: torch.Tensor   # bf16 [n, k/32]
+
+    @property
+    def n(self) -> int:
+        return self.packed.shape[0]
+
+    @property
+    def k(self) -> int:
+        return self.packed.shape[1] * 8
+
+    def nbytes(self) -> int:
+        return self.packed.numel() * 4 + self.scales.numel() * 2 + self.biases.numel() * 2
+
+
+@dataclass
+class Stage:
+    x: torch.Tensor                     # bf16 [k]
+    mats: List[Q4Matrix]
+    outs: List[torch.Tensor] = field(default_factory=list)
+
+
+class Chain:
+    def __init__(self, stages: List[Stage], out_dtype: torch.dtype = torch.bfloat16):
+        self.stages = stages
+        self.out_dtype = out_dtype
+        dev = stages[0].x.device
+        for st in stages:
+            if not st.outs:
+                st.outs = [torch.empty((m.n,), dtype=out_dtype, device=dev) for m in st.mats]
+        self._plan = None
+        self._ws: Optional[torch.Tensor] = None
+        self.device = dev
+
+    def weight_bytes(self) -> int:
+        return sum(m.nbytes() for st in self.stages for m in st.mats)
+
+    def num_matrices(self) -> int:
+        return sum(len(st.mats) for st in self.stages)
+
+    # ---- executor 1: one launch per matrix
+    def run_launches(self) -> None:
+        for st in self.stages:
+            for m, y in zip(st.mats, st.outs):
+                q4_gemv(st.x, m.packed, m.scales, m.biases, out=y)
+
+    # ---- executor 2: one persistent launch for the whole chain
+    def prepare_chain(self) -> None:
+        if self._plan is None:
+            self._plan = q4_chain_build(self.stages, self.out_dtype)
+            self._ws = torch.zeros(q4_chain_workspace_bytes() // 4, dtype=torch.int32, device=self.device)
+
+    def run_chain(self) -> None:
+        self.prepare_chain()
+        q4_chain_run(self._plan, self._ws)
+
+    def chain_status(self) -> int:
+        """Device-side status word of the persistent executor (0 = ok)."""
+        self.prepare_chain()
+        return int(self._ws[0].item())

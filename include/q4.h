@@ -129,6 +129,73 @@ q4_status q4_multilinear_step(const uint16_t* x, int64_t m, const uint32_t* pack
                               int64_t out, int64_t k, int64_t step, void* y,
                               q4_out_dtype y_dtype, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Chain executor: an ordered list of GEMV stages run by ONE persistent launch.
+ *
+ * The per-frame temporal step is such a chain ("NVIDIA PersonaPlex 7B on Apple
+ * Silicon", pipeline diagram: 32 layers of width 4096; the layers reuse KV
+ * cache, RoPE, SwiGLU and RMSNorm parts per the GeekNews summary's audio
+ * pipeline section). Read as a standard decoder layer, the attention input
+ * feeds q, k, v, the attention output feeds o, the FFN input feeds gate and
+ * up, and the gated product feeds down. A stage is one activation vector x
+ * (bf16 [k]) multiplied by one or more matrices that share it:
+ *   y_i[r] = sum_k w_hat_i[r][k] * x[k]   for every matrix i of the stage.
+ * Stages run in order: no product of stage s+1 starts before every output of
+ * stage s is written and visible, so a stage's x may be (the bf16 output of)
+ * an earlier stage. Weight bytes of later stages are fetched ahead of that
+ * point (weights never depend on activations).
+ *
+ * Use: describe the chain with host arrays, q4_chain_encode() it into a host
+ * buffer of q4_chain_plan_bytes(), copy that buffer to device memory
+ * (64-byte aligned), then call q4_chain_run() as often as needed. The plan
+ * holds the device pointers given at encode time; it stays valid while those
+ * buffers live. Each stage's k must satisfy the q4_gemv limits; every
+ * stage needs >= 1 matrix, all of that stage's k.
+ *
+ * Workspace: Q4_CHAIN_WORKSPACE_BYTES of device memory, 128-byte aligned,
+ * zero-filled once by the caller before its first use; the executor leaves it
+ * ready for the next call. Calls sharing one workspace must not overlap in
+ * time (use one workspace per stream). Word 0 of the workspace is a status:
+ * 0 = ok, 1 = a stage barrier timed out (the launch ended early, outputs
+ * undefined), 2 = the plan buffer is not a valid plan. A nonzero status stays
+ * set until the caller clears the workspace again.
+ */
+#define Q4_CHAIN_WORKSPACE_BYTES 131328 /* 256 + 128 per block, up to 1024 blocks */
+
+typedef struct q4_chain_matrix {
+  const uint32_t* packed; /* [n][k/8]  */
+  const uint16_t* scales; /* [n][k/32] */
+  const uint16_t* biases; /* [n][k/32] */
+  void* y;                /* [n] of the chain's output dtype */
+  int64_t n;
+} q4_chain_matrix;
+
+typedef struct q4_chain_stage {
+  const uint16_t* x;      /* bf16 [k], 16-byte aligned */
+  int64_t k;
+  int32_t first_matrix;   /* index into the matrix array */
+  int32_t num_matrices;
+} q4_chain_stage;
+
+/* Bytes of the plan buffer for a chain of this size (< 0 on invalid counts). */
+int64_t q4_chain_plan_bytes(int32_t num_stages, int32_t num_matrices);
+
+/* Validate the chain (same pointer/shape/alignment rules as q4_gemv for every
+ * matrix) and write the plan into host_plan (plan_bytes long). No HIP call. */
+q4_status q4_chain_encode(const q4_chain_stage* stages, int32_t num_stages,
+                          const q4_chain_matrix* matrices, int32_t num_matrices,
+                          q4_out_dtype y_dtype, void* host_plan, int64_t plan_bytes);
+
+/* Run an encoded chain (device copy of the plan) on `stream`: one launch of one
+ * 1024-thread block per compute unit, all resident at once (the stage
+ * barrier needs that; Q4_ERR_UNSUPPORTED if the kernel cannot fit one block
+ * per compute unit or the device has more than 1024 of them). y_dtype must
+ * match the dtype the plan was encoded with. Nothing else should occupy the
+ * device's compute units during the call: a block that cannot start makes
+ * the others' bounded waits expire (status 1) instead of hanging. */
+q4_status q4_chain_run(const void* device_plan, q4_out_dtype y_dtype, void* workspace,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

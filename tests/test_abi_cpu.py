@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "q4.h")
 
 def header_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:q4_status|int|const char\*)\s+(q4_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:q4_status|int64_t|int|const char\*)\s+(q4_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_boundary():
@@ -105,3 +105,42 @@ def test_binding_refuses_cpu_tensors():
     w = torch.zeros(4, 64)
     with pytest.raises(ValueError):
         q4.q4_pack(w)
+
+
+def _chain(n_stages=2, k=64, n=16, x=A16, y=A16, packed=A16):
+    stages = (q4._ChainStage * n_stages)(*[q4._ChainStage(x, k, i, 1) for i in range(n_stages)])
+    mats = (q4._ChainMatrix * n_stages)(*[q4._ChainMatrix(packed, A16, A16, y, n) for _ in range(n_stages)])
+    return stages, mats
+
+
+def test_chain_encode_validation_and_layout():
+    lib = q4.load()
+    assert lib.q4_chain_plan_bytes(0, 1) < 0
+    nb = lib.q4_chain_plan_bytes(2, 2)
+    assert nb == 64 + 2 * 64 + 2 * 48
+    buf = (ctypes.c_uint8 * nb)()
+    stages, mats = _chain()
+    assert lib.q4_chain_encode(ctypes.byref(stages), 2, ctypes.byref(mats), 2, 0, ctypes.byref(buf), nb) == q4.Q4_OK
+    hdr = bytes(buf[:16])
+    assert int.from_bytes(hdr[0:4], "little") == 0x48433451
+    assert int.from_bytes(hdr[4:8], "little") == 2
+    # too small a buffer, bad dtype, misaligned x, k not a multiple of 32, stage coverage errors
+    assert lib.q4_chain_encode(ctypes.byref(stages), 2, ctypes.byref(mats), 2, 0, ctypes.byref(buf), nb - 1) == q4.Q4_ERR_SHAPE
+    assert lib.q4_chain_encode(ctypes.byref(stages), 2, ctypes.byref(mats), 2, 5, ctypes.byref(buf), nb) == q4.Q4_ERR_SHAPE
+    s2, m2 = _chain(x=ODD)
+    assert lib.q4_chain_encode(ctypes.byref(s2), 2, ctypes.byref(m2), 2, 0, ctypes.byref(buf), nb) == q4.Q4_ERR_ALIGN
+    s3, m3 = _chain(k=40)
+    assert lib.q4_chain_encode(ctypes.byref(s3), 2, ctypes.byref(m3), 2, 0, ctypes.byref(buf), nb) == q4.Q4_ERR_SHAPE
+    s4, m4 = _chain()
+    s4[1].first_matrix = 0
+    assert lib.q4_chain_encode(ctypes.byref(s4), 2, ctypes.byref(m4), 2, 0, ctypes.byref(buf), nb) == q4.Q4_ERR_SHAPE
+    s5, m5 = _chain(packed=0)
+    assert lib.q4_chain_encode(ctypes.byref(s5), 2, ctypes.byref(m5), 2, 0, ctypes.byref(buf), nb) == q4.Q4_ERR_NULL
+
+
+def test_chain_run_validation():
+    lib = q4.load()
+    assert lib.q4_chain_run(None, 0, _p(A16), None) == q4.Q4_ERR_NULL
+    assert lib.q4_chain_run(_p(A16), 0, _p(A16 + 64), None) == q4.Q4_ERR_ALIGN
+    assert lib.q4_chain_run(_p(A16 + 16), 0, _p(A16), None) == q4.Q4_ERR_ALIGN
+    assert lib.q4_chain_run(_p(A16), 3, _p(A16), None) == q4.Q4_ERR_SHAPE
