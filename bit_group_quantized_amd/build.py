@@ -7,7 +7,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "q4_api.hip")
-DEPS = [SRC, os.path.join(HERE, "csrc", "q4_kernels.h"), os.path.join(ROOT, "include", "q4.h")]
+DEPS = [SRC, os.path.join(HERE, "csrc", "q4_kernels.h"), os.path.join(HERE, "csrc", "q4_chain.h"),
+        os.path.join(ROOT, "include", "q4.h")]
 LIB = os.path.join(HERE, "libq4.so")
 
 HIPCC_FLAGS = [

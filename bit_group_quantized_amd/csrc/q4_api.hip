@@ -350,6 +350,8 @@ q4_status q4_chain_encode(const q4_chain_stage* stages, int32_t num_stages,
       const q4_status c = check_product(st.x, 1, m.packed, m.scales, m.biases, m.n, st.k, m.y, y_dtype);
       if (c != Q4_OK) return c;
       if (m.n >= (1 << 22)) return Q4_ERR_UNSUPPORTED;
+      // scales/biases are read as aligned 32-bit words
+      if ((st.k / 32) % 2 != 0 || !aligned(m.scales, 4) || !aligned(m.biases, 4)) return Q4_ERR_UNSUPPORTED;
       rows += m.n;
     }
     int lg, ch;

@@ -199,8 +199,9 @@ __device__ __forceinline__ void cursor_advance(Cursor& c, const ChainStageDesc* 
 // (C*CH > G) the lanes past G read group 0 of their own row instead. Their
 // activations are zero, so the weights they read do not count.
 struct LaneOffsets {
-  uint32_t lw, lw_last;  // packed
-  uint32_t ls, ls_last;  // scales / biases
+  uint32_t lw, lw_last;    // packed
+  uint32_t ls, ls_last;    // scales / biases: byte offset of the aligned word holding the lane's bf16
+  uint32_t sel, sel_last;  // which half of that word (byte selector for bf16_half_to_f32)
 };
 
 __device__ __forceinline__ LaneOffsets lane_offsets(const StageView& v) {
@@ -213,8 +214,12 @@ __device__ __forceinline__ LaneOffsets lane_offsets(const StageView& v) {
   LaneOffsets o;
   o.lw = grp * 16u;
   o.lw_last = grp_last * 16u;
-  o.ls = grp * 2u;
-  o.ls_last = grp_last * 2u;
+  // G is even and the arrays are 4-byte aligned, so a group's parity decides
+  // the half of its 32-bit word
+  o.ls = (grp & ~1u) * 2u;
+  o.ls_last = (grp_last & ~1u) * 2u;
+  o.sel = (grp & 1u) ? kSelHiHalf : kSelLoHalf;
+  o.sel_last = (grp_last & 1u) ? kSelHiHalf : kSelLoHalf;
   return o;
 }
 
@@ -253,8 +258,8 @@ __device__ __forceinline__ void round_issue(const Cursor& cu, const ChainMatDesc
       const int64_t gbase = row_g + (last ? 0 : ch * v.C);
       const u32x4_t t = gload_off<u32x4_t>(pk + gbase * 16, last ? lo.lw_last : lo.lw);
       buf.w[i] = make_uint4(t.x, t.y, t.z, t.w);
-      buf.s[i] = gload_off<uint16_t>(sc + gbase * 2, last ? lo.ls_last : lo.ls);
-      buf.b[i] = gload_off<uint16_t>(bi + gbase * 2, last ? lo.ls_last : lo.ls);
+      buf.s[i] = gload_off<uint32_t>(sc + gbase * 2, last ? lo.ls_last : lo.ls);
+      buf.b[i] = gload_off<uint32_t>(bi + gbase * 2, last ? lo.ls_last : lo.ls);
     }
   }
 }
@@ -272,8 +277,8 @@ __device__ __forceinline__ float dpp_sum(float v, int C) {
 }
 
 template <int CH>
-__device__ __forceinline__ void round_compute(const Cursor& cu, int gw, int wct, const RoundBuf& buf, ChainLds& L,
-                                              int cw) {
+__device__ __forceinline__ void round_compute(const Cursor& cu, const LaneOffsets& lo, int gw, int wct,
+                                              const RoundBuf& buf, ChainLds& L, int cw) {
   constexpr int UPR = kSlots / CH;
   const StageView& v = cu.v;
   if (gw + cu.r * UPR * wct >= cu.nunits) return;  // no rows for this wave in this round
@@ -300,7 +305,9 @@ __device__ __forceinline__ void round_compute(const Cursor& cu, int gw, int wct,
         xp[8] = a2.x; xp[9] = a2.y; xp[10] = a2.z; xp[11] = a2.w;
         xp[12] = a3.x; xp[13] = a3.y; xp[14] = a3.z; xp[15] = a3.w;
         const float xsum = __uint_as_float(xg[16]);
-        acc = fmaf(bf16_to_f32(buf.s[i]), group_dot(buf.w[i], xp), fmaf(bf16_to_f32(buf.b[i]), xsum, acc));
+        const uint32_t sel = ch == CH - 1 ? lo.sel_last : lo.sel;
+        acc = fmaf(bf16_half_to_f32(buf.s[i], sel), group_dot(buf.w[i], xp),
+                   fmaf(bf16_half_to_f32(buf.b[i], sel), xsum, acc));
       }
       const float tot = dpp_sum(acc, v.C);
       if (c == v.C - 1) {
@@ -325,15 +332,15 @@ __device__ __forceinline__ void dispatch_issue(const Cursor& cu, const ChainMatD
   }
 }
 
-__device__ __forceinline__ void dispatch_compute(const Cursor& cu, int gw, int wct, const RoundBuf& b, ChainLds& L,
-                                                 int cw) {
+__device__ __forceinline__ void dispatch_compute(const Cursor& cu, const LaneOffsets& lo, int gw, int wct,
+                                                 const RoundBuf& b, ChainLds& L, int cw) {
   switch (cu.v.CH) {
-    case 1: round_compute<1>(cu, gw, wct, b, L, cw); break;
-    case 2: round_compute<2>(cu, gw, wct, b, L, cw); break;
-    case 3: round_compute<3>(cu, gw, wct, b, L, cw); break;
-    case 4: round_compute<4>(cu, gw, wct, b, L, cw); break;
-    case 5: round_compute<5>(cu, gw, wct, b, L, cw); break;
-    default: round_compute<6>(cu, gw, wct, b, L, cw); break;
+    case 1: round_compute<1>(cu, lo, gw, wct, b, L, cw); break;
+    case 2: round_compute<2>(cu, lo, gw, wct, b, L, cw); break;
+    case 3: round_compute<3>(cu, lo, gw, wct, b, L, cw); break;
+    case 4: round_compute<4>(cu, lo, gw, wct, b, L, cw); break;
+    case 5: round_compute<5>(cu, lo, gw, wct, b, L, cw); break;
+    default: round_compute<6>(cu, lo, gw, wct, b, L, cw); break;
   }
 }
 
@@ -498,12 +505,13 @@ __global__ void __launch_bounds__(768) chain_kernel(const ChainHeader* __restric
     }
   }
   __syncthreads();  // S2 of stage 0
+  LaneOffsets clo = lane_offsets(cc.v);  // offsets of the stage being computed
   bool running = true;
   while (running) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       RoundBuf& b = k == 0 ? bufA : bufB;
-      dispatch_compute(cc, gw, wct, b, L, cw);
+      dispatch_compute(cc, clo, gw, wct, b, L, cw);
       const bool stage_end = cursor_stage_end(cc);
       if (stage_end) __syncthreads();  // S1: hand the stage's records to the service wave
       // refill this buffer two rounds ahead (after S1 at a stage end, so a
@@ -519,6 +527,7 @@ __global__ void __launch_bounds__(768) chain_kernel(const ChainHeader* __restric
         if (L.ok == 0) { running = false; break; }
       }
       cursor_advance(cc, stages, mats, num_stages, wct);
+      if (stage_end) clo = lane_offsets(cc.v);
     }
   }
 }

@@ -80,6 +80,25 @@ __device__ __forceinline__ float group_dot(uint4 w, const uint32_t (&xp)[16]) {
   return acc;
 }
 
+// bf16 bit pattern -> fp32, taken from either half of a 32-bit word: the
+// selector keeps bytes (lo) or (hi) of the word as the upper half and zeroes
+// the lower half. Scales and biases are fetched as the aligned 32-bit word
+// holding the wanted bf16: on gfx950 whole-word loads stream at full rate
+// while 2-byte loads do not.
+constexpr uint32_t kSelLoHalf = 0x01000C0Cu;
+constexpr uint32_t kSelHiHalf = 0x03020C0Cu;
+__device__ __forceinline__ float bf16_half_to_f32(uint32_t word, uint32_t sel) {
+  return __uint_as_float(__builtin_amdgcn_perm(0u, word, sel));
+}
+
+// Load the bf16 at p (2-byte aligned) through its aligned 32-bit word; returns
+// the value as fp32.
+__device__ __forceinline__ float load_bf16_word(const uint16_t* p) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(a & ~(uintptr_t)3);
+  return bf16_half_to_f32(w, (a & 2) ? kSelHiHalf : kSelLoHalf);
+}
+
 template <bool OUT_F32>
 __device__ __forceinline__ void store_out(void* y, int64_t idx, float v) {
   if constexpr (OUT_F32) {
@@ -226,25 +245,25 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const uint16_t* __restrict__
   const int64_t wpr = (int64_t)G * 4;  // words per row
   for (int r0 = row_begin; r0 < row_end; r0 += ROWS) {
     uint4 wv[U];
-    uint32_t sv[U], bv[U];
+    float sv[U], bv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int row = r0 + u * RPI + slot;
       if (gv && row < row_end) {
         wv[u] = *reinterpret_cast<const uint4*>(packed + (int64_t)row * wpr + 4 * g);
-        sv[u] = scales[(int64_t)row * G + g];
-        bv[u] = biases[(int64_t)row * G + g];
+        sv[u] = load_bf16_word(scales + (int64_t)row * G + g);
+        bv[u] = load_bf16_word(biases + (int64_t)row * G + g);
       } else {
         wv[u] = make_uint4(0u, 0u, 0u, 0u);
-        sv[u] = 0u;
-        bv[u] = 0u;
+        sv[u] = 0.f;
+        bv[u] = 0.f;
       }
     }
     float part[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const float acc = group_dot(wv[u], xp);
-      part[u] = fmaf(bf16_to_f32(sv[u]), acc, bf16_to_f32(bv[u]) * xsum);
+      part[u] = fmaf(sv[u], acc, bv[u] * xsum);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {

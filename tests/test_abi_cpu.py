@@ -134,6 +134,8 @@ def test_chain_encode_validation_and_layout():
     s4, m4 = _chain()
     s4[1].first_matrix = 0
     assert lib.q4_chain_encode(ctypes.byref(s4), 2, ctypes.byref(m4), 2, 0, ctypes.byref(buf), nb) == q4.Q4_ERR_SHAPE
+    s6, m6 = _chain(k=96)  # odd number of groups: scales are read as 32-bit words
+    assert lib.q4_chain_encode(ctypes.byref(s6), 2, ctypes.byref(m6), 2, 0, ctypes.byref(buf), nb) == q4.Q4_ERR_UNSUPPORTED
     s5, m5 = _chain(packed=0)
     assert lib.q4_chain_encode(ctypes.byref(s5), 2, ctypes.byref(m5), 2, 0, ctypes.byref(buf), nb) == q4.Q4_ERR_NULL
 

@@ -35,7 +35,7 @@ def test_independent_stages(out_dtype):
         (1024, [1024, 37]),
         (4096, [11264, 11264]),
         (2816, [1024]),
-        (96, [300]),
+        (64, [300]),
     ]
     stages, refs = [], []
     item = 0
