@@ -36,6 +36,20 @@ import numpy as np  # noqa: E402
 import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+
+# HBM traffic of one chain_kernel launch over the full step, from two rocprofv3
+# --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch),
+# each scaled by what the same counter reads for a plain 1 GiB copy
+# (``--calibrate-copy 1024``: FETCH_SIZE reads 524301.5 KiB for 1 GiB fetched,
+# WRITE_SIZE 1048576.0 KiB for 1 GiB written). Valid only for the kernel sources
+# whose hash is recorded: any change to them reports traffic as null until the
+# counters are taken again (profiles/chain_kernel_temporal_step_m1_pmc.md).
+CHAIN_TRAFFIC = {
+    "sources_sha256_16": "88b8a8147c955759",
+    "fetch_kib": 2028810.2, "fetch_scale": 1048576.0 / 524301.5,
+    "write_kib": 44024.0, "write_scale": 1048576.0 / 1048576.0,
+}
+KERNEL_SOURCES = ("q4_chain.h", "q4_kernels.h", "q4_api.hip")
 METRIC = "packed-weight GB/s (% HBM peak) + us per 32-layer Q4 temporal step, M=1"
 
 
@@ -46,6 +60,25 @@ def log(*a):
 def packed_bytes(n: int, k: int) -> int:
     """Stored bytes of an [n, k] Q4 matrix: k/2 code bytes + 2 bf16 per 32 per row."""
     return n * k // 2 + 2 * 2 * n * (k // 32)
+
+
+def kernel_sources_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bit_group_quantized_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def chain_traffic_bytes(full_step: bool):
+    """Measured HBM bytes per chain launch, or None when the counters do not
+    belong to this kernel build or this workload."""
+    t = CHAIN_TRAFFIC
+    if not full_step or kernel_sources_hash() != t["sources_sha256_16"]:
+        return None
+    return int(round(1024 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"])))
 
 
 def make_temporal_chain(seed: int = 0, layers: int = workloads.TEMPORAL_LAYERS,
@@ -84,30 +117,38 @@ def make_temporal_chain(seed: int = 0, layers: int = workloads.TEMPORAL_LAYERS,
     return Chain(stages, out_dtype)
 
 
-def cpu_baseline(seed: int, budget_s: float):
-    """The oracle (plain C, OpenMP over rows) on whole temporal layers until the
-    time budget is spent; reported as packed-weight GB/s and us per 32-layer step."""
+def cpu_baseline(seed: int, budget_s: float, sample_layers: int = 2):
+    """The oracle (plain C, OpenMP over rows) on a bounded sample of the step: the
+    first ``sample_layers`` temporal layers (7 GEMVs each, M=1), quantized once
+    (not timed), then their products run pass after pass until the time budget is
+    spent. Reported as packed-weight GB/s and the implied us per 32-layer step."""
     import oracle
 
     lin = workloads.temporal_layer()
-    elapsed, bytes_done, layers = 0.0, 0, 0
-    while elapsed < budget_s and layers < workloads.TEMPORAL_LAYERS:
-        ws = workloads.weights_many([(seed, workloads.CFG_STEP, layers, li.item, li.n, li.k) for li in lin])
-        qs = [oracle.quantize(w) for w in ws]      # not timed: offline conversion
+    layers = []
+    for layer in range(sample_layers):
+        ws = workloads.weights_many([(seed, workloads.CFG_STEP, layer, li.item, li.n, li.k) for li in lin])
+        qs = [oracle.quantize(w) for w in ws]
         del ws
-        xs = {st: workloads.activations(seed, workloads.CFG_STEP, layers, 100 + st, 1, k)
+        xs = {st: workloads.activations(seed, workloads.CFG_STEP, layer, 100 + st, 1, k)
               for st, k in {(li.stage, li.k) for li in lin}}
+        layers.append((qs, xs))
+    layer_bytes = sum(packed_bytes(li.n, li.k) for li in lin)
+    elapsed, bytes_done, passes = 0.0, 0, 0
+    while elapsed < budget_s:
         t0 = time.perf_counter()
-        for li, (P, S, B) in zip(lin, qs):
-            oracle.matmul(xs[li.stage], P, S, B, li.k)
+        for qs, xs in layers:
+            for li, (P, S, B) in zip(lin, qs):
+                oracle.matmul(xs[li.stage], P, S, B, li.k)
         elapsed += time.perf_counter() - t0
-        bytes_done += sum(packed_bytes(li.n, li.k) for li in lin)
-        layers += 1
+        bytes_done += layer_bytes * len(layers)
+        passes += 1
     gbs = bytes_done / elapsed / 1e9
-    us_step = elapsed / layers * workloads.TEMPORAL_LAYERS * 1e6
+    us_step = elapsed / (passes * len(layers)) * workloads.TEMPORAL_LAYERS * 1e6
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"{layers} of 32 temporal layers (7 GEMVs each, M=1), oracle product timed "
-                      f"({elapsed:.1f} s); quantization not timed",
+            "sample": f"temporal layers 0..{sample_layers - 1} of 32 (7 GEMVs each, M=1, "
+                      f"{layer_bytes * len(layers) / 1e6:.0f} MB packed), {passes} passes, oracle product "
+                      f"timed ({elapsed:.1f} s); quantization not timed",
             "us_per_step": round(us_step, 1)}
 
 
@@ -122,6 +163,10 @@ def main(argv=None) -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the step, run 5 plain device copies of MIB MiB (int32 "
+                         "bitwise_not, MIB MiB read + MIB MiB written each) so that HBM byte "
+                         "counters can be scaled against a kernel of known traffic")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -138,6 +183,16 @@ def main(argv=None) -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.randint(-2**31, 2**31 - 1, (n,), dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": 4 * n, "calibrate_copy_bytes_written": 4 * n,
+                          "dispatches": 5}), flush=True)
+        return 0
     chain = make_temporal_chain(args.seed, args.layers, device=dev)
     wbytes = chain.weight_bytes()
     launches_per_step = 1 if args.mode == "chain" else chain.num_matrices()
@@ -207,7 +262,9 @@ def main(argv=None) -> int:
                    "launches_per_step": launches_per_step, "stages_per_step": len(chain.stages)},
         "step_ms_p10_p50_p90": [round(float(np.percentile(per, q)), 4) for q in (10, 50, 90)],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": chain_traffic_bytes(full) if args.mode == "chain" else None,
+                     "traffic_unit": "bytes per launch",
                      "kernel": "chain_kernel" if args.mode == "chain" else "gemv_kernel",
                      "bytes_per_launch": wbytes // launches_per_step},
     }
