@@ -264,10 +264,18 @@ int device_cu_count() {
   return cus;
 }
 
+// Number of XCDs (chiplets with their own L2) of the current device.
+uint32_t device_xcc_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || n <= 0) return 1;
+  return static_cast<uint32_t>(n);
+}
+
 constexpr size_t kChainLdsBytes = sizeof(q4k::ChainLds);
 
 // Per device: raise the dynamic-LDS limit of the chain kernels once and check
-// that one 1024-thread block fits per compute unit.
+// that one block of the chain kernel fits per compute unit.
 bool chain_ready_on_device() {
   static int state[64] = {0};  // 0 unknown, 1 ready, -1 not possible
   int dev = 0;
@@ -291,15 +299,16 @@ bool chain_ready_on_device() {
 }
 
 // Lanes per row for a stage of G groups: among 64/32/16/8 lanes, the split
-// with the fewest idle lanes whose chunk count CH = ceil(G/C) fits one round
-// and whose rows per unit (64/C) divide every matrix's row count.
+// with the fewest idle lanes (ties: more lanes per row) whose padded width
+// fits the activation buffer and whose rows per unit (64/lanes) divide every
+// matrix's row count.
 bool plan_stage(int64_t G, int* c_log2, int* CH, const q4_chain_matrix* mats = nullptr, int32_t nm = 0) {
   int best_c = 0;
   int64_t best_waste = -1, best_ch = 0;
   const int cs[4] = {64, 32, 16, 8};
   for (int i = 0; i < 4; ++i) {
     const int64_t ch = ceil_div(G, cs[i]);
-    if (ch > q4k::kSlots || ch * cs[i] > q4k::kMaxGroups) continue;
+    if (ch > q4k::kChainMaxCH || ch * cs[i] > q4k::kChainMaxGroups) continue;
     bool whole_units = true;
     for (int32_t j = 0; j < nm; ++j) whole_units = whole_units && mats[j].n % (64 / cs[i]) == 0;
     if (!whole_units) continue;
@@ -316,6 +325,11 @@ bool plan_stage(int64_t G, int* c_log2, int* CH, const q4_chain_matrix* mats = n
   *c_log2 = lg;
   *CH = static_cast<int>(best_ch);
   return true;
+}
+
+bool ranges_overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + static_cast<uintptr_t>(bbytes) && b0 < a0 + static_cast<uintptr_t>(abytes);
 }
 
 }  // namespace
@@ -337,6 +351,7 @@ q4_status q4_chain_encode(const q4_chain_stage* stages, int32_t num_stages,
   if (y_dtype != Q4_OUT_BF16 && y_dtype != Q4_OUT_F32) return Q4_ERR_SHAPE;
   const int64_t need = q4_chain_plan_bytes(num_stages, num_matrices);
   if (plan_bytes < need) return Q4_ERR_SHAPE;
+  const int64_t ybytes = y_dtype == Q4_OUT_F32 ? 4 : 2;
   int32_t next_matrix = 0;
   for (int32_t s = 0; s < num_stages; ++s) {
     const q4_chain_stage& st = stages[s];
@@ -344,23 +359,22 @@ q4_status q4_chain_encode(const q4_chain_stage* stages, int32_t num_stages,
         st.first_matrix + (int64_t)st.num_matrices > num_matrices)
       return Q4_ERR_SHAPE;
     next_matrix += st.num_matrices;
-    int64_t rows = 0;
     for (int32_t i = 0; i < st.num_matrices; ++i) {
       const q4_chain_matrix& m = matrices[st.first_matrix + i];
       const q4_status c = check_product(st.x, 1, m.packed, m.scales, m.biases, m.n, st.k, m.y, y_dtype);
       if (c != Q4_OK) return c;
       if (m.n >= (1 << 22)) return Q4_ERR_UNSUPPORTED;
-      // scales/biases are read as aligned 32-bit words
-      if ((st.k / 32) % 2 != 0 || !aligned(m.scales, 4) || !aligned(m.biases, 4)) return Q4_ERR_UNSUPPORTED;
-      rows += m.n;
+      // scales/biases are read in 16-byte pieces of 8 groups
+      if ((st.k / 32) % 8 != 0 || !aligned(m.scales, 16) || !aligned(m.biases, 16)) return Q4_ERR_UNSUPPORTED;
+      // a stage may not write its own input
+      if (ranges_overlap(st.x, 2 * st.k, m.y, ybytes * m.n)) return Q4_ERR_UNSUPPORTED;
     }
     int lg, ch;
-    if (st.num_matrices > q4k::kMaxMatsPerStage || rows > (1 << 24) || num_matrices > 1024 ||
+    if (st.num_matrices > q4k::kMaxMatsPerStage || num_matrices > 4096 ||
         !plan_stage(st.k / 32, &lg, &ch, matrices + st.first_matrix, st.num_matrices))
       return Q4_ERR_UNSUPPORTED;
   }
   if (next_matrix != num_matrices) return Q4_ERR_SHAPE;
-  if (need > q4k::kPlanLdsBytes) return Q4_ERR_UNSUPPORTED;
 
   unsigned char* out = static_cast<unsigned char*>(host_plan);
   auto* hdr = reinterpret_cast<q4k::ChainHeader*>(out);
@@ -371,27 +385,34 @@ q4_status q4_chain_encode(const q4_chain_stage* stages, int32_t num_stages,
   hdr->out_f32 = y_dtype == Q4_OUT_F32 ? 1 : 0;
   hdr->plan_bytes = static_cast<int32_t>(need);
   auto* sd = reinterpret_cast<q4k::ChainStageDesc*>(hdr + 1);
-  int32_t max_rows = 0;
   for (int32_t s = 0; s < num_stages; ++s) {
     const q4_chain_stage& st = stages[s];
     q4k::ChainStageDesc d{};
     d.x = st.x;
     d.G = static_cast<int32_t>(st.k / 32);
     plan_stage(d.G, &d.c_log2, &d.CH, matrices + st.first_matrix, st.num_matrices);
-    d.UPR = q4k::kSlots / d.CH;
     d.num_mats = st.num_matrices;
     d.mat_begin = st.first_matrix;
-    int32_t off = 0;
-    for (int32_t i = 0; i < st.num_matrices; ++i) {
-      d.row_off[i] = off;
-      off += static_cast<int32_t>(matrices[st.first_matrix + i].n);
-    }
-    for (int32_t i = st.num_matrices; i <= q4k::kMaxMatsPerStage; ++i) d.row_off[i] = off;
-    d.nrows = off;
-    if (off > max_rows) max_rows = off;
     sd[s] = d;
   }
-  hdr->max_rows = max_rows;
+  // Dependencies through memory: a stage whose x overlaps an earlier stage's
+  // outputs loads it only after the preceding stage barrier (device-coherent
+  // loads), and that earlier stage makes its outputs visible before it
+  // arrives at its barrier. Activations no stage writes are prefetched.
+  for (int32_t s = 0; s < num_stages; ++s) {
+    const q4_chain_stage& st = stages[s];
+    for (int32_t t = 0; t < s; ++t) {
+      for (int32_t i = 0; i < stages[t].num_matrices; ++i) {
+        const q4_chain_matrix& m = matrices[stages[t].first_matrix + i];
+        // (a later stage writing x is harmless: x is read before that stage
+        // starts, prefetch included)
+        if (t < s && ranges_overlap(st.x, 2 * st.k, m.y, ybytes * m.n)) {
+          sd[s].x_internal = 1;
+          sd[t].sync_outputs = 1;
+        }
+      }
+    }
+  }
   auto* md = reinterpret_cast<q4k::ChainMatDesc*>(sd + num_stages);
   for (int32_t i = 0; i < num_matrices; ++i) {
     q4k::ChainMatDesc d{};
@@ -409,18 +430,20 @@ q4_status q4_chain_run(const void* device_plan, q4_out_dtype y_dtype, void* work
   if (!device_plan || !workspace) return Q4_ERR_NULL;
   if (y_dtype != Q4_OUT_BF16 && y_dtype != Q4_OUT_F32) return Q4_ERR_SHAPE;
   if (!aligned(device_plan, 64) || !aligned(workspace, 128)) return Q4_ERR_ALIGN;
-  // One block of 16 waves per compute unit, all resident at once (the stage
+  // One block of 12 waves per compute unit, all resident at once (the stage
   // barrier needs that); bounded waits turn a violation into a status.
   const int cus = device_cu_count();
   if (cus > q4k::kChainMaxBlocks) return Q4_ERR_UNSUPPORTED;
   if (!chain_ready_on_device()) return Q4_ERR_UNSUPPORTED;
   const dim3 grid(cus), block(64 * q4k::kChainWaves);
+  const uint32_t nxcc = device_xcc_count();
+  if (nxcc < 1 || nxcc > q4k::kMaxXcc) return Q4_ERR_UNSUPPORTED;
   const q4k::ChainHeader* plan = static_cast<const q4k::ChainHeader*>(device_plan);
   uint32_t* ws = static_cast<uint32_t*>(workspace);
   if (y_dtype == Q4_OUT_F32)
-    hipLaunchKernelGGL(q4k::chain_kernel<true>, grid, block, kChainLdsBytes, as_stream(stream), plan, ws);
+    hipLaunchKernelGGL(q4k::chain_kernel<true>, grid, block, kChainLdsBytes, as_stream(stream), plan, ws, nxcc);
   else
-    hipLaunchKernelGGL(q4k::chain_kernel<false>, grid, block, kChainLdsBytes, as_stream(stream), plan, ws);
+    hipLaunchKernelGGL(q4k::chain_kernel<false>, grid, block, kChainLdsBytes, as_stream(stream), plan, ws, nxcc);
   return launch_status();
 }
 

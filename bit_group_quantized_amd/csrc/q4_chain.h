@@ -5,47 +5,63 @@
 // Apple Silicon", pipeline diagram: 32 layers; read as standard decoder
 // layers: attention input -> q,k,v; attention output -> o; FFN input ->
 // gate,up; gated product -> down). A stage multiplies one activation vector by
-// one or more matrices that share it and may consume the previous stage's
-// outputs, so its products may not start before every output of the previous
-// stage is written and visible.
+// one or more matrices that share it; no product of stage s+1 starts before
+// every output of stage s is written and visible.
 //
-// One launch runs the whole chain, one block of 16 waves per compute unit:
-//  - 15 compute waves only stream weights and do arithmetic. The rows of a
-//    stage are cut into units of RPI rows (C lanes per row, one 32-input group
-//    per lane and chunk, CH chunks per row) dealt round-robin to every compute
-//    wave of the grid. A wave's units of a stage form rounds of at most
-//    kSlots 16-byte loads per lane; two rounds are always in flight (double
-//    buffer), across stage boundaries, because weights never depend on
-//    activations. Activations come from LDS; finished rows are handed to LDS
-//    as (row, value) records.
-//  - 1 service wave owns everything with device-wide ordering: it writes the
-//    records to global memory with device-coherent stores, waits for them,
-//    raises the block's flag (one 128-byte line per block holding a running
-//    barrier count), waits until block 0 has gathered every flag and
-//    published the count, and loads the next stage's activations with
-//    device-coherent loads into LDS. Keeping these off the compute waves
-//    matters because a wave's vector-memory counter completes in order: a
-//    compute wave waiting on a coherent load or store would also wait for all
-//    weight loads it issued before.
-//  - compute and service waves meet at two block barriers per stage (outputs
-//    handed over; next activations ready). Waits on other blocks are bounded
-//    and report a timeout in the workspace instead of hanging.
+// One launch runs the whole chain with one block per compute unit. The waves
+// have three roles that meet only through LDS counters:
+//  - waves 1..kLoaders, the loaders, stream the block's share of every
+//    stage's weights in chain order, in "slots" (64 lanes x one 16-byte group
+//    of codes plus those groups' scales and biases), with loads that write
+//    straight into a ring of landed slots in LDS per compute wave. Each keeps
+//    kLoaderDepth slots in flight and runs ahead across stage boundaries,
+//    limited only by ring space, so HBM keeps streaming while the grid
+//    synchronises.
+//  - the next kComputeWaves waves compute: each takes its slots from its ring in order, forms
+//    the dequantized dot products with the stage's activations (in LDS),
+//    reduces each row over its lanes and stores the row's output. They issue
+//    no global loads.
+//  - wave 0, the service wave, synchronises the grid between stages and
+//    stages activations into LDS (double buffered: the next stage's
+//    activations are fetched during the current stage unless an earlier stage
+//    of the chain writes them).
+// Keeping few weight loads in flight per compute unit matters: the service
+// wave's device-wide messages queue behind them in the unit's memory pipeline.
+//
+// Grid synchronisation is two-level: blocks on one XCD (which share an L2)
+// count arrivals with L2 atomics; the last arrival of each XCD exchanges a
+// flag with the other XCDs through device-coherent memory and then releases
+// its XCD through the L2. All waits are bounded and report a status in the
+// workspace instead of hanging.
 #pragma once
 
 namespace q4k {
 
-constexpr uint32_t kChainMagic = 0x48433451u;  // "Q4CH"
-constexpr int kChainWaves = 12;
-constexpr int kComputeWaves = 11;
-constexpr int kServiceWave = 11;
-constexpr int kSlots = 6;              // 16-byte loads per lane per round
+constexpr uint32_t kChainMagic = 0x34433451u;  // "Q4C4"
+#ifndef Q4_CHAIN_LOADERS
+#define Q4_CHAIN_LOADERS 4
+#endif
+#ifndef Q4_CHAIN_LOADER_DEPTH
+#define Q4_CHAIN_LOADER_DEPTH 6
+#endif
+constexpr int kServiceWave = 0;
+constexpr int kLoaders = Q4_CHAIN_LOADERS;  // waves 1..kLoaders; loader l feeds compute waves l, l + kLoaders, ...
+constexpr int kComputeWaves = 8;
+constexpr int kFirstCompute = 1 + kLoaders;
+constexpr int kChainWaves = kFirstCompute + kComputeWaves;
+constexpr int kRingSlots = 8;       // landed slots per compute wave
+constexpr int kSlotBytes = 1280;    // 64 lanes x 16 B codes, then 64 bf16 scales, then 64 bf16 biases
+constexpr int kLoaderDepth = Q4_CHAIN_LOADER_DEPTH;  // slots in flight per loader
 constexpr int kMaxMatsPerStage = 4;
-constexpr int kMaxRecPerWave = 64;     // finished rows per compute wave per stage
-constexpr int kMaxGroups = 512;        // k <= 16384
-constexpr int kXWordsPerGroup = 20;    // 16 re-paired words + sum + pad (bank spread)
-constexpr int kPlanLdsBytes = 96 * 1024;
+constexpr int kChainMaxGroups = 384;  // k <= 12288
+constexpr int kChainMaxCH = 12;
+constexpr int kXWordsPerGroup = 20;   // 16 re-paired words + sum + pad (bank spread)
 constexpr int kChainMaxBlocks = 1024;
-constexpr uint32_t kBarrierSpinLimit = 1u << 21;
+constexpr int kMaxXcc = 16;
+constexpr uint32_t kSpinLimit = 1u << 22;
+static_assert(kComputeWaves % kLoaders == 0 && kLoaderDepth < kRingSlots && 3 * kLoaderDepth <= 63 &&
+                  (kRingSlots & (kRingSlots - 1)) == 0 && kChainWaves <= 16,
+              "chain shape");
 
 struct alignas(16) ChainHeader {
   uint32_t magic;
@@ -53,20 +69,18 @@ struct alignas(16) ChainHeader {
   int32_t num_mats;
   int32_t out_f32;
   int32_t plan_bytes;
-  int32_t max_rows;  // largest stage row count
-  int32_t pad[10];
+  int32_t pad[11];
 };
 struct alignas(16) ChainStageDesc {
   const uint16_t* x;
-  int32_t G;        // groups of 32 inputs
-  int32_t c_log2;   // lanes per row = 1 << c_log2
-  int32_t CH;       // chunks per row (ceil(G / C) <= kSlots)
-  int32_t UPR;      // units per round = kSlots / CH
-  int32_t nrows;    // rows of all matrices of the stage
+  int32_t G;             // groups of 32 inputs
+  int32_t c_log2;        // lanes per row = 1 << c_log2
+  int32_t CH;            // chunks per row: ceil(G / lanes per row)
   int32_t num_mats;
   int32_t mat_begin;
-  int32_t row_off[kMaxMatsPerStage + 1];  // first row of each matrix; [num_mats] = nrows
-  int32_t pad[2];
+  int32_t x_internal;    // x is written by an earlier stage of the chain
+  int32_t sync_outputs;  // a later stage reads this stage's outputs
+  int32_t pad[7];
 };
 struct alignas(16) ChainMatDesc {
   const uint32_t* packed;
@@ -79,20 +93,36 @@ struct alignas(16) ChainMatDesc {
 static_assert(sizeof(ChainHeader) == 64 && sizeof(ChainStageDesc) == 64 && sizeof(ChainMatDesc) == 48,
               "descriptor sizes");
 
-// workspace words: status on its own 128-byte line, then one flag word per
-// block (dense, so a wave reads all flags with a few wide loads)
-constexpr int kWsStatus = 0;  // 0 ok, 1 barrier timeout, 2 bad plan
-constexpr int kWsFlags = 64;  // block b's flag at kWsFlags + b
+// Workspace words: status on its own line; per XCD an arrival counter and a
+// release word (L2 scope, one 128-byte line each); the XCDs' exchange flags
+// (device scope).
+constexpr int kWsStatus = 0;  // 0 ok, 1 wait timed out, 2 bad plan, 3 block not on the expected XCD
+constexpr int kWsXcnt = 64;                       // + 32 * xcc
+constexpr int kWsXgen = kWsXcnt + 32 * kMaxXcc;   // + 32 * xcc
+constexpr int kWsGflag = kWsXgen + 32 * kMaxXcc;  // + xcc
+constexpr int kWsWords = kWsGflag + 64;
 
-// Pointers read from the plan are generic; loads through them must be issued
-// as global (not flat) accesses, which count only in the vector-memory
-// counter and let the weight loads stay in flight.
+// Plan reads go through the constant address space, so that (at wave-uniform
+// addresses) they become scalar loads and never enter the vector memory
+// pipeline that streams the weights.
+#define Q4_CONST __attribute__((address_space(4)))
+template <typename T>
+__device__ __forceinline__ T cload(const T* p) {
+  return *(const Q4_CONST T*)p;
+}
+// Loads through plan pointers are issued as global (not flat) accesses, which
+// count only in the vector-memory counter.
 #define Q4_GLOBAL __attribute__((address_space(1)))
 template <typename T>
 __device__ __forceinline__ T gload(const T* p) {
   return *(const Q4_GLOBAL T*)p;
 }
+template <typename T>
+__device__ __forceinline__ T gload_off(const unsigned char* base, uint32_t off) {
+  return gload(reinterpret_cast<const T*>(base + off));
+}
 
+// device-coherent accesses (all XCDs)
 __device__ __forceinline__ uint32_t coh_load(const uint32_t* p) {
   return __hip_atomic_load((const Q4_GLOBAL uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -105,259 +135,341 @@ __device__ __forceinline__ void coh_store(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ void coh_store16(uint16_t* p, uint16_t v) {
   __hip_atomic_store((Q4_GLOBAL uint16_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint32_t coh_add(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add((Q4_GLOBAL uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// XCD-local accesses, performed at the XCD's L2 (coherent for the blocks that
+// share that L2). The read is a returning atomic add of zero, written in
+// assembly (with its wait) so that it cannot be turned into a cached load.
+__device__ __forceinline__ uint32_t l2_add(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add((Q4_GLOBAL uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ uint32_t l2_read(uint32_t* p) {
+  uint32_t old;
+  asm volatile("global_atomic_add %0, %1, %2, off sc0\n\ts_waitcnt vmcnt(0)"
+               : "=v"(old)
+               : "v"(p), "v"(0u)
+               : "memory");
+  return old;
+}
+__device__ __forceinline__ void l2_store(uint32_t* p, uint32_t v) {
+  __hip_atomic_store((Q4_GLOBAL uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// hardware id of the XCD this wave runs on
+__device__ __forceinline__ uint32_t xcc_id() {
+  return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 15u;
+}
 
-// Shared-memory layout of the chain kernel (dynamic LDS).
+// Shared memory: activations and landed-slot rings (dynamic LDS) and the
+// flag words that connect the roles (a separate static object, so that the
+// compiler never orders flag accesses behind the loader's direct-to-LDS
+// loads).
 struct ChainLds {
-  uint32_t x[kMaxGroups * kXWordsPerGroup];          // re-paired activations + group sums
-  uint32_t rec_row[kComputeWaves][kMaxRecPerWave];   // (matrix << 24) | local row
-  float rec_val[kComputeWaves][kMaxRecPerWave];
-  int32_t rec_count[kComputeWaves];
-  int32_t ok;
-  int32_t pad[16 - ((kComputeWaves + 1) % 16)];
-  unsigned char plan[kPlanLdsBytes];
+  uint32_t x[2][kChainMaxGroups * kXWordsPerGroup];                 // activations, double buffered
+  unsigned char ring[kComputeWaves][kRingSlots][kSlotBytes];         // landed slots
+};
+struct ChainFlags {
+  uint32_t landed[kComputeWaves];    // slots landed, per compute wave
+  uint32_t consumed[kComputeWaves];  // slots released, per compute wave
+  uint32_t done_total;               // stage completions of all compute waves
+  int32_t x_stage;                   // last stage whose activations are in LDS
+  uint32_t abort;
+  uint32_t go;
 };
 
-// Uniform (per-wave) reads of plan fields held in LDS.
-__device__ __forceinline__ int u32r(const int32_t* p) { return __builtin_amdgcn_readfirstlane(*p); }
-__device__ __forceinline__ const void* ptrr(const void* const* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(*p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+// LDS flag words, accessed through explicit LDS pointers (a volatile access
+// through a generic pointer would become a flat access, which also counts in
+// the vector-memory counter).
+#define Q4_LDS __attribute__((address_space(3)))
+__device__ __forceinline__ uint32_t lds_get(const uint32_t* p) { return *(const volatile Q4_LDS uint32_t*)p; }
+__device__ __forceinline__ int32_t lds_geti(const int32_t* p) { return *(const volatile Q4_LDS int32_t*)p; }
+__device__ __forceinline__ void lds_put(uint32_t* p, uint32_t v) { *(volatile Q4_LDS uint32_t*)p = v; }
+__device__ __forceinline__ void lds_puti(int32_t* p, int32_t v) { *(volatile Q4_LDS int32_t*)p = v; }
+__device__ __forceinline__ void lds_add(uint32_t* p, uint32_t v) {
+  __hip_atomic_fetch_add((Q4_LDS uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
+__device__ __forceinline__ void lds_wait() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0)
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+__device__ __forceinline__ int ufl(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Per-stage geometry (wave-uniform).
-struct StageView {
-  int idx;
-  int G, C, clog, CH, UPR, RPI, num_mats, mat_begin;
+// Stage geometry (wave-uniform).
+struct Geo {
+  int G, clog, LPR, RPI, CH, num_mats, mat_begin;
 };
-
-__device__ __forceinline__ StageView stage_view(const ChainStageDesc* stages, int s) {
-  StageView v;
-  const ChainStageDesc* sd = stages + s;
-  v.idx = s;
-  v.G = u32r(&sd->G);
-  v.clog = u32r(&sd->c_log2);
-  v.C = 1 << v.clog;
-  v.CH = u32r(&sd->CH);
-  v.UPR = u32r(&sd->UPR);
-  v.RPI = 64 >> v.clog;
-  v.num_mats = u32r(&sd->num_mats);
-  v.mat_begin = u32r(&sd->mat_begin);
-  return v;
+__device__ __forceinline__ Geo geo_of(const ChainStageDesc* sd) {
+  Geo g;
+  g.G = cload(&sd->G);
+  g.clog = cload(&sd->c_log2);
+  g.LPR = 1 << g.clog;
+  g.RPI = 64 >> g.clog;
+  g.CH = cload(&sd->CH);
+  g.num_mats = cload(&sd->num_mats);
+  g.mat_begin = cload(&sd->mat_begin);
+  return g;
 }
 
-// Position in the work sequence: stage s, matrix m (absolute index), round r
-// of that matrix. A matrix's units (RPI consecutive rows) are dealt
-// round-robin to every compute wave of the grid; a wave takes its units of a
-// matrix UPR at a time (one round). Every matrix has >= 1 round per wave so
-// that every wave walks the same sequence.
-struct Cursor {
-  StageView v;
-  int m, r, nrounds, nunits;
-  bool valid;
+// Units (RPI consecutive rows) of a matrix: block b owns a contiguous range
+// (sizes differ by at most one unit over the grid), and deals it round-robin
+// to its compute waves: local unit i goes to compute wave i % kComputeWaves.
+struct BlockRange {
+  int u0, count;
 };
-
-__device__ __forceinline__ void cursor_matrix(Cursor& c, const ChainMatDesc* mats, int wct) {
-  const int n = u32r(&mats[c.m].n);
-  c.nunits = n >> (6 - c.v.clog);  // matrices hold whole units (n % RPI == 0)
-  const int per_wave = (c.nunits + wct - 1) / wct;
-  c.nrounds = max(1, (per_wave + c.v.UPR - 1) / c.v.UPR);
-  c.r = 0;
+__device__ __forceinline__ BlockRange block_range(int nunits) {
+  const int nb = (int)gridDim.x, b = (int)blockIdx.x;
+  const int per = nunits / nb, rem = nunits - per * nb;
+  BlockRange r;
+  r.u0 = b * per + (b < rem ? b : rem);
+  r.count = per + (b < rem ? 1 : 0);
+  return r;
 }
 
-__device__ __forceinline__ Cursor cursor_stage(const ChainStageDesc* stages, const ChainMatDesc* mats,
-                                               int num_stages, int s, int wct) {
-  Cursor c;
-  c.valid = s < num_stages;
-  if (!c.valid) return c;
-  c.v = stage_view(stages, s);
-  c.m = c.v.mat_begin;
-  cursor_matrix(c, mats, wct);
-  return c;
-}
+// s_waitcnt immediate that waits for the vector-memory counter only
+constexpr int vmcnt_imm(int n) { return 0xF70 | (n & 15) | (((n >> 4) & 3) << 14); }
 
-// true when the cursor sits on the last round of its stage
-__device__ __forceinline__ bool cursor_stage_end(const Cursor& c) {
-  return c.r + 1 >= c.nrounds && c.m + 1 >= c.v.mat_begin + c.v.num_mats;
-}
+// ---------------------------------------------------------------- loader
 
-__device__ __forceinline__ void cursor_advance(Cursor& c, const ChainStageDesc* stages, const ChainMatDesc* mats,
-                                               int num_stages, int wct) {
-  if (++c.r < c.nrounds) return;
-  if (++c.m < c.v.mat_begin + c.v.num_mats) {
-    cursor_matrix(c, mats, wct);
-    return;
-  }
-  c = cursor_stage(stages, mats, num_stages, c.v.idx + 1, wct);
-}
-
-// Issue-side state of the stage being issued: per-lane byte offsets (all
-// non-negative) of the lane's group relative to group 0 of the unit's first
-// row. Chunk ch < CH-1 adds ch*C groups through the uniform base; the last
-// chunk carries its column in the lane offset, so that in a ragged row
-// (C*CH > G) the lanes past G read group 0 of their own row instead. Their
-// activations are zero, so the weights they read do not count.
-struct LaneOffsets {
-  uint32_t lw, lw_last;    // packed
-  uint32_t ls, ls_last;    // scales / biases: byte offset of the aligned word holding the lane's bf16
-  uint32_t sel, sel_last;  // which half of that word (byte selector for bf16_half_to_f32)
-};
-
-__device__ __forceinline__ LaneOffsets lane_offsets(const StageView& v) {
+// Loader l: walks the block's units owned by compute waves w = l (mod
+// kLoaders) in chain order (stage, matrix, local unit, chunk) and moves each
+// slot into the owning wave's ring with three direct-to-LDS loads: 64 lanes x
+// 16 bytes of codes, and 8 lanes x 16 bytes each of the slot's 64 bf16
+// scales and biases (G % 8 == 0, so a 16-byte piece never straddles a row
+// end). kLoaderDepth slots stay in flight; a slot is published to its compute
+// wave once the counter shows its loads complete (every slot is exactly three
+// loads, so the wait is static). Before it waits for ring space the loader
+// publishes everything it has issued: the compute wave may be waiting for
+// exactly those slots.
+//
+// Lane offsets: chunk ch < CH-1 adds ch*LPR groups to the lane's offset; the
+// last chunk carries its column in the offset, so that in a ragged row
+// (LPR*CH > G) lanes past G read group 0 of their own row instead (the
+// compute waves give those lanes zero weight).
+__device__ __forceinline__ void loader_run(const ChainStageDesc* stages, const ChainMatDesc* mats, int num_stages,
+                                           int l, ChainLds& L, ChainFlags& F, uint32_t* ws) {
   const int lane = threadIdx.x & 63;
-  const int c = lane & (v.C - 1);
-  const int slot_row = lane >> v.clog;
-  const uint32_t grp = (uint32_t)(slot_row * v.G + c);
-  const int last_col = (v.CH - 1) * v.C + c;
-  const uint32_t grp_last = (uint32_t)(slot_row * v.G + (last_col < v.G ? last_col : 0));
-  LaneOffsets o;
-  o.lw = grp * 16u;
-  o.lw_last = grp_last * 16u;
-  // G is even and the arrays are 4-byte aligned, so a group's parity decides
-  // the half of its 32-bit word
-  o.ls = (grp & ~1u) * 2u;
-  o.ls_last = (grp_last & ~1u) * 2u;
-  o.sel = (grp & 1u) ? kSelHiHalf : kSelLoHalf;
-  o.sel_last = (grp_last & 1u) ? kSelHiHalf : kSelLoHalf;
-  return o;
-}
+  uint32_t widx = 0;  // lane w: next ring index of compute wave w
+  uint32_t cons = 0;  // lane w: cached released count of compute wave w
+  uint32_t pend = 0;  // lane j: (wave << 24) | landed value of the j-th slot in flight
+  int issued = 0, published = 0;
+  bool ok = true;
+  unsigned char* ring0 = &L.ring[0][0][0];
 
-struct RoundBuf {
-  uint4 w[kSlots];
-  uint32_t s[kSlots];
-  uint32_t b[kSlots];
-};
+  // publish slot j (its loads are complete)
+  auto publish = [&](int j) {
+    const uint32_t pv = (uint32_t)__builtin_amdgcn_readlane((int)pend, j % kLoaderDepth);
+    if (lane == 0) lds_put(&F.landed[pv >> 24], pv & 0xFFFFFFu);
+  };
+  // publish every slot issued so far
+  auto publish_all = [&]() {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    compiler_fence();
+    for (; published < issued; ++published) publish(published);
+  };
 
-template <typename T>
-__device__ __forceinline__ T gload_off(const unsigned char* base, uint32_t off) {
-  return gload(reinterpret_cast<const T*>(base + off));
-}
-
-// Issue the weight loads of one round: slot jj*CH+ch is chunk ch of unit jj.
-// All kSlots*3 loads are issued unconditionally (units past the matrix
-// re-read unit 0 and are skipped at compute time), so every round issues the
-// same loads in the same order and the compiler's load counting stays exact.
-template <int CH>
-__device__ __forceinline__ void round_issue(const Cursor& cu, const ChainMatDesc* mats, const LaneOffsets& lo,
-                                            int gw, int wct, RoundBuf& buf) {
-  constexpr int UPR = kSlots / CH;
-  const StageView& v = cu.v;
-  const unsigned char* pk = static_cast<const unsigned char*>(ptrr(reinterpret_cast<const void* const*>(&mats[cu.m].packed)));
-  const unsigned char* sc = static_cast<const unsigned char*>(ptrr(reinterpret_cast<const void* const*>(&mats[cu.m].scales)));
-  const unsigned char* bi = static_cast<const unsigned char*>(ptrr(reinterpret_cast<const void* const*>(&mats[cu.m].biases)));
-#pragma unroll
-  for (int jj = 0; jj < UPR; ++jj) {
-    int unit = gw + (cu.r * UPR + jj) * wct;
-    unit = unit < cu.nunits ? unit : 0;
-    const int64_t row_g = (int64_t)unit * v.RPI * v.G;  // group index of the unit's first row
-#pragma unroll
-    for (int ch = 0; ch < CH; ++ch) {
-      const int i = jj * CH + ch;
-      const bool last = ch == CH - 1;
-      const int64_t gbase = row_g + (last ? 0 : ch * v.C);
-      const u32x4_t t = gload_off<u32x4_t>(pk + gbase * 16, last ? lo.lw_last : lo.lw);
-      buf.w[i] = make_uint4(t.x, t.y, t.z, t.w);
-      buf.s[i] = gload_off<uint32_t>(sc + gbase * 2, last ? lo.ls_last : lo.ls);
-      buf.b[i] = gload_off<uint32_t>(bi + gbase * 2, last ? lo.ls_last : lo.ls);
+  for (int s = 0; s < num_stages && ok; ++s) {
+    const Geo g = geo_of(stages + s);
+    // codes: lane (srow, c) reads group (srow, ch*LPR + c) of its unit
+    const int c = lane & (g.LPR - 1);
+    const int srow = lane >> g.clog;
+    const uint32_t grp = (uint32_t)(srow * g.G + c);
+    const int last_col = (g.CH - 1) * g.LPR + c;
+    const uint32_t grp_last = (uint32_t)(srow * g.G + (last_col < g.G ? last_col : 0));
+    const uint32_t lw = grp * 16u, lw_last = grp_last * 16u;
+    // scales/biases: lane j < 8 reads the 8 groups (srow_j, ch*LPR + (j % (LPR/8))*8 ...)
+    const int lpr8 = g.LPR >> 3;
+    const int sj = lane & 7;
+    const int s_row = sj / lpr8, s_col = (sj - s_row * lpr8) * 8;
+    const int s_last_col = (g.CH - 1) * g.LPR + s_col;
+    const uint32_t ls = (uint32_t)(s_row * g.G + s_col) * 2u;
+    const uint32_t ls_last = (uint32_t)(s_row * g.G + (s_last_col < g.G ? s_last_col : 0)) * 2u;
+    const uint32_t unit_w = (uint32_t)(g.RPI * g.G) * 16u, unit_s = (uint32_t)(g.RPI * g.G) * 2u;
+    for (int mi = 0; mi < g.num_mats && ok; ++mi) {
+      const int m = g.mat_begin + mi;
+      const BlockRange br = block_range(cload(&mats[m].n) >> (6 - g.clog));
+      const unsigned char* pw = reinterpret_cast<const unsigned char*>(cload(&mats[m].packed)) + (uint64_t)(br.u0 + l) * unit_w;
+      const unsigned char* ps = reinterpret_cast<const unsigned char*>(cload(&mats[m].scales)) + (uint64_t)(br.u0 + l) * unit_s;
+      const unsigned char* pb = reinterpret_cast<const unsigned char*>(cload(&mats[m].biases)) + (uint64_t)(br.u0 + l) * unit_s;
+      int w = l;
+      for (int i = l; i < br.count && ok; i += kLoaders) {
+        const uint32_t idx0 = (uint32_t)__builtin_amdgcn_readlane((int)widx, w);
+        widx += lane == w ? (uint32_t)g.CH : 0u;
+        for (int ch = 0; ch < g.CH; ++ch) {
+          const uint32_t idx = idx0 + (uint32_t)ch;
+          // wait for the ring position (cached released count first)
+          uint32_t spins = 0;
+          while ((int)((uint32_t)__builtin_amdgcn_readlane((int)cons, w) - (idx + 1u - (uint32_t)kRingSlots)) < 0) {
+            if (published < issued) publish_all();
+            cons = lane < kComputeWaves ? lds_get(&F.consumed[lane]) : 0u;
+            if ((int)((uint32_t)__builtin_amdgcn_readlane((int)cons, w) - (idx + 1u - (uint32_t)kRingSlots)) >= 0) break;
+            __builtin_amdgcn_s_sleep(1);
+            if (lds_get(&F.abort) != 0u || ++spins > kSpinLimit) {
+              if (lane == 0 && spins > kSpinLimit) {
+                coh_store(ws + kWsStatus, 1u);
+                lds_put(&F.abort, 1u);
+              }
+              ok = false;
+              break;
+            }
+          }
+          if (!ok) break;
+          const bool last = ch == g.CH - 1;
+          const uint32_t ow = last ? lw_last : lw + (uint32_t)(ch * g.LPR) * 16u;
+          const uint32_t os = last ? ls_last : ls + (uint32_t)(ch * g.LPR) * 2u;
+          unsigned char* dst = ring0 + ((uint32_t)w * kRingSlots + (idx & (kRingSlots - 1))) * kSlotBytes;
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(pw + ow), reinterpret_cast<void*>(dst), 16, 0, 0);
+          if (lane < 8) {
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(ps + os), reinterpret_cast<void*>(dst + 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(pb + os), reinterpret_cast<void*>(dst + 1152), 16, 0, 0);
+          }
+          // remember what to publish for this slot
+          const uint32_t pv = ((uint32_t)w << 24) | (idx + 1u);
+          pend = lane == issued % kLoaderDepth ? pv : pend;
+          ++issued;
+          if (issued - published == kLoaderDepth) {
+            // exactly kLoaderDepth slots unpublished: the oldest is complete
+            // once at most the newer ones' 3 * (kLoaderDepth - 1) loads remain
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * (kLoaderDepth - 1)));
+            compiler_fence();
+            publish(published++);
+          }
+        }
+        pw += (uint64_t)unit_w * kLoaders;
+        ps += (uint64_t)unit_s * kLoaders;
+        pb += (uint64_t)unit_s * kLoaders;
+        w += kLoaders;
+        if (w >= kComputeWaves) w -= kComputeWaves;
+      }
     }
   }
+  // drain
+  if (ok) publish_all();
 }
 
-// Sum over the C lanes of a row slot with DPP adds; the total lands in the
-// slot's last lane (lane % C == C - 1).
-__device__ __forceinline__ float dpp_sum(float v, int C) {
+// ---------------------------------------------------------------- compute
+
+// Sum over the LPR lanes of a row slot with DPP adds; the total lands in the
+// slot's last lane (lane % LPR == LPR - 1).
+__device__ __forceinline__ float dpp_sum(float v, int LPR) {
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));  // xor 1
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));  // xor 2
-  if (C >= 8) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // half-row mirror
-  if (C >= 16) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // row mirror
-  if (C >= 32) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));  // row bcast 15
-  if (C >= 64) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));  // row bcast 31
+  if (LPR >= 8) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // half-row mirror
+  if (LPR >= 16) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // row mirror
+  if (LPR >= 32) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));  // row bcast 15
+  if (LPR >= 64) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));  // row bcast 31
   return v;
 }
 
-template <int CH>
-__device__ __forceinline__ void round_compute(const Cursor& cu, const LaneOffsets& lo, int gw, int wct,
-                                              const RoundBuf& buf, ChainLds& L, int cw) {
-  constexpr int UPR = kSlots / CH;
-  const StageView& v = cu.v;
-  if (gw + cu.r * UPR * wct >= cu.nunits) return;  // no rows for this wave in this round
+__device__ __forceinline__ void compute_fail(uint32_t* ws, ChainFlags& F) {
+  if ((threadIdx.x & 63) == 0) {
+    coh_store(ws + kWsStatus, 1u);
+    lds_put(&F.abort, 1u);
+  }
+}
+
+template <bool OUT_F32>
+__device__ __forceinline__ void compute_run(const ChainStageDesc* stages, const ChainMatDesc* mats, int num_stages,
+                                            int cw, ChainLds& L, ChainFlags& F, uint32_t* ws) {
   const int lane = threadIdx.x & 63;
-  const int c = lane & (v.C - 1);
-  const int slot_row = lane >> v.clog;
-  int cnt = u32r(&L.rec_count[cw]);
-#pragma unroll
-  for (int jj = 0; jj < UPR; ++jj) {
-    const int unit = gw + (cu.r * UPR + jj) * wct;
-    if (unit < cu.nunits) {  // wave-uniform
-      float acc = 0.f;
-#pragma unroll
-      for (int ch = 0; ch < CH; ++ch) {
-        const int i = jj * CH + ch;
-        const uint32_t* xg = L.x + (ch * v.C + c) * kXWordsPerGroup;  // padded groups hold zeros
-        uint32_t xp[16];
-        const uint4 a0 = *reinterpret_cast<const uint4*>(xg + 0);
-        const uint4 a1 = *reinterpret_cast<const uint4*>(xg + 4);
-        const uint4 a2 = *reinterpret_cast<const uint4*>(xg + 8);
-        const uint4 a3 = *reinterpret_cast<const uint4*>(xg + 12);
-        xp[0] = a0.x; xp[1] = a0.y; xp[2] = a0.z; xp[3] = a0.w;
-        xp[4] = a1.x; xp[5] = a1.y; xp[6] = a1.z; xp[7] = a1.w;
-        xp[8] = a2.x; xp[9] = a2.y; xp[10] = a2.z; xp[11] = a2.w;
-        xp[12] = a3.x; xp[13] = a3.y; xp[14] = a3.z; xp[15] = a3.w;
-        const float xsum = __uint_as_float(xg[16]);
-        const uint32_t sel = ch == CH - 1 ? lo.sel_last : lo.sel;
-        acc = fmaf(bf16_half_to_f32(buf.s[i], sel), group_dot(buf.w[i], xp),
-                   fmaf(bf16_half_to_f32(buf.b[i], sel), xsum, acc));
+  uint32_t k = 0;      // slots consumed
+  uint32_t avail = 0;  // slots known to have landed
+  const unsigned char* myring = &L.ring[cw][0][0];
+  for (int s = 0; s < num_stages; ++s) {
+    const Geo g = geo_of(stages + s);
+    const bool sync_out = cload(&stages[s].sync_outputs) != 0;
+    const int c = lane & (g.LPR - 1);
+    const int srow = lane >> g.clog;
+    const uint32_t sb_off = (uint32_t)(srow * g.LPR + c) * 2u;  // lane's bf16 in the slot's scales/biases
+    {  // activations of stage s
+      uint32_t spins = 0;
+      while (lds_geti(&F.x_stage) < s) {
+        __builtin_amdgcn_s_sleep(1);
+        if (lds_get(&F.abort) != 0u) return;
+        if (++spins > kSpinLimit) {
+          compute_fail(ws, F);
+          return;
+        }
       }
-      const float tot = dpp_sum(acc, v.C);
-      if (c == v.C - 1) {
-        L.rec_row[cw][cnt + slot_row] = ((uint32_t)cu.m << 22) | (uint32_t)(unit * v.RPI + slot_row);
-        L.rec_val[cw][cnt + slot_row] = tot;
-      }
-      cnt += v.RPI;
     }
+    compiler_fence();
+    const uint32_t* xb = L.x[s & 1];
+    for (int mi = 0; mi < g.num_mats; ++mi) {
+      const int m = g.mat_begin + mi;
+      const BlockRange br = block_range(cload(&mats[m].n) >> (6 - g.clog));
+      void* y = cload(&mats[m].y);
+      for (int i = cw; i < br.count; i += kComputeWaves) {
+        float acc = 0.f;
+        for (int ch = 0; ch < g.CH; ++ch) {
+          if (k >= avail) {
+            uint32_t spins = 0;
+            while ((avail = lds_get(&F.landed[cw])) <= k) {
+              __builtin_amdgcn_s_sleep(1);
+              if (lds_get(&F.abort) != 0u) return;
+              if (++spins > kSpinLimit) {
+                compute_fail(ws, F);
+                return;
+              }
+            }
+            compiler_fence();
+          }
+          const unsigned char* slot = myring + (k & (kRingSlots - 1)) * kSlotBytes;
+          const uint4 w = *reinterpret_cast<const uint4*>(slot + lane * 16);
+          const bool live = ch * g.LPR + c < g.G;  // lanes past G in a ragged last chunk weigh zero
+          const uint32_t sv = live ? (uint32_t)*reinterpret_cast<const uint16_t*>(slot + 1024 + sb_off) << 16 : 0u;
+          const uint32_t bv = live ? (uint32_t)*reinterpret_cast<const uint16_t*>(slot + 1152 + sb_off) << 16 : 0u;
+          const uint32_t* xg = xb + (ch * g.LPR + c) * kXWordsPerGroup;  // padded groups hold zeros
+          uint32_t xp[16];
+          const uint4 a0 = *reinterpret_cast<const uint4*>(xg + 0);
+          const uint4 a1 = *reinterpret_cast<const uint4*>(xg + 4);
+          const uint4 a2 = *reinterpret_cast<const uint4*>(xg + 8);
+          const uint4 a3 = *reinterpret_cast<const uint4*>(xg + 12);
+          xp[0] = a0.x; xp[1] = a0.y; xp[2] = a0.z; xp[3] = a0.w;
+          xp[4] = a1.x; xp[5] = a1.y; xp[6] = a1.z; xp[7] = a1.w;
+          xp[8] = a2.x; xp[9] = a2.y; xp[10] = a2.z; xp[11] = a2.w;
+          xp[12] = a3.x; xp[13] = a3.y; xp[14] = a3.z; xp[15] = a3.w;
+          const float xsum = __uint_as_float(xg[16]);
+          acc = fmaf(__uint_as_float(sv), group_dot(w, xp), fmaf(__uint_as_float(bv), xsum, acc));
+          ++k;
+          lds_wait();  // this slot's reads are complete before its position is released
+          compiler_fence();
+          if (lane == 0) lds_put(&F.consumed[cw], k);
+        }
+        const float tot = dpp_sum(acc, g.LPR);
+        if (c == g.LPR - 1) {
+          const int row = (br.u0 + i) * g.RPI + srow;
+          if constexpr (OUT_F32) {
+            coh_store(static_cast<uint32_t*>(y) + row, __float_as_uint(tot));
+          } else {
+            coh_store16(static_cast<uint16_t*>(y) + row, f32_to_bf16_rne(tot));
+          }
+        }
+      }
+    }
+    // stage done; outputs read by a later stage must be visible first
+    if (sync_out) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    compiler_fence();
+    if (lane == 0) lds_add(&F.done_total, 1u);
   }
-  if (lane == 0) L.rec_count[cw] = cnt;
 }
 
-__device__ __forceinline__ void dispatch_issue(const Cursor& cu, const ChainMatDesc* mats, const LaneOffsets& lo,
-                                               int gw, int wct, RoundBuf& b) {
-  switch (cu.v.CH) {
-    case 1: round_issue<1>(cu, mats, lo, gw, wct, b); break;
-    case 2: round_issue<2>(cu, mats, lo, gw, wct, b); break;
-    case 3: round_issue<3>(cu, mats, lo, gw, wct, b); break;
-    case 4: round_issue<4>(cu, mats, lo, gw, wct, b); break;
-    case 5: round_issue<5>(cu, mats, lo, gw, wct, b); break;
-    default: round_issue<6>(cu, mats, lo, gw, wct, b); break;
-  }
-}
+// ---------------------------------------------------------------- service
 
-__device__ __forceinline__ void dispatch_compute(const Cursor& cu, const LaneOffsets& lo, int gw, int wct,
-                                                 const RoundBuf& b, ChainLds& L, int cw) {
-  switch (cu.v.CH) {
-    case 1: round_compute<1>(cu, lo, gw, wct, b, L, cw); break;
-    case 2: round_compute<2>(cu, lo, gw, wct, b, L, cw); break;
-    case 3: round_compute<3>(cu, lo, gw, wct, b, L, cw); break;
-    case 4: round_compute<4>(cu, lo, gw, wct, b, L, cw); break;
-    case 5: round_compute<5>(cu, lo, gw, wct, b, L, cw); break;
-    default: round_compute<6>(cu, lo, gw, wct, b, L, cw); break;
-  }
-}
-
-// ---- service wave helpers (all 64 lanes of the service wave call these)
-
-// Load stage s's activations (device-coherent) into LDS, re-paired, with group
-// sums; groups past G up to the padded count are zero.
-__device__ __forceinline__ void service_load_x(const StageView& v, const void* x, ChainLds& L) {
+// Load a stage's activations into an LDS buffer, re-paired, with group sums;
+// groups past G up to LPR*CH are zero. Coherent loads when an earlier stage of
+// this launch wrote them.
+__device__ __forceinline__ void service_load_x(const Geo& g, const void* x, bool coherent, uint32_t* dst_buf) {
   const int lane = threadIdx.x & 63;
-  const int gpad = v.C * v.CH;
+  const int gpad = g.LPR * g.CH;
   const uint64_t* x64 = static_cast<const uint64_t*>(x);
-  for (int g = lane; g < gpad; g += 64) {
-    uint32_t* dst = L.x + g * kXWordsPerGroup;
-    if (g < v.G) {
+  for (int grp = lane; grp < gpad; grp += 64) {
+    uint32_t* dst = dst_buf + grp * kXWordsPerGroup;
+    if (grp < g.G) {
       uint64_t q[8];
+      if (coherent) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = coh_load64(x64 + (int64_t)g * 8 + i);
+        for (int i = 0; i < 8; ++i) q[i] = coh_load64(x64 + (int64_t)grp * 8 + i);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = gload(x64 + (int64_t)grp * 8 + i);
+      }
       float xs = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -378,157 +490,141 @@ __device__ __forceinline__ void service_load_x(const StageView& v, const void* x
       dst[16] = 0u;
     }
   }
+  lds_wait();
 }
 
-template <bool OUT_F32>
-__device__ __forceinline__ void service_store_records(const ChainMatDesc* mats, ChainLds& L) {
+struct GridSync {
+  uint32_t xcc;
+  uint32_t per;      // blocks on this XCD
+  uint32_t present;  // mask of XCDs that hold blocks
+  uint32_t epoch;
+};
+
+__device__ __forceinline__ bool service_fail(uint32_t* ws, ChainFlags& F, uint32_t code) {
+  if ((threadIdx.x & 63) == 0) {
+    coh_store(ws + kWsStatus, code);
+    lds_put(&F.abort, 1u);
+  }
+  return false;
+}
+
+// Start of a launch. The hardware deals the blocks of a launch round-robin
+// over the device's nxcc XCDs, so block b runs on XCD b % nxcc (checked: a
+// block on any other XCD reports status 3). The XCD's counters continue from
+// earlier launches: the release word holds the last completed epoch, and it
+// cannot move before every block of this launch has arrived at its first
+// barrier, so every block reads the same value here.
+__device__ __forceinline__ bool service_start(uint32_t* ws, ChainFlags& F, GridSync& gs, uint32_t nxcc) {
+  const uint32_t nb = gridDim.x;
+  gs.xcc = blockIdx.x % nxcc;
+  if (xcc_id() != gs.xcc) return service_fail(ws, F, 3u);
+  gs.per = nb / nxcc + (gs.xcc < nb % nxcc ? 1u : 0u);
+  gs.present = nxcc >= 32u ? 0xFFFFFFFFu : ((1u << (nxcc < nb ? nxcc : nb)) - 1u);
+  gs.epoch = l2_read(ws + kWsXgen + 32 * gs.xcc);
+  return true;
+}
+
+// Grid barrier: arrive on this XCD's L2 counter; the XCD's last arrival
+// publishes the XCD's flag device-wide, waits for every XCD's flag and
+// releases its XCD through the L2; the others wait for that release.
+__device__ __forceinline__ bool service_barrier(uint32_t* ws, ChainFlags& F, GridSync& gs) {
   const int lane = threadIdx.x & 63;
-  for (int w = 0; w < kComputeWaves; ++w) {
-    const int cnt = L.rec_count[w];
-    for (int i = lane; i < cnt; i += 64) {
-      const uint32_t code = L.rec_row[w][i];
-      const ChainMatDesc& md = mats[code >> 22];
-      const int row = (int)(code & 0x3FFFFFu);
-      const float val = L.rec_val[w][i];
-      if constexpr (OUT_F32) {
-        coh_store(static_cast<uint32_t*>(md.y) + row, __float_as_uint(val));
-      } else {
-        coh_store16(static_cast<uint16_t*>(md.y) + row, f32_to_bf16_rne(val));
+  const uint32_t e = ++gs.epoch;
+  uint32_t old = 0;
+  if (lane == 0) old = l2_add(ws + kWsXcnt + 32 * gs.xcc, 1u);
+  old = __shfl(old, 0);
+  uint32_t spins = 0;
+  if ((old + 1u) % gs.per == 0u) {
+    if (lane == 0) coh_store(ws + kWsGflag + gs.xcc, e);
+    while (true) {
+      bool mine = true;
+      if (lane < kMaxXcc && ((gs.present >> lane) & 1u)) mine = (int)(coh_load(ws + kWsGflag + lane) - e) >= 0;
+      if (__all(mine)) break;
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit || coh_load(ws + kWsStatus) != 0u) return service_fail(ws, F, 1u);
+    }
+    if (lane == 0) l2_store(ws + kWsXgen + 32 * gs.xcc, e);
+  } else {
+    while (true) {
+      uint32_t gen = 0;
+      if (lane == 0) gen = l2_read(ws + kWsXgen + 32 * gs.xcc);
+      gen = __shfl(gen, 0);
+      if ((int)(gen - e) >= 0) break;
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit || coh_load(ws + kWsStatus) != 0u) return service_fail(ws, F, 1u);
+    }
+  }
+  return true;
+}
+
+__device__ __forceinline__ void service_run(const ChainStageDesc* stages, int num_stages, ChainLds& L,
+                                            ChainFlags& F, uint32_t* ws, uint32_t nxcc) {
+  GridSync gs;
+  if (!service_start(ws, F, gs, nxcc)) return;
+  service_load_x(geo_of(stages), cload(&stages[0].x), false, L.x[0]);
+  if (num_stages > 1 && cload(&stages[1].x_internal) == 0)
+    service_load_x(geo_of(stages + 1), cload(&stages[1].x), false, L.x[1]);
+  compiler_fence();
+  if ((threadIdx.x & 63) == 0) lds_puti(&F.x_stage, 0);
+  for (int s = 0; s < num_stages; ++s) {
+    uint32_t spins = 0;
+    while ((int)(lds_get(&F.done_total) - (uint32_t)(kComputeWaves * (s + 1))) < 0) {
+      __builtin_amdgcn_s_sleep(1);
+      if (lds_get(&F.abort) != 0u) return;
+      if (++spins > kSpinLimit) {
+        service_fail(ws, F, 1u);
+        return;
       }
     }
+    if (s + 1 >= num_stages) break;
+    if (!service_barrier(ws, F, gs)) return;
+    if (cload(&stages[s + 1].x_internal) != 0)
+      service_load_x(geo_of(stages + s + 1), cload(&stages[s + 1].x), true, L.x[(s + 1) & 1]);
+    compiler_fence();
+    if ((threadIdx.x & 63) == 0) lds_puti(&F.x_stage, s + 1);
+    // every compute wave has finished stage s, so its buffer is free
+    if (s + 2 < num_stages && cload(&stages[s + 2].x_internal) == 0)
+      service_load_x(geo_of(stages + s + 2), cload(&stages[s + 2].x), false, L.x[s & 1]);
   }
 }
 
-// Cross-block stage barrier, service wave only: raise this block's flag to
-// `epoch`, then read every block's flag (four per lane per poll) until all
-// have reached it. One memory round trip after the last block arrives.
-// Returns false on timeout or a reported error (then the status word is set).
-__device__ __forceinline__ bool service_barrier(uint32_t* ws, uint32_t epoch) {
-  const int lane = threadIdx.x & 63;
-  const int nb = gridDim.x;
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's output stores are complete
-  if (lane == 0) coh_store(ws + kWsFlags + blockIdx.x, epoch);
-  const uint64_t* f64 = reinterpret_cast<const uint64_t*>(ws + kWsFlags);
-  bool ok = true;
-  uint32_t spins = 0;
-  while (true) {
-    bool mine = true;
-    for (int b4 = lane; 4 * b4 < nb; b4 += 64) {
-      const uint64_t a = coh_load64(f64 + 2 * b4);
-      const uint64_t c = coh_load64(f64 + 2 * b4 + 1);
-      const uint32_t f[4] = {(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)c, (uint32_t)(c >> 32)};
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (4 * b4 + j < nb && (int)(f[j] - epoch) < 0) mine = false;
-    }
-    if (__all(mine)) break;
-    __builtin_amdgcn_s_sleep(1);
-    if (++spins > kBarrierSpinLimit || coh_load(ws + kWsStatus) != 0u) {
-      ok = false;
-      break;
-    }
-  }
-  if (!ok && lane == 0) coh_store(ws + kWsStatus, 1u);
-  return ok;
-}
+// ---------------------------------------------------------------- kernel
 
 template <bool OUT_F32>
-__global__ void __launch_bounds__(768) chain_kernel(const ChainHeader* __restrict__ plan_g,
-                                                      uint32_t* __restrict__ ws) {
+__global__ void __launch_bounds__(64 * kChainWaves) __attribute__((amdgpu_waves_per_eu((kChainWaves + 3) / 4, (kChainWaves + 3) / 4)))
+chain_kernel(const ChainHeader* __restrict__ plan, uint32_t* __restrict__ ws, uint32_t nxcc) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
+  __shared__ ChainFlags F;
   ChainLds& L = *reinterpret_cast<ChainLds*>(lds_raw);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
-  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  if (coh_load(ws + kWsStatus) != 0u) return;  // earlier failure: workspace must be cleared
-  if (plan_g->magic != kChainMagic || plan_g->plan_bytes > kPlanLdsBytes) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) coh_store(ws + kWsStatus, 2u);
-    return;
+  if (threadIdx.x < kComputeWaves) {
+    F.landed[threadIdx.x] = 0u;
+    F.consumed[threadIdx.x] = 0u;
   }
-  // copy the plan into LDS
-  {
-    const int words = plan_g->plan_bytes / 16;
-    const uint4* src = reinterpret_cast<const uint4*>(plan_g);
-    uint4* dst = reinterpret_cast<uint4*>(L.plan);
-    for (int i = threadIdx.x; i < words; i += blockDim.x) dst[i] = src[i];
+  if (threadIdx.x == 0) {
+    F.done_total = 0u;
+    F.x_stage = -1;
+    F.abort = 0u;
+    // the plan must be one this library encoded
+    const bool ok = coh_load(ws + kWsStatus) == 0u && cload(&plan->magic) == kChainMagic &&
+                    cload(&plan->num_stages) > 0 && cload(&plan->num_mats) > 0 &&
+                    gridDim.x <= (unsigned)kChainMaxBlocks && nxcc >= 1u && nxcc <= (unsigned)kMaxXcc;
+    F.go = ok ? 1u : 0u;
+    if (!ok && blockIdx.x == 0 && coh_load(ws + kWsStatus) == 0u) coh_store(ws + kWsStatus, 2u);
   }
-  if (threadIdx.x < kComputeWaves) L.rec_count[threadIdx.x] = 0;
-  if (threadIdx.x == 0) L.ok = 1;
   __syncthreads();
-  const ChainHeader* plan = reinterpret_cast<const ChainHeader*>(L.plan);
-  const int num_stages = plan->num_stages;
+  if (F.go == 0u) return;
+  const int num_stages = cload(&plan->num_stages);
   const ChainStageDesc* stages = reinterpret_cast<const ChainStageDesc*>(plan + 1);
   const ChainMatDesc* mats = reinterpret_cast<const ChainMatDesc*>(stages + num_stages);
-  const int wct = kComputeWaves * gridDim.x;  // compute waves in the grid
-  // each compute wave must be able to hold its rows of any stage as records
-  // (a wave's rows of one matrix: at most n/(wct*RPI) + 1 units of RPI <= 8 rows)
-  if (plan->max_rows > (kMaxRecPerWave - 8 * kMaxMatsPerStage) * wct) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) coh_store(ws + kWsStatus, 2u);
-    return;
-  }
 
   if (wave == kServiceWave) {
-    // running barrier count, equal in all blocks after a completed launch
-    uint32_t epoch = coh_load(ws + kWsFlags + blockIdx.x);
-    service_load_x(stage_view(stages, 0), ptrr(reinterpret_cast<const void* const*>(&stages[0].x)), L);
-    __syncthreads();  // S2 of stage 0: activations ready
-    for (int s = 0; s < num_stages; ++s) {
-      __syncthreads();  // S1: compute waves finished stage s, records complete
-      service_store_records<OUT_F32>(mats, L);
-      if (s + 1 < num_stages) {
-        const bool ok = service_barrier(ws, ++epoch);
-        if (lane < kComputeWaves) L.rec_count[lane] = 0;
-        if (ok) service_load_x(stage_view(stages, s + 1), ptrr(reinterpret_cast<const void* const*>(&stages[s + 1].x)), L);
-        else if (lane == 0) L.ok = 0;
-        __syncthreads();  // S2: next activations ready (or abort)
-        if (!ok) return;
-      }
-    }
-    return;
-  }
-
-  // ---- compute waves
-  const int cw = wave;
-  const int gw = cw * gridDim.x + blockIdx.x;
-  RoundBuf bufA, bufB;
-  // issue cursor runs two rounds ahead of the compute cursor
-  Cursor ic = cursor_stage(stages, mats, num_stages, 0, wct);
-  LaneOffsets lo = lane_offsets(ic.v);
-  int lo_stage = 0;
-  Cursor cc = ic;
-  for (int k = 0; k < 2; ++k) {
-    RoundBuf& b = k == 0 ? bufA : bufB;
-    if (ic.valid) {
-      if (ic.v.idx != lo_stage) { lo = lane_offsets(ic.v); lo_stage = ic.v.idx; }
-      dispatch_issue(ic, mats, lo, gw, wct, b);
-      cursor_advance(ic, stages, mats, num_stages, wct);
-    }
-  }
-  __syncthreads();  // S2 of stage 0
-  LaneOffsets clo = lane_offsets(cc.v);  // offsets of the stage being computed
-  bool running = true;
-  while (running) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      RoundBuf& b = k == 0 ? bufA : bufB;
-      dispatch_compute(cc, clo, gw, wct, b, L, cw);
-      const bool stage_end = cursor_stage_end(cc);
-      if (stage_end) __syncthreads();  // S1: hand the stage's records to the service wave
-      // refill this buffer two rounds ahead (after S1 at a stage end, so a
-      // wait on older loads cannot delay the hand-over)
-      if (ic.valid) {
-        if (ic.v.idx != lo_stage) { lo = lane_offsets(ic.v); lo_stage = ic.v.idx; }
-        dispatch_issue(ic, mats, lo, gw, wct, b);
-        cursor_advance(ic, stages, mats, num_stages, wct);
-      }
-      if (stage_end) {
-        if (cc.v.idx + 1 >= num_stages) { running = false; break; }
-        __syncthreads();  // S2: next stage's activations ready
-        if (L.ok == 0) { running = false; break; }
-      }
-      cursor_advance(cc, stages, mats, num_stages, wct);
-      if (stage_end) clo = lane_offsets(cc.v);
-    }
+    service_run(stages, num_stages, L, F, ws, nxcc);
+  } else if (wave < kFirstCompute) {
+    loader_run(stages, mats, num_stages, wave - 1, L, F, ws);
+  } else {
+    compute_run<OUT_F32>(stages, mats, num_stages, wave - kFirstCompute, L, F, ws);
   }
 }
 

@@ -40,6 +40,7 @@ def test_layout_version_and_status_strings():
 
 A16 = 0x10000   # a 16-byte aligned fake address: validation fails before any use
 ODD = 0x10001
+Y16 = 0x400000  # another one, far from A16 (chain outputs must not overlap their own input)
 
 
 def _p(v):
@@ -107,10 +108,15 @@ def test_binding_refuses_cpu_tensors():
         q4.q4_pack(w)
 
 
-def _chain(n_stages=2, k=64, n=16, x=A16, y=A16, packed=A16):
+def _chain(n_stages=2, k=256, n=16, x=A16, y=Y16, packed=A16):
     stages = (q4._ChainStage * n_stages)(*[q4._ChainStage(x, k, i, 1) for i in range(n_stages)])
     mats = (q4._ChainMatrix * n_stages)(*[q4._ChainMatrix(packed, A16, A16, y, n) for _ in range(n_stages)])
     return stages, mats
+
+
+def _stage_field(buf, s, off):
+    base = 64 + 64 * s
+    return int.from_bytes(bytes(buf[base + off:base + off + 4]), "little", signed=True)
 
 
 def test_chain_encode_validation_and_layout():
@@ -122,7 +128,7 @@ def test_chain_encode_validation_and_layout():
     stages, mats = _chain()
     assert lib.q4_chain_encode(ctypes.byref(stages), 2, ctypes.byref(mats), 2, 0, ctypes.byref(buf), nb) == q4.Q4_OK
     hdr = bytes(buf[:16])
-    assert int.from_bytes(hdr[0:4], "little") == 0x48433451
+    assert int.from_bytes(hdr[0:4], "little") == 0x34433451
     assert int.from_bytes(hdr[4:8], "little") == 2
     # too small a buffer, bad dtype, misaligned x, k not a multiple of 32, stage coverage errors
     assert lib.q4_chain_encode(ctypes.byref(stages), 2, ctypes.byref(mats), 2, 0, ctypes.byref(buf), nb - 1) == q4.Q4_ERR_SHAPE
@@ -134,10 +140,34 @@ def test_chain_encode_validation_and_layout():
     s4, m4 = _chain()
     s4[1].first_matrix = 0
     assert lib.q4_chain_encode(ctypes.byref(s4), 2, ctypes.byref(m4), 2, 0, ctypes.byref(buf), nb) == q4.Q4_ERR_SHAPE
-    s6, m6 = _chain(k=96)  # odd number of groups: scales are read as 32-bit words
+    s6, m6 = _chain(k=96)  # groups not a multiple of 8: scales are read in 16-byte pieces
     assert lib.q4_chain_encode(ctypes.byref(s6), 2, ctypes.byref(m6), 2, 0, ctypes.byref(buf), nb) == q4.Q4_ERR_UNSUPPORTED
     s5, m5 = _chain(packed=0)
     assert lib.q4_chain_encode(ctypes.byref(s5), 2, ctypes.byref(m5), 2, 0, ctypes.byref(buf), nb) == q4.Q4_ERR_NULL
+    s7, m7 = _chain(y=A16)  # a stage writing its own input
+    assert lib.q4_chain_encode(ctypes.byref(s7), 2, ctypes.byref(m7), 2, 0, ctypes.byref(buf), nb) == q4.Q4_ERR_UNSUPPORTED
+    s8, m8 = _chain(k=12288 + 256, n=64)  # wider than the executor's activation buffer
+    assert lib.q4_chain_encode(ctypes.byref(s8), 2, ctypes.byref(m8), 2, 0, ctypes.byref(buf), nb) == q4.Q4_ERR_UNSUPPORTED
+
+
+def test_chain_stage_geometry_and_dependencies():
+    """Lanes per row and chunk count per stage, and the dependency flags the
+    encoder derives from buffer overlap: stage 1 reads stage 0's output."""
+    lib = q4.load()
+    nb = lib.q4_chain_plan_bytes(3, 3)
+    buf = (ctypes.c_uint8 * nb)()
+    Y0, Y1, Y2 = 0x400000, 0x800000, 0xC00000
+    stages = (q4._ChainStage * 3)(q4._ChainStage(A16, 4096, 0, 1), q4._ChainStage(Y0, 11264, 1, 1),
+                                   q4._ChainStage(A16 + 0x100000, 2816, 2, 1))
+    mats = (q4._ChainMatrix * 3)(q4._ChainMatrix(A16, A16, A16, Y0, 11264), q4._ChainMatrix(A16, A16, A16, Y1, 4096),
+                                 q4._ChainMatrix(A16, A16, A16, Y2, 1024))
+    assert lib.q4_chain_encode(ctypes.byref(stages), 3, ctypes.byref(mats), 3, 0, ctypes.byref(buf), nb) == q4.Q4_OK
+    # G, c_log2, CH at byte offsets 8, 12, 16; x_internal 28, sync_outputs 32
+    assert [_stage_field(buf, 0, o) for o in (8, 12, 16)] == [128, 6, 2]    # 64 lanes x 2 chunks
+    assert [_stage_field(buf, 1, o) for o in (8, 12, 16)] == [352, 5, 11]   # 32 lanes x 11 chunks, no idle lane
+    assert [_stage_field(buf, 2, o) for o in (8, 12, 16)] == [88, 3, 11]    # 8 lanes x 11 chunks
+    assert [_stage_field(buf, s, 28) for s in range(3)] == [0, 1, 0]
+    assert [_stage_field(buf, s, 32) for s in range(3)] == [1, 0, 0]
 
 
 def test_chain_run_validation():

@@ -35,7 +35,8 @@ def test_independent_stages(out_dtype):
         (1024, [1024, 37]),
         (4096, [11264, 11264]),
         (2816, [1024]),
-        (64, [300]),
+        (256, [300]),    # 16 lanes per row, 4 rows per unit
+        (6400, [128]),   # 32 lanes x 7 chunks: a ragged last chunk
     ]
     stages, refs = [], []
     item = 0
