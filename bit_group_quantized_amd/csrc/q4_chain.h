@@ -9,24 +9,21 @@
 // every output of stage s is written and visible.
 //
 // One launch runs the whole chain with one block per compute unit. The waves
-// have three roles that meet only through LDS counters:
-//  - waves 1..kLoaders, the loaders, stream the block's share of every
-//    stage's weights in chain order, in "slots" (64 lanes x one 16-byte group
-//    of codes plus those groups' scales and biases), with loads that write
-//    straight into a ring of landed slots in LDS per compute wave. Each keeps
-//    kLoaderDepth slots in flight and runs ahead across stage boundaries,
-//    limited only by ring space, so HBM keeps streaming while the grid
-//    synchronises.
-//  - the next kComputeWaves waves compute: each takes its slots from its ring in order, forms
-//    the dequantized dot products with the stage's activations (in LDS),
-//    reduces each row over its lanes and stores the row's output. They issue
-//    no global loads.
+// have two roles that meet only through LDS counters:
+//  - waves 1..kComputeWaves compute. Each owns a ring of kRingSlots slot
+//    buffers in LDS; a slot is 64 lanes x one 16-byte group of codes plus
+//    those 64 groups' scales and biases. A wave walks its share of every
+//    stage's rows in chain order and keeps the next kRingSlots slots in
+//    flight with loads that write straight into its ring, so its own vector
+//    memory counter says when a slot has landed. It forms the dequantized dot
+//    products with the stage's activations (in LDS), reduces each row over its
+//    lanes and stores the row's output. The loads run ahead across stage
+//    boundaries: the first slots of stage s+1 stream in while the grid
+//    synchronises after stage s.
 //  - wave 0, the service wave, synchronises the grid between stages and
 //    stages activations into LDS (double buffered: the next stage's
 //    activations are fetched during the current stage unless an earlier stage
 //    of the chain writes them).
-// Keeping few weight loads in flight per compute unit matters: the service
-// wave's device-wide messages queue behind them in the unit's memory pipeline.
 //
 // Grid synchronisation is two-level: blocks on one XCD (which share an L2)
 // count arrivals with L2 atomics; the last arrival of each XCD exchanges a
@@ -38,20 +35,17 @@
 namespace q4k {
 
 constexpr uint32_t kChainMagic = 0x34433451u;  // "Q4C4"
-#ifndef Q4_CHAIN_LOADERS
-#define Q4_CHAIN_LOADERS 4
+#ifndef Q4_CHAIN_COMPUTE_WAVES
+#define Q4_CHAIN_COMPUTE_WAVES 12
 #endif
-#ifndef Q4_CHAIN_LOADER_DEPTH
-#define Q4_CHAIN_LOADER_DEPTH 6
+#ifndef Q4_CHAIN_RING_SLOTS
+#define Q4_CHAIN_RING_SLOTS 6
 #endif
 constexpr int kServiceWave = 0;
-constexpr int kLoaders = Q4_CHAIN_LOADERS;  // waves 1..kLoaders; loader l feeds compute waves l, l + kLoaders, ...
-constexpr int kComputeWaves = 8;
-constexpr int kFirstCompute = 1 + kLoaders;
-constexpr int kChainWaves = kFirstCompute + kComputeWaves;
-constexpr int kRingSlots = 8;       // landed slots per compute wave
+constexpr int kComputeWaves = Q4_CHAIN_COMPUTE_WAVES;  // waves 1..kComputeWaves
+constexpr int kChainWaves = 1 + kComputeWaves;
+constexpr int kRingSlots = Q4_CHAIN_RING_SLOTS;  // slot buffers per compute wave = slots in flight ahead of it
 constexpr int kSlotBytes = 1280;    // 64 lanes x 16 B codes, then 64 bf16 scales, then 64 bf16 biases
-constexpr int kLoaderDepth = Q4_CHAIN_LOADER_DEPTH;  // slots in flight per loader
 constexpr int kMaxMatsPerStage = 4;
 constexpr int kChainMaxGroups = 384;  // k <= 12288
 constexpr int kChainMaxCH = 12;
@@ -59,9 +53,7 @@ constexpr int kXWordsPerGroup = 20;   // 16 re-paired words + sum + pad (bank sp
 constexpr int kChainMaxBlocks = 1024;
 constexpr int kMaxXcc = 16;
 constexpr uint32_t kSpinLimit = 1u << 22;
-static_assert(kComputeWaves % kLoaders == 0 && kLoaderDepth < kRingSlots && 3 * kLoaderDepth <= 63 &&
-                  (kRingSlots & (kRingSlots - 1)) == 0 && kChainWaves <= 16,
-              "chain shape");
+static_assert(kChainWaves <= 16 && kRingSlots >= 2 && 2 * kRingSlots <= 63, "chain shape");
 
 struct alignas(16) ChainHeader {
   uint32_t magic;
@@ -160,17 +152,13 @@ __device__ __forceinline__ uint32_t xcc_id() {
   return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 15u;
 }
 
-// Shared memory: activations and landed-slot rings (dynamic LDS) and the
-// flag words that connect the roles (a separate static object, so that the
-// compiler never orders flag accesses behind the loader's direct-to-LDS
-// loads).
+// Shared memory: activations and slot rings (dynamic LDS) and the flag words
+// that connect the roles (a separate static object).
 struct ChainLds {
-  uint32_t x[2][kChainMaxGroups * kXWordsPerGroup];                 // activations, double buffered
-  unsigned char ring[kComputeWaves][kRingSlots][kSlotBytes];         // landed slots
+  uint32_t x[2][kChainMaxGroups * kXWordsPerGroup];          // activations, double buffered
+  unsigned char ring[kComputeWaves][kRingSlots][kSlotBytes];  // slot buffers
 };
 struct ChainFlags {
-  uint32_t landed[kComputeWaves];    // slots landed, per compute wave
-  uint32_t consumed[kComputeWaves];  // slots released, per compute wave
   uint32_t done_total;               // stage completions of all compute waves
   int32_t x_stage;                   // last stage whose activations are in LDS
   uint32_t abort;
@@ -226,124 +214,6 @@ __device__ __forceinline__ BlockRange block_range(int nunits) {
 // s_waitcnt immediate that waits for the vector-memory counter only
 constexpr int vmcnt_imm(int n) { return 0xF70 | (n & 15) | (((n >> 4) & 3) << 14); }
 
-// ---------------------------------------------------------------- loader
-
-// Loader l: walks the block's units owned by compute waves w = l (mod
-// kLoaders) in chain order (stage, matrix, local unit, chunk) and moves each
-// slot into the owning wave's ring with three direct-to-LDS loads: 64 lanes x
-// 16 bytes of codes, and 8 lanes x 16 bytes each of the slot's 64 bf16
-// scales and biases (G % 8 == 0, so a 16-byte piece never straddles a row
-// end). kLoaderDepth slots stay in flight; a slot is published to its compute
-// wave once the counter shows its loads complete (every slot is exactly three
-// loads, so the wait is static). Before it waits for ring space the loader
-// publishes everything it has issued: the compute wave may be waiting for
-// exactly those slots.
-//
-// Lane offsets: chunk ch < CH-1 adds ch*LPR groups to the lane's offset; the
-// last chunk carries its column in the offset, so that in a ragged row
-// (LPR*CH > G) lanes past G read group 0 of their own row instead (the
-// compute waves give those lanes zero weight).
-__device__ __forceinline__ void loader_run(const ChainStageDesc* stages, const ChainMatDesc* mats, int num_stages,
-                                           int l, ChainLds& L, ChainFlags& F, uint32_t* ws) {
-  const int lane = threadIdx.x & 63;
-  uint32_t widx = 0;  // lane w: next ring index of compute wave w
-  uint32_t cons = 0;  // lane w: cached released count of compute wave w
-  uint32_t pend = 0;  // lane j: (wave << 24) | landed value of the j-th slot in flight
-  int issued = 0, published = 0;
-  bool ok = true;
-  unsigned char* ring0 = &L.ring[0][0][0];
-
-  // publish slot j (its loads are complete)
-  auto publish = [&](int j) {
-    const uint32_t pv = (uint32_t)__builtin_amdgcn_readlane((int)pend, j % kLoaderDepth);
-    if (lane == 0) lds_put(&F.landed[pv >> 24], pv & 0xFFFFFFu);
-  };
-  // publish every slot issued so far
-  auto publish_all = [&]() {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    compiler_fence();
-    for (; published < issued; ++published) publish(published);
-  };
-
-  for (int s = 0; s < num_stages && ok; ++s) {
-    const Geo g = geo_of(stages + s);
-    // codes: lane (srow, c) reads group (srow, ch*LPR + c) of its unit
-    const int c = lane & (g.LPR - 1);
-    const int srow = lane >> g.clog;
-    const uint32_t grp = (uint32_t)(srow * g.G + c);
-    const int last_col = (g.CH - 1) * g.LPR + c;
-    const uint32_t grp_last = (uint32_t)(srow * g.G + (last_col < g.G ? last_col : 0));
-    const uint32_t lw = grp * 16u, lw_last = grp_last * 16u;
-    // scales/biases: lane j < 8 reads the 8 groups (srow_j, ch*LPR + (j % (LPR/8))*8 ...)
-    const int lpr8 = g.LPR >> 3;
-    const int sj = lane & 7;
-    const int s_row = sj / lpr8, s_col = (sj - s_row * lpr8) * 8;
-    const int s_last_col = (g.CH - 1) * g.LPR + s_col;
-    const uint32_t ls = (uint32_t)(s_row * g.G + s_col) * 2u;
-    const uint32_t ls_last = (uint32_t)(s_row * g.G + (s_last_col < g.G ? s_last_col : 0)) * 2u;
-    const uint32_t unit_w = (uint32_t)(g.RPI * g.G) * 16u, unit_s = (uint32_t)(g.RPI * g.G) * 2u;
-    for (int mi = 0; mi < g.num_mats && ok; ++mi) {
-      const int m = g.mat_begin + mi;
-      const BlockRange br = block_range(cload(&mats[m].n) >> (6 - g.clog));
-      const unsigned char* pw = reinterpret_cast<const unsigned char*>(cload(&mats[m].packed)) + (uint64_t)(br.u0 + l) * unit_w;
-      const unsigned char* ps = reinterpret_cast<const unsigned char*>(cload(&mats[m].scales)) + (uint64_t)(br.u0 + l) * unit_s;
-      const unsigned char* pb = reinterpret_cast<const unsigned char*>(cload(&mats[m].biases)) + (uint64_t)(br.u0 + l) * unit_s;
-      int w = l;
-      for (int i = l; i < br.count && ok; i += kLoaders) {
-        const uint32_t idx0 = (uint32_t)__builtin_amdgcn_readlane((int)widx, w);
-        widx += lane == w ? (uint32_t)g.CH : 0u;
-        for (int ch = 0; ch < g.CH; ++ch) {
-          const uint32_t idx = idx0 + (uint32_t)ch;
-          // wait for the ring position (cached released count first)
-          uint32_t spins = 0;
-          while ((int)((uint32_t)__builtin_amdgcn_readlane((int)cons, w) - (idx + 1u - (uint32_t)kRingSlots)) < 0) {
-            if (published < issued) publish_all();
-            cons = lane < kComputeWaves ? lds_get(&F.consumed[lane]) : 0u;
-            if ((int)((uint32_t)__builtin_amdgcn_readlane((int)cons, w) - (idx + 1u - (uint32_t)kRingSlots)) >= 0) break;
-            __builtin_amdgcn_s_sleep(1);
-            if (lds_get(&F.abort) != 0u || ++spins > kSpinLimit) {
-              if (lane == 0 && spins > kSpinLimit) {
-                coh_store(ws + kWsStatus, 1u);
-                lds_put(&F.abort, 1u);
-              }
-              ok = false;
-              break;
-            }
-          }
-          if (!ok) break;
-          const bool last = ch == g.CH - 1;
-          const uint32_t ow = last ? lw_last : lw + (uint32_t)(ch * g.LPR) * 16u;
-          const uint32_t os = last ? ls_last : ls + (uint32_t)(ch * g.LPR) * 2u;
-          unsigned char* dst = ring0 + ((uint32_t)w * kRingSlots + (idx & (kRingSlots - 1))) * kSlotBytes;
-          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(pw + ow), reinterpret_cast<void*>(dst), 16, 0, 0);
-          if (lane < 8) {
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(ps + os), reinterpret_cast<void*>(dst + 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(pb + os), reinterpret_cast<void*>(dst + 1152), 16, 0, 0);
-          }
-          // remember what to publish for this slot
-          const uint32_t pv = ((uint32_t)w << 24) | (idx + 1u);
-          pend = lane == issued % kLoaderDepth ? pv : pend;
-          ++issued;
-          if (issued - published == kLoaderDepth) {
-            // exactly kLoaderDepth slots unpublished: the oldest is complete
-            // once at most the newer ones' 3 * (kLoaderDepth - 1) loads remain
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * (kLoaderDepth - 1)));
-            compiler_fence();
-            publish(published++);
-          }
-        }
-        pw += (uint64_t)unit_w * kLoaders;
-        ps += (uint64_t)unit_s * kLoaders;
-        pb += (uint64_t)unit_s * kLoaders;
-        w += kLoaders;
-        if (w >= kComputeWaves) w -= kComputeWaves;
-      }
-    }
-  }
-  // drain
-  if (ok) publish_all();
-}
-
 // ---------------------------------------------------------------- compute
 
 // Sum over the LPR lanes of a row slot with DPP adds; the total lands in the
@@ -358,6 +228,37 @@ __device__ __forceinline__ float dpp_sum(float v, int LPR) {
   return v;
 }
 
+// One slot's operands, read from LDS: the lane's 16 bytes of codes, its
+// group's bf16 scale and bias (as fp32 bit patterns), and the group's
+// re-paired activations and their sum.
+struct SlotRegs {
+  uint4 w;
+  uint32_t sv, bv;
+  uint4 x0, x1, x2, x3;
+  uint32_t xs;
+};
+__device__ __forceinline__ void read_slot(const unsigned char* slot, const uint32_t* xg, int lane, uint32_t sb_off,
+                                          SlotRegs& r) {
+  r.w = *reinterpret_cast<const uint4*>(slot + lane * 16);
+  r.sv = (uint32_t)*reinterpret_cast<const uint16_t*>(slot + 1024 + sb_off) << 16;
+  r.bv = (uint32_t)*reinterpret_cast<const uint16_t*>(slot + 1152 + sb_off) << 16;
+  r.x0 = *reinterpret_cast<const uint4*>(xg + 0);
+  r.x1 = *reinterpret_cast<const uint4*>(xg + 4);
+  r.x2 = *reinterpret_cast<const uint4*>(xg + 8);
+  r.x3 = *reinterpret_cast<const uint4*>(xg + 12);
+  r.xs = xg[16];
+}
+__device__ __forceinline__ float slot_dot(const SlotRegs& r, bool live, float acc) {
+  uint32_t xp[16];
+  xp[0] = r.x0.x; xp[1] = r.x0.y; xp[2] = r.x0.z; xp[3] = r.x0.w;
+  xp[4] = r.x1.x; xp[5] = r.x1.y; xp[6] = r.x1.z; xp[7] = r.x1.w;
+  xp[8] = r.x2.x; xp[9] = r.x2.y; xp[10] = r.x2.z; xp[11] = r.x2.w;
+  xp[12] = r.x3.x; xp[13] = r.x3.y; xp[14] = r.x3.z; xp[15] = r.x3.w;
+  const float sc = __uint_as_float(live ? r.sv : 0u);
+  const float bi = __uint_as_float(live ? r.bv : 0u);
+  return fmaf(sc, group_dot(r.w, xp), fmaf(bi, __uint_as_float(r.xs), acc));
+}
+
 __device__ __forceinline__ void compute_fail(uint32_t* ws, ChainFlags& F) {
   if ((threadIdx.x & 63) == 0) {
     coh_store(ws + kWsStatus, 1u);
@@ -365,13 +266,130 @@ __device__ __forceinline__ void compute_fail(uint32_t* ws, ChainFlags& F) {
   }
 }
 
+// Direct-to-LDS load of 16 bytes per active lane: lane t's bytes land at LDS
+// byte address lds + 16 t. The LDS base goes in M0, which the compiler never
+// allocates. The load is issued from assembly so that the compiler does not
+// hold later LDS reads behind it; every read of a slot buffer is preceded by
+// an explicit wait on the vector memory counter instead.
+__device__ __forceinline__ void dma16_s(const unsigned char* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+               : "memory");
+}
+__device__ __forceinline__ void dma16_v(const unsigned char* addr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(lds) : "memory");
+}
+
+// The next slot a compute wave loads: its position in chain order (stage,
+// matrix, the wave's local unit, chunk), the unit's addresses and the stage's
+// per-lane offsets. All fields but the lane offsets are wave-uniform.
+struct LoadCursor {
+  int s, m, m_end, i, count, ch, CH, LPR, clog;
+  uint32_t unit_w, unit_s;           // bytes of codes / of scales per unit
+  const unsigned char *pw, *ps, *pb;  // current unit's codes, scales, biases
+  uint32_t lw, lw_last, ls, ls_last;  // lane offsets (chunk 0 / last chunk)
+};
+
+// Slot loads: 64 lanes x 16 bytes of codes, and 16 lanes x 16 bytes holding
+// the slot's 64 bf16 scales (lanes 0..7) and biases (lanes 8..15) (G % 8 == 0,
+// so a 16-byte piece never straddles a row end). Lane (srow, c) reads group
+// (srow, ch*LPR + c) of its unit; the last chunk carries its column in the
+// offset, so that in a ragged row (LPR*CH > G) lanes past G read group 0 of
+// their own row instead (they are given zero weight).
+__device__ __forceinline__ void lc_stage(LoadCursor& lc, const ChainStageDesc* stages, int lane) {
+  const Geo g = geo_of(stages + lc.s);
+  lc.CH = g.CH;
+  lc.LPR = g.LPR;
+  lc.clog = g.clog;
+  lc.unit_w = (uint32_t)(g.RPI * g.G) * 16u;
+  lc.unit_s = (uint32_t)(g.RPI * g.G) * 2u;
+  const int c = lane & (g.LPR - 1);
+  const int srow = lane >> g.clog;
+  const int last_col = (g.CH - 1) * g.LPR + c;
+  lc.lw = (uint32_t)(srow * g.G + c) * 16u;
+  lc.lw_last = (uint32_t)(srow * g.G + (last_col < g.G ? last_col : 0)) * 16u;
+  const int lpr8 = g.LPR >> 3;
+  const int sj = lane & 7;
+  const int s_row = sj / lpr8, s_col = (sj - s_row * lpr8) * 8;
+  const int s_last_col = (g.CH - 1) * g.LPR + s_col;
+  lc.ls = (uint32_t)(s_row * g.G + s_col) * 2u;
+  lc.ls_last = (uint32_t)(s_row * g.G + (s_last_col < g.G ? s_last_col : 0)) * 2u;
+  lc.m = g.mat_begin;
+  lc.m_end = g.mat_begin + g.num_mats;
+}
+__device__ __forceinline__ void lc_mat(LoadCursor& lc, const ChainMatDesc* mats, int cw) {
+  const BlockRange br = block_range(cload(&mats[lc.m].n) >> (6 - lc.clog));
+  lc.i = cw;
+  lc.count = br.count;
+  lc.ch = 0;
+  const uint64_t u = (uint64_t)(br.u0 + cw);
+  lc.pw = reinterpret_cast<const unsigned char*>(cload(&mats[lc.m].packed)) + u * lc.unit_w;
+  lc.ps = reinterpret_cast<const unsigned char*>(cload(&mats[lc.m].scales)) + u * lc.unit_s;
+  lc.pb = reinterpret_cast<const unsigned char*>(cload(&mats[lc.m].biases)) + u * lc.unit_s;
+}
+// move to the first position at or after the cursor that holds a slot of this
+// wave (lc.s == num_stages: none left)
+__device__ __forceinline__ void lc_seek(LoadCursor& lc, const ChainStageDesc* stages, const ChainMatDesc* mats,
+                                        int num_stages, int cw, int lane) {
+  while (lc.s < num_stages && lc.i >= lc.count) {
+    if (++lc.m < lc.m_end) {
+      lc_mat(lc, mats, cw);
+    } else if (++lc.s < num_stages) {
+      lc_stage(lc, stages, lane);
+      lc_mat(lc, mats, cw);
+    }
+  }
+}
+__device__ __forceinline__ void lc_issue(LoadCursor& lc, uint32_t dst, int lane, const ChainStageDesc* stages,
+                                         const ChainMatDesc* mats, int num_stages, int cw) {
+  const bool last = lc.ch == lc.CH - 1;
+  const uint32_t ow = last ? lc.lw_last : lc.lw + (uint32_t)(lc.ch * lc.LPR) * 16u;
+  const uint32_t os = last ? lc.ls_last : lc.ls + (uint32_t)(lc.ch * lc.LPR) * 2u;
+  dma16_s(lc.pw, ow, dst);
+  if (lane < 16) dma16_v((lane >= 8 ? lc.pb : lc.ps) + os, dst + 1024u);
+  if (++lc.ch == lc.CH) {
+    lc.ch = 0;
+    lc.i += kComputeWaves;
+    lc.pw += (uint64_t)lc.unit_w * kComputeWaves;
+    lc.ps += (uint64_t)lc.unit_s * kComputeWaves;
+    lc.pb += (uint64_t)lc.unit_s * kComputeWaves;
+    lc_seek(lc, stages, mats, num_stages, cw, lane);
+  }
+}
+
+// Wait until every slot load older than the newest `younger` slots is
+// complete (two loads per slot; the counter completes in issue order).
+__device__ __forceinline__ void wait_slots(uint32_t younger) {
+  if (younger == (uint32_t)(kRingSlots - 2)) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (kRingSlots - 2)));
+  } else if (younger == (uint32_t)(kRingSlots - 1)) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (kRingSlots - 1)));
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+  compiler_fence();
+}
+
+// Compute wave cw: consumes its slots in the order it loads them. Per pair of
+// chunks it waits for both slots, reads them (and the activations) from LDS,
+// refills the two freed buffers with the slots kRingSlots further on, and
+// only then does the arithmetic.
 template <bool OUT_F32>
-__device__ __forceinline__ void compute_run(const ChainStageDesc* stages, const ChainMatDesc* mats, int num_stages,
-                                            int cw, ChainLds& L, ChainFlags& F, uint32_t* ws) {
+__device__ __forceinline__ void compute_body(const ChainStageDesc* stages, const ChainMatDesc* mats, int num_stages,
+                                             int cw, ChainLds& L, ChainFlags& F, uint32_t* ws) {
   const int lane = threadIdx.x & 63;
-  uint32_t k = 0;      // slots consumed
-  uint32_t avail = 0;  // slots known to have landed
+  const uint32_t ring = (uint32_t)ufl((int)(uint32_t)(uintptr_t)(Q4_LDS unsigned char*)&L.ring[cw][0][0]);
   const unsigned char* myring = &L.ring[cw][0][0];
+  LoadCursor lc;
+  lc.s = 0;
+  lc_stage(lc, stages, lane);
+  lc_mat(lc, mats, cw);
+  lc_seek(lc, stages, mats, num_stages, cw, lane);
+  uint32_t issued = 0, k = 0;  // slots issued / consumed
+  int ipos = 0, kpos = 0;      // their ring positions
+  for (; issued < (uint32_t)kRingSlots && lc.s < num_stages; ++issued) {
+    lc_issue(lc, ring + (uint32_t)ipos * kSlotBytes, lane, stages, mats, num_stages, cw);
+    ipos = ipos + 1 == kRingSlots ? 0 : ipos + 1;
+  }
   for (int s = 0; s < num_stages; ++s) {
     const Geo g = geo_of(stages + s);
     const bool sync_out = cload(&stages[s].sync_outputs) != 0;
@@ -397,40 +415,26 @@ __device__ __forceinline__ void compute_run(const ChainStageDesc* stages, const 
       void* y = cload(&mats[m].y);
       for (int i = cw; i < br.count; i += kComputeWaves) {
         float acc = 0.f;
-        for (int ch = 0; ch < g.CH; ++ch) {
-          if (k >= avail) {
-            uint32_t spins = 0;
-            while ((avail = lds_get(&F.landed[cw])) <= k) {
-              __builtin_amdgcn_s_sleep(1);
-              if (lds_get(&F.abort) != 0u) return;
-              if (++spins > kSpinLimit) {
-                compute_fail(ws, F);
-                return;
-              }
-            }
-            compiler_fence();
-          }
-          const unsigned char* slot = myring + (k & (kRingSlots - 1)) * kSlotBytes;
-          const uint4 w = *reinterpret_cast<const uint4*>(slot + lane * 16);
-          const bool live = ch * g.LPR + c < g.G;  // lanes past G in a ragged last chunk weigh zero
-          const uint32_t sv = live ? (uint32_t)*reinterpret_cast<const uint16_t*>(slot + 1024 + sb_off) << 16 : 0u;
-          const uint32_t bv = live ? (uint32_t)*reinterpret_cast<const uint16_t*>(slot + 1152 + sb_off) << 16 : 0u;
-          const uint32_t* xg = xb + (ch * g.LPR + c) * kXWordsPerGroup;  // padded groups hold zeros
-          uint32_t xp[16];
-          const uint4 a0 = *reinterpret_cast<const uint4*>(xg + 0);
-          const uint4 a1 = *reinterpret_cast<const uint4*>(xg + 4);
-          const uint4 a2 = *reinterpret_cast<const uint4*>(xg + 8);
-          const uint4 a3 = *reinterpret_cast<const uint4*>(xg + 12);
-          xp[0] = a0.x; xp[1] = a0.y; xp[2] = a0.z; xp[3] = a0.w;
-          xp[4] = a1.x; xp[5] = a1.y; xp[6] = a1.z; xp[7] = a1.w;
-          xp[8] = a2.x; xp[9] = a2.y; xp[10] = a2.z; xp[11] = a2.w;
-          xp[12] = a3.x; xp[13] = a3.y; xp[14] = a3.z; xp[15] = a3.w;
-          const float xsum = __uint_as_float(xg[16]);
-          acc = fmaf(__uint_as_float(sv), group_dot(w, xp), fmaf(__uint_as_float(bv), xsum, acc));
-          ++k;
-          lds_wait();  // this slot's reads are complete before its position is released
+        for (int ch = 0; ch < g.CH; ch += 2) {
+          const int n2 = g.CH - ch >= 2 ? 2 : 1;
+          wait_slots(issued - (k + (uint32_t)n2));
+          const int kpos1 = kpos + 1 == kRingSlots ? 0 : kpos + 1;
+          SlotRegs r0, r1;
+          read_slot(myring + kpos * kSlotBytes, xb + (ch * g.LPR + c) * kXWordsPerGroup, lane, sb_off, r0);
+          if (n2 == 2) read_slot(myring + kpos1 * kSlotBytes, xb + ((ch + 1) * g.LPR + c) * kXWordsPerGroup, lane, sb_off, r1);
+          lds_wait();  // the reads are complete: the buffers may be refilled
           compiler_fence();
-          if (lane == 0) lds_put(&F.consumed[cw], k);
+          for (int j = 0; j < n2; ++j) {
+            if (lc.s < num_stages) {
+              lc_issue(lc, ring + (uint32_t)ipos * kSlotBytes, lane, stages, mats, num_stages, cw);
+              ipos = ipos + 1 == kRingSlots ? 0 : ipos + 1;
+              ++issued;
+            }
+          }
+          acc = slot_dot(r0, ch * g.LPR + c < g.G, acc);  // lanes past G in a ragged last chunk weigh zero
+          if (n2 == 2) acc = slot_dot(r1, (ch + 1) * g.LPR + c < g.G, acc);
+          k += (uint32_t)n2;
+          kpos = n2 == 2 ? (kpos1 + 1 == kRingSlots ? 0 : kpos1 + 1) : kpos1;
         }
         const float tot = dpp_sum(acc, g.LPR);
         if (c == g.LPR - 1) {
@@ -448,6 +452,14 @@ __device__ __forceinline__ void compute_run(const ChainStageDesc* stages, const 
     compiler_fence();
     if (lane == 0) lds_add(&F.done_total, 1u);
   }
+}
+template <bool OUT_F32>
+__device__ __forceinline__ void compute_run(const ChainStageDesc* stages, const ChainMatDesc* mats, int num_stages,
+                                            int cw, ChainLds& L, ChainFlags& F, uint32_t* ws) {
+  compute_body<OUT_F32>(stages, mats, num_stages, cw, L, F, ws);
+  // no load into this block's LDS may outlive the wave (an aborted wave may
+  // leave some in flight)
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
 // ---------------------------------------------------------------- service
@@ -511,16 +523,19 @@ __device__ __forceinline__ bool service_fail(uint32_t* ws, ChainFlags& F, uint32
 // Start of a launch. The hardware deals the blocks of a launch round-robin
 // over the device's nxcc XCDs, so block b runs on XCD b % nxcc (checked: a
 // block on any other XCD reports status 3). The XCD's counters continue from
-// earlier launches: the release word holds the last completed epoch, and it
-// cannot move before every block of this launch has arrived at its first
-// barrier, so every block reads the same value here.
+// earlier launches: the exchange flag holds the last completed epoch, and it
+// cannot move before every block of this XCD has arrived at the first
+// barrier of this launch, so every block of the XCD reads the same value here.
 __device__ __forceinline__ bool service_start(uint32_t* ws, ChainFlags& F, GridSync& gs, uint32_t nxcc) {
   const uint32_t nb = gridDim.x;
   gs.xcc = blockIdx.x % nxcc;
   if (xcc_id() != gs.xcc) return service_fail(ws, F, 3u);
   gs.per = nb / nxcc + (gs.xcc < nb % nxcc ? 1u : 0u);
   gs.present = nxcc >= 32u ? 0xFFFFFFFFu : ((1u << (nxcc < nb ? nxcc : nb)) - 1u);
-  gs.epoch = l2_read(ws + kWsXgen + 32 * gs.xcc);
+  // the XCD's exchange flag equals its release word between launches, and
+  // (unlike an L2 atomic on one line for every block of the XCD) reading it
+  // does not serialise
+  gs.epoch = coh_load(ws + kWsGflag + gs.xcc);
   return true;
 }
 
@@ -598,10 +613,6 @@ chain_kernel(const ChainHeader* __restrict__ plan, uint32_t* __restrict__ ws, ui
   ChainLds& L = *reinterpret_cast<ChainLds*>(lds_raw);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  if (threadIdx.x < kComputeWaves) {
-    F.landed[threadIdx.x] = 0u;
-    F.consumed[threadIdx.x] = 0u;
-  }
   if (threadIdx.x == 0) {
     F.done_total = 0u;
     F.x_stage = -1;
@@ -621,10 +632,8 @@ chain_kernel(const ChainHeader* __restrict__ plan, uint32_t* __restrict__ ws, ui
 
   if (wave == kServiceWave) {
     service_run(stages, num_stages, L, F, ws, nxcc);
-  } else if (wave < kFirstCompute) {
-    loader_run(stages, mats, num_stages, wave - 1, L, F, ws);
   } else {
-    compute_run<OUT_F32>(stages, mats, num_stages, wave - kFirstCompute, L, F, ws);
+    compute_run<OUT_F32>(stages, mats, num_stages, wave - 1, L, F, ws);
   }
 }
 
