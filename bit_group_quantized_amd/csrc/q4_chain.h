@@ -26,10 +26,10 @@
 //    of the chain writes them).
 //
 // Grid synchronisation is two-level: blocks on one XCD (which share an L2)
-// count arrivals with L2 atomics; the last arrival of each XCD exchanges a
-// flag with the other XCDs through device-coherent memory and then releases
-// its XCD through the L2. All waits are bounded and report a status in the
-// workspace instead of hanging.
+// count arrivals with L2 atomics; the last arrival of each XCD raises the
+// XCD's flag in device-coherent memory, and every block waits for all XCDs'
+// flags. All waits are bounded and report a status in the workspace instead
+// of hanging.
 #pragma once
 
 namespace q4k {
@@ -85,13 +85,11 @@ struct alignas(16) ChainMatDesc {
 static_assert(sizeof(ChainHeader) == 64 && sizeof(ChainStageDesc) == 64 && sizeof(ChainMatDesc) == 48,
               "descriptor sizes");
 
-// Workspace words: status on its own line; per XCD an arrival counter and a
-// release word (L2 scope, one 128-byte line each); the XCDs' exchange flags
-// (device scope).
+// Workspace words: status on its own line; per XCD an arrival counter (L2
+// scope, one 128-byte line each); the XCDs' flags (device scope, one line).
 constexpr int kWsStatus = 0;  // 0 ok, 1 wait timed out, 2 bad plan, 3 block not on the expected XCD
 constexpr int kWsXcnt = 64;                       // + 32 * xcc
-constexpr int kWsXgen = kWsXcnt + 32 * kMaxXcc;   // + 32 * xcc
-constexpr int kWsGflag = kWsXgen + 32 * kMaxXcc;  // + xcc
+constexpr int kWsGflag = kWsXcnt + 32 * kMaxXcc;  // + xcc
 constexpr int kWsWords = kWsGflag + 64;
 
 // Plan reads go through the constant address space, so that (at wave-uniform
@@ -130,22 +128,10 @@ __device__ __forceinline__ void coh_store16(uint16_t* p, uint16_t v) {
 __device__ __forceinline__ uint32_t coh_add(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add((Q4_GLOBAL uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// XCD-local accesses, performed at the XCD's L2 (coherent for the blocks that
-// share that L2). The read is a returning atomic add of zero, written in
-// assembly (with its wait) so that it cannot be turned into a cached load.
+// XCD-local arrival counter, updated at the XCD's L2 (coherent for the
+// blocks that share that L2).
 __device__ __forceinline__ uint32_t l2_add(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add((Q4_GLOBAL uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-__device__ __forceinline__ uint32_t l2_read(uint32_t* p) {
-  uint32_t old;
-  asm volatile("global_atomic_add %0, %1, %2, off sc0\n\ts_waitcnt vmcnt(0)"
-               : "=v"(old)
-               : "v"(p), "v"(0u)
-               : "memory");
-  return old;
-}
-__device__ __forceinline__ void l2_store(uint32_t* p, uint32_t v) {
-  __hip_atomic_store((Q4_GLOBAL uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 // hardware id of the XCD this wave runs on
 __device__ __forceinline__ uint32_t xcc_id() {
@@ -532,42 +518,28 @@ __device__ __forceinline__ bool service_start(uint32_t* ws, ChainFlags& F, GridS
   if (xcc_id() != gs.xcc) return service_fail(ws, F, 3u);
   gs.per = nb / nxcc + (gs.xcc < nb % nxcc ? 1u : 0u);
   gs.present = nxcc >= 32u ? 0xFFFFFFFFu : ((1u << (nxcc < nb ? nxcc : nb)) - 1u);
-  // the XCD's exchange flag equals its release word between launches, and
-  // (unlike an L2 atomic on one line for every block of the XCD) reading it
-  // does not serialise
+  // (unlike an L2 atomic on one line for every block of the XCD, reading the
+  // flag does not serialise)
   gs.epoch = coh_load(ws + kWsGflag + gs.xcc);
   return true;
 }
 
 // Grid barrier: arrive on this XCD's L2 counter; the XCD's last arrival
-// publishes the XCD's flag device-wide, waits for every XCD's flag and
-// releases its XCD through the L2; the others wait for that release.
+// publishes the XCD's flag device-wide; every block waits until all XCDs'
+// flags (one 64-byte line) carry this epoch.
 __device__ __forceinline__ bool service_barrier(uint32_t* ws, ChainFlags& F, GridSync& gs) {
   const int lane = threadIdx.x & 63;
   const uint32_t e = ++gs.epoch;
   uint32_t old = 0;
   if (lane == 0) old = l2_add(ws + kWsXcnt + 32 * gs.xcc, 1u);
   old = __shfl(old, 0);
+  if ((old + 1u) % gs.per == 0u && lane == 0) coh_store(ws + kWsGflag + gs.xcc, e);
   uint32_t spins = 0;
-  if ((old + 1u) % gs.per == 0u) {
-    if (lane == 0) coh_store(ws + kWsGflag + gs.xcc, e);
-    while (true) {
-      bool mine = true;
-      if (lane < kMaxXcc && ((gs.present >> lane) & 1u)) mine = (int)(coh_load(ws + kWsGflag + lane) - e) >= 0;
-      if (__all(mine)) break;
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit || coh_load(ws + kWsStatus) != 0u) return service_fail(ws, F, 1u);
-    }
-    if (lane == 0) l2_store(ws + kWsXgen + 32 * gs.xcc, e);
-  } else {
-    while (true) {
-      uint32_t gen = 0;
-      if (lane == 0) gen = l2_read(ws + kWsXgen + 32 * gs.xcc);
-      gen = __shfl(gen, 0);
-      if ((int)(gen - e) >= 0) break;
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit || coh_load(ws + kWsStatus) != 0u) return service_fail(ws, F, 1u);
-    }
+  while (true) {
+    bool mine = true;
+    if (lane < kMaxXcc && ((gs.present >> lane) & 1u)) mine = (int)(coh_load(ws + kWsGflag + lane) - e) >= 0;
+    if (__all(mine)) break;
+    if (++spins > kSpinLimit || coh_load(ws + kWsStatus) != 0u) return service_fail(ws, F, 1u);
   }
   return true;
 }
