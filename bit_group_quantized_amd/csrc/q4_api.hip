@@ -302,28 +302,14 @@ bool chain_ready_on_device() {
 // with the fewest idle lanes (ties: more lanes per row) whose padded width
 // fits the activation buffer and whose rows per unit (64/lanes) divide every
 // matrix's row count.
-bool plan_stage(int64_t G, int* c_log2, int* CH, const q4_chain_matrix* mats = nullptr, int32_t nm = 0) {
-  int best_c = 0;
-  int64_t best_waste = -1, best_ch = 0;
-  const int cs[4] = {64, 32, 16, 8};
-  for (int i = 0; i < 4; ++i) {
-    const int64_t ch = ceil_div(G, cs[i]);
-    if (ch > q4k::kChainMaxCH || ch * cs[i] > q4k::kChainMaxGroups) continue;
-    bool whole_units = true;
-    for (int32_t j = 0; j < nm; ++j) whole_units = whole_units && mats[j].n % (64 / cs[i]) == 0;
-    if (!whole_units) continue;
-    const int64_t waste = ch * cs[i] - G;
-    if (best_waste < 0 || waste < best_waste) {
-      best_waste = waste;
-      best_c = cs[i];
-      best_ch = ch;
-    }
-  }
-  if (best_waste < 0) return false;
-  int lg = 0;
-  while ((1 << lg) < best_c) ++lg;
-  *c_log2 = lg;
-  *CH = static_cast<int>(best_ch);
+// A chain stage processes units of 4 rows in chunks of 16 groups per row, so
+// its geometry depends on G only: chunks per row CH = ceil(G / 16), with the
+// activations padded to 16 * CH groups.
+bool plan_stage(int64_t G, int* c_log2, int* CH) {
+  const int64_t ch = ceil_div(G, q4k::kChunkGroups);
+  if (G % 8 != 0 || ch * q4k::kChunkGroups > q4k::kChainMaxGroups) return false;
+  *c_log2 = 4;
+  *CH = static_cast<int>(ch);
   return true;
 }
 
@@ -364,14 +350,16 @@ q4_status q4_chain_encode(const q4_chain_stage* stages, int32_t num_stages,
       const q4_status c = check_product(st.x, 1, m.packed, m.scales, m.biases, m.n, st.k, m.y, y_dtype);
       if (c != Q4_OK) return c;
       if (m.n >= (1 << 22)) return Q4_ERR_UNSUPPORTED;
+      // each block stages its rows of a matrix in LDS
+      if (ceil_div(ceil_div(m.n, q4k::kUnitRows), device_cu_count()) > q4k::kStageUnits) return Q4_ERR_UNSUPPORTED;
       // scales/biases are read in 16-byte pieces of 8 groups
       if ((st.k / 32) % 8 != 0 || !aligned(m.scales, 16) || !aligned(m.biases, 16)) return Q4_ERR_UNSUPPORTED;
       // a stage may not write its own input
       if (ranges_overlap(st.x, 2 * st.k, m.y, ybytes * m.n)) return Q4_ERR_UNSUPPORTED;
     }
     int lg, ch;
-    if (st.num_matrices > q4k::kMaxMatsPerStage || num_matrices > 4096 ||
-        !plan_stage(st.k / 32, &lg, &ch, matrices + st.first_matrix, st.num_matrices))
+    if (st.num_matrices > q4k::kMaxMatsPerStage || num_matrices > q4k::kTabMats || num_stages > q4k::kTabStages ||
+        !plan_stage(st.k / 32, &lg, &ch))
       return Q4_ERR_UNSUPPORTED;
   }
   if (next_matrix != num_matrices) return Q4_ERR_SHAPE;
@@ -390,7 +378,7 @@ q4_status q4_chain_encode(const q4_chain_stage* stages, int32_t num_stages,
     q4k::ChainStageDesc d{};
     d.x = st.x;
     d.G = static_cast<int32_t>(st.k / 32);
-    plan_stage(d.G, &d.c_log2, &d.CH, matrices + st.first_matrix, st.num_matrices);
+    plan_stage(d.G, &d.c_log2, &d.CH);
     d.num_mats = st.num_matrices;
     d.mat_begin = st.first_matrix;
     sd[s] = d;

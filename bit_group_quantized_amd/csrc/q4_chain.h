@@ -8,22 +8,28 @@
 // one or more matrices that share it; no product of stage s+1 starts before
 // every output of stage s is written and visible.
 //
-// One launch runs the whole chain with one block per compute unit. The waves
-// have two roles that meet only through LDS counters:
-//  - waves 1..kComputeWaves compute. Each owns a ring of kRingSlots slot
-//    buffers in LDS; a slot is 64 lanes x one 16-byte group of codes plus
-//    those 64 groups' scales and biases. A wave walks its share of every
-//    stage's rows in chain order and keeps the next kRingSlots slots in
-//    flight with loads that write straight into its ring, so its own vector
-//    memory counter says when a slot has landed. It forms the dequantized dot
-//    products with the stage's activations (in LDS), reduces each row over its
-//    lanes and stores the row's output. The loads run ahead across stage
-//    boundaries: the first slots of stage s+1 stream in while the grid
-//    synchronises after stage s.
-//  - wave 0, the service wave, synchronises the grid between stages and
-//    stages activations into LDS (double buffered: the next stage's
-//    activations are fetched during the current stage unless an earlier stage
-//    of the chain writes them).
+// One launch runs the whole chain with one block per compute unit. At the
+// start every block copies the plan into LDS (stage and matrix records, with
+// its own share of each stage worked out), so no wave walks the plan in
+// device memory afterwards. The waves have two roles that meet only through
+// LDS words:
+//  - waves 1..kComputeWaves compute. A stage's rows are cut into units of 4
+//    rows, dealt round-robin to the blocks; a block's units (or pieces of
+//    them, when a stage has few units per block) are its items. A compute
+//    wave takes its own item of each stage, then claims further items from a
+//    per-stage counter, so waves that run faster take more. A slot is one
+//    chunk of an item: 16 groups of 4 rows, one group per lane (16 bytes of
+//    codes and the group's scale and bias). Each wave keeps the next
+//    kRegRing slots in flight in its registers with buffer loads issued in
+//    chain order, across stage boundaries (weights never depend on
+//    activations), so the first slots of stage s+1 stream in while the grid
+//    synchronises after stage s. The dot products run on the matrix cores
+//    against the stage's activations in LDS; finished rows go to LDS.
+//  - wave 0, the service wave, waits for the block's compute waves to finish
+//    a stage, stores the stage's rows, synchronises the grid between stages,
+//    and stages activations into LDS (double buffered: the next stage's
+//    activations are fetched during the current stage unless an earlier
+//    stage of the chain writes them).
 //
 // Grid synchronisation is two-level: blocks on one XCD (which share an L2)
 // count arrivals with L2 atomics; the last arrival of each XCD raises the
@@ -38,22 +44,42 @@ constexpr uint32_t kChainMagic = 0x34433451u;  // "Q4C4"
 #ifndef Q4_CHAIN_COMPUTE_WAVES
 #define Q4_CHAIN_COMPUTE_WAVES 12
 #endif
-#ifndef Q4_CHAIN_RING_SLOTS
-#define Q4_CHAIN_RING_SLOTS 6
-#endif
 constexpr int kServiceWave = 0;
 constexpr int kComputeWaves = Q4_CHAIN_COMPUTE_WAVES;  // waves 1..kComputeWaves
 constexpr int kChainWaves = 1 + kComputeWaves;
-constexpr int kRingSlots = Q4_CHAIN_RING_SLOTS;  // slot buffers per compute wave = slots in flight ahead of it
-constexpr int kSlotBytes = 1280;    // 64 lanes x 16 B codes, then 64 bf16 scales, then 64 bf16 biases
 constexpr int kMaxMatsPerStage = 4;
 constexpr int kChainMaxGroups = 384;  // k <= 12288
-constexpr int kChainMaxCH = 12;
+constexpr int kUnitRows = 4;      // rows per unit
+constexpr int kStageUnits = 128;  // units of one matrix per block and stage (staged in LDS)
+constexpr int kMaxPieces = 8;     // pieces a unit's chunks may be cut into
+#ifndef Q4_CHAIN_SPLIT_UNITS
+#define Q4_CHAIN_SPLIT_UNITS 8
+#endif
+constexpr int kSplitUnits = Q4_CHAIN_SPLIT_UNITS;  // units are cut until a stage has this many items
+constexpr int kSplitItems = 2 * kSplitUnits;       // (so a cut stage has fewer items than this)
+#ifndef Q4_CHAIN_REG_RING
+#define Q4_CHAIN_REG_RING 6
+#endif
+constexpr int kRegRing = Q4_CHAIN_REG_RING;  // slots each compute wave keeps in flight, in registers
+static_assert(kRegRing == 4 || kRegRing == 6 || kRegRing == 8 || kRegRing == 12 || kRegRing == 16,
+              "register ring depth");
+constexpr int kQueueLen = 32;     // claimed items a wave may hold between its loads and its arithmetic
+static_assert(kRegRing + 1 <= kQueueLen, "item queue");
+constexpr uint32_t kQueueEnd = 0xFFFFFFFFu;
+constexpr int kChunkGroups = 16;  // groups of each row per slot
 constexpr int kXWordsPerGroup = 20;   // 16 re-paired words + sum + pad (bank spread)
 constexpr int kChainMaxBlocks = 1024;
+constexpr int kTabStages = 256;   // stages of a chain (the plan is copied into LDS)
+constexpr int kTabMats = 512;     // matrices of a chain
 constexpr int kMaxXcc = 16;
 constexpr uint32_t kSpinLimit = 1u << 22;
-static_assert(kChainWaves <= 16 && kRingSlots >= 2 && 2 * kRingSlots <= 63, "chain shape");
+
+// Waits between waves of a block sleep (the sleeping wave takes no issue
+// slots from the working ones) and are cut short by the producer's wakeup;
+// a wakeup that arrives just before the sleep only costs the sleep.
+__device__ __forceinline__ void nap() { __builtin_amdgcn_s_sleep(8); }
+__device__ __forceinline__ void wake_block() { asm volatile("s_wakeup" ::: "memory"); }
+static_assert(kChainWaves <= 16, "chain shape");
 
 struct alignas(16) ChainHeader {
   uint32_t magic;
@@ -66,8 +92,8 @@ struct alignas(16) ChainHeader {
 struct alignas(16) ChainStageDesc {
   const uint16_t* x;
   int32_t G;             // groups of 32 inputs
-  int32_t c_log2;        // lanes per row = 1 << c_log2
-  int32_t CH;            // chunks per row: ceil(G / lanes per row)
+  int32_t c_log2;        // lanes per row = 1 << c_log2 (always 16)
+  int32_t CH;            // chunks per row: ceil(G / 16)
   int32_t num_mats;
   int32_t mat_begin;
   int32_t x_internal;    // x is written by an earlier stage of the chain
@@ -98,7 +124,12 @@ constexpr int kWsWords = kWsGflag + 64;
 #define Q4_CONST __attribute__((address_space(4)))
 template <typename T>
 __device__ __forceinline__ T cload(const T* p) {
-  return *(const Q4_CONST T*)p;
+  // the address is wave-uniform; saying so keeps the load scalar even where
+  // the compiler cannot prove it
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  const uintptr_t u = (uintptr_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a) |
+                      ((uintptr_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) << 32);
+  return *(const Q4_CONST T*)u;
 }
 // Loads through plan pointers are issued as global (not flat) accesses, which
 // count only in the vector-memory counter.
@@ -106,6 +137,11 @@ __device__ __forceinline__ T cload(const T* p) {
 template <typename T>
 __device__ __forceinline__ T gload(const T* p) {
   return *(const Q4_GLOBAL T*)p;
+}
+typedef uint32_t q4_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 gload16(const void* p) {
+  const q4_u32x4 v = *(const Q4_GLOBAL q4_u32x4*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 template <typename T>
 __device__ __forceinline__ T gload_off(const unsigned char* base, uint32_t off) {
@@ -138,29 +174,68 @@ __device__ __forceinline__ uint32_t xcc_id() {
   return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 15u;
 }
 
-// Shared memory: activations and slot rings (dynamic LDS) and the flag words
+// The plan as one block sees it, copied into LDS at the start of a launch
+// (every wave then reads its stages and matrices with LDS latency instead of
+// chains of dependent memory loads). Block-specific fields (its units, the
+// pieces its units are cut into) are worked out in that copy.
+struct StageRec {
+  int32_t G, CH, nm, mat_begin;
+  int32_t P, total;           // pieces per unit, items of the block
+  uint32_t inv_p;             // ceil(2^16 / P): i / P == (i * inv_p) >> 16 for the small i here
+  int32_t flags;              // 1 ragged (16 CH > G), 2 x written in the chain, 4 outputs read in the chain
+  int32_t U[kMaxMatsPerStage];  // the block's units of each matrix
+  const uint16_t* x;
+  int32_t pad[2];
+};
+struct MatRec {
+  const uint32_t* packed;
+  const uint16_t* scales;
+  const uint16_t* biases;
+  void* y;
+  int32_t n, pad[3];
+};
+static_assert(sizeof(StageRec) == 64 && sizeof(MatRec) == 48, "table records");
+constexpr int kStageRagged = 1, kStageXInternal = 2, kStageSyncOut = 4;
+
+// Shared memory: activations and the plan tables (dynamic LDS), and the words
 // that connect the roles (a separate static object).
 struct ChainLds {
-  uint32_t x[2][kChainMaxGroups * kXWordsPerGroup];          // activations, double buffered
-  unsigned char ring[kComputeWaves][kRingSlots][kSlotBytes];  // slot buffers
+  uint32_t x[2][kChainMaxGroups * kXWordsPerGroup];  // activations, double buffered
+  StageRec st[kTabStages];
+  MatRec mt[kTabMats];
 };
 struct ChainFlags {
+  float parts[kSplitItems][kUnitRows];   // partial row sums of the pieces of a stage
+  uint32_t pieces_done[kSplitUnits];     // pieces of a unit of the stage finished
+  float out[kMaxMatsPerStage][kStageUnits][kUnitRows];  // the stage's finished rows
   uint32_t done_total;               // stage completions of all compute waves
   int32_t x_stage;                   // last stage whose activations are in LDS
   uint32_t abort;
   uint32_t go;
+  uint32_t misfit;                   // a matrix has more units per block than the row staging holds
+  uint32_t claim[kTabStages];        // items of each stage claimed so far by the block's waves
+  uint32_t queue[kComputeWaves][kQueueLen];  // each wave's claimed items, oldest first
 };
 
 // LDS flag words, accessed through explicit LDS pointers (a volatile access
 // through a generic pointer would become a flat access, which also counts in
 // the vector-memory counter).
 #define Q4_LDS __attribute__((address_space(3)))
-__device__ __forceinline__ uint32_t lds_get(const uint32_t* p) { return *(const volatile Q4_LDS uint32_t*)p; }
-__device__ __forceinline__ int32_t lds_geti(const int32_t* p) { return *(const volatile Q4_LDS int32_t*)p; }
+// Every lane reads the same word, so the value is wave-uniform; saying so
+// keeps the control flow that depends on it scalar.
+__device__ __forceinline__ uint32_t lds_get(const uint32_t* p) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)*(const volatile Q4_LDS uint32_t*)p);
+}
+__device__ __forceinline__ int32_t lds_geti(const int32_t* p) {
+  return __builtin_amdgcn_readfirstlane(*(const volatile Q4_LDS int32_t*)p);
+}
 __device__ __forceinline__ void lds_put(uint32_t* p, uint32_t v) { *(volatile Q4_LDS uint32_t*)p = v; }
 __device__ __forceinline__ void lds_puti(int32_t* p, int32_t v) { *(volatile Q4_LDS int32_t*)p = v; }
 __device__ __forceinline__ void lds_add(uint32_t* p, uint32_t v) {
   __hip_atomic_fetch_add((Q4_LDS uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ uint32_t lds_add_rtn(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add((Q4_LDS uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 __device__ __forceinline__ void lds_wait() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0)
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
@@ -168,324 +243,500 @@ __device__ __forceinline__ int ufl(int v) { return __builtin_amdgcn_readfirstlan
 
 // Stage geometry (wave-uniform).
 struct Geo {
-  int G, clog, LPR, RPI, CH, num_mats, mat_begin;
+  int G, CH, num_mats, mat_begin;
 };
-__device__ __forceinline__ Geo geo_of(const ChainStageDesc* sd) {
+__device__ __forceinline__ Geo geo_of(const StageRec& r) {
   Geo g;
-  g.G = cload(&sd->G);
-  g.clog = cload(&sd->c_log2);
-  g.LPR = 1 << g.clog;
-  g.RPI = 64 >> g.clog;
-  g.CH = cload(&sd->CH);
-  g.num_mats = cload(&sd->num_mats);
-  g.mat_begin = cload(&sd->mat_begin);
+  g.G = ufl(r.G);
+  g.CH = ufl(r.CH);
+  g.num_mats = ufl(r.nm);
+  g.mat_begin = ufl(r.mat_begin);
   return g;
 }
+// a pointer field of a table record, wave-uniform
+template <typename T>
+__device__ __forceinline__ T* ufl_ptr(T* p) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return reinterpret_cast<T*>((uintptr_t)(uint32_t)ufl((int)(uint32_t)a) |
+                              ((uintptr_t)(uint32_t)ufl((int)(uint32_t)(a >> 32)) << 32));
+}
 
-// Units (RPI consecutive rows) of a matrix: block b owns a contiguous range
-// (sizes differ by at most one unit over the grid), and deals it round-robin
-// to its compute waves: local unit i goes to compute wave i % kComputeWaves.
+// Units (4 consecutive rows) of a matrix are dealt to the blocks round-robin:
+// block b's local unit i is unit b + i * gridDim.x. The grid thus streams a
+// dense window of consecutive units at a time (HBM delivers markedly more
+// to such a sweep than to one contiguous range per block).
 struct BlockRange {
-  int u0, count;
+  int u0, count;  // first unit, units of this block
 };
 __device__ __forceinline__ BlockRange block_range(int nunits) {
   const int nb = (int)gridDim.x, b = (int)blockIdx.x;
-  const int per = nunits / nb, rem = nunits - per * nb;
   BlockRange r;
-  r.u0 = b * per + (b < rem ? b : rem);
-  r.count = per + (b < rem ? 1 : 0);
+  r.u0 = b;
+  r.count = b < nunits ? (nunits - 1 - b) / nb + 1 : 0;
   return r;
 }
+__device__ __forceinline__ int unit_of(const BlockRange& br, int i) { return br.u0 + i * (int)gridDim.x; }
+
 
 // s_waitcnt immediate that waits for the vector-memory counter only
 constexpr int vmcnt_imm(int n) { return 0xF70 | (n & 15) | (((n >> 4) & 3) << 14); }
 
 // ---------------------------------------------------------------- compute
 
-// Sum over the LPR lanes of a row slot with DPP adds; the total lands in the
-// slot's last lane (lane % LPR == LPR - 1).
-__device__ __forceinline__ float dpp_sum(float v, int LPR) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));  // xor 1
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));  // xor 2
-  if (LPR >= 8) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // half-row mirror
-  if (LPR >= 16) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // row mirror
-  if (LPR >= 32) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));  // row bcast 15
-  if (LPR >= 64) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));  // row bcast 31
-  return v;
+// Lane t of a slot holds row (t & 3) of its unit and group (16 ch + (t >> 2))
+// of that row. Sum over the 16 lanes that hold one row (lanes congruent mod
+// 4): two rotations within each 16-lane DPP row, then across the four rows.
+__device__ __forceinline__ float row_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));  // row_ror:4
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror:8
+  // (the swaps give every lane the same two addends, its own and its
+  // partner's, so both lanes of a pair hold the same sum)
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// One slot's operands, read from LDS: the lane's 16 bytes of codes, its
-// group's bf16 scale and bias (as fp32 bit patterns), and the group's
-// re-paired activations and their sum.
-struct SlotRegs {
+// One slot in a lane's registers: its 16 bytes of codes and its group's bf16
+// scale and bias (zero-extended).
+struct Slot {
   uint4 w;
-  uint32_t sv, bv;
-  uint4 x0, x1, x2, x3;
-  uint32_t xs;
+  uint32_t s, b;
 };
-__device__ __forceinline__ void read_slot(const unsigned char* slot, const uint32_t* xg, int lane, uint32_t sb_off,
-                                          SlotRegs& r) {
-  r.w = *reinterpret_cast<const uint4*>(slot + lane * 16);
-  r.sv = (uint32_t)*reinterpret_cast<const uint16_t*>(slot + 1024 + sb_off) << 16;
-  r.bv = (uint32_t)*reinterpret_cast<const uint16_t*>(slot + 1152 + sb_off) << 16;
-  r.x0 = *reinterpret_cast<const uint4*>(xg + 0);
-  r.x1 = *reinterpret_cast<const uint4*>(xg + 4);
-  r.x2 = *reinterpret_cast<const uint4*>(xg + 8);
-  r.x3 = *reinterpret_cast<const uint4*>(xg + 12);
-  r.xs = xg[16];
-}
-__device__ __forceinline__ float slot_dot(const SlotRegs& r, bool live, float acc) {
-  uint32_t xp[16];
-  xp[0] = r.x0.x; xp[1] = r.x0.y; xp[2] = r.x0.z; xp[3] = r.x0.w;
-  xp[4] = r.x1.x; xp[5] = r.x1.y; xp[6] = r.x1.z; xp[7] = r.x1.w;
-  xp[8] = r.x2.x; xp[9] = r.x2.y; xp[10] = r.x2.z; xp[11] = r.x2.w;
-  xp[12] = r.x3.x; xp[13] = r.x3.y; xp[14] = r.x3.z; xp[15] = r.x3.w;
-  const float sc = __uint_as_float(live ? r.sv : 0u);
-  const float bi = __uint_as_float(live ? r.bv : 0u);
-  return fmaf(sc, group_dot(r.w, xp), fmaf(bi, __uint_as_float(r.xs), acc));
+
+typedef short mfma_bf16x4 __attribute__((ext_vector_type(4)));
+typedef float mfma_f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ mfma_bf16x4 as_bf16x4(uint32_t lo, uint32_t hi) {
+  return __builtin_bit_cast(mfma_bf16x4, make_uint2(lo, hi));
 }
 
-__device__ __forceinline__ void compute_fail(uint32_t* ws, ChainFlags& F) {
-  if ((threadIdx.x & 63) == 0) {
-    coh_store(ws + kWsStatus, 1u);
-    lds_put(&F.abort, 1u);
+// The lane's group term of a slot, scale * (codes . activations) + bias * (sum
+// of activations), with the dot product on the matrix cores. The 4x4x4 bf16
+// MFMA works on 16 independent 4x4 blocks; block b (lanes 4b..4b+3)
+// multiplies A (4 rows x 4 inputs, row i from lane 4b+i) by B (4 inputs x 4
+// columns, column j from lane 4b+j), and lane 4b+j receives column j of the
+// product, row i in register i. Here B column j is lane 4b+j's own dequantized
+// codes (exact small integers in bf16) and every lane supplies its group's
+// activations as A, so register 0 of each lane accumulates exactly its own
+// group's sum of code x activation in fp32: two MFMAs per 8 codes, codes and
+// activations in the same re-paired input order. xg: the group's 16
+// re-paired activation words and their sum (LDS).
+__device__ __forceinline__ float slot_term(const Slot& d, const uint32_t* xg, bool live) {
+  const uint4 x0 = *reinterpret_cast<const uint4*>(xg + 0);
+  const uint4 x1 = *reinterpret_cast<const uint4*>(xg + 4);
+  const uint4 x2 = *reinterpret_cast<const uint4*>(xg + 8);
+  const uint4 x3 = *reinterpret_cast<const uint4*>(xg + 12);
+  const float xs = __uint_as_float(xg[16]);
+  const uint32_t ws[4] = {d.w.x, d.w.y, d.w.z, d.w.w};
+  const uint32_t xp[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                           x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+  mfma_f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    uint32_t q02, q46, q13, q57;
+    word_to_bf16_pairs(ws[t], q02, q46, q13, q57);
+    c = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(as_bf16x4(xp[4 * t], xp[4 * t + 1]), as_bf16x4(q02, q46), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(as_bf16x4(xp[4 * t + 2], xp[4 * t + 3]), as_bf16x4(q13, q57), c, 0, 0, 0);
   }
+  // lanes past G in a ragged last chunk weigh zero
+  const float sc = __uint_as_float(live ? d.s << 16 : 0u);
+  const float bi = __uint_as_float(live ? d.b << 16 : 0u);
+  return fmaf(sc, c[0], bi * xs);
 }
 
-// Direct-to-LDS load of 16 bytes per active lane: lane t's bytes land at LDS
-// byte address lds + 16 t. The LDS base goes in M0, which the compiler never
-// allocates. The load is issued from assembly so that the compiler does not
-// hold later LDS reads behind it; every read of a slot buffer is preceded by
-// an explicit wait on the vector memory counter instead.
-__device__ __forceinline__ void dma16_s(const unsigned char* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
-               : "memory");
-}
-__device__ __forceinline__ void dma16_v(const unsigned char* addr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(lds) : "memory");
+// Lanes 0..3 leave the 4 rows of local unit u of matrix mi of the stage in
+// LDS; the service wave stores them. Compute waves issue no global stores at
+// all, so that every step of their loop issues exactly the same loads.
+__device__ __forceinline__ void stage_rows(ChainFlags& F, int mi, int u, int lane, float v) {
+  if (lane < kUnitRows) *(volatile Q4_LDS float*)&F.out[mi][u][lane] = v;
 }
 
-// The next slot a compute wave loads: its position in chain order (stage,
-// matrix, the wave's local unit, chunk), the unit's addresses and the stage's
-// per-lane offsets. All fields but the lane offsets are wave-uniform.
-struct LoadCursor {
-  int s, m, m_end, i, count, ch, CH, LPR, clog;
-  uint32_t unit_w, unit_s;           // bytes of codes / of scales per unit
-  const unsigned char *pw, *ps, *pb;  // current unit's codes, scales, biases
-  uint32_t lw, lw_last, ls, ls_last;  // lane offsets (chunk 0 / last chunk)
+// a wait timed out: the service wave reports it
+__device__ __forceinline__ void compute_fail(ChainFlags& F) {
+  if ((threadIdx.x & 63) == 0) lds_put(&F.abort, 2u);
+  wake_block();
+}
+
+// Work of one block in one stage. The stage's matrices, in order, contribute
+// U[mi] units each (the block's round-robin share); every unit is cut into P
+// pieces of consecutive chunks, piece p covering chunks [p CH / P,
+// (p + 1) CH / P). Item i of the stage is (matrix, unit, piece) in that
+// order. Compute wave w takes item w of every stage, then claims further items
+// one at a time from a counter per stage (a wave that runs faster takes more
+// of them); it runs its items in the order it took them. P grows (up
+// to 8, and not past CH) while the stage holds fewer than 3 items per compute
+// wave, so a cut stage has fewer than 3 kComputeWaves units and fewer than
+// 6 kComputeWaves items.
+struct StageInfo {
+  int s, G, CH, nm, mat_begin, P, total;
+  uint32_t inv_p;  // ceil(2^16 / P): i / P == (i * inv_p) >> 16 for the small i here
+  bool ragged;     // 16 CH > G: the last chunk has lanes past the row end
+  int U[kMaxMatsPerStage];
 };
-
-// Slot loads: 64 lanes x 16 bytes of codes, and 16 lanes x 16 bytes holding
-// the slot's 64 bf16 scales (lanes 0..7) and biases (lanes 8..15) (G % 8 == 0,
-// so a 16-byte piece never straddles a row end). Lane (srow, c) reads group
-// (srow, ch*LPR + c) of its unit; the last chunk carries its column in the
-// offset, so that in a ragged row (LPR*CH > G) lanes past G read group 0 of
-// their own row instead (they are given zero weight).
-__device__ __forceinline__ void lc_stage(LoadCursor& lc, const ChainStageDesc* stages, int lane) {
-  const Geo g = geo_of(stages + lc.s);
-  lc.CH = g.CH;
-  lc.LPR = g.LPR;
-  lc.clog = g.clog;
-  lc.unit_w = (uint32_t)(g.RPI * g.G) * 16u;
-  lc.unit_s = (uint32_t)(g.RPI * g.G) * 2u;
-  const int c = lane & (g.LPR - 1);
-  const int srow = lane >> g.clog;
-  const int last_col = (g.CH - 1) * g.LPR + c;
-  lc.lw = (uint32_t)(srow * g.G + c) * 16u;
-  lc.lw_last = (uint32_t)(srow * g.G + (last_col < g.G ? last_col : 0)) * 16u;
-  const int lpr8 = g.LPR >> 3;
-  const int sj = lane & 7;
-  const int s_row = sj / lpr8, s_col = (sj - s_row * lpr8) * 8;
-  const int s_last_col = (g.CH - 1) * g.LPR + s_col;
-  lc.ls = (uint32_t)(s_row * g.G + s_col) * 2u;
-  lc.ls_last = (uint32_t)(s_row * g.G + (s_last_col < g.G ? s_last_col : 0)) * 2u;
-  lc.m = g.mat_begin;
-  lc.m_end = g.mat_begin + g.num_mats;
+// Fill the block's record of a stage (one lane per stage, at the start of a
+// launch). Returns false if a matrix has more units per block than the LDS
+// staging of rows holds.
+__device__ __forceinline__ bool build_stage_rec(StageRec& r, const ChainStageDesc* sd, const ChainMatDesc* mats) {
+  r.G = sd->G;
+  r.CH = sd->CH;
+  r.nm = sd->num_mats;
+  r.mat_begin = sd->mat_begin;
+  r.x = sd->x;
+  r.flags = (r.CH * kChunkGroups != r.G ? kStageRagged : 0) | (sd->x_internal ? kStageXInternal : 0) |
+            (sd->sync_outputs ? kStageSyncOut : 0);
+  int units = 0;
+  bool fits = true;
+  for (int mi = 0; mi < kMaxMatsPerStage; ++mi) {
+    const int nunits = mi < r.nm ? (mats[r.mat_begin + mi].n + kUnitRows - 1) / kUnitRows : 0;
+    r.U[mi] = block_range(nunits).count;
+    // (block 0 has the most units; every block takes the same decision)
+    fits = fits && (nunits + (int)gridDim.x - 1) / (int)gridDim.x <= kStageUnits;
+    units += r.U[mi];
+  }
+  int P = 1;
+  // (a cut stage has fewer than kSplitUnits units and, since P stops growing
+  // once units * P reaches kSplitUnits, fewer than 2 kSplitUnits items)
+  while (P < kMaxPieces && P < r.CH && units * P < kSplitUnits) ++P;
+  r.P = P;
+  r.inv_p = (65536u + (uint32_t)P - 1u) / (uint32_t)P;
+  r.total = units * P;
+  r.pad[0] = r.pad[1] = 0;
+  return fits;
 }
-__device__ __forceinline__ void lc_mat(LoadCursor& lc, const ChainMatDesc* mats, int cw) {
-  const BlockRange br = block_range(cload(&mats[lc.m].n) >> (6 - lc.clog));
-  lc.i = cw;
-  lc.count = br.count;
-  lc.ch = 0;
-  const uint64_t u = (uint64_t)(br.u0 + cw);
-  lc.pw = reinterpret_cast<const unsigned char*>(cload(&mats[lc.m].packed)) + u * lc.unit_w;
-  lc.ps = reinterpret_cast<const unsigned char*>(cload(&mats[lc.m].scales)) + u * lc.unit_s;
-  lc.pb = reinterpret_cast<const unsigned char*>(cload(&mats[lc.m].biases)) + u * lc.unit_s;
+__device__ __forceinline__ void stage_info(StageInfo& si, const ChainLds& L, int s) {
+  const StageRec& r = L.st[s];
+  si.s = s;
+  si.G = ufl(r.G);
+  si.CH = ufl(r.CH);
+  si.nm = ufl(r.nm);
+  si.mat_begin = ufl(r.mat_begin);
+  si.ragged = (ufl(r.flags) & kStageRagged) != 0;
+  si.P = ufl(r.P);
+  si.inv_p = (uint32_t)ufl((int)r.inv_p);
+  si.total = ufl(r.total);
+#pragma unroll
+  for (int mi = 0; mi < kMaxMatsPerStage; ++mi) si.U[mi] = ufl(r.U[mi]);
 }
-// move to the first position at or after the cursor that holds a slot of this
-// wave (lc.s == num_stages: none left)
-__device__ __forceinline__ void lc_seek(LoadCursor& lc, const ChainStageDesc* stages, const ChainMatDesc* mats,
-                                        int num_stages, int cw, int lane) {
-  while (lc.s < num_stages && lc.i >= lc.count) {
-    if (++lc.m < lc.m_end) {
-      lc_mat(lc, mats, cw);
-    } else if (++lc.s < num_stages) {
-      lc_stage(lc, stages, lane);
-      lc_mat(lc, mats, cw);
+struct Item {
+  int mi, u, p, ca, cb;
+};
+__device__ __forceinline__ void decode_item(const StageInfo& si, int i, Item& it) {
+  it.mi = 0;
+#pragma unroll
+  for (int mi = 0; mi < kMaxMatsPerStage - 1; ++mi) {
+    const int n = si.U[it.mi] * si.P;
+    if (i >= n) {
+      i -= n;
+      ++it.mi;
     }
   }
-}
-__device__ __forceinline__ void lc_issue(LoadCursor& lc, uint32_t dst, int lane, const ChainStageDesc* stages,
-                                         const ChainMatDesc* mats, int num_stages, int cw) {
-  const bool last = lc.ch == lc.CH - 1;
-  const uint32_t ow = last ? lc.lw_last : lc.lw + (uint32_t)(lc.ch * lc.LPR) * 16u;
-  const uint32_t os = last ? lc.ls_last : lc.ls + (uint32_t)(lc.ch * lc.LPR) * 2u;
-  dma16_s(lc.pw, ow, dst);
-  if (lane < 16) dma16_v((lane >= 8 ? lc.pb : lc.ps) + os, dst + 1024u);
-  if (++lc.ch == lc.CH) {
-    lc.ch = 0;
-    lc.i += kComputeWaves;
-    lc.pw += (uint64_t)lc.unit_w * kComputeWaves;
-    lc.ps += (uint64_t)lc.unit_s * kComputeWaves;
-    lc.pb += (uint64_t)lc.unit_s * kComputeWaves;
-    lc_seek(lc, stages, mats, num_stages, cw, lane);
-  }
+  it.mi = ufl(it.mi);
+  it.u = ufl((int)(((uint32_t)i * si.inv_p) >> 16));
+  it.p = ufl(i - it.u * si.P);
+  it.ca = ufl((int)(((uint32_t)(it.p * si.CH) * si.inv_p) >> 16));
+  it.cb = ufl((int)(((uint32_t)((it.p + 1) * si.CH) * si.inv_p) >> 16));
 }
 
-// Wait until every slot load older than the newest `younger` slots is
-// complete (two loads per slot; the counter completes in issue order).
-__device__ __forceinline__ void wait_slots(uint32_t younger) {
-  if (younger == (uint32_t)(kRingSlots - 2)) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (kRingSlots - 2)));
-  } else if (younger == (uint32_t)(kRingSlots - 1)) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (kRingSlots - 1)));
-  } else {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  }
-  compiler_fence();
+// Buffer descriptor of a raw byte range: loads at offsets at or past nbytes
+// return zero without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)nbytes, 0x00020000);
 }
 
-// Compute wave cw: consumes its slots in the order it loads them. Per pair of
-// chunks it waits for both slots, reads them (and the activations) from LDS,
-// refills the two freed buffers with the slots kRingSlots further on, and
-// only then does the arithmetic.
+// The slot a compute wave loads next: item i of stage si (the last item the
+// wave claimed) and its next chunk. Loads go through buffer descriptors of the
+// item's unit's codes, scales and biases, sized to the rows that exist: lanes
+// that run past a ragged row's end read the next row (given zero weight) or,
+// past the matrix, zeros. Wave-uniform except the lane offsets.
+struct LoadCursor {
+  StageInfo si;
+  int i;                                 // current item
+  int left;                              // its slots not yet loaded
+  __amdgpu_buffer_rsrc_t rw, rs, rb;     // the unit's codes, scales, biases
+  uint32_t vw, vs;                       // lane offsets of the next slot
+  uint32_t lw, ls;                       // lane offsets of chunk 0 (per stage)
+  bool done;                             // no slots left in the chain
+  uint32_t qh;                           // items the wave has claimed
+  bool fresh;                            // no item of this stage taken yet
+};
+
+// Lane (row r = t & 3, col c = t >> 2) loads the 16 bytes of codes of group
+// 16 ch + c of row r of the unit, and that group's scale and bias: chunk ch
+// adds 256 (codes) and 32 (scales) bytes to the lane's offset in the unit.
+__device__ __forceinline__ void lc_lanes(LoadCursor& lc, int lane) {
+  const int G = lc.si.G;
+  const int row = lane & 3, col = lane >> 2;
+  // (24-bit products: a full 32-bit multiply-add would be a 64-bit one whose
+  // unused high half can alias a register with a load in flight)
+  const uint32_t e = __umul24((uint32_t)row, (uint32_t)G) + (uint32_t)col;
+  lc.lw = e * 16u;
+  lc.ls = e * 2u;
+}
+// set up item lc.i of stage lc.si
+__device__ __forceinline__ void lc_item(LoadCursor& lc, const ChainLds& L) {
+  Item it;
+  decode_item(lc.si, lc.i, it);
+  const MatRec& mr = L.mt[lc.si.mat_begin + it.mi];
+  const int n = ufl(mr.n);
+  const int gu = unit_of(block_range((n + kUnitRows - 1) / kUnitRows), it.u);
+  const uint32_t rows = (uint32_t)min(kUnitRows, n - gu * kUnitRows);
+  const uint32_t row_w = (uint32_t)lc.si.G * 16u, row_s = (uint32_t)lc.si.G * 2u;
+  lc.rw = byte_range(reinterpret_cast<const unsigned char*>(ufl_ptr(mr.packed)) + (uint64_t)gu * kUnitRows * row_w, rows * row_w);
+  lc.rs = byte_range(reinterpret_cast<const unsigned char*>(ufl_ptr(mr.scales)) + (uint64_t)gu * kUnitRows * row_s, rows * row_s);
+  lc.rb = byte_range(reinterpret_cast<const unsigned char*>(ufl_ptr(mr.biases)) + (uint64_t)gu * kUnitRows * row_s, rows * row_s);
+  lc.vw = lc.lw + (uint32_t)it.ca * 256u;
+  lc.vs = lc.ls + (uint32_t)it.ca * 32u;
+  lc.left = ufl(it.cb - it.ca);
+}
+// claim the wave's next item (through the stages) and queue it for the
+// arithmetic, or queue the end
+__device__ __forceinline__ void lc_next_item(LoadCursor& lc, const ChainLds& L, ChainFlags& F, int num_stages, int cw,
+                                             int lane) {
+  while (true) {
+    // a wave's first item of a stage is its own (item cw); the rest are
+    // claimed in turn
+    uint32_t item = (uint32_t)cw;
+    if (lc.fresh) {
+      lc.fresh = false;
+    } else {
+      if (lane == 0) item = lds_add_rtn(&F.claim[lc.si.s], 1u);
+      item = kComputeWaves + (uint32_t)ufl((int)item);
+    }
+    uint32_t code;
+    if (item < (uint32_t)lc.si.total) {
+      lc.i = (int)item;
+      code = ((uint32_t)lc.si.s << 16) | item;
+    } else if (lc.si.s + 1 >= num_stages) {
+      // nothing left: empty ranges, whose loads return zeros without
+      // touching memory
+      lc.done = true;
+      lc.rw = lc.rs = lc.rb = byte_range(nullptr, 0u);
+      lc.left = 0x7FFFFFFF;
+      code = kQueueEnd;
+    } else {
+      stage_info(lc.si, L, lc.si.s + 1);
+      lc_lanes(lc, lane);
+      lc.fresh = true;
+      continue;
+    }
+    if (lane == 0) lds_put(&F.queue[cw][lc.qh % kQueueLen], code);
+    lc.qh = (uint32_t)ufl((int)(lc.qh + 1u));
+    if (!lc.done) lc_item(lc, L);
+    return;
+  }
+}
+// Issue the loads of the cursor's slot into d and advance (every step issues
+// the same three loads, which lets the compiler wait for exactly the slot it
+// is about to use).
+__device__ __forceinline__ void lc_load(LoadCursor& lc, Slot& d, int lane, const ChainLds& L, ChainFlags& F,
+                                        int num_stages, int cw) {
+  const q4_u32x4 w = __builtin_bit_cast(q4_u32x4, __builtin_amdgcn_raw_buffer_load_b128(lc.rw, (int)lc.vw, 0, 0));
+  d.w = make_uint4(w.x, w.y, w.z, w.w);
+  d.s = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(lc.rs, (int)lc.vs, 0, 0);
+  d.b = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(lc.rb, (int)lc.vs, 0, 0);
+  lc.vw += 256u;
+  lc.vs += 32u;
+  lc.left = ufl(lc.left - 1);
+  if (lc.left == 0) lc_next_item(lc, L, F, num_stages, cw, lane);
+}
+
 template <bool OUT_F32>
-__device__ __forceinline__ void compute_body(const ChainStageDesc* stages, const ChainMatDesc* mats, int num_stages,
+__device__ __forceinline__ void compute_body(int num_stages,
                                              int cw, ChainLds& L, ChainFlags& F, uint32_t* ws) {
   const int lane = threadIdx.x & 63;
-  const uint32_t ring = (uint32_t)ufl((int)(uint32_t)(uintptr_t)(Q4_LDS unsigned char*)&L.ring[cw][0][0]);
-  const unsigned char* myring = &L.ring[cw][0][0];
+  const int col = lane >> 2;
   LoadCursor lc;
-  lc.s = 0;
-  lc_stage(lc, stages, lane);
-  lc_mat(lc, mats, cw);
-  lc_seek(lc, stages, mats, num_stages, cw, lane);
-  uint32_t issued = 0, k = 0;  // slots issued / consumed
-  int ipos = 0, kpos = 0;      // their ring positions
-  for (; issued < (uint32_t)kRingSlots && lc.s < num_stages; ++issued) {
-    lc_issue(lc, ring + (uint32_t)ipos * kSlotBytes, lane, stages, mats, num_stages, cw);
-    ipos = ipos + 1 == kRingSlots ? 0 : ipos + 1;
-  }
-  for (int s = 0; s < num_stages; ++s) {
-    const Geo g = geo_of(stages + s);
-    const bool sync_out = cload(&stages[s].sync_outputs) != 0;
-    const int c = lane & (g.LPR - 1);
-    const int srow = lane >> g.clog;
-    const uint32_t sb_off = (uint32_t)(srow * g.LPR + c) * 2u;  // lane's bf16 in the slot's scales/biases
-    {  // activations of stage s
-      uint32_t spins = 0;
-      while (lds_geti(&F.x_stage) < s) {
-        __builtin_amdgcn_s_sleep(1);
-        if (lds_get(&F.abort) != 0u) return;
-        if (++spins > kSpinLimit) {
-          compute_fail(ws, F);
-          return;
-        }
-      }
+  lc.done = false;
+  lc.qh = 0;
+  lc.fresh = true;
+  stage_info(lc.si, L, 0);
+  lc_lanes(lc, lane);
+  lc_next_item(lc, L, F, num_stages, cw, lane);
+  Slot d[kRegRing];  // slots k .. k + kRegRing - 1 in flight (indexed only by unrolled constants)
+#pragma unroll
+  for (int j = 0; j < kRegRing; ++j) lc_load(lc, d[j], lane, L, F, num_stages, cw);
+
+  StageInfo si;      // the stage being computed (si.s == num_stages: done)
+  int i = 0;         // the item being computed
+  uint32_t qt = 0;   // items taken from the wave's queue
+  Item it;
+  int left = 0;      // its slots not yet computed
+  int gch = 0;       // first group of its next chunk
+  const uint32_t* x0 = nullptr;  // group col of chunk 0 of the stage's activations
+  float acc = 0.f;
+  bool stop = false;  // a wait timed out or another wave failed: finish without waiting
+
+  // stage si.s may start once its activations are in LDS (every wave of the
+  // grid has finished the stages before it)
+  auto enter_stage = [&]() {
+    uint32_t spins = 0;
+    while (!stop && lds_geti(&F.x_stage) < si.s) {
+      nap();
+      stop = lds_get(&F.abort) != 0u || ++spins > kSpinLimit;
     }
     compiler_fence();
-    const uint32_t* xb = L.x[s & 1];
-    for (int mi = 0; mi < g.num_mats; ++mi) {
-      const int m = g.mat_begin + mi;
-      const BlockRange br = block_range(cload(&mats[m].n) >> (6 - g.clog));
-      void* y = cload(&mats[m].y);
-      for (int i = cw; i < br.count; i += kComputeWaves) {
-        float acc = 0.f;
-        for (int ch = 0; ch < g.CH; ch += 2) {
-          const int n2 = g.CH - ch >= 2 ? 2 : 1;
-          wait_slots(issued - (k + (uint32_t)n2));
-          const int kpos1 = kpos + 1 == kRingSlots ? 0 : kpos + 1;
-          SlotRegs r0, r1;
-          read_slot(myring + kpos * kSlotBytes, xb + (ch * g.LPR + c) * kXWordsPerGroup, lane, sb_off, r0);
-          if (n2 == 2) read_slot(myring + kpos1 * kSlotBytes, xb + ((ch + 1) * g.LPR + c) * kXWordsPerGroup, lane, sb_off, r1);
-          lds_wait();  // the reads are complete: the buffers may be refilled
-          compiler_fence();
-          for (int j = 0; j < n2; ++j) {
-            if (lc.s < num_stages) {
-              lc_issue(lc, ring + (uint32_t)ipos * kSlotBytes, lane, stages, mats, num_stages, cw);
-              ipos = ipos + 1 == kRingSlots ? 0 : ipos + 1;
-              ++issued;
-            }
-          }
-          acc = slot_dot(r0, ch * g.LPR + c < g.G, acc);  // lanes past G in a ragged last chunk weigh zero
-          if (n2 == 2) acc = slot_dot(r1, (ch + 1) * g.LPR + c < g.G, acc);
-          k += (uint32_t)n2;
-          kpos = n2 == 2 ? (kpos1 + 1 == kRingSlots ? 0 : kpos1 + 1) : kpos1;
-        }
-        const float tot = dpp_sum(acc, g.LPR);
-        if (c == g.LPR - 1) {
-          const int row = (br.u0 + i) * g.RPI + srow;
-          if constexpr (OUT_F32) {
-            coh_store(static_cast<uint32_t*>(y) + row, __float_as_uint(tot));
-          } else {
-            coh_store16(static_cast<uint16_t*>(y) + row, f32_to_bf16_rne(tot));
-          }
-        }
+    x0 = L.x[si.s & 1] + col * kXWordsPerGroup;
+  };
+  // move to the wave's next claimed item, closing the stages it leaves (every
+  // stage is counted once, after the wave's rows of it are in LDS) and
+  // entering the next ones
+  auto next_item = [&]() {
+    const uint32_t code = lds_get(&F.queue[cw][qt % kQueueLen]);
+    qt = (uint32_t)ufl((int)(qt + 1u));
+    const int s_next = code == kQueueEnd ? num_stages : (int)(code >> 16);
+    while (si.s < s_next) {
+      compiler_fence();
+      if (lane == 0) lds_add(&F.done_total, 1u);
+      wake_block();
+      if (si.s + 1 >= num_stages) {
+        si.s = num_stages;
+        return;
       }
+      stage_info(si, L, si.s + 1);
+      enter_stage();
     }
-    // stage done; outputs read by a later stage must be visible first
-    if (sync_out) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    i = (int)(code & 0xFFFFu);
+    decode_item(si, i, it);
+    left = ufl(it.cb - it.ca);
+    gch = ufl(it.ca * kChunkGroups);
+  };
+  // the item's partial row sums are complete: a whole unit's rows go to LDS;
+  // a piece's go to its place, and the wave that completes a unit's last
+  // piece adds the pieces up in piece order
+  auto end_item = [&]() {
+    const float tot = row_sum(acc);
+    acc = 0.f;
+    if (si.P == 1) {
+      stage_rows(F, it.mi, it.u, lane, tot);
+      return;
+    }
+    // pieces of unit j of the stage are items j P .. j P + P - 1
+    const int j = ufl((int)(((uint32_t)i * si.inv_p) >> 16));
+    if (lane < kUnitRows) *(volatile Q4_LDS float*)&F.parts[i][lane] = tot;
     compiler_fence();
-    if (lane == 0) lds_add(&F.done_total, 1u);
+    uint32_t old = 0;
+    if (lane == 0) old = lds_add_rtn(&F.pieces_done[j], 1u);
+    old = (uint32_t)__builtin_amdgcn_readfirstlane((int)old);
+    if (old == (uint32_t)si.P - 1u) {
+      compiler_fence();
+      float sum = 0.f;
+      for (int p = 0; p < si.P; ++p) sum += *(volatile Q4_LDS float*)&F.parts[j * si.P + p][lane & 3];
+      stage_rows(F, it.mi, it.u, lane, sum);
+      if (lane == 0) lds_put(&F.pieces_done[j], 0u);
+    }
+  };
+  // consume the slot in d (the current item's next chunk), then refill d
+  // with the slot kRegRing further on
+  auto step = [&](Slot& d) {
+    // lanes past G (only in the last chunk of a ragged row) weigh zero
+    const bool live = !si.ragged || gch + col < si.G;
+    const float term = slot_term(d, x0 + gch * kXWordsPerGroup, live);
+    asm volatile("" ::"v"(term));
+    lc_load(lc, d, lane, L, F, num_stages, cw);
+    acc += term;
+    gch = ufl(gch + kChunkGroups);
+    left = ufl(left - 1);
+    if (left == 0) {
+      end_item();
+      next_item();
+    }
+  };
+
+  stage_info(si, L, 0);
+  enter_stage();
+  next_item();
+  // (the steps are written out, with one exit test after the last: every
+  // path round the loop then issues the same loads in the same order, which
+  // keeps the compiler's count of loads in flight exact. Steps past the
+  // wave's last item change nothing: left never returns to zero, the loads
+  // read empty ranges and the x reads stay inside the last stage's buffer.)
+  while (true) {
+    step(d[0]);
+    step(d[1]);
+    step(d[2]);
+#if Q4_CHAIN_REG_RING >= 6
+    step(d[3]);
+    step(d[4]);
+#endif
+#if Q4_CHAIN_REG_RING >= 8
+    step(d[5]);
+    step(d[6]);
+#endif
+#if Q4_CHAIN_REG_RING >= 12
+    step(d[7]);
+    step(d[8]);
+    step(d[9]);
+    step(d[10]);
+#endif
+#if Q4_CHAIN_REG_RING >= 16
+    step(d[11]);
+    step(d[12]);
+    step(d[13]);
+    step(d[14]);
+#endif
+    step(d[kRegRing - 1]);
+    if (si.s >= num_stages || stop) break;
   }
+  if (stop && lds_get(&F.abort) == 0u) compute_fail(F);
 }
+
 template <bool OUT_F32>
-__device__ __forceinline__ void compute_run(const ChainStageDesc* stages, const ChainMatDesc* mats, int num_stages,
+__device__ __forceinline__ void compute_run(int num_stages,
                                             int cw, ChainLds& L, ChainFlags& F, uint32_t* ws) {
-  compute_body<OUT_F32>(stages, mats, num_stages, cw, L, F, ws);
-  // no load into this block's LDS may outlive the wave (an aborted wave may
-  // leave some in flight)
+  compute_body<OUT_F32>(num_stages, cw, L, F, ws);
+  // loads still in flight (the refills past the wave's last slot, or an
+  // aborted wave's) complete before the wave ends
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
 // ---------------------------------------------------------------- service
 
 // Load a stage's activations into an LDS buffer, re-paired, with group sums;
-// groups past G up to LPR*CH are zero. Coherent loads when an earlier stage of
+// groups past G up to 16 CH are zero. Coherent loads when an earlier stage of
 // this launch wrote them.
 __device__ __forceinline__ void service_load_x(const Geo& g, const void* x, bool coherent, uint32_t* dst_buf) {
+  constexpr int kBatch = 3;  // groups per lane whose loads are in flight together
   const int lane = threadIdx.x & 63;
-  const int gpad = g.LPR * g.CH;
+  const int gpad = kChunkGroups * g.CH;
   const uint64_t* x64 = static_cast<const uint64_t*>(x);
-  for (int grp = lane; grp < gpad; grp += 64) {
-    uint32_t* dst = dst_buf + grp * kXWordsPerGroup;
-    if (grp < g.G) {
-      uint64_t q[8];
-      if (coherent) {
+  for (int base = 0; base < gpad; base += 64 * kBatch) {
+    uint64_t q[kBatch][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = coh_load64(x64 + (int64_t)grp * 8 + i);
-      } else {
+    for (int b = 0; b < kBatch; ++b) {
+      const int grp = base + 64 * b + lane;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = gload(x64 + (int64_t)grp * 8 + i);
+      for (int i = 0; i < 8; ++i) q[b][i] = 0u;
+      if (grp < g.G) {
+        if (coherent) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) q[b][i] = coh_load64(x64 + (int64_t)grp * 8 + i);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) q[b][i] = gload(x64 + (int64_t)grp * 8 + i);
+        }
       }
-      float xs = 0.f;
+    }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint4 e;
-        e.x = (uint32_t)q[2 * j];
-        e.y = (uint32_t)(q[2 * j] >> 32);
-        e.z = (uint32_t)q[2 * j + 1];
-        e.w = (uint32_t)(q[2 * j + 1] >> 32);
-        uint32_t p02, p46, p13, p57;
-        x_to_pairs(e, p02, p46, p13, p57);
-        *reinterpret_cast<uint4*>(dst + 4 * j) = make_uint4(p02, p46, p13, p57);
-        xs += x_sum8(e);
+    for (int b = 0; b < kBatch; ++b) {
+      const int grp = base + 64 * b + lane;
+      if (grp < gpad) {
+        // (groups past G are zero)
+        uint32_t* dst = dst_buf + grp * kXWordsPerGroup;
+        float xs = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint4 e;
+          e.x = (uint32_t)q[b][2 * j];
+          e.y = (uint32_t)(q[b][2 * j] >> 32);
+          e.z = (uint32_t)q[b][2 * j + 1];
+          e.w = (uint32_t)(q[b][2 * j + 1] >> 32);
+          uint32_t p02, p46, p13, p57;
+          x_to_pairs(e, p02, p46, p13, p57);
+          *reinterpret_cast<uint4*>(dst + 4 * j) = make_uint4(p02, p46, p13, p57);
+          xs += x_sum8(e);
+        }
+        dst[16] = __float_as_uint(xs);
       }
-      dst[16] = __float_as_uint(xs);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(dst + 4 * j) = make_uint4(0u, 0u, 0u, 0u);
-      dst[16] = 0u;
     }
   }
   lds_wait();
@@ -503,6 +754,7 @@ __device__ __forceinline__ bool service_fail(uint32_t* ws, ChainFlags& F, uint32
     coh_store(ws + kWsStatus, code);
     lds_put(&F.abort, 1u);
   }
+  wake_block();
   return false;
 }
 
@@ -527,13 +779,18 @@ __device__ __forceinline__ bool service_start(uint32_t* ws, ChainFlags& F, GridS
 // Grid barrier: arrive on this XCD's L2 counter; the XCD's last arrival
 // publishes the XCD's flag device-wide; every block waits until all XCDs'
 // flags (one 64-byte line) carry this epoch.
-__device__ __forceinline__ bool service_barrier(uint32_t* ws, ChainFlags& F, GridSync& gs) {
+// (in two halves: work issued between arrive and wait overlaps the wait)
+__device__ __forceinline__ void service_arrive(uint32_t* ws, GridSync& gs) {
   const int lane = threadIdx.x & 63;
   const uint32_t e = ++gs.epoch;
   uint32_t old = 0;
   if (lane == 0) old = l2_add(ws + kWsXcnt + 32 * gs.xcc, 1u);
   old = __shfl(old, 0);
   if ((old + 1u) % gs.per == 0u && lane == 0) coh_store(ws + kWsGflag + gs.xcc, e);
+}
+__device__ __forceinline__ bool service_wait(uint32_t* ws, ChainFlags& F, GridSync& gs) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t e = gs.epoch;
   uint32_t spins = 0;
   while (true) {
     bool mine = true;
@@ -544,34 +801,80 @@ __device__ __forceinline__ bool service_barrier(uint32_t* ws, ChainFlags& F, Gri
   return true;
 }
 
-__device__ __forceinline__ void service_run(const ChainStageDesc* stages, int num_stages, ChainLds& L,
-                                            ChainFlags& F, uint32_t* ws, uint32_t nxcc) {
+// Store stage s's rows from LDS: entry (mi, u, r) is row 4 unit + r of the
+// stage's matrix mi, for the block's local unit u.
+template <bool OUT_F32>
+__device__ __forceinline__ void service_store(const ChainLds& L, int s, ChainFlags& F) {
+  const int lane = threadIdx.x & 63;
+  const Geo g = geo_of(L.st[s]);
+  for (int mi = 0; mi < g.num_mats; ++mi) {
+    const MatRec& mr = L.mt[g.mat_begin + mi];
+    const int n = ufl(mr.n);
+    const BlockRange br = block_range((n + kUnitRows - 1) / kUnitRows);
+    void* y = ufl_ptr(mr.y);
+    for (int e = lane; e < br.count * kUnitRows; e += 64) {
+      const int u = e >> 2, r = e & 3;
+      const int orow = unit_of(br, u) * kUnitRows + r;
+      if (orow < n) {
+        const float v = *(volatile Q4_LDS float*)&F.out[mi][u][r];
+        if constexpr (OUT_F32) {
+          coh_store(static_cast<uint32_t*>(y) + orow, __float_as_uint(v));
+        } else {
+          coh_store16(static_cast<uint16_t*>(y) + orow, f32_to_bf16_rne(v));
+        }
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ int stage_flags(const ChainLds& L, int s) { return ufl(L.st[s].flags); }
+__device__ __forceinline__ const uint16_t* stage_x(const ChainLds& L, int s) { return ufl_ptr(L.st[s].x); }
+
+template <bool OUT_F32>
+__device__ __forceinline__ void service_run(int num_stages, ChainLds& L, ChainFlags& F, uint32_t* ws, uint32_t nxcc) {
   GridSync gs;
   if (!service_start(ws, F, gs, nxcc)) return;
-  service_load_x(geo_of(stages), cload(&stages[0].x), false, L.x[0]);
-  if (num_stages > 1 && cload(&stages[1].x_internal) == 0)
-    service_load_x(geo_of(stages + 1), cload(&stages[1].x), false, L.x[1]);
+  service_load_x(geo_of(L.st[0]), stage_x(L, 0), false, L.x[0]);
   compiler_fence();
   if ((threadIdx.x & 63) == 0) lds_puti(&F.x_stage, 0);
+  wake_block();
+  if (num_stages > 1 && !(stage_flags(L, 1) & kStageXInternal))
+    service_load_x(geo_of(L.st[1]), stage_x(L, 1), false, L.x[1]);
   for (int s = 0; s < num_stages; ++s) {
     uint32_t spins = 0;
     while ((int)(lds_get(&F.done_total) - (uint32_t)(kComputeWaves * (s + 1))) < 0) {
-      __builtin_amdgcn_s_sleep(1);
-      if (lds_get(&F.abort) != 0u) return;
-      if (++spins > kSpinLimit) {
+      nap();
+      if (lds_get(&F.abort) != 0u || ++spins > kSpinLimit) {
         service_fail(ws, F, 1u);
         return;
       }
     }
-    if (s + 1 >= num_stages) break;
-    if (!service_barrier(ws, F, gs)) return;
-    if (cload(&stages[s + 1].x_internal) != 0)
-      service_load_x(geo_of(stages + s + 1), cload(&stages[s + 1].x), true, L.x[(s + 1) & 1]);
+    compiler_fence();
+    if (s + 1 >= num_stages) {
+      service_store<OUT_F32>(L, s, F);
+      break;
+    }
+    if (stage_flags(L, s) & kStageSyncOut) {
+      // outputs read by a later stage must be visible before the barrier
+      service_store<OUT_F32>(L, s, F);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      service_arrive(ws, gs);
+    } else {
+      // arrive first: the stores then overlap the wait instead of delaying
+      // the arrival
+      service_arrive(ws, gs);
+      service_store<OUT_F32>(L, s, F);
+    }
+    if (!service_wait(ws, F, gs)) return;
+    if (stage_flags(L, s + 1) & kStageXInternal)
+      service_load_x(geo_of(L.st[s + 1]), stage_x(L, s + 1), true, L.x[(s + 1) & 1]);
     compiler_fence();
     if ((threadIdx.x & 63) == 0) lds_puti(&F.x_stage, s + 1);
-    // every compute wave has finished stage s, so its buffer is free
-    if (s + 2 < num_stages && cload(&stages[s + 2].x_internal) == 0)
-      service_load_x(geo_of(stages + s + 2), cload(&stages[s + 2].x), false, L.x[s & 1]);
+    wake_block();
+    // every compute wave has finished stage s, so its buffer is free:
+    // activations no stage writes are fetched while stage s + 1 runs
+    if (s + 2 < num_stages && !(stage_flags(L, s + 2) & kStageXInternal))
+      service_load_x(geo_of(L.st[s + 2]), stage_x(L, s + 2), false, L.x[s & 1]);
   }
 }
 
@@ -585,27 +888,50 @@ chain_kernel(const ChainHeader* __restrict__ plan, uint32_t* __restrict__ ws, ui
   ChainLds& L = *reinterpret_cast<ChainLds*>(lds_raw);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
+  if (threadIdx.x < kSplitUnits) F.pieces_done[threadIdx.x] = 0u;
+  for (int e = threadIdx.x; e < kTabStages; e += blockDim.x) F.claim[e] = 0u;
   if (threadIdx.x == 0) {
     F.done_total = 0u;
     F.x_stage = -1;
     F.abort = 0u;
-    // the plan must be one this library encoded
-    const bool ok = coh_load(ws + kWsStatus) == 0u && cload(&plan->magic) == kChainMagic &&
-                    cload(&plan->num_stages) > 0 && cload(&plan->num_mats) > 0 &&
-                    gridDim.x <= (unsigned)kChainMaxBlocks && nxcc >= 1u && nxcc <= (unsigned)kMaxXcc;
+    F.misfit = 0u;
+    // the plan must be one this library encoded, and fit the LDS tables
+    const int ns = cload(&plan->num_stages), nm = cload(&plan->num_mats);
+    const bool ok = coh_load(ws + kWsStatus) == 0u && cload(&plan->magic) == kChainMagic && ns > 0 &&
+                    ns <= kTabStages && nm > 0 && nm <= kTabMats && gridDim.x <= (unsigned)kChainMaxBlocks &&
+                    nxcc >= 1u && nxcc <= (unsigned)kMaxXcc;
     F.go = ok ? 1u : 0u;
     if (!ok && blockIdx.x == 0 && coh_load(ws + kWsStatus) == 0u) coh_store(ws + kWsStatus, 2u);
   }
   __syncthreads();
   if (F.go == 0u) return;
   const int num_stages = cload(&plan->num_stages);
+  const int num_mats = cload(&plan->num_mats);
   const ChainStageDesc* stages = reinterpret_cast<const ChainStageDesc*>(plan + 1);
   const ChainMatDesc* mats = reinterpret_cast<const ChainMatDesc*>(stages + num_stages);
+  // the plan into LDS, one lane per stage and per matrix
+  for (int s = threadIdx.x; s < num_stages; s += blockDim.x)
+    if (!build_stage_rec(L.st[s], stages + s, mats)) lds_put(&F.misfit, 1u);
+  for (int m = threadIdx.x; m < num_mats; m += blockDim.x) {
+    MatRec r;
+    r.packed = mats[m].packed;
+    r.scales = mats[m].scales;
+    r.biases = mats[m].biases;
+    r.y = mats[m].y;
+    r.n = mats[m].n;
+    r.pad[0] = r.pad[1] = r.pad[2] = 0;
+    L.mt[m] = r;
+  }
+  __syncthreads();
+  if (F.misfit != 0u) {
+    if (threadIdx.x == 0 && blockIdx.x == 0 && coh_load(ws + kWsStatus) == 0u) coh_store(ws + kWsStatus, 2u);
+    return;
+  }
 
   if (wave == kServiceWave) {
-    service_run(stages, num_stages, L, F, ws, nxcc);
+    service_run<OUT_F32>(num_stages, L, F, ws, nxcc);
   } else {
-    compute_run<OUT_F32>(stages, mats, num_stages, wave - 1, L, F, ws);
+    compute_run<OUT_F32>(num_stages, wave - 1, L, F, ws);
   }
 }
 

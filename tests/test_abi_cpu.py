@@ -163,9 +163,10 @@ def test_chain_stage_geometry_and_dependencies():
                                  q4._ChainMatrix(A16, A16, A16, Y2, 1024))
     assert lib.q4_chain_encode(ctypes.byref(stages), 3, ctypes.byref(mats), 3, 0, ctypes.byref(buf), nb) == q4.Q4_OK
     # G, c_log2, CH at byte offsets 8, 12, 16; x_internal 28, sync_outputs 32
-    assert [_stage_field(buf, 0, o) for o in (8, 12, 16)] == [128, 6, 2]    # 64 lanes x 2 chunks
-    assert [_stage_field(buf, 1, o) for o in (8, 12, 16)] == [352, 5, 11]   # 32 lanes x 11 chunks, no idle lane
-    assert [_stage_field(buf, 2, o) for o in (8, 12, 16)] == [88, 3, 11]    # 8 lanes x 11 chunks
+    # (16 lanes per row, chunks of 16 groups: CH = ceil(G / 16))
+    assert [_stage_field(buf, 0, o) for o in (8, 12, 16)] == [128, 4, 8]
+    assert [_stage_field(buf, 1, o) for o in (8, 12, 16)] == [352, 4, 22]
+    assert [_stage_field(buf, 2, o) for o in (8, 12, 16)] == [88, 4, 6]     # ragged last chunk
     assert [_stage_field(buf, s, 28) for s in range(3)] == [0, 1, 0]
     assert [_stage_field(buf, s, 32) for s in range(3)] == [1, 0, 0]
 
