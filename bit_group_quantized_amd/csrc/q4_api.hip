@@ -307,7 +307,7 @@ bool chain_ready_on_device() {
 // activations padded to 16 * CH groups.
 bool plan_stage(int64_t G, int* c_log2, int* CH) {
   const int64_t ch = ceil_div(G, q4k::kChunkGroups);
-  if (G % 8 != 0 || ch * q4k::kChunkGroups > q4k::kChainMaxGroups) return false;
+  if (ch * q4k::kChunkGroups > q4k::kChainMaxGroups) return false;
   *c_log2 = 4;
   *CH = static_cast<int>(ch);
   return true;
@@ -352,8 +352,7 @@ q4_status q4_chain_encode(const q4_chain_stage* stages, int32_t num_stages,
       if (m.n >= (1 << 22)) return Q4_ERR_UNSUPPORTED;
       // each block stages its rows of a matrix in LDS
       if (ceil_div(ceil_div(m.n, q4k::kUnitRows), device_cu_count()) > q4k::kStageUnits) return Q4_ERR_UNSUPPORTED;
-      // scales/biases are read in 16-byte pieces of 8 groups
-      if ((st.k / 32) % 8 != 0 || !aligned(m.scales, 16) || !aligned(m.biases, 16)) return Q4_ERR_UNSUPPORTED;
+      if (!aligned(m.scales, 16) || !aligned(m.biases, 16)) return Q4_ERR_UNSUPPORTED;
       // a stage may not write its own input
       if (ranges_overlap(st.x, 2 * st.k, m.y, ybytes * m.n)) return Q4_ERR_UNSUPPORTED;
     }

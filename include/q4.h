@@ -150,15 +150,22 @@ q4_status q4_multilinear_step(const uint16_t* x, int64_t m, const uint32_t* pack
  * (64-byte aligned), then call q4_chain_run() as often as needed. The plan
  * holds the device pointers given at encode time; it stays valid while those
  * buffers live. Each stage's k must satisfy the q4_gemv limits; every
- * stage needs >= 1 matrix, all of that stage's k.
+ * stage needs >= 1 matrix, all of that stage's k. Limits of the executor
+ * (Q4_ERR_UNSUPPORTED from q4_chain_encode otherwise): at most 256 stages and
+ * 512 matrices per chain (the block copies the plan into LDS), at most 4
+ * matrices per stage, k <= 12288, n < 2^22, at most 128
+ * units of 4 rows of one matrix per block (n <= 512 x the number of compute
+ * units), scales and biases 16-byte aligned, and no stage's output may
+ * overlap its own input.
  *
  * Workspace: Q4_CHAIN_WORKSPACE_BYTES of device memory, 128-byte aligned,
  * zero-filled once by the caller before its first use; the executor leaves it
  * ready for the next call. Calls sharing one workspace must not overlap in
  * time (use one workspace per stream). Word 0 of the workspace is a status:
- * 0 = ok, 1 = a stage barrier timed out (the launch ended early, outputs
- * undefined), 2 = the plan buffer is not a valid plan. A nonzero status stays
- * set until the caller clears the workspace again.
+ * 0 = ok, 1 = a wait timed out (the launch ended early, outputs undefined),
+ * 2 = the plan buffer is not a valid plan, 3 = a block did not run on the XCD
+ * the launch order implies (the barrier's per-XCD counters need it). A
+ * nonzero status stays set until the caller clears the workspace again.
  */
 #define Q4_CHAIN_WORKSPACE_BYTES 131328 /* 256 + 128 per block, up to 1024 blocks */
 

@@ -35,8 +35,12 @@ def test_independent_stages(out_dtype):
         (1024, [1024, 37]),
         (4096, [11264, 11264]),
         (2816, [1024]),
-        (256, [300]),    # 16 lanes per row, 4 rows per unit
-        (6400, [128]),   # 32 lanes x 7 chunks: a ragged last chunk
+        (256, [300]),    # 8 groups: one chunk, half of its lanes past the row end
+        (6400, [128]),   # 200 groups: 13 chunks, the last one ragged
+        (96, [40]),      # 3 groups
+        (4128, [70]),    # 129 groups: an odd group count
+        (11264, [37]),   # 10 units: blocks with one unit cut into pieces of 22 chunks
+        (12288, [64]),   # the widest activation the executor stages
     ]
     stages, refs = [], []
     item = 0
