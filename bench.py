@@ -117,6 +117,53 @@ def make_temporal_chain(seed: int = 0, layers: int = workloads.TEMPORAL_LAYERS,
     return Chain(stages, out_dtype)
 
 
+def make_depformer(seed: int = 0, device=None):
+    """The Depformer's 6 layers x 7 linears, each stored as one stacked packed tensor
+    [16 * out, in] (weights drawn on the host, seeded, quantized and packed by q4_pack
+    on the GPU). Returns {(layer, name): Q4Matrix}."""
+    import torch
+
+    import bit_group_quantized_amd as q4
+    from bit_group_quantized_amd.step import Q4Matrix
+
+    mats = {}
+    for layer in range(workloads.DEP_LAYERS):
+        lin = workloads.depformer_layer()
+        ws = workloads.weights_many([(seed, workloads.CFG_DEPFORMER, layer, li.item, workloads.DEP_STEPS * li.n, li.k)
+                                     for li in lin])
+        for li, w in zip(lin, ws):
+            wt = torch.from_numpy(w).to(device)
+            mats[(layer, li.name)] = Q4Matrix(*q4.q4_pack(wt))
+            del wt
+        del ws
+    torch.cuda.synchronize()
+    return mats
+
+
+def make_depformer_frame(mats, seed: int = 0, out_dtype=None, device=None):
+    """One frame of the Depformer as one chain: 16 codebook steps x 6 layers x 4
+    stages, each matrix the step's row slice of its stacked tensor; activations
+    drawn per (step, layer, stage)."""
+    import torch
+
+    from bit_group_quantized_amd.step import Chain, Stage
+
+    out_dtype = out_dtype or torch.bfloat16
+    lin = workloads.depformer_layer()
+    stages = []
+    for step in range(workloads.DEP_STEPS):
+        for layer in range(workloads.DEP_LAYERS):
+            by_stage = {}
+            for li in lin:
+                by_stage.setdefault(li.stage, []).append(li)
+            for st in sorted(by_stage):
+                k = by_stage[st][0].k
+                x = workloads.activations(seed, workloads.CFG_DEPFORMER, layer, 1000 + 4 * step + st, 1, k)[0]
+                xt = torch.from_numpy(x.view(np.int16)).to(device).view(torch.bfloat16)
+                stages.append(Stage(xt, [mats[(layer, li.name)].rows(step * li.n, li.n) for li in by_stage[st]]))
+    return Chain(stages, out_dtype)
+
+
 def cpu_baseline(seed: int, budget_s: float, sample_layers: int = 2):
     """The oracle (plain C, OpenMP over rows) on a bounded sample of the step: the
     first ``sample_layers`` temporal layers (7 GEMVs each, M=1), quantized once
@@ -158,6 +205,13 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--mode", choices=("chain", "launches"), default="chain")
+    ap.add_argument("--workload", choices=("step", "depformer", "gemm", "gemv"), default="step",
+                    help="step: the 32-layer temporal step at M=1 (the headline); depformer: one "
+                         "Depformer frame (16 codebook steps x 6 layers, M=1); gemm: the temporal "
+                         "step's 224 matrices against X [M, k] (q4_gemm_small, --m rows); gemv: "
+                         "one 4096x4096 GEMV, M=1, over 64 distinct matrices in turn (671 MB, past "
+                         "the 256 MB last-level cache)")
+    ap.add_argument("--m", type=int, default=4, help="rows of X for --workload gemm")
     ap.add_argument("--layers", type=int, default=workloads.TEMPORAL_LAYERS,
                     help="temporal layers (32 = the full step; fewer only for profiling runs)")
     ap.add_argument("--seed", type=int, default=0)
@@ -193,6 +247,8 @@ def main(argv=None) -> int:
         print(json.dumps({"calibrate_copy_bytes_read": 4 * n, "calibrate_copy_bytes_written": 4 * n,
                           "dispatches": 5}), flush=True)
         return 0
+    if args.workload != "step":
+        return bench_other(args, dev)
     chain = make_temporal_chain(args.seed, args.layers, device=dev)
     wbytes = chain.weight_bytes()
     launches_per_step = 1 if args.mode == "chain" else chain.num_matrices()
@@ -271,6 +327,160 @@ def main(argv=None) -> int:
     if not args.no_cpu:
         log("[bench] cpu baseline ...")
         result["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def time_replays(run, steps: int, warmup: int):
+    """HIP events on the launch stream around each of `steps` calls of run()."""
+    import torch
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        run()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return ev[0].elapsed_time(ev[-1]) / steps, per
+
+
+def graph_of(fn):
+    """Capture fn (a sequence of launches on the current stream) into a HIP graph."""
+    import torch
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # warm the kernels outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def bench_other(args, dev) -> int:
+    """The Depformer frame and the small-GEMM step (one JSON line each); no
+    oracle baseline and no byte counters for these."""
+    import torch
+
+    import bit_group_quantized_amd as q4
+
+    if args.workload == "gemv":
+        from bit_group_quantized_amd.step import Q4Matrix
+
+        copies, n, k = 64, workloads.HIDDEN, workloads.HIDDEN
+        mats = []
+        for c in range(copies):
+            w = workloads.weights(args.seed, workloads.CFG_GEMV, 0, c, n, k)
+            wt = torch.from_numpy(w).to(dev)
+            mats.append(Q4Matrix(*q4.q4_pack(wt)))
+            del wt
+        x = workloads.activations(args.seed, workloads.CFG_GEMV, 0, 0, 1, k)[0]
+        xt = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        ys = [torch.empty((n,), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+
+        def calls():
+            for mt, y in zip(mats, ys):
+                q4.q4_gemv(xt, mt.packed, mt.scales, mt.biases, out=y)
+
+        g = graph_of(calls)
+        ms, per = time_replays(g.replay, args.steps, args.warmup)
+        wbytes = sum(mt.nbytes() for mt in mats)
+        per_call_us = ms * 1e3 / copies
+        achieved = (wbytes / copies) / (per_call_us * 1e-6) / 1e9
+        result = {
+            "metric": "packed-weight GB/s (% HBM peak) + us per 4096x4096 GEMV, M=1",
+            "value": round(achieved, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "us_per_gemv": round(per_call_us, 2), "pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "gemv_4096x4096_m1", "n": n, "k": k, "m": 1, "group": 32, "copies": copies,
+                       "packed_bytes_per_gemv": wbytes // copies, "executor": "graph of 64 launches"},
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "traffic_unit": "bytes per launch",
+                         "kernel": "gemv_kernel", "bytes_per_launch": wbytes // copies},
+        }
+        print(json.dumps(result), flush=True)
+        return 0
+    if args.workload == "depformer":
+        mats = make_depformer(args.seed, dev)
+        chain = make_depformer_frame(mats, args.seed, device=dev)
+        wbytes = chain.weight_bytes()
+        if args.mode == "chain":
+            chain.prepare_chain()
+            run, launches, kernel = chain.run_chain, 1, "chain_kernel"
+        else:
+            # one q4_multilinear_step call per linear, on the stacked tensor
+            lin = workloads.depformer_layer()
+            calls = []
+            si = 0
+            for step in range(workloads.DEP_STEPS):
+                for layer in range(workloads.DEP_LAYERS):
+                    by_stage = {}
+                    for li in lin:
+                        by_stage.setdefault(li.stage, []).append(li)
+                    for st in sorted(by_stage):
+                        stage = chain.stages[si]
+                        si += 1
+                        for li, y in zip(by_stage[st], stage.outs):
+                            calls.append((stage.x, mats[(layer, li.name)], step, y))
+
+            def run_calls():
+                for x, mt, step, y in calls:
+                    q4.q4_multilinear_step(x, mt.packed, mt.scales, mt.biases, workloads.DEP_STEPS, step, out=y)
+
+            g = graph_of(run_calls)
+            run, launches, kernel = g.replay, len(calls), "gemv_kernel"
+        ms, per = time_replays(run, args.steps, args.warmup)
+        if args.mode == "chain" and chain.chain_status() != 0:
+            print(f"chain executor reported status {chain.chain_status()}", file=sys.stderr)
+            return 1
+        config = {"workload": "depformer_frame_m1", "layers": workloads.DEP_LAYERS, "codebook_steps": workloads.DEP_STEPS,
+                  "dim": workloads.DEP_DIM, "ffn": workloads.DEP_FFN, "m": 1, "group": 32,
+                  "packed_bytes_per_frame": wbytes, "executor": args.mode, "launches_per_frame": launches,
+                  "stages_per_frame": len(chain.stages)}
+        unit_name = "frame"
+    else:
+        if not 1 <= args.m <= 16:
+            print("--m must be in 1..16", file=sys.stderr)
+            return 2
+        chain = make_temporal_chain(args.seed, args.layers, device=dev)
+        wbytes = chain.weight_bytes()
+        xs = [torch.randn((args.m, st.x.numel()), device=dev, generator=torch.Generator(device=dev).manual_seed(si))
+              .to(torch.bfloat16) for si, st in enumerate(chain.stages)]
+        outs = [[torch.empty((args.m, mt.n), dtype=torch.bfloat16, device=dev) for mt in st.mats] for st in chain.stages]
+
+        def calls():
+            for x, st, ys in zip(xs, chain.stages, outs):
+                for mt, y in zip(st.mats, ys):
+                    q4.q4_gemm_small(x, mt.packed, mt.scales, mt.biases, out=y)
+
+        g = graph_of(calls)
+        run, launches, kernel = g.replay, chain.num_matrices(), ("gemv_kernel" if args.m <= 4 else "gemm_mfma_kernel")
+        ms, per = time_replays(run, args.steps, args.warmup)
+        config = {"workload": f"small_gemm_m{args.m}_temporal_step", "layers": args.layers, "hidden": workloads.HIDDEN,
+                  "ffn": workloads.FFN, "m": args.m, "group": 32, "packed_bytes_per_step": wbytes,
+                  "executor": "launches", "launches_per_step": launches}
+        unit_name = "step"
+    gbs = wbytes / (ms * 1e-3) / 1e9
+    achieved = (wbytes / launches) / ((ms / launches) * 1e-3) / 1e9
+    result = {
+        "metric": f"packed-weight GB/s (% HBM peak) + us per {unit_name}",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        f"ms_per_{unit_name}": round(ms, 4), f"us_per_{unit_name}": round(ms * 1e3, 1),
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": config,
+        f"{unit_name}_ms_p10_p50_p90": [round(float(np.percentile(per, q)), 4) for q in (10, 50, 90)],
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "traffic_unit": "bytes per launch",
+                     "kernel": kernel, "bytes_per_launch": wbytes // launches},
+    }
     print(json.dumps(result), flush=True)
     return 0
 

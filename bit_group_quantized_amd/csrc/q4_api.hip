@@ -42,9 +42,11 @@ struct GemvPlan {
   int blocks;
 };
 
-constexpr int kGemvU = 8;
+// weight rows each lane keeps in flight: 8 for one activation row; 4 when
+// up to 4 activation rows hold their slices in registers too
+constexpr int gemv_u(int mv) { return mv == 1 ? 8 : 4; }
 
-bool plan_gemv(int64_t n, int64_t G, GemvPlan* p) {
+bool plan_gemv(int64_t n, int64_t G, int mv, GemvPlan* p) {
   int best_c = 0, best_s = 0;
   int64_t best_waste = -1;
   const int cs[4] = {64, 32, 16, 8};
@@ -60,7 +62,7 @@ bool plan_gemv(int64_t n, int64_t G, GemvPlan* p) {
     }
   }
   if (best_waste < 0) return false;
-  const int rows_iter = (64 / best_c) * kGemvU;
+  const int rows_iter = (64 / best_c) * gemv_u(mv);
   // Aim for >= 2 blocks per CU; each block covers at least one iteration.
   const int64_t target_blocks = 2 * kNumCU;
   int64_t rpb = ceil_div(n, target_blocks);
@@ -73,33 +75,41 @@ bool plan_gemv(int64_t n, int64_t G, GemvPlan* p) {
   return true;
 }
 
-template <int C>
-void launch_gemv_c(const GemvPlan& p, bool f32, const uint16_t* x, const uint32_t* packed,
+template <int C, int MV>
+void launch_gemv_c(const GemvPlan& p, bool f32, const uint16_t* x, int64_t k, const uint32_t* packed,
                    const uint16_t* scales, const uint16_t* biases, int n, int G, void* y,
                    hipStream_t st) {
   const dim3 grid(p.blocks), block(64 * p.waves);
+  constexpr int U = gemv_u(MV);
   if (f32)
-    hipLaunchKernelGGL((q4k::gemv_kernel<C, kGemvU, true>), grid, block, 0, st, x, packed, scales,
-                       biases, n, G, p.rows_per_block, y);
+    hipLaunchKernelGGL((q4k::gemv_kernel<C, U, MV, true>), grid, block, 0, st, x, k, packed, scales,
+                       biases, n, G, p.rows_per_block, y, (int64_t)n);
   else
-    hipLaunchKernelGGL((q4k::gemv_kernel<C, kGemvU, false>), grid, block, 0, st, x, packed, scales,
-                       biases, n, G, p.rows_per_block, y);
+    hipLaunchKernelGGL((q4k::gemv_kernel<C, U, MV, false>), grid, block, 0, st, x, k, packed, scales,
+                       biases, n, G, p.rows_per_block, y, (int64_t)n);
+}
+
+template <int MV>
+q4_status run_gemv_mv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                      const uint16_t* biases, int64_t n, int64_t k, void* y, q4_out_dtype dt,
+                      hipStream_t st) {
+  const int64_t G = k / 32;
+  GemvPlan p;
+  if (!plan_gemv(n, G, MV, &p)) return Q4_ERR_UNSUPPORTED;
+  const bool f32 = dt == Q4_OUT_F32;
+  switch (p.c) {
+    case 64: launch_gemv_c<64, MV>(p, f32, x, k, packed, scales, biases, (int)n, (int)G, y, st); break;
+    case 32: launch_gemv_c<32, MV>(p, f32, x, k, packed, scales, biases, (int)n, (int)G, y, st); break;
+    case 16: launch_gemv_c<16, MV>(p, f32, x, k, packed, scales, biases, (int)n, (int)G, y, st); break;
+    default: launch_gemv_c<8, MV>(p, f32, x, k, packed, scales, biases, (int)n, (int)G, y, st); break;
+  }
+  return launch_status();
 }
 
 q4_status run_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
                    const uint16_t* biases, int64_t n, int64_t k, void* y, q4_out_dtype dt,
                    hipStream_t st) {
-  const int64_t G = k / 32;
-  GemvPlan p;
-  if (!plan_gemv(n, G, &p)) return Q4_ERR_UNSUPPORTED;
-  const bool f32 = dt == Q4_OUT_F32;
-  switch (p.c) {
-    case 64: launch_gemv_c<64>(p, f32, x, packed, scales, biases, (int)n, (int)G, y, st); break;
-    case 32: launch_gemv_c<32>(p, f32, x, packed, scales, biases, (int)n, (int)G, y, st); break;
-    case 16: launch_gemv_c<16>(p, f32, x, packed, scales, biases, (int)n, (int)G, y, st); break;
-    default: launch_gemv_c<8>(p, f32, x, packed, scales, biases, (int)n, (int)G, y, st); break;
-  }
-  return launch_status();
+  return run_gemv_mv<1>(x, packed, scales, biases, n, k, y, dt, st);
 }
 
 // ---- small GEMM launch (MFMA): S waves of GS groups each, T row tiles of 16.
@@ -117,10 +127,19 @@ void launch_gemm_gs(int waves, bool f32, const uint16_t* x, int m, const uint32_
                        scales, biases, n, G, y);
 }
 
+// Small GEMM: up to 4 activation rows share one pass of the GEMV kernel
+// (each loaded group dequantized once, dotted with every row); more rows go
+// to the MFMA kernel, one 16-row tile per group.
 q4_status run_gemm_small(const uint16_t* x, int64_t m, const uint32_t* packed,
                          const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
                          void* y, q4_out_dtype dt, hipStream_t st) {
-  if (m == 1) return run_gemv(x, packed, scales, biases, n, k, y, dt, st);
+  switch (m) {
+    case 1: return run_gemv_mv<1>(x, packed, scales, biases, n, k, y, dt, st);
+    case 2: return run_gemv_mv<2>(x, packed, scales, biases, n, k, y, dt, st);
+    case 3: return run_gemv_mv<3>(x, packed, scales, biases, n, k, y, dt, st);
+    case 4: return run_gemv_mv<4>(x, packed, scales, biases, n, k, y, dt, st);
+    default: break;
+  }
   const int64_t G = k / 32;
   const bool f32 = dt == Q4_OUT_F32;
   constexpr int T = 1;

@@ -69,8 +69,8 @@ constexpr uint32_t kQueueEnd = 0xFFFFFFFFu;
 constexpr int kChunkGroups = 16;  // groups of each row per slot
 constexpr int kXWordsPerGroup = 20;   // 16 re-paired words + sum + pad (bank spread)
 constexpr int kChainMaxBlocks = 1024;
-constexpr int kTabStages = 256;   // stages of a chain (the plan is copied into LDS)
-constexpr int kTabMats = 512;     // matrices of a chain
+constexpr int kTabStages = 384;   // stages of a chain (the plan is copied into LDS)
+constexpr int kTabMats = 768;     // matrices of a chain
 constexpr int kMaxXcc = 16;
 constexpr uint32_t kSpinLimit = 1u << 22;
 

@@ -196,27 +196,30 @@ __global__ void __launch_bounds__(256) unpack_kernel(const uint32_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// GEMV, one activation row.
+// GEMV against MV activation rows (MV = 1: the GEMV; up to 4 rows share one
+// weight stream).
 //
 // Mapping: a wave is split into 64/C row slots of C lanes; lane (slot, c) of
 // wave w owns group g = w*C + c of the input dimension for every row it
-// visits, so its 32 activations live in 16 registers (re-paired bf16) for the
-// whole kernel and the weight stream needs no shared memory. A block has
-// S = ceil(G/C) waves covering all groups; each load instruction of a wave
-// reads C consecutive 16-byte groups of one row per slot (C*16 contiguous
-// bytes). Each lane handles U rows per iteration (U independent loads in
-// flight), reduces each row's partial over its C lanes with butterfly
-// shuffles, and the S waves' partials are added in fixed order through LDS.
-template <int C, int U, bool OUT_F32>
-__global__ void __launch_bounds__(1024) gemv_kernel(const uint16_t* __restrict__ x,
+// visits, so its 32 activations of each of the MV rows live in 16 registers
+// each (re-paired bf16) for the whole kernel and the weight stream needs no
+// shared memory. A block has S = ceil(G/C) waves covering all groups; each
+// load instruction of a wave reads C consecutive 16-byte groups of one row per
+// slot (C*16 contiguous bytes). Each lane handles U weight rows per iteration
+// (U independent loads in flight), dequantizes each loaded group once and
+// takes its dot product with every activation row, reduces each partial over
+// its C lanes with butterfly shuffles, and the S waves' partials are added in
+// fixed order through LDS.
+template <int C, int U, int MV, bool OUT_F32>
+__global__ void __launch_bounds__(1024) gemv_kernel(const uint16_t* __restrict__ x, int64_t x_stride,
                                                      const uint32_t* __restrict__ packed,
                                                      const uint16_t* __restrict__ scales,
                                                      const uint16_t* __restrict__ biases, int n,
                                                      int G, int rows_per_block,
-                                                     void* __restrict__ y) {
+                                                     void* __restrict__ y, int64_t y_stride) {
   constexpr int RPI = 64 / C;   // row slots per wave
-  constexpr int ROWS = RPI * U; // rows per iteration
-  __shared__ float red[16][ROWS];
+  constexpr int ROWS = RPI * U; // weight rows per iteration
+  __shared__ float red[16][ROWS * MV];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
@@ -225,19 +228,23 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const uint16_t* __restrict__
   const int g = wave * C + c;
   const bool gv = g < G;
 
-  uint32_t xp[16];
-  float xsum = 0.f;
-  if (gv) {
-    const uint4* xs = reinterpret_cast<const uint4*>(x + (int64_t)g * 32);
+  uint32_t xp[MV][16];
+  float xsum[MV];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint4 e = xs[j];
-      x_to_pairs(e, xp[4 * j + 0], xp[4 * j + 1], xp[4 * j + 2], xp[4 * j + 3]);
-      xsum += x_sum8(e);
+  for (int v = 0; v < MV; ++v) {
+    xsum[v] = 0.f;
+    if (gv) {
+      const uint4* xs = reinterpret_cast<const uint4*>(x + v * x_stride + (int64_t)g * 32);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint4 e = xs[j];
+        x_to_pairs(e, xp[v][4 * j + 0], xp[v][4 * j + 1], xp[v][4 * j + 2], xp[v][4 * j + 3]);
+        xsum[v] += x_sum8(e);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) xp[v][j] = 0u;
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) xp[j] = 0u;
   }
 
   const int row_begin = blockIdx.x * rows_per_block;
@@ -259,35 +266,43 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const uint16_t* __restrict__
         bv[u] = 0.f;
       }
     }
-    float part[U];
+    float part[U][MV];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float acc = group_dot(wv[u], xp);
-      part[u] = fmaf(sv[u], acc, bv[u] * xsum);
+#pragma unroll
+      for (int v = 0; v < MV; ++v) part[u][v] = fmaf(sv[u], group_dot(wv[u], xp[v]), bv[u] * xsum[v]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
-      for (int off = C / 2; off > 0; off >>= 1) part[u] += __shfl_xor(part[u], off, 64);
+      for (int v = 0; v < MV; ++v) {
+#pragma unroll
+        for (int off = C / 2; off > 0; off >>= 1) part[u][v] += __shfl_xor(part[u][v], off, 64);
+      }
     }
     if (c == 0) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) red[wave][u * RPI + slot] = part[u];
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int v = 0; v < MV; ++v) red[wave][v * ROWS + u * RPI + slot] = part[u][v];
+      }
     }
     __syncthreads();
-    if (threadIdx.x < ROWS) {
-      const int rr = threadIdx.x;
+    // (a block may have fewer threads than ROWS * MV outputs)
+    for (int idx = threadIdx.x; idx < ROWS * MV; idx += blockDim.x) {
+      const int rr = idx % ROWS;
+      const int v = idx / ROWS;
       float s = 0.f;
-      for (int w2 = 0; w2 < nwaves; ++w2) s += red[w2][rr];
+      for (int w2 = 0; w2 < nwaves; ++w2) s += red[w2][idx];
       const int row = r0 + rr;
-      if (row < row_end) store_out<OUT_F32>(y, row, s);
+      if (row < row_end) store_out<OUT_F32>(y, v * y_stride + row, s);
     }
     __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
-// Small GEMM, M in [2, 16] activation rows, on MFMA.
+// Small GEMM, M in [5, 16] activation rows, on MFMA.
 //
 // One v_mfma_f32_16x16x32_bf16 covers exactly one group (32 inputs) for 16
 // activation rows (A operand, zero-padded past m) and 16 weight rows (B

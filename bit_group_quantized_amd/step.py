@@ -40,6 +40,12 @@ class Q4Matrix:
     def nbytes(self) -> int:
         return self.packed.numel() * 4 + self.scales.numel() * 2 + self.biases.numel() * 2
 
+    def rows(self, start: int, count: int) -> "Q4Matrix":
+        """Rows [start, start + count) as views of the same storage (the
+        Depformer's per-step slice of a stacked tensor: a pointer offset)."""
+        return Q4Matrix(self.packed[start:start + count], self.scales[start:start + count],
+                        self.biases[start:start + count])
+
 
 @dataclass
 class Stage:

@@ -151,8 +151,8 @@ q4_status q4_multilinear_step(const uint16_t* x, int64_t m, const uint32_t* pack
  * holds the device pointers given at encode time; it stays valid while those
  * buffers live. Each stage's k must satisfy the q4_gemv limits; every
  * stage needs >= 1 matrix, all of that stage's k. Limits of the executor
- * (Q4_ERR_UNSUPPORTED from q4_chain_encode otherwise): at most 256 stages and
- * 512 matrices per chain (the block copies the plan into LDS), at most 4
+ * (Q4_ERR_UNSUPPORTED from q4_chain_encode otherwise): at most 384 stages and
+ * 768 matrices per chain (the block copies the plan into LDS), at most 4
  * matrices per stage, k <= 12288, n < 2^22, at most 128
  * units of 4 rows of one matrix per block (n <= 512 x the number of compute
  * units), scales and biases 16-byte aligned, and no stage's output may

@@ -143,14 +143,14 @@ def test_chain_encode_validation_and_layout():
     s6, m6 = _chain(k=96)  # 3 groups: one chunk, mostly past the row end
     assert lib.q4_chain_encode(ctypes.byref(s6), 2, ctypes.byref(m6), 2, 0, ctypes.byref(buf), nb) == q4.Q4_OK
     # the LDS copy of the plan bounds stages and matrices
-    big = lib.q4_chain_plan_bytes(257, 257)
+    big = lib.q4_chain_plan_bytes(385, 385)
     bigbuf = (ctypes.c_uint8 * big)()
-    s9, m9 = _chain(n_stages=257)
-    assert lib.q4_chain_encode(ctypes.byref(s9), 257, ctypes.byref(m9), 257, 0, ctypes.byref(bigbuf), big) == q4.Q4_ERR_UNSUPPORTED
-    ok = lib.q4_chain_plan_bytes(256, 256)
+    s9, m9 = _chain(n_stages=385)
+    assert lib.q4_chain_encode(ctypes.byref(s9), 385, ctypes.byref(m9), 385, 0, ctypes.byref(bigbuf), big) == q4.Q4_ERR_UNSUPPORTED
+    ok = lib.q4_chain_plan_bytes(384, 384)
     okbuf = (ctypes.c_uint8 * ok)()
-    s10, m10 = _chain(n_stages=256)
-    assert lib.q4_chain_encode(ctypes.byref(s10), 256, ctypes.byref(m10), 256, 0, ctypes.byref(okbuf), ok) == q4.Q4_OK
+    s10, m10 = _chain(n_stages=384)
+    assert lib.q4_chain_encode(ctypes.byref(s10), 384, ctypes.byref(m10), 384, 0, ctypes.byref(okbuf), ok) == q4.Q4_OK
     s5, m5 = _chain(packed=0)
     assert lib.q4_chain_encode(ctypes.byref(s5), 2, ctypes.byref(m5), 2, 0, ctypes.byref(buf), nb) == q4.Q4_ERR_NULL
     s7, m7 = _chain(y=A16)  # a stage writing its own input

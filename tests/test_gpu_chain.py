@@ -159,3 +159,44 @@ def test_full_temporal_step_sampled_layers():
                 assert np.array_equal(bf16_bits_np(m.biases), B)
                 ref = oracle.matmul(x, P, S, B, li.k)[0]
                 assert oracle.floored_rel_err(out_np(y), ref) <= TOL_BF16, (layer, li.name)
+
+
+def test_depformer_frame_chain_sampled_steps():
+    """One Depformer frame as the benchmark runs it: 16 codebook steps x 6
+    layers x 4 stages in one persistent launch, every matrix the step's row
+    slice of its stacked packed tensor. Layers 0 and 5 are rebuilt on the host
+    for codebook steps 0, 7 and 15: the stacked weights are compared bit for
+    bit, the outputs against the oracle on the step's rows."""
+    import bench
+
+    seed = 0
+    dev = torch.device("cuda:0")
+    mats = bench.make_depformer(seed, dev)
+    chain = bench.make_depformer_frame(mats, seed, device=dev)
+    assert len(chain.stages) == workloads.DEP_STEPS * workloads.DEP_LAYERS * 4
+    chain.run_chain()
+    chain.run_chain()
+    torch.cuda.synchronize()
+    assert chain.chain_status() == 0
+    lin = workloads.depformer_layer()
+    by_stage = {}
+    for li in lin:
+        by_stage.setdefault(li.stage, []).append(li)
+    for layer in (0, 5):
+        quant = {}
+        for li in lin:
+            w = workloads.weights(seed, workloads.CFG_DEPFORMER, layer, li.item, workloads.DEP_STEPS * li.n, li.k)
+            quant[li.name] = oracle.quantize(w)
+            m = mats[(layer, li.name)]
+            assert np.array_equal(packed_np(m.packed), quant[li.name][0])
+        for step in (0, 7, 15):
+            for si, st in enumerate(sorted(by_stage)):
+                stage = chain.stages[(step * workloads.DEP_LAYERS + layer) * 4 + si]
+                k = by_stage[st][0].k
+                x = workloads.activations(seed, workloads.CFG_DEPFORMER, layer, 1000 + 4 * step + st, 1, k)
+                assert np.array_equal(bf16_bits_np(stage.x), x[0])
+                for li, y in zip(by_stage[st], stage.outs):
+                    P, S, B = quant[li.name]
+                    rows = slice(step * li.n, (step + 1) * li.n)
+                    ref = oracle.matmul(x, P[rows], S[rows], B[rows], k)[0]
+                    assert oracle.floored_rel_err(out_np(y), ref) <= TOL_BF16, (layer, step, li.name)
