@@ -228,6 +228,32 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const uint16_t* __restrict__
   const int g = wave * C + c;
   const bool gv = g < G;
 
+  const int row_begin = blockIdx.x * rows_per_block;
+  const int row_end = min(n, row_begin + rows_per_block);
+  const int64_t wpr = (int64_t)G * 4;  // words per row
+  // with one activation row, the first iteration's weight loads go out
+  // before the activation loads, so the two memory round trips overlap (with
+  // more rows the registers held across the activation loads cost more than
+  // the overlap gains)
+  uint4 wv[U];
+  float sv[U], bv[U];
+  auto load_rows = [&](int r0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = r0 + u * RPI + slot;
+      if (gv && row < row_end) {
+        wv[u] = *reinterpret_cast<const uint4*>(packed + (int64_t)row * wpr + 4 * g);
+        sv[u] = load_bf16_word(scales + (int64_t)row * G + g);
+        bv[u] = load_bf16_word(biases + (int64_t)row * G + g);
+      } else {
+        wv[u] = make_uint4(0u, 0u, 0u, 0u);
+        sv[u] = 0.f;
+        bv[u] = 0.f;
+      }
+    }
+  };
+  if constexpr (MV == 1) load_rows(row_begin);
+
   uint32_t xp[MV][16];
   float xsum[MV];
 #pragma unroll
@@ -247,25 +273,8 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const uint16_t* __restrict__
     }
   }
 
-  const int row_begin = blockIdx.x * rows_per_block;
-  const int row_end = min(n, row_begin + rows_per_block);
-  const int64_t wpr = (int64_t)G * 4;  // words per row
   for (int r0 = row_begin; r0 < row_end; r0 += ROWS) {
-    uint4 wv[U];
-    float sv[U], bv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int row = r0 + u * RPI + slot;
-      if (gv && row < row_end) {
-        wv[u] = *reinterpret_cast<const uint4*>(packed + (int64_t)row * wpr + 4 * g);
-        sv[u] = load_bf16_word(scales + (int64_t)row * G + g);
-        bv[u] = load_bf16_word(biases + (int64_t)row * G + g);
-      } else {
-        wv[u] = make_uint4(0u, 0u, 0u, 0u);
-        sv[u] = 0.f;
-        bv[u] = 0.f;
-      }
-    }
+    if (MV != 1 || r0 != row_begin) load_rows(r0);
     float part[U][MV];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
