@@ -212,6 +212,10 @@ def main(argv=None) -> int:
                          "one 4096x4096 GEMV, M=1, over 64 distinct matrices in turn (671 MB, past "
                          "the 256 MB last-level cache)")
     ap.add_argument("--m", type=int, default=4, help="rows of X for --workload gemm")
+    ap.add_argument("--dependent", action="store_true",
+                    help="step: every stage's activation is the previous stage's first output (q -> o "
+                         "-> gate/up -> down -> next q): each stage stores its outputs before the "
+                         "barrier and the next stage loads them after it")
     ap.add_argument("--layers", type=int, default=workloads.TEMPORAL_LAYERS,
                     help="temporal layers (32 = the full step; fewer only for profiling runs)")
     ap.add_argument("--seed", type=int, default=0)
@@ -250,6 +254,11 @@ def main(argv=None) -> int:
     if args.workload != "step":
         return bench_other(args, dev)
     chain = make_temporal_chain(args.seed, args.layers, device=dev)
+    if args.dependent:
+        # (the sizes line up: q, o and down give 4096 outputs, gate 11264)
+        for prev, st in zip(chain.stages, chain.stages[1:]):
+            assert prev.outs[0].numel() == st.x.numel()
+            st.x = prev.outs[0]
     wbytes = chain.weight_bytes()
     launches_per_step = 1 if args.mode == "chain" else chain.num_matrices()
 
@@ -311,7 +320,8 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "temporal_step_m1" if full else f"temporal_{args.layers}_layers_m1",
+        "config": {"workload": ("temporal_step_m1" if full else f"temporal_{args.layers}_layers_m1")
+                   + ("_dependent" if args.dependent else ""),
                    "layers": args.layers, "hidden": workloads.HIDDEN, "ffn": workloads.FFN, "m": 1,
                    "group": 32, "weights_per_step": sum(li.n * li.k for li in workloads.temporal_layer()) * args.layers,
                    "packed_bytes_per_step": wbytes, "executor": args.mode,
@@ -319,7 +329,7 @@ def main(argv=None) -> int:
         "step_ms_p10_p50_p90": [round(float(np.percentile(per, q)), 4) for q in (10, 50, 90)],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": chain_traffic_bytes(full) if args.mode == "chain" else None,
+                     "traffic": chain_traffic_bytes(full and not args.dependent) if args.mode == "chain" else None,
                      "traffic_unit": "bytes per launch",
                      "kernel": "chain_kernel" if args.mode == "chain" else "gemv_kernel",
                      "bytes_per_launch": wbytes // launches_per_step},
