@@ -14,7 +14,7 @@
 // device memory afterwards. The waves have two roles that meet only through
 // LDS words:
 //  - waves 1..kComputeWaves compute. A stage's rows are cut into units of 4
-//    rows, dealt round-robin to the blocks; a block's units (or pieces of
+//    rows, dealt to the blocks in contiguous runs; a block's units (or pieces of
 //    them, when a stage has few units per block) are its items. A compute
 //    wave takes its own item of each stage, then claims further items from a
 //    per-stage counter, so waves that run faster take more. A slot is one
@@ -261,21 +261,22 @@ __device__ __forceinline__ T* ufl_ptr(T* p) {
                               ((uintptr_t)(uint32_t)ufl((int)(uint32_t)(a >> 32)) << 32));
 }
 
-// Units (4 consecutive rows) of a matrix are dealt to the blocks round-robin:
-// block b's local unit i is unit b + i * gridDim.x. The grid thus streams a
-// dense window of consecutive units at a time (HBM delivers markedly more
-// to such a sweep than to one contiguous range per block).
+// Units (4 consecutive rows) of a matrix are dealt to the blocks in
+// contiguous runs: block b takes units [u0, u0 + count), the first
+// nunits % gridDim.x blocks one more than the others (measured ~1% faster on
+// the temporal step than dealing units round-robin).
 struct BlockRange {
   int u0, count;  // first unit, units of this block
 };
 __device__ __forceinline__ BlockRange block_range(int nunits) {
   const int nb = (int)gridDim.x, b = (int)blockIdx.x;
   BlockRange r;
-  r.u0 = b;
-  r.count = b < nunits ? (nunits - 1 - b) / nb + 1 : 0;
+  const int q = nunits / nb, rem = nunits - q * nb;
+  r.u0 = b * q + min(b, rem);
+  r.count = q + (b < rem ? 1 : 0);
   return r;
 }
-__device__ __forceinline__ int unit_of(const BlockRange& br, int i) { return br.u0 + i * (int)gridDim.x; }
+__device__ __forceinline__ int unit_of(const BlockRange& br, int i) { return br.u0 + i; }
 
 
 // s_waitcnt immediate that waits for the vector-memory counter only
@@ -358,7 +359,7 @@ __device__ __forceinline__ void compute_fail(ChainFlags& F) {
 }
 
 // Work of one block in one stage. The stage's matrices, in order, contribute
-// U[mi] units each (the block's round-robin share); every unit is cut into P
+// U[mi] units each (the block's share); every unit is cut into P
 // pieces of consecutive chunks, piece p covering chunks [p CH / P,
 // (p + 1) CH / P). Item i of the stage is (matrix, unit, piece) in that
 // order. Compute wave w takes item w of every stage, then claims further items
