@@ -42,9 +42,9 @@ struct GemvPlan {
   int blocks;
 };
 
-// weight rows each lane keeps in flight: 8 for one activation row; 4 when
+// weight rows each lane keeps in flight: 8 for one activation row; 2 when
 // up to 4 activation rows hold their slices in registers too
-constexpr int gemv_u(int mv) { return mv == 1 ? 8 : 4; }
+constexpr int gemv_u(int mv) { return mv == 1 ? 8 : 2; }
 
 bool plan_gemv(int64_t n, int64_t G, int mv, GemvPlan* p) {
   int best_c = 0, best_s = 0;
@@ -68,6 +68,10 @@ bool plan_gemv(int64_t n, int64_t G, int mv, GemvPlan* p) {
   int64_t rpb = ceil_div(n, target_blocks);
   rpb = ceil_div(rpb, rows_iter) * rows_iter;
   if (rpb < rows_iter) rpb = rows_iter;
+  // a block's rows are addressed through 32-bit buffer ranges
+  const int64_t max_rpb = ((int64_t)INT32_MAX / (G * 16)) / rows_iter * rows_iter;
+  if (max_rpb < rows_iter) return false;
+  if (rpb > max_rpb) rpb = max_rpb;
   p->c = best_c;
   p->waves = best_s;
   p->rows_per_block = static_cast<int>(rpb);

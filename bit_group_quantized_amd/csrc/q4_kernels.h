@@ -235,21 +235,32 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const uint16_t* __restrict__
   // before the activation loads, so the two memory round trips overlap (with
   // more rows the registers held across the activation loads cost more than
   // the overlap gains)
+  // Loads go through buffer descriptors of the block's rows: a lane past the
+  // last row or past G gets an offset outside the range and reads zeros, so
+  // every lane issues the same loads with no branch (a branch whose other
+  // side zeroes the same registers makes the compiler wait for each load
+  // before the next one is issued).
+  const int nrows = max(0, row_end - row_begin);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(packed + (int64_t)row_begin * wpr), 0, (int)(nrows * wpr * 4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(scales + (int64_t)row_begin * G), 0, (int)(nrows * G * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(biases + (int64_t)row_begin * G), 0, (int)(nrows * G * 2), 0x00020000);
   uint4 wv[U];
   float sv[U], bv[U];
   auto load_rows = [&](int r0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int row = r0 + u * RPI + slot;
-      if (gv && row < row_end) {
-        wv[u] = *reinterpret_cast<const uint4*>(packed + (int64_t)row * wpr + 4 * g);
-        sv[u] = load_bf16_word(scales + (int64_t)row * G + g);
-        bv[u] = load_bf16_word(biases + (int64_t)row * G + g);
-      } else {
-        wv[u] = make_uint4(0u, 0u, 0u, 0u);
-        sv[u] = 0.f;
-        bv[u] = 0.f;
-      }
+      const int lr = r0 - row_begin + u * RPI + slot;  // row within the block
+      const bool ok = gv && lr < nrows;
+      const uint32_t ow = ok ? (uint32_t)(lr * wpr + 4 * g) * 4u : 0xFFFFFFF0u;
+      const uint32_t os = ok ? (uint32_t)(lr * G + g) * 2u : 0xFFFFFFF0u;
+      typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+      const v4u w = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)ow, 0, 0));
+      wv[u] = make_uint4(w.x, w.y, w.z, w.w);
+      sv[u] = bf16_to_f32((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)os, 0, 0));
+      bv[u] = bf16_to_f32((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, (int)os, 0, 0));
     }
   };
   if constexpr (MV == 1) load_rows(row_begin);
