@@ -122,7 +122,11 @@ void launch_gemm_gs(int waves, bool f32, const uint16_t* x, int m, const uint32_
                     const uint16_t* scales, const uint16_t* biases, int n, int G, void* y,
                     hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(ceil_div(n, 16 * T))), block(64 * waves);
-  const size_t shmem = static_cast<size_t>(waves) * T * 256 * sizeof(float);
+  // the waves' partial tiles, then each wave's code staging (2 batches of
+  // KB groups x 16 rows per row tile, rows padded by 16 bytes)
+  constexpr int KB = 4;
+  const size_t shmem = static_cast<size_t>(waves) * T * 256 * sizeof(float) +
+                       static_cast<size_t>(waves) * 2 * T * 16 * (KB * 4 + 4) * sizeof(uint32_t);
   if (f32)
     hipLaunchKernelGGL((q4k::gemm_mfma_kernel<GS, T, true>), grid, block, shmem, st, x, m, packed,
                        scales, biases, n, G, y);
@@ -147,14 +151,14 @@ q4_status run_gemm_small(const uint16_t* x, int64_t m, const uint32_t* packed,
   const int64_t G = k / 32;
   const bool f32 = dt == Q4_OUT_F32;
   constexpr int T = 1;
-  const int gss[4] = {8, 16, 24, 32};
-  for (int i = 0; i < 4; ++i) {
+  // (24 groups per wave would spill registers)
+  const int gss[3] = {8, 16, 32};
+  for (int i = 0; i < 3; ++i) {
     const int64_t waves = ceil_div(G, gss[i]);
     if (waves > 16) continue;
     switch (gss[i]) {
       case 8: launch_gemm_gs<8, T>((int)waves, f32, x, (int)m, packed, scales, biases, (int)n, (int)G, y, st); break;
       case 16: launch_gemm_gs<16, T>((int)waves, f32, x, (int)m, packed, scales, biases, (int)n, (int)G, y, st); break;
-      case 24: launch_gemm_gs<24, T>((int)waves, f32, x, (int)m, packed, scales, biases, (int)n, (int)G, y, st); break;
       default: launch_gemm_gs<32, T>((int)waves, f32, x, (int)m, packed, scales, biases, (int)n, (int)G, y, st); break;
     }
     return launch_status();

@@ -342,7 +342,7 @@ __global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restr
                                                           const uint16_t* __restrict__ scales,
                                                           const uint16_t* __restrict__ biases,
                                                           int n, int G, void* __restrict__ y) {
-  extern __shared__ float red_dyn[];  // [nwaves][T][4][64]
+  extern __shared__ float red_dyn[];  // [nwaves][T][4][64], then each wave's code staging
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
@@ -352,16 +352,29 @@ __global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restr
   const int gcount = max(0, min(G - g0, GS));
   const int64_t K = (int64_t)G * 32;
 
-  u32x4_t a[GS];
+  // All loads go through buffer descriptors: lanes past m, G or n get an
+  // offset outside the range and read zeros, so the loads carry no branch
+  // and the compiler can keep many in flight.
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, (int)(m * K * 2), 0x00020000);
+  auto x_load = [&](int i) {
+    const bool ok = i < gcount && r16 < m;
+    const uint32_t off = ok ? (uint32_t)(((int64_t)r16 * K + (int64_t)(g0 + i) * 32 + 8 * kb) * 2) : 0xFFFFFFF0u;
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0));
+  };
+  auto x_pairs = [](const u32x4_t e4) {
+    uint32_t p02, p46, p13, p57;
+    x_to_pairs(make_uint4(e4.x, e4.y, e4.z, e4.w), p02, p46, p13, p57);
+    return u32x4_t{p02, p46, p13, p57};
+  };
+  // Up to 16 groups per wave keep their activation tile in registers for the
+  // whole kernel; wider waves load it with each batch of weights instead
+  // (holding 24 or 32 tiles would spill).
+  constexpr bool kXReg = GS <= 16;
+  u32x4_t a[kXReg ? GS : 1];
+  if constexpr (kXReg) {
 #pragma unroll
-  for (int i = 0; i < GS; ++i) {
-    a[i] = u32x4_t{0u, 0u, 0u, 0u};
-    if (i < gcount && r16 < m) {
-      const uint4 e = *reinterpret_cast<const uint4*>(x + (int64_t)r16 * K + (int64_t)(g0 + i) * 32 + 8 * kb);
-      uint32_t p02, p46, p13, p57;
-      x_to_pairs(e, p02, p46, p13, p57);
-      a[i] = u32x4_t{p02, p46, p13, p57};
-    }
+    for (int i = 0; i < GS; ++i) a[i] = x_pairs(x_load(i));
   }
   const u32x4_t ones = u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const f32x4_t zero = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -371,27 +384,91 @@ __global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restr
 
   const int nbase = blockIdx.x * 16 * T;
   const int64_t wpr = (int64_t)G * 4;
+  const int tile_rows = max(0, min(16 * T, n - nbase));
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(packed + (int64_t)nbase * wpr), 0, (int)(tile_rows * wpr * 4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(scales + (int64_t)nbase * G), 0, (int)(tile_rows * G * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(biases + (int64_t)nbase * G), 0, (int)(tile_rows * G * 2), 0x00020000);
+  // Weight loads in batches of KB groups, one batch ahead of the arithmetic
+  // (written out so that every wait is for exactly the batch in use); groups
+  // past this wave's share read zeros (scale and bias 0: no term).
+  constexpr int KB = 4;
+  static_assert(GS % KB == 0, "group batches");
+  // Codes are loaded 16 bytes (one group of one row) per lane, lanes along a
+  // row's consecutive groups, and passed through a per-wave LDS staging area
+  // to the lanes whose MFMA operand they are (lane (row, kb) needs word kb of
+  // each group of its row). Staging rows are padded by 16 bytes so that the
+  // 64 word reads hit 64 different banks.
+  constexpr int kPieces = 16 * KB;                       // 16-byte pieces per batch and row tile
+  constexpr int kPerLane = (kPieces + 63) / 64;
+  constexpr int kRowWords = KB * 4 + 4;
+  uint32_t* stage = reinterpret_cast<uint32_t*>(red_dyn + nwaves * T * 256) + wave * (2 * T * 16 * kRowWords);
+  u32x4_t wq[2][T][kPerLane];
+  uint32_t sb[2][T][KB], bb[2][T][KB];
+  u32x4_t xb[2][kXReg ? 1 : KB];
+  auto load_batch = [&](int i0, int buf) {
 #pragma unroll
-  for (int i = 0; i < GS; ++i) {
-    if (i < gcount) {
-      const int g = g0 + i;
-      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a[i]);
+    for (int ii = 0; ii < KB; ++ii) {
+      if constexpr (!kXReg) xb[buf][ii] = x_load(i0 + ii);
+      const bool gok = i0 + ii < gcount;
+      const int g = g0 + i0 + ii;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const int lr = 16 * t + r16;  // row within the tile (the range ends at n)
+        const uint32_t os = gok ? (uint32_t)((lr * G + g) * 2) : 0xFFFFFFF0u;
+        sb[buf][t][ii] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)os, 0, 0);
+        bb[buf][t][ii] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, (int)os, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+#pragma unroll
+      for (int j = 0; j < kPerLane; ++j) {
+        const int pc = lane + 64 * j;
+        const int prow = pc / KB, pg = pc % KB;
+        const bool ok = pc < kPieces && i0 + pg < gcount;
+        const uint32_t ow = ok ? (uint32_t)(((16 * t + prow) * wpr + 4 * (g0 + i0 + pg)) * 4) : 0xFFFFFFF0u;
+        wq[buf][t][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)ow, 0, 0));
+      }
+    }
+  };
+  load_batch(0, 0);
+#pragma unroll
+  for (int i0 = 0; i0 < GS; i0 += KB) {
+    const int buf = (i0 / KB) & 1;
+    if (i0 + KB < GS) load_batch(i0 + KB, buf ^ 1);
+    // this batch's codes into the staging area, then each lane's words out
+    // (a wave's LDS accesses complete in order)
+    uint32_t* sbuf = stage + buf * (T * 16 * kRowWords);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+#pragma unroll
+      for (int j = 0; j < kPerLane; ++j) {
+        const int pc = lane + 64 * j;
+        if (pc < kPieces)
+          *reinterpret_cast<u32x4_t*>(sbuf + (t * 16 + pc / KB) * kRowWords + (pc % KB) * 4) = wq[buf][t][j];
+      }
+    }
+#pragma unroll
+    for (int ii = 0; ii < KB; ++ii) {
+      u32x4_t ai;
+      if constexpr (kXReg) {
+        ai = a[i0 + ii];
+      } else {
+        ai = x_pairs(xb[buf][ii]);
+      }
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, ai);
       const f32x4_t xg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, ones), zero, 0, 0, 0);
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        const int row = nbase + 16 * t + r16;
-        uint32_t wd = 0u, sb = 0u, bb = 0u;
-        if (row < n) {
-          wd = packed[(int64_t)row * wpr + 4 * g + kb];
-          sb = scales[(int64_t)row * G + g];
-          bb = biases[(int64_t)row * G + g];
-        }
         uint32_t q02, q46, q13, q57;
-        word_to_bf16_pairs(wd, q02, q46, q13, q57);
+        word_to_bf16_pairs(sbuf[(t * 16 + r16) * kRowWords + ii * 4 + kb], q02, q46, q13, q57);
         const u32x4_t bq = u32x4_t{q02, q46, q13, q57};
         const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bq), zero, 0, 0, 0);
-        const float s = bf16_to_f32(sb);
-        const float b = bf16_to_f32(bb);
+        const float s = bf16_to_f32(sb[buf][t][ii]);
+        const float b = bf16_to_f32(bb[buf][t][ii]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[t][j] = fmaf(s, d[j], fmaf(b, xg[j], acc[t][j]));
       }
