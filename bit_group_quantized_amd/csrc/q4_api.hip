@@ -444,7 +444,7 @@ q4_status q4_chain_run(const void* device_plan, q4_out_dtype y_dtype, void* work
   if (!device_plan || !workspace) return Q4_ERR_NULL;
   if (y_dtype != Q4_OUT_BF16 && y_dtype != Q4_OUT_F32) return Q4_ERR_SHAPE;
   if (!aligned(device_plan, 64) || !aligned(workspace, 128)) return Q4_ERR_ALIGN;
-  // One block of 12 waves per compute unit, all resident at once (the stage
+  // One block of 15 waves per compute unit, all resident at once (the stage
   // barrier needs that); bounded waits turn a violation into a status.
   const int cus = device_cu_count();
   if (cus > q4k::kChainMaxBlocks) return Q4_ERR_UNSUPPORTED;

@@ -42,7 +42,7 @@ namespace q4k {
 
 constexpr uint32_t kChainMagic = 0x34433451u;  // "Q4C4"
 #ifndef Q4_CHAIN_COMPUTE_WAVES
-#define Q4_CHAIN_COMPUTE_WAVES 12
+#define Q4_CHAIN_COMPUTE_WAVES 14
 #endif
 constexpr int kServiceWave = 0;
 constexpr int kComputeWaves = Q4_CHAIN_COMPUTE_WAVES;  // waves 1..kComputeWaves

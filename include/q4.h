@@ -194,7 +194,7 @@ q4_status q4_chain_encode(const q4_chain_stage* stages, int32_t num_stages,
                           q4_out_dtype y_dtype, void* host_plan, int64_t plan_bytes);
 
 /* Run an encoded chain (device copy of the plan) on `stream`: one launch of one
- * 1024-thread block per compute unit, all resident at once (the stage
+ * 960-thread block per compute unit, all resident at once (the stage
  * barrier needs that; Q4_ERR_UNSUPPORTED if the kernel cannot fit one block
  * per compute unit or the device has more than 1024 of them). y_dtype must
  * match the dtype the plan was encoded with. Nothing else should occupy the
