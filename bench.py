@@ -40,14 +40,14 @@ HBM_PEAK_GBS = 8000.0
 # HBM traffic of one chain_kernel launch over the full step, from two rocprofv3
 # --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch),
 # each scaled by what the same counter reads for a plain 1 GiB copy
-# (``--calibrate-copy 1024``: FETCH_SIZE reads 524301.6 KiB for 1 GiB fetched,
+# (``--calibrate-copy 1024``: FETCH_SIZE reads 524301.8 KiB for 1 GiB fetched,
 # WRITE_SIZE 1048576.0 KiB for 1 GiB written). Valid only for the kernel sources
 # whose hash is recorded: any change to them reports traffic as null until the
 # counters are taken again (profiles/chain_kernel_temporal_step_m1_pmc.md).
 CHAIN_TRAFFIC = {
-    "sources_sha256_16": "482fb5b0093ed393",
-    "fetch_kib": 2038828.1, "fetch_scale": 1048576.0 / 524301.6,
-    "write_kib": 11799.8, "write_scale": 1048576.0 / 1048576.0,
+    "sources_sha256_16": "42615515ed6af7d7",
+    "fetch_kib": 2049826.7, "fetch_scale": 1048576.0 / 524301.8,
+    "write_kib": 4119.8, "write_scale": 1048576.0 / 1048576.0,
 }
 KERNEL_SOURCES = ("q4_chain.h", "q4_kernels.h", "q4_api.hip")
 METRIC = "packed-weight GB/s (% HBM peak) + us per 32-layer Q4 temporal step, M=1"
