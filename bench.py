@@ -208,7 +208,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", choices=("step", "depformer", "gemm", "gemv"), default="step",
                     help="step: the 32-layer temporal step at M=1 (the headline); depformer: one "
                          "Depformer frame (16 codebook steps x 6 layers, M=1); gemm: the temporal "
-                         "step's 224 matrices against X [M, k] (q4_gemm_small, --m rows); gemv: "
+                         "step's 224 matrices against X [M, k] (--m rows; one persistent chain launch for "
+                         "M <= 4 in --mode chain, else one q4_gemm_small call per matrix); gemv: "
                          "one 4096x4096 GEMV, M=1, over 64 distinct matrices in turn (671 MB, past "
                          "the 256 MB last-level cache)")
     ap.add_argument("--m", type=int, default=4, help="rows of X for --workload gemm")
@@ -466,17 +467,30 @@ def bench_other(args, dev) -> int:
               .to(torch.bfloat16) for si, st in enumerate(chain.stages)]
         outs = [[torch.empty((args.m, mt.n), dtype=torch.bfloat16, device=dev) for mt in st.mats] for st in chain.stages]
 
-        def calls():
-            for x, st, ys in zip(xs, chain.stages, outs):
-                for mt, y in zip(st.mats, ys):
-                    q4.q4_gemm_small(x, mt.packed, mt.scales, mt.biases, out=y)
+        use_chain = args.mode == "chain" and args.m <= 4
+        if use_chain:
+            # the same weights and activation rows through one persistent launch
+            from bit_group_quantized_amd.step import Chain, Stage
 
-        g = graph_of(calls)
-        run, launches, kernel = g.replay, chain.num_matrices(), ("gemv_kernel" if args.m <= 4 else "gemm_mfma_kernel")
+            rows_chain = Chain([Stage(x, st.mats, ys) for x, st, ys in zip(xs, chain.stages, outs)])
+            rows_chain.prepare_chain()
+            run, launches, kernel = rows_chain.run_chain, 1, "chain_kernel"
+        else:
+            def calls():
+                for x, st, ys in zip(xs, chain.stages, outs):
+                    for mt, y in zip(st.mats, ys):
+                        q4.q4_gemm_small(x, mt.packed, mt.scales, mt.biases, out=y)
+
+            g = graph_of(calls)
+            run, launches = g.replay, chain.num_matrices()
+            kernel = "gemv_kernel" if args.m <= 4 else "gemm_mfma_kernel"
         ms, per = time_replays(run, args.steps, args.warmup)
+        if use_chain and rows_chain.chain_status() != 0:
+            print(f"chain executor reported status {rows_chain.chain_status()}", file=sys.stderr)
+            return 1
         config = {"workload": f"small_gemm_m{args.m}_temporal_step", "layers": args.layers, "hidden": workloads.HIDDEN,
                   "ffn": workloads.FFN, "m": args.m, "group": 32, "packed_bytes_per_step": wbytes,
-                  "executor": "launches", "launches_per_step": launches}
+                  "executor": "chain" if use_chain else "launches", "launches_per_step": launches}
         unit_name = "step"
     gbs = wbytes / (ms * 1e-3) / 1e9
     achieved = (wbytes / launches) / ((ms / launches) * 1e-3) / 1e9

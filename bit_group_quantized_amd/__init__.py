@@ -36,6 +36,7 @@ _lib = None
 _EXPORTS = (
     "q4_layout_version", "q4_status_str", "q4_last_hip_error", "q4_pack", "q4_unpack", "q4_gemv",
     "q4_gemm_small", "q4_multilinear_step", "q4_chain_plan_bytes", "q4_chain_encode", "q4_chain_run",
+    "q4_chain_encode_rows", "q4_chain_run_rows",
 )
 CHAIN_WORKSPACE_BYTES = 131328
 
@@ -82,8 +83,10 @@ def load():
     lib.q4_chain_plan_bytes.restype = ctypes.c_int64
     lib.q4_chain_encode.argtypes = [P, ctypes.c_int32, P, ctypes.c_int32, V, P, I]
     lib.q4_chain_run.argtypes = [P, V, P, P]
+    lib.q4_chain_encode_rows.argtypes = [P, ctypes.c_int32, P, ctypes.c_int32, ctypes.c_int32, V, P, I]
+    lib.q4_chain_run_rows.argtypes = [P, ctypes.c_int32, V, P, P]
     for f in ("q4_pack", "q4_unpack", "q4_gemv", "q4_gemm_small", "q4_multilinear_step", "q4_chain_encode",
-              "q4_chain_run"):
+              "q4_chain_run", "q4_chain_encode_rows", "q4_chain_run_rows"):
         getattr(lib, f).restype = V
     _lib = lib
     return lib
@@ -250,9 +253,10 @@ class ChainPlan:
     """An encoded chain: the device copy of the plan plus what it references
     (kept alive here so the device pointers in the plan stay valid)."""
 
-    def __init__(self, device_plan: torch.Tensor, out_dtype: torch.dtype, keep: list):
+    def __init__(self, device_plan: torch.Tensor, out_dtype: torch.dtype, keep: list, m: int = 1):
         self.device_plan = device_plan
         self.out_dtype = out_dtype
+        self.m = m
         self._keep = keep
 
 
@@ -262,15 +266,25 @@ def q4_chain_workspace_bytes() -> int:
 
 def q4_chain_build(stages, out_dtype: Optional[torch.dtype] = None) -> ChainPlan:
     """Encode stages (objects with .x, .mats (each .packed/.scales/.biases) and
-    .outs) and upload the plan. All outputs must share one dtype."""
+    .outs) and upload the plan. All outputs must share one dtype. Every stage's
+    x is either a vector [k] (one activation row) or a matrix [m, k] with the
+    same m (1..4) in every stage; each output then holds m*n elements."""
     lib = load()
     mats = []
     descs = []
     keep = []
+    rows = None
     for st in stages:
         _need(st.x, "x", torch.bfloat16)
+        m_st = 1 if st.x.dim() == 1 else st.x.shape[0]
+        if st.x.dim() > 2:
+            raise ValueError("x must be [k] or [m, k]")
+        if rows is None:
+            rows = m_st
+        elif rows != m_st:
+            raise ValueError("every stage must have the same number of activation rows")
         first = len(mats)
-        k = st.x.numel()
+        k = st.x.shape[-1]
         for m, y in zip(st.mats, st.outs):
             n, km = _check_matrix(m.packed, m.scales, m.biases)
             if km != k:
@@ -278,8 +292,8 @@ def q4_chain_build(stages, out_dtype: Optional[torch.dtype] = None) -> ChainPlan
             if out_dtype is None:
                 out_dtype = y.dtype
             _need(y, "y", out_dtype)
-            if y.numel() != n:
-                raise ValueError("output must hold n elements")
+            if y.numel() != rows * n:
+                raise ValueError("output must hold m*n elements")
             mats.append(_ChainMatrix(m.packed.data_ptr(), m.scales.data_ptr(), m.biases.data_ptr(), y.data_ptr(), n))
             keep += [m.packed, m.scales, m.biases, y]
         descs.append(_ChainStage(st.x.data_ptr(), k, first, len(mats) - first))
@@ -292,13 +306,13 @@ def q4_chain_build(stages, out_dtype: Optional[torch.dtype] = None) -> ChainPlan
     host = (ctypes.c_uint8 * nbytes)()
     sarr = (_ChainStage * ns)(*descs)
     marr = (_ChainMatrix * nm)(*mats)
-    _check("q4_chain_encode", lib.q4_chain_encode(ctypes.byref(sarr), ns, ctypes.byref(marr), nm, code,
-                                                  ctypes.byref(host), nbytes))
+    _check("q4_chain_encode_rows", lib.q4_chain_encode_rows(ctypes.byref(sarr), ns, ctypes.byref(marr), nm, rows,
+                                                            code, ctypes.byref(host), nbytes))
     dev = stages[0].x.device
     host_t = torch.frombuffer(bytearray(host), dtype=torch.uint8)
     plan = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     plan.copy_(host_t)
-    return ChainPlan(plan, out_dtype, keep)
+    return ChainPlan(plan, out_dtype, keep, rows)
 
 
 def q4_chain_run(plan: ChainPlan, workspace: torch.Tensor) -> None:
@@ -306,5 +320,5 @@ def q4_chain_run(plan: ChainPlan, workspace: torch.Tensor) -> None:
     of at least CHAIN_WORKSPACE_BYTES (its word 0 reports barrier timeouts)."""
     if workspace.numel() * workspace.element_size() < CHAIN_WORKSPACE_BYTES or not workspace.is_cuda:
         raise ValueError("workspace must be a device tensor of >= %d bytes" % CHAIN_WORKSPACE_BYTES)
-    _check("q4_chain_run", load().q4_chain_run(_ptr(plan.device_plan), _out_code(plan.out_dtype), _ptr(workspace),
-                                               _ptr_stream(workspace)))
+    _check("q4_chain_run_rows", load().q4_chain_run_rows(_ptr(plan.device_plan), plan.m, _out_code(plan.out_dtype),
+                                                         _ptr(workspace), _ptr_stream(workspace)))

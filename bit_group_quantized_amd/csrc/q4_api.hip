@@ -299,31 +299,69 @@ uint32_t device_xcc_count() {
   return static_cast<uint32_t>(n);
 }
 
-constexpr size_t kChainLdsBytes = sizeof(q4k::ChainLds);
+template <int MV>
+constexpr size_t chain_lds_bytes() { return sizeof(q4k::ChainLds<MV>); }
 
-// Per device: raise the dynamic-LDS limit of the chain kernels once and check
-// that one block of the chain kernel fits per compute unit.
-bool chain_ready_on_device() {
+// Per device and activation-row count: raise the dynamic-LDS limit of the
+// chain kernels once and check that one block fits per compute unit.
+template <int MV>
+bool chain_ready_rows(int dev) {
   static int state[64] = {0};  // 0 unknown, 1 ready, -1 not possible
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  if (dev < 0 || dev >= 64) return false;
   if (state[dev] == 0) {
-    bool ok = hipFuncSetAttribute(reinterpret_cast<const void*>(&q4k::chain_kernel<true>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kChainLdsBytes) == hipSuccess &&
-              hipFuncSetAttribute(reinterpret_cast<const void*>(&q4k::chain_kernel<false>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kChainLdsBytes) == hipSuccess;
+    constexpr size_t lds = chain_lds_bytes<MV>();
+    bool ok = hipFuncSetAttribute(reinterpret_cast<const void*>(&q4k::chain_kernel<MV, true>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess &&
+              hipFuncSetAttribute(reinterpret_cast<const void*>(&q4k::chain_kernel<MV, false>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess;
     int a = 0, b = 0;
     ok = ok &&
-         hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, q4k::chain_kernel<true>, 64 * q4k::kChainWaves,
-                                                      kChainLdsBytes) == hipSuccess &&
-         hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, q4k::chain_kernel<false>, 64 * q4k::kChainWaves,
-                                                      kChainLdsBytes) == hipSuccess &&
+         hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, q4k::chain_kernel<MV, true>, 64 * q4k::kChainWaves,
+                                                      lds) == hipSuccess &&
+         hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, q4k::chain_kernel<MV, false>, 64 * q4k::kChainWaves,
+                                                      lds) == hipSuccess &&
          a >= 1 && b >= 1;
     (void)hipGetLastError();
     state[dev] = ok ? 1 : -1;
   }
   return state[dev] == 1;
 }
+
+template <int MV>
+q4_status launch_chain(const q4k::ChainHeader* plan, q4_out_dtype y_dtype, uint32_t* ws, hipStream_t st) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || !chain_ready_rows<MV>(dev)) return Q4_ERR_UNSUPPORTED;
+  // One block of 15 waves per compute unit, all resident at once (the stage
+  // barrier needs that); bounded waits turn a violation into a status.
+  const int cus = device_cu_count();
+  if (cus > q4k::kChainMaxBlocks) return Q4_ERR_UNSUPPORTED;
+  const uint32_t nxcc = device_xcc_count();
+  if (nxcc < 1 || nxcc > q4k::kMaxXcc) return Q4_ERR_UNSUPPORTED;
+  const dim3 grid(cus), block(64 * q4k::kChainWaves);
+  constexpr size_t lds = chain_lds_bytes<MV>();
+  if (y_dtype == Q4_OUT_F32)
+    hipLaunchKernelGGL((q4k::chain_kernel<MV, true>), grid, block, lds, st, plan, ws, nxcc);
+  else
+    hipLaunchKernelGGL((q4k::chain_kernel<MV, false>), grid, block, lds, st, plan, ws, nxcc);
+  return launch_status();
+}
+
+// Limits of a chain with m activation rows.
+struct ChainLimits {
+  int tab_stages, tab_mats, stage_units, max_groups;
+};
+ChainLimits chain_limits(int m) {
+  if (m == 1)
+    return {q4k::ChainShape<1>::kTabStages, q4k::ChainShape<1>::kTabMats, q4k::ChainShape<1>::kStageUnits,
+            q4k::ChainShape<1>::kMaxGroups};
+  return {q4k::ChainShape<2>::kTabStages, q4k::ChainShape<2>::kTabMats, q4k::ChainShape<2>::kStageUnits,
+          q4k::ChainShape<2>::kMaxGroups};
+}
+static_assert(q4k::ChainShape<2>::kTabStages == q4k::ChainShape<4>::kTabStages &&
+                  q4k::ChainShape<2>::kStageUnits == q4k::ChainShape<4>::kStageUnits &&
+                  q4k::ChainShape<2>::kMaxGroups == q4k::ChainShape<4>::kMaxGroups &&
+                  q4k::ChainShape<2>::kTabMats == q4k::ChainShape<4>::kTabMats,
+              "one set of limits for several activation rows");
 
 // Lanes per row for a stage of G groups: among 64/32/16/8 lanes, the split
 // with the fewest idle lanes (ties: more lanes per row) whose padded width
@@ -332,9 +370,9 @@ bool chain_ready_on_device() {
 // A chain stage processes units of 4 rows in chunks of 16 groups per row, so
 // its geometry depends on G only: chunks per row CH = ceil(G / 16), with the
 // activations padded to 16 * CH groups.
-bool plan_stage(int64_t G, int* c_log2, int* CH) {
+bool plan_stage(int64_t G, int max_groups, int* c_log2, int* CH) {
   const int64_t ch = ceil_div(G, q4k::kChunkGroups);
-  if (ch * q4k::kChunkGroups > q4k::kChainMaxGroups) return false;
+  if (ch * q4k::kChunkGroups > max_groups) return false;
   *c_log2 = 4;
   *CH = static_cast<int>(ch);
   return true;
@@ -356,11 +394,13 @@ int64_t q4_chain_plan_bytes(int32_t num_stages, int32_t num_matrices) {
          static_cast<int64_t>(num_matrices) * sizeof(q4k::ChainMatDesc);
 }
 
-q4_status q4_chain_encode(const q4_chain_stage* stages, int32_t num_stages,
-                          const q4_chain_matrix* matrices, int32_t num_matrices,
-                          q4_out_dtype y_dtype, void* host_plan, int64_t plan_bytes) {
+q4_status q4_chain_encode_rows(const q4_chain_stage* stages, int32_t num_stages,
+                               const q4_chain_matrix* matrices, int32_t num_matrices, int32_t m_rows,
+                               q4_out_dtype y_dtype, void* host_plan, int64_t plan_bytes) {
   if (!stages || !matrices || !host_plan) return Q4_ERR_NULL;
   if (num_stages <= 0 || num_matrices <= 0) return Q4_ERR_SHAPE;
+  if (m_rows < 1 || m_rows > q4k::kMaxRows) return Q4_ERR_SHAPE;
+  const ChainLimits lim = chain_limits(m_rows);
   if (y_dtype != Q4_OUT_BF16 && y_dtype != Q4_OUT_F32) return Q4_ERR_SHAPE;
   const int64_t need = q4_chain_plan_bytes(num_stages, num_matrices);
   if (plan_bytes < need) return Q4_ERR_SHAPE;
@@ -374,18 +414,18 @@ q4_status q4_chain_encode(const q4_chain_stage* stages, int32_t num_stages,
     next_matrix += st.num_matrices;
     for (int32_t i = 0; i < st.num_matrices; ++i) {
       const q4_chain_matrix& m = matrices[st.first_matrix + i];
-      const q4_status c = check_product(st.x, 1, m.packed, m.scales, m.biases, m.n, st.k, m.y, y_dtype);
+      const q4_status c = check_product(st.x, m_rows, m.packed, m.scales, m.biases, m.n, st.k, m.y, y_dtype);
       if (c != Q4_OK) return c;
       if (m.n >= (1 << 22)) return Q4_ERR_UNSUPPORTED;
       // each block stages its rows of a matrix in LDS
-      if (ceil_div(ceil_div(m.n, q4k::kUnitRows), device_cu_count()) > q4k::kStageUnits) return Q4_ERR_UNSUPPORTED;
+      if (ceil_div(ceil_div(m.n, q4k::kUnitRows), device_cu_count()) > lim.stage_units) return Q4_ERR_UNSUPPORTED;
       if (!aligned(m.scales, 16) || !aligned(m.biases, 16)) return Q4_ERR_UNSUPPORTED;
       // a stage may not write its own input
-      if (ranges_overlap(st.x, 2 * st.k, m.y, ybytes * m.n)) return Q4_ERR_UNSUPPORTED;
+      if (ranges_overlap(st.x, 2 * st.k * m_rows, m.y, ybytes * m.n * m_rows)) return Q4_ERR_UNSUPPORTED;
     }
     int lg, ch;
-    if (st.num_matrices > q4k::kMaxMatsPerStage || num_matrices > q4k::kTabMats || num_stages > q4k::kTabStages ||
-        !plan_stage(st.k / 32, &lg, &ch))
+    if (st.num_matrices > q4k::kMaxMatsPerStage || num_matrices > lim.tab_mats || num_stages > lim.tab_stages ||
+        !plan_stage(st.k / 32, lim.max_groups, &lg, &ch))
       return Q4_ERR_UNSUPPORTED;
   }
   if (next_matrix != num_matrices) return Q4_ERR_SHAPE;
@@ -398,13 +438,14 @@ q4_status q4_chain_encode(const q4_chain_stage* stages, int32_t num_stages,
   hdr->num_mats = num_matrices;
   hdr->out_f32 = y_dtype == Q4_OUT_F32 ? 1 : 0;
   hdr->plan_bytes = static_cast<int32_t>(need);
+  hdr->rows = m_rows;
   auto* sd = reinterpret_cast<q4k::ChainStageDesc*>(hdr + 1);
   for (int32_t s = 0; s < num_stages; ++s) {
     const q4_chain_stage& st = stages[s];
     q4k::ChainStageDesc d{};
     d.x = st.x;
     d.G = static_cast<int32_t>(st.k / 32);
-    plan_stage(d.G, &d.c_log2, &d.CH);
+    plan_stage(d.G, lim.max_groups, &d.c_log2, &d.CH);
     d.num_mats = st.num_matrices;
     d.mat_begin = st.first_matrix;
     sd[s] = d;
@@ -420,7 +461,7 @@ q4_status q4_chain_encode(const q4_chain_stage* stages, int32_t num_stages,
         const q4_chain_matrix& m = matrices[stages[t].first_matrix + i];
         // (a later stage writing x is harmless: x is read before that stage
         // starts, prefetch included)
-        if (t < s && ranges_overlap(st.x, 2 * st.k, m.y, ybytes * m.n)) {
+        if (t < s && ranges_overlap(st.x, 2 * st.k * m_rows, m.y, ybytes * m.n * m_rows)) {
           sd[s].x_internal = 1;
           sd[t].sync_outputs = 1;
         }
@@ -440,25 +481,30 @@ q4_status q4_chain_encode(const q4_chain_stage* stages, int32_t num_stages,
   return Q4_OK;
 }
 
-q4_status q4_chain_run(const void* device_plan, q4_out_dtype y_dtype, void* workspace, void* stream) {
+q4_status q4_chain_encode(const q4_chain_stage* stages, int32_t num_stages,
+                          const q4_chain_matrix* matrices, int32_t num_matrices,
+                          q4_out_dtype y_dtype, void* host_plan, int64_t plan_bytes) {
+  return q4_chain_encode_rows(stages, num_stages, matrices, num_matrices, 1, y_dtype, host_plan, plan_bytes);
+}
+
+q4_status q4_chain_run_rows(const void* device_plan, int32_t m_rows, q4_out_dtype y_dtype, void* workspace,
+                            void* stream) {
   if (!device_plan || !workspace) return Q4_ERR_NULL;
   if (y_dtype != Q4_OUT_BF16 && y_dtype != Q4_OUT_F32) return Q4_ERR_SHAPE;
+  if (m_rows < 1 || m_rows > q4k::kMaxRows) return Q4_ERR_SHAPE;
   if (!aligned(device_plan, 64) || !aligned(workspace, 128)) return Q4_ERR_ALIGN;
-  // One block of 15 waves per compute unit, all resident at once (the stage
-  // barrier needs that); bounded waits turn a violation into a status.
-  const int cus = device_cu_count();
-  if (cus > q4k::kChainMaxBlocks) return Q4_ERR_UNSUPPORTED;
-  if (!chain_ready_on_device()) return Q4_ERR_UNSUPPORTED;
-  const dim3 grid(cus), block(64 * q4k::kChainWaves);
-  const uint32_t nxcc = device_xcc_count();
-  if (nxcc < 1 || nxcc > q4k::kMaxXcc) return Q4_ERR_UNSUPPORTED;
   const q4k::ChainHeader* plan = static_cast<const q4k::ChainHeader*>(device_plan);
   uint32_t* ws = static_cast<uint32_t*>(workspace);
-  if (y_dtype == Q4_OUT_F32)
-    hipLaunchKernelGGL(q4k::chain_kernel<true>, grid, block, kChainLdsBytes, as_stream(stream), plan, ws, nxcc);
-  else
-    hipLaunchKernelGGL(q4k::chain_kernel<false>, grid, block, kChainLdsBytes, as_stream(stream), plan, ws, nxcc);
-  return launch_status();
+  switch (m_rows) {
+    case 1: return launch_chain<1>(plan, y_dtype, ws, as_stream(stream));
+    case 2: return launch_chain<2>(plan, y_dtype, ws, as_stream(stream));
+    case 3: return launch_chain<3>(plan, y_dtype, ws, as_stream(stream));
+    default: return launch_chain<4>(plan, y_dtype, ws, as_stream(stream));
+  }
+}
+
+q4_status q4_chain_run(const void* device_plan, q4_out_dtype y_dtype, void* workspace, void* stream) {
+  return q4_chain_run_rows(device_plan, 1, y_dtype, workspace, stream);
 }
 
 }  // extern "C"

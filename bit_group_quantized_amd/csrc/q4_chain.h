@@ -48,9 +48,7 @@ constexpr int kServiceWave = 0;
 constexpr int kComputeWaves = Q4_CHAIN_COMPUTE_WAVES;  // waves 1..kComputeWaves
 constexpr int kChainWaves = 1 + kComputeWaves;
 constexpr int kMaxMatsPerStage = 4;
-constexpr int kChainMaxGroups = 384;  // k <= 12288
 constexpr int kUnitRows = 4;      // rows per unit
-constexpr int kStageUnits = 128;  // units of one matrix per block and stage (staged in LDS)
 constexpr int kMaxPieces = 8;     // pieces a unit's chunks may be cut into
 #ifndef Q4_CHAIN_SPLIT_UNITS
 #define Q4_CHAIN_SPLIT_UNITS 8
@@ -69,8 +67,22 @@ constexpr uint32_t kQueueEnd = 0xFFFFFFFFu;
 constexpr int kChunkGroups = 16;  // groups of each row per slot
 constexpr int kXWordsPerGroup = 20;   // 16 re-paired words + sum + pad (bank spread)
 constexpr int kChainMaxBlocks = 1024;
-constexpr int kTabStages = 384;   // stages of a chain (the plan is copied into LDS)
-constexpr int kTabMats = 768;     // matrices of a chain
+constexpr int kMaxRows = 4;       // activation rows a chain may carry
+// Limits and LDS shape of a chain carrying MV activation rows. One row keeps
+// two activation buffers (the next stage's activations arrive during the
+// current stage) and large plan tables; several rows share one weight stream
+// (every MFMA row is one activation row), fill one buffer during the stage
+// barrier instead, and take smaller tables so that the rows fit.
+template <int MV>
+struct ChainShape {
+  static_assert(MV >= 1 && MV <= kMaxRows, "activation rows");
+  static constexpr int kTabStages = MV == 1 ? 384 : 128;  // stages of a chain (the plan is copied into LDS)
+  static constexpr int kTabMats = MV == 1 ? 768 : 256;    // matrices of a chain
+  static constexpr int kStageUnits = MV == 1 ? 128 : 32;  // units of one matrix per block and stage
+  static constexpr int kXBuffers = MV == 1 ? 2 : 1;
+  static constexpr int kMaxGroups = MV == 1 ? 384 : 352;  // k <= 12288 (11264 with several rows)
+  static constexpr int kVecWords = kMaxGroups * kXWordsPerGroup + (MV == 1 ? 0 : 4);  // one row (bank shift)
+};
 constexpr int kMaxXcc = 16;
 constexpr uint32_t kSpinLimit = 1u << 22;
 
@@ -87,7 +99,8 @@ struct alignas(16) ChainHeader {
   int32_t num_mats;
   int32_t out_f32;
   int32_t plan_bytes;
-  int32_t pad[11];
+  int32_t rows;          // activation rows (1..kMaxRows)
+  int32_t pad[10];
 };
 struct alignas(16) ChainStageDesc {
   const uint16_t* x;
@@ -199,21 +212,25 @@ constexpr int kStageRagged = 1, kStageXInternal = 2, kStageSyncOut = 4;
 
 // Shared memory: activations and the plan tables (dynamic LDS), and the words
 // that connect the roles (a separate static object).
+template <int MV>
 struct ChainLds {
-  uint32_t x[2][kChainMaxGroups * kXWordsPerGroup];  // activations, double buffered
-  StageRec st[kTabStages];
-  MatRec mt[kTabMats];
+  using S = ChainShape<MV>;
+  uint32_t x[S::kXBuffers][MV * S::kVecWords];  // activations: per buffer, row v at v * kVecWords
+  StageRec st[S::kTabStages];
+  MatRec mt[S::kTabMats];
 };
+template <int MV>
 struct ChainFlags {
-  float parts[kSplitItems][kUnitRows];   // partial row sums of the pieces of a stage
-  uint32_t pieces_done[kSplitUnits];     // pieces of a unit of the stage finished
-  float out[kMaxMatsPerStage][kStageUnits][kUnitRows];  // the stage's finished rows
+  using S = ChainShape<MV>;
+  float parts[kSplitItems][kUnitRows][MV];   // partial row sums of the pieces of a stage
+  uint32_t pieces_done[kSplitUnits];         // pieces of a unit of the stage finished
+  float out[kMaxMatsPerStage][S::kStageUnits][kUnitRows][MV];  // the stage's finished rows
   uint32_t done_total;               // stage completions of all compute waves
   int32_t x_stage;                   // last stage whose activations are in LDS
   uint32_t abort;
   uint32_t go;
   uint32_t misfit;                   // a matrix has more units per block than the row staging holds
-  uint32_t claim[kTabStages];        // items of each stage claimed so far by the block's waves
+  uint32_t claim[S::kTabStages];     // items of each stage claimed so far by the block's waves
   uint32_t queue[kComputeWaves][kQueueLen];  // each wave's claimed items, oldest first
 };
 
@@ -322,12 +339,18 @@ __device__ __forceinline__ mfma_bf16x4 as_bf16x4(uint32_t lo, uint32_t hi) {
 // group's sum of code x activation in fp32: two MFMAs per 8 codes, codes and
 // activations in the same re-paired input order. xg: the group's 16
 // re-paired activation words and their sum (LDS).
-__device__ __forceinline__ float slot_term(const Slot& d, const uint32_t* xg, bool live) {
+// With MV activation rows, lane 4b+i supplies row min(i, MV - 1) as A row i,
+// so register i accumulates activation row i against the lane's codes: MV
+// rows cost the same 8 MFMAs. xg is then the lane's own A row's group and
+// xrow the distance between rows in LDS (the group sums of every row are
+// read from there), vown the row the lane supplies.
+template <int MV>
+__device__ __forceinline__ void slot_terms(const Slot& d, const uint32_t* xg, int xrow, int vown, bool live,
+                                           float (&term)[MV]) {
   const uint4 x0 = *reinterpret_cast<const uint4*>(xg + 0);
   const uint4 x1 = *reinterpret_cast<const uint4*>(xg + 4);
   const uint4 x2 = *reinterpret_cast<const uint4*>(xg + 8);
   const uint4 x3 = *reinterpret_cast<const uint4*>(xg + 12);
-  const float xs = __uint_as_float(xg[16]);
   const uint32_t ws[4] = {d.w.x, d.w.y, d.w.z, d.w.w};
   const uint32_t xp[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
                            x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
@@ -342,18 +365,31 @@ __device__ __forceinline__ float slot_term(const Slot& d, const uint32_t* xg, bo
   // lanes past G in a ragged last chunk weigh zero
   const float sc = __uint_as_float(live ? d.s << 16 : 0u);
   const float bi = __uint_as_float(live ? d.b << 16 : 0u);
-  return fmaf(sc, c[0], bi * xs);
+  if constexpr (MV == 1) {
+    term[0] = fmaf(sc, c[0], bi * __uint_as_float(xg[16]));
+  } else {
+    // (row i's sum sits at the same place of row i's activations; vown is
+    // the row this lane supplies)
+    const uint32_t* x_row0 = xg - vown * xrow;
+#pragma unroll
+    for (int i = 0; i < MV; ++i) term[i] = fmaf(sc, c[i], bi * __uint_as_float(x_row0[i * xrow + 16]));
+  }
 }
 
 // Lanes 0..3 leave the 4 rows of local unit u of matrix mi of the stage in
 // LDS; the service wave stores them. Compute waves issue no global stores at
 // all, so that every step of their loop issues exactly the same loads.
-__device__ __forceinline__ void stage_rows(ChainFlags& F, int mi, int u, int lane, float v) {
-  if (lane < kUnitRows) *(volatile Q4_LDS float*)&F.out[mi][u][lane] = v;
+template <int MV>
+__device__ __forceinline__ void stage_rows(ChainFlags<MV>& F, int mi, int u, int lane, const float (&v)[MV]) {
+  if (lane < kUnitRows) {
+#pragma unroll
+    for (int i = 0; i < MV; ++i) *(volatile Q4_LDS float*)&F.out[mi][u][lane][i] = v[i];
+  }
 }
 
 // a wait timed out: the service wave reports it
-__device__ __forceinline__ void compute_fail(ChainFlags& F) {
+template <int MV>
+__device__ __forceinline__ void compute_fail(ChainFlags<MV>& F) {
   if ((threadIdx.x & 63) == 0) lds_put(&F.abort, 2u);
   wake_block();
 }
@@ -377,6 +413,7 @@ struct StageInfo {
 // Fill the block's record of a stage (one lane per stage, at the start of a
 // launch). Returns false if a matrix has more units per block than the LDS
 // staging of rows holds.
+template <int MV>
 __device__ __forceinline__ bool build_stage_rec(StageRec& r, const ChainStageDesc* sd, const ChainMatDesc* mats) {
   r.G = sd->G;
   r.CH = sd->CH;
@@ -391,7 +428,7 @@ __device__ __forceinline__ bool build_stage_rec(StageRec& r, const ChainStageDes
     const int nunits = mi < r.nm ? (mats[r.mat_begin + mi].n + kUnitRows - 1) / kUnitRows : 0;
     r.U[mi] = block_range(nunits).count;
     // (block 0 has the most units; every block takes the same decision)
-    fits = fits && (nunits + (int)gridDim.x - 1) / (int)gridDim.x <= kStageUnits;
+    fits = fits && (nunits + (int)gridDim.x - 1) / (int)gridDim.x <= ChainShape<MV>::kStageUnits;
     units += r.U[mi];
   }
   int P = 1;
@@ -404,7 +441,8 @@ __device__ __forceinline__ bool build_stage_rec(StageRec& r, const ChainStageDes
   r.pad[0] = r.pad[1] = 0;
   return fits;
 }
-__device__ __forceinline__ void stage_info(StageInfo& si, const ChainLds& L, int s) {
+template <int MV>
+__device__ __forceinline__ void stage_info(StageInfo& si, const ChainLds<MV>& L, int s) {
   const StageRec& r = L.st[s];
   si.s = s;
   si.G = ufl(r.G);
@@ -474,7 +512,8 @@ __device__ __forceinline__ void lc_lanes(LoadCursor& lc, int lane) {
   lc.ls = e * 2u;
 }
 // set up item lc.i of stage lc.si
-__device__ __forceinline__ void lc_item(LoadCursor& lc, const ChainLds& L) {
+template <int MV>
+__device__ __forceinline__ void lc_item(LoadCursor& lc, const ChainLds<MV>& L) {
   Item it;
   decode_item(lc.si, lc.i, it);
   const MatRec& mr = L.mt[lc.si.mat_begin + it.mi];
@@ -491,7 +530,8 @@ __device__ __forceinline__ void lc_item(LoadCursor& lc, const ChainLds& L) {
 }
 // claim the wave's next item (through the stages) and queue it for the
 // arithmetic, or queue the end
-__device__ __forceinline__ void lc_next_item(LoadCursor& lc, const ChainLds& L, ChainFlags& F, int num_stages, int cw,
+template <int MV>
+__device__ __forceinline__ void lc_next_item(LoadCursor& lc, const ChainLds<MV>& L, ChainFlags<MV>& F, int num_stages, int cw,
                                              int lane) {
   while (true) {
     // a wave's first item of a stage is its own (item cw); the rest are
@@ -529,7 +569,8 @@ __device__ __forceinline__ void lc_next_item(LoadCursor& lc, const ChainLds& L, 
 // Issue the loads of the cursor's slot into d and advance (every step issues
 // the same three loads, which lets the compiler wait for exactly the slot it
 // is about to use).
-__device__ __forceinline__ void lc_load(LoadCursor& lc, Slot& d, int lane, const ChainLds& L, ChainFlags& F,
+template <int MV>
+__device__ __forceinline__ void lc_load(LoadCursor& lc, Slot& d, int lane, const ChainLds<MV>& L, ChainFlags<MV>& F,
                                         int num_stages, int cw) {
   const q4_u32x4 w = __builtin_bit_cast(q4_u32x4, __builtin_amdgcn_raw_buffer_load_b128(lc.rw, (int)lc.vw, 0, 0));
   d.w = make_uint4(w.x, w.y, w.z, w.w);
@@ -541,11 +582,13 @@ __device__ __forceinline__ void lc_load(LoadCursor& lc, Slot& d, int lane, const
   if (lc.left == 0) lc_next_item(lc, L, F, num_stages, cw, lane);
 }
 
-template <bool OUT_F32>
-__device__ __forceinline__ void compute_body(int num_stages,
-                                             int cw, ChainLds& L, ChainFlags& F, uint32_t* ws) {
+template <int MV, bool OUT_F32>
+__device__ __forceinline__ void compute_body(int num_stages, int cw, ChainLds<MV>& L, ChainFlags<MV>& F,
+                                             uint32_t* ws) {
+  using S = ChainShape<MV>;
   const int lane = threadIdx.x & 63;
   const int col = lane >> 2;
+  const int vown = (lane & 3) < MV ? (lane & 3) : MV - 1;  // the activation row this lane supplies
   LoadCursor lc;
   lc.done = false;
   lc.qh = 0;
@@ -563,8 +606,10 @@ __device__ __forceinline__ void compute_body(int num_stages,
   Item it;
   int left = 0;      // its slots not yet computed
   int gch = 0;       // first group of its next chunk
-  const uint32_t* x0 = nullptr;  // group col of chunk 0 of the stage's activations
-  float acc = 0.f;
+  const uint32_t* x0 = nullptr;  // group col of chunk 0 of the lane's activation row
+  float acc[MV];
+#pragma unroll
+  for (int v = 0; v < MV; ++v) acc[v] = 0.f;
   bool stop = false;  // a wait timed out or another wave failed: finish without waiting
 
   // stage si.s may start once its activations are in LDS (every wave of the
@@ -576,7 +621,7 @@ __device__ __forceinline__ void compute_body(int num_stages,
       stop = lds_get(&F.abort) != 0u || ++spins > kSpinLimit;
     }
     compiler_fence();
-    x0 = L.x[si.s & 1] + col * kXWordsPerGroup;
+    x0 = L.x[S::kXBuffers == 2 ? si.s & 1 : 0] + vown * S::kVecWords + col * kXWordsPerGroup;
   };
   // move to the wave's next claimed item, closing the stages it leaves (every
   // stage is counted once, after the wave's rows of it are in LDS) and
@@ -605,23 +650,35 @@ __device__ __forceinline__ void compute_body(int num_stages,
   // a piece's go to its place, and the wave that completes a unit's last
   // piece adds the pieces up in piece order
   auto end_item = [&]() {
-    const float tot = row_sum(acc);
-    acc = 0.f;
+    float tot[MV];
+#pragma unroll
+    for (int v = 0; v < MV; ++v) {
+      tot[v] = row_sum(acc[v]);
+      acc[v] = 0.f;
+    }
     if (si.P == 1) {
       stage_rows(F, it.mi, it.u, lane, tot);
       return;
     }
     // pieces of unit j of the stage are items j P .. j P + P - 1
     const int j = ufl((int)(((uint32_t)i * si.inv_p) >> 16));
-    if (lane < kUnitRows) *(volatile Q4_LDS float*)&F.parts[i][lane] = tot;
+    if (lane < kUnitRows) {
+#pragma unroll
+      for (int v = 0; v < MV; ++v) *(volatile Q4_LDS float*)&F.parts[i][lane][v] = tot[v];
+    }
     compiler_fence();
     uint32_t old = 0;
     if (lane == 0) old = lds_add_rtn(&F.pieces_done[j], 1u);
     old = (uint32_t)__builtin_amdgcn_readfirstlane((int)old);
     if (old == (uint32_t)si.P - 1u) {
       compiler_fence();
-      float sum = 0.f;
-      for (int p = 0; p < si.P; ++p) sum += *(volatile Q4_LDS float*)&F.parts[j * si.P + p][lane & 3];
+      float sum[MV];
+#pragma unroll
+      for (int v = 0; v < MV; ++v) sum[v] = 0.f;
+      for (int p = 0; p < si.P; ++p) {
+#pragma unroll
+        for (int v = 0; v < MV; ++v) sum[v] += *(volatile Q4_LDS float*)&F.parts[j * si.P + p][lane & 3][v];
+      }
       stage_rows(F, it.mi, it.u, lane, sum);
       if (lane == 0) lds_put(&F.pieces_done[j], 0u);
     }
@@ -631,10 +688,13 @@ __device__ __forceinline__ void compute_body(int num_stages,
   auto step = [&](Slot& d) {
     // lanes past G (only in the last chunk of a ragged row) weigh zero
     const bool live = !si.ragged || gch + col < si.G;
-    const float term = slot_term(d, x0 + gch * kXWordsPerGroup, live);
-    asm volatile("" ::"v"(term));
+    float term[MV];
+    slot_terms<MV>(d, x0 + gch * kXWordsPerGroup, S::kVecWords, vown, live, term);
+#pragma unroll
+    for (int v = 0; v < MV; ++v) asm volatile("" ::"v"(term[v]));
     lc_load(lc, d, lane, L, F, num_stages, cw);
-    acc += term;
+#pragma unroll
+    for (int v = 0; v < MV; ++v) acc[v] += term[v];
     gch = ufl(gch + kChunkGroups);
     left = ufl(left - 1);
     if (left == 0) {
@@ -681,10 +741,10 @@ __device__ __forceinline__ void compute_body(int num_stages,
   if (stop && lds_get(&F.abort) == 0u) compute_fail(F);
 }
 
-template <bool OUT_F32>
-__device__ __forceinline__ void compute_run(int num_stages,
-                                            int cw, ChainLds& L, ChainFlags& F, uint32_t* ws) {
-  compute_body<OUT_F32>(num_stages, cw, L, F, ws);
+template <int MV, bool OUT_F32>
+__device__ __forceinline__ void compute_run(int num_stages, int cw, ChainLds<MV>& L, ChainFlags<MV>& F,
+                                            uint32_t* ws) {
+  compute_body<MV, OUT_F32>(num_stages, cw, L, F, ws);
   // loads still in flight (the refills past the wave's last slot, or an
   // aborted wave's) complete before the wave ends
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -695,46 +755,58 @@ __device__ __forceinline__ void compute_run(int num_stages,
 // Load a stage's activations into an LDS buffer, re-paired, with group sums;
 // groups past G up to 16 CH are zero. Coherent loads when an earlier stage of
 // this launch wrote them.
+template <int MV>
 __device__ __forceinline__ void service_load_x(const Geo& g, const void* x, bool coherent, uint32_t* dst_buf) {
+  // (MV activation rows [MV][k] in memory; row v goes to dst_buf + v * kVecWords)
   constexpr int kBatch = 3;  // groups per lane whose loads are in flight together
   const int lane = threadIdx.x & 63;
   const int gpad = kChunkGroups * g.CH;
+  const int total = MV * gpad;
   const uint64_t* x64 = static_cast<const uint64_t*>(x);
-  for (int base = 0; base < gpad; base += 64 * kBatch) {
+  for (int base = 0; base < total; base += 64 * kBatch) {
     uint64_t q[kBatch][8];
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
-      const int grp = base + 64 * b + lane;
+      const int e = base + 64 * b + lane;
+      int v = 0;
+#pragma unroll
+      for (int r = 1; r < MV; ++r) v += e >= r * gpad ? 1 : 0;
+      const int grp = e - v * gpad;
 #pragma unroll
       for (int i = 0; i < 8; ++i) q[b][i] = 0u;
-      if (grp < g.G) {
+      if (e < total && grp < g.G) {
+        const uint64_t* src = x64 + ((int64_t)v * g.G + grp) * 8;
         if (coherent) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) q[b][i] = coh_load64(x64 + (int64_t)grp * 8 + i);
+          for (int i = 0; i < 8; ++i) q[b][i] = coh_load64(src + i);
         } else {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) q[b][i] = gload(x64 + (int64_t)grp * 8 + i);
+          for (int i = 0; i < 8; ++i) q[b][i] = gload(src + i);
         }
       }
     }
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
-      const int grp = base + 64 * b + lane;
-      if (grp < gpad) {
+      const int e = base + 64 * b + lane;
+      int v = 0;
+#pragma unroll
+      for (int r = 1; r < MV; ++r) v += e >= r * gpad ? 1 : 0;
+      const int grp = e - v * gpad;
+      if (e < total) {
         // (groups past G are zero)
-        uint32_t* dst = dst_buf + grp * kXWordsPerGroup;
+        uint32_t* dst = dst_buf + v * ChainShape<MV>::kVecWords + grp * kXWordsPerGroup;
         float xs = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          uint4 e;
-          e.x = (uint32_t)q[b][2 * j];
-          e.y = (uint32_t)(q[b][2 * j] >> 32);
-          e.z = (uint32_t)q[b][2 * j + 1];
-          e.w = (uint32_t)(q[b][2 * j + 1] >> 32);
+          uint4 e4;
+          e4.x = (uint32_t)q[b][2 * j];
+          e4.y = (uint32_t)(q[b][2 * j] >> 32);
+          e4.z = (uint32_t)q[b][2 * j + 1];
+          e4.w = (uint32_t)(q[b][2 * j + 1] >> 32);
           uint32_t p02, p46, p13, p57;
-          x_to_pairs(e, p02, p46, p13, p57);
+          x_to_pairs(e4, p02, p46, p13, p57);
           *reinterpret_cast<uint4*>(dst + 4 * j) = make_uint4(p02, p46, p13, p57);
-          xs += x_sum8(e);
+          xs += x_sum8(e4);
         }
         dst[16] = __float_as_uint(xs);
       }
@@ -750,7 +822,8 @@ struct GridSync {
   uint32_t epoch;
 };
 
-__device__ __forceinline__ bool service_fail(uint32_t* ws, ChainFlags& F, uint32_t code) {
+template <int MV>
+__device__ __forceinline__ bool service_fail(uint32_t* ws, ChainFlags<MV>& F, uint32_t code) {
   if ((threadIdx.x & 63) == 0) {
     coh_store(ws + kWsStatus, code);
     lds_put(&F.abort, 1u);
@@ -765,7 +838,8 @@ __device__ __forceinline__ bool service_fail(uint32_t* ws, ChainFlags& F, uint32
 // earlier launches: the exchange flag holds the last completed epoch, and it
 // cannot move before every block of this XCD has arrived at the first
 // barrier of this launch, so every block of the XCD reads the same value here.
-__device__ __forceinline__ bool service_start(uint32_t* ws, ChainFlags& F, GridSync& gs, uint32_t nxcc) {
+template <int MV>
+__device__ __forceinline__ bool service_start(uint32_t* ws, ChainFlags<MV>& F, GridSync& gs, uint32_t nxcc) {
   const uint32_t nb = gridDim.x;
   gs.xcc = blockIdx.x % nxcc;
   if (xcc_id() != gs.xcc) return service_fail(ws, F, 3u);
@@ -789,7 +863,8 @@ __device__ __forceinline__ void service_arrive(uint32_t* ws, GridSync& gs) {
   old = __shfl(old, 0);
   if ((old + 1u) % gs.per == 0u && lane == 0) coh_store(ws + kWsGflag + gs.xcc, e);
 }
-__device__ __forceinline__ bool service_wait(uint32_t* ws, ChainFlags& F, GridSync& gs) {
+template <int MV>
+__device__ __forceinline__ bool service_wait(uint32_t* ws, ChainFlags<MV>& F, GridSync& gs) {
   const int lane = threadIdx.x & 63;
   const uint32_t e = gs.epoch;
   uint32_t spins = 0;
@@ -804,8 +879,9 @@ __device__ __forceinline__ bool service_wait(uint32_t* ws, ChainFlags& F, GridSy
 
 // Store stage s's rows from LDS: entry (mi, u, r) is row 4 unit + r of the
 // stage's matrix mi, for the block's local unit u.
-template <bool OUT_F32>
-__device__ __forceinline__ void service_store(const ChainLds& L, int s, ChainFlags& F) {
+// With MV activation rows the outputs are [MV][n].
+template <int MV, bool OUT_F32>
+__device__ __forceinline__ void service_store(const ChainLds<MV>& L, int s, ChainFlags<MV>& F) {
   const int lane = threadIdx.x & 63;
   const Geo g = geo_of(L.st[s]);
   for (int mi = 0; mi < g.num_mats; ++mi) {
@@ -817,30 +893,37 @@ __device__ __forceinline__ void service_store(const ChainLds& L, int s, ChainFla
       const int u = e >> 2, r = e & 3;
       const int orow = unit_of(br, u) * kUnitRows + r;
       if (orow < n) {
-        const float v = *(volatile Q4_LDS float*)&F.out[mi][u][r];
-        if constexpr (OUT_F32) {
-          coh_store(static_cast<uint32_t*>(y) + orow, __float_as_uint(v));
-        } else {
-          coh_store16(static_cast<uint16_t*>(y) + orow, f32_to_bf16_rne(v));
+#pragma unroll
+        for (int v = 0; v < MV; ++v) {
+          const float val = *(volatile Q4_LDS float*)&F.out[mi][u][r][v];
+          if constexpr (OUT_F32) {
+            coh_store(static_cast<uint32_t*>(y) + (int64_t)v * n + orow, __float_as_uint(val));
+          } else {
+            coh_store16(static_cast<uint16_t*>(y) + (int64_t)v * n + orow, f32_to_bf16_rne(val));
+          }
         }
       }
     }
   }
 }
 
-__device__ __forceinline__ int stage_flags(const ChainLds& L, int s) { return ufl(L.st[s].flags); }
-__device__ __forceinline__ const uint16_t* stage_x(const ChainLds& L, int s) { return ufl_ptr(L.st[s].x); }
+template <int MV>
+__device__ __forceinline__ int stage_flags(const ChainLds<MV>& L, int s) { return ufl(L.st[s].flags); }
+template <int MV>
+__device__ __forceinline__ const uint16_t* stage_x(const ChainLds<MV>& L, int s) { return ufl_ptr(L.st[s].x); }
 
-template <bool OUT_F32>
-__device__ __forceinline__ void service_run(int num_stages, ChainLds& L, ChainFlags& F, uint32_t* ws, uint32_t nxcc) {
+template <int MV, bool OUT_F32>
+__device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, ChainFlags<MV>& F, uint32_t* ws,
+                                            uint32_t nxcc) {
+  constexpr bool kDouble = ChainShape<MV>::kXBuffers == 2;
   GridSync gs;
   if (!service_start(ws, F, gs, nxcc)) return;
-  service_load_x(geo_of(L.st[0]), stage_x(L, 0), false, L.x[0]);
+  service_load_x<MV>(geo_of(L.st[0]), stage_x(L, 0), false, L.x[0]);
   compiler_fence();
   if ((threadIdx.x & 63) == 0) lds_puti(&F.x_stage, 0);
   wake_block();
-  if (num_stages > 1 && !(stage_flags(L, 1) & kStageXInternal))
-    service_load_x(geo_of(L.st[1]), stage_x(L, 1), false, L.x[1]);
+  if (kDouble && num_stages > 1 && !(stage_flags(L, 1) & kStageXInternal))
+    service_load_x<MV>(geo_of(L.st[1]), stage_x(L, 1), false, L.x[kDouble ? 1 : 0]);
   for (int s = 0; s < num_stages; ++s) {
     uint32_t spins = 0;
     while ((int)(lds_get(&F.done_total) - (uint32_t)(kComputeWaves * (s + 1))) < 0) {
@@ -852,45 +935,50 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds& L, ChainFl
     }
     compiler_fence();
     if (s + 1 >= num_stages) {
-      service_store<OUT_F32>(L, s, F);
+      service_store<MV, OUT_F32>(L, s, F);
       break;
     }
     if (stage_flags(L, s) & kStageSyncOut) {
       // outputs read by a later stage must be visible before the barrier
-      service_store<OUT_F32>(L, s, F);
+      service_store<MV, OUT_F32>(L, s, F);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       service_arrive(ws, gs);
     } else {
       // arrive first: the stores then overlap the wait instead of delaying
       // the arrival
       service_arrive(ws, gs);
-      service_store<OUT_F32>(L, s, F);
+      service_store<MV, OUT_F32>(L, s, F);
     }
+    // with one buffer, the block's compute waves have all finished stage s,
+    // so activations no stage writes are fetched during the wait
+    if (!kDouble && !(stage_flags(L, s + 1) & kStageXInternal))
+      service_load_x<MV>(geo_of(L.st[s + 1]), stage_x(L, s + 1), false, L.x[0]);
     if (!service_wait(ws, F, gs)) return;
     if (stage_flags(L, s + 1) & kStageXInternal)
-      service_load_x(geo_of(L.st[s + 1]), stage_x(L, s + 1), true, L.x[(s + 1) & 1]);
+      service_load_x<MV>(geo_of(L.st[s + 1]), stage_x(L, s + 1), true, L.x[kDouble ? (s + 1) & 1 : 0]);
     compiler_fence();
     if ((threadIdx.x & 63) == 0) lds_puti(&F.x_stage, s + 1);
     wake_block();
     // every compute wave has finished stage s, so its buffer is free:
     // activations no stage writes are fetched while stage s + 1 runs
-    if (s + 2 < num_stages && !(stage_flags(L, s + 2) & kStageXInternal))
-      service_load_x(geo_of(L.st[s + 2]), stage_x(L, s + 2), false, L.x[s & 1]);
+    if (kDouble && s + 2 < num_stages && !(stage_flags(L, s + 2) & kStageXInternal))
+      service_load_x<MV>(geo_of(L.st[s + 2]), stage_x(L, s + 2), false, L.x[s & 1]);
   }
 }
 
 // ---------------------------------------------------------------- kernel
 
-template <bool OUT_F32>
+template <int MV, bool OUT_F32>
 __global__ void __launch_bounds__(64 * kChainWaves) __attribute__((amdgpu_waves_per_eu((kChainWaves + 3) / 4, (kChainWaves + 3) / 4)))
 chain_kernel(const ChainHeader* __restrict__ plan, uint32_t* __restrict__ ws, uint32_t nxcc) {
+  using S = ChainShape<MV>;
   extern __shared__ __align__(16) unsigned char lds_raw[];
-  __shared__ ChainFlags F;
-  ChainLds& L = *reinterpret_cast<ChainLds*>(lds_raw);
+  __shared__ ChainFlags<MV> F;
+  ChainLds<MV>& L = *reinterpret_cast<ChainLds<MV>*>(lds_raw);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   if (threadIdx.x < kSplitUnits) F.pieces_done[threadIdx.x] = 0u;
-  for (int e = threadIdx.x; e < kTabStages; e += blockDim.x) F.claim[e] = 0u;
+  for (int e = threadIdx.x; e < S::kTabStages; e += blockDim.x) F.claim[e] = 0u;
   if (threadIdx.x == 0) {
     F.done_total = 0u;
     F.x_stage = -1;
@@ -899,8 +987,8 @@ chain_kernel(const ChainHeader* __restrict__ plan, uint32_t* __restrict__ ws, ui
     // the plan must be one this library encoded, and fit the LDS tables
     const int ns = cload(&plan->num_stages), nm = cload(&plan->num_mats);
     const bool ok = coh_load(ws + kWsStatus) == 0u && cload(&plan->magic) == kChainMagic && ns > 0 &&
-                    ns <= kTabStages && nm > 0 && nm <= kTabMats && gridDim.x <= (unsigned)kChainMaxBlocks &&
-                    nxcc >= 1u && nxcc <= (unsigned)kMaxXcc;
+                    ns <= S::kTabStages && nm > 0 && nm <= S::kTabMats && cload(&plan->rows) == MV &&
+                    gridDim.x <= (unsigned)kChainMaxBlocks && nxcc >= 1u && nxcc <= (unsigned)kMaxXcc;
     F.go = ok ? 1u : 0u;
     if (!ok && blockIdx.x == 0 && coh_load(ws + kWsStatus) == 0u) coh_store(ws + kWsStatus, 2u);
   }
@@ -912,7 +1000,7 @@ chain_kernel(const ChainHeader* __restrict__ plan, uint32_t* __restrict__ ws, ui
   const ChainMatDesc* mats = reinterpret_cast<const ChainMatDesc*>(stages + num_stages);
   // the plan into LDS, one lane per stage and per matrix
   for (int s = threadIdx.x; s < num_stages; s += blockDim.x)
-    if (!build_stage_rec(L.st[s], stages + s, mats)) lds_put(&F.misfit, 1u);
+    if (!build_stage_rec<MV>(L.st[s], stages + s, mats)) lds_put(&F.misfit, 1u);
   for (int m = threadIdx.x; m < num_mats; m += blockDim.x) {
     MatRec r;
     r.packed = mats[m].packed;
@@ -930,9 +1018,9 @@ chain_kernel(const ChainHeader* __restrict__ plan, uint32_t* __restrict__ ws, ui
   }
 
   if (wave == kServiceWave) {
-    service_run<OUT_F32>(num_stages, L, F, ws, nxcc);
+    service_run<MV, OUT_F32>(num_stages, L, F, ws, nxcc);
   } else {
-    compute_run<OUT_F32>(num_stages, wave - 1, L, F, ws);
+    compute_run<MV, OUT_F32>(num_stages, wave - 1, L, F, ws);
   }
 }
 

@@ -9,7 +9,8 @@ pipeline diagram: 32 layers of width 4096) and the Depformer's per-codebook
 step (same page, MultiLinear figure).
 
 Two executors:
-* ``launches``: one q4_gemv call per matrix, in order, on the current stream
+* ``launches``: one q4_gemv (or, for several activation rows, q4_gemm_small)
+  call per matrix, in order, on the current stream
   (capturable into a HIP graph with ``torch.cuda.graph``);
 * ``chain``: the whole chain in one persistent launch (q4_chain_run).
 """
@@ -20,7 +21,7 @@ from typing import List, Optional
 
 import torch
 
-from . import q4_chain_build, q4_chain_run, q4_chain_workspace_bytes, q4_gemv
+from . import q4_chain_build, q4_chain_run, q4_chain_workspace_bytes, q4_gemm_small, q4_gemv
 
 
 @dataclass
@@ -49,7 +50,7 @@ class Q4Matrix:
 
 @dataclass
 class Stage:
-    x: torch.Tensor                     # bf16 [k]
+    x: torch.Tensor                     # bf16 [k], or [m, k] for m activation rows
     mats: List[Q4Matrix]
     outs: List[torch.Tensor] = field(default_factory=list)
 
@@ -61,7 +62,8 @@ class Chain:
         dev = stages[0].x.device
         for st in stages:
             if not st.outs:
-                st.outs = [torch.empty((m.n,), dtype=out_dtype, device=dev) for m in st.mats]
+                shape = (st.x.shape[0],) if st.x.dim() == 2 else ()
+                st.outs = [torch.empty(shape + (m.n,), dtype=out_dtype, device=dev) for m in st.mats]
         self._plan = None
         self._ws: Optional[torch.Tensor] = None
         self.device = dev
@@ -76,7 +78,10 @@ class Chain:
     def run_launches(self) -> None:
         for st in self.stages:
             for m, y in zip(st.mats, st.outs):
-                q4_gemv(st.x, m.packed, m.scales, m.biases, out=y)
+                if st.x.dim() == 1:
+                    q4_gemv(st.x, m.packed, m.scales, m.biases, out=y)
+                else:
+                    q4_gemm_small(st.x, m.packed, m.scales, m.biases, out=y)
 
     # ---- executor 2: one persistent launch for the whole chain
     def prepare_chain(self) -> None:

@@ -188,7 +188,9 @@ typedef struct q4_chain_stage {
 int64_t q4_chain_plan_bytes(int32_t num_stages, int32_t num_matrices);
 
 /* Validate the chain (same pointer/shape/alignment rules as q4_gemv for every
- * matrix) and write the plan into host_plan (plan_bytes long). No HIP call. */
+ * matrix) and write the plan into host_plan (plan_bytes long). Reads the
+ * device's compute-unit count (each block stages its share of a matrix's
+ * rows); launches nothing. */
 q4_status q4_chain_encode(const q4_chain_stage* stages, int32_t num_stages,
                           const q4_chain_matrix* matrices, int32_t num_matrices,
                           q4_out_dtype y_dtype, void* host_plan, int64_t plan_bytes);
@@ -202,6 +204,25 @@ q4_status q4_chain_encode(const q4_chain_stage* stages, int32_t num_stages,
  * the others' bounded waits expire (status 1) instead of hanging. */
 q4_status q4_chain_run(const void* device_plan, q4_out_dtype y_dtype, void* workspace,
                        void* stream);
+
+/* The same chain with m_rows (1..4) activation rows sharing every weight
+ * stream: concurrent conversations ("A smaller voice model", Concurrency
+ * section: several conversations read one copy of the weights). Each stage's
+ * x is bf16 [m_rows][k] and each matrix's y is [m_rows][n] (row-major,
+ * contiguous); every row r is the product of that matrix with x row r.
+ * m_rows == 1 is q4_chain_encode. With 2..4 rows the executor keeps one
+ * activation buffer per block (the next stage's rows are fetched during the
+ * stage barrier), which lowers its limits: at most 128 stages, 256 matrices,
+ * k <= 11264 and 32 units of 4 rows of one matrix per block
+ * (Q4_ERR_UNSUPPORTED otherwise); Q4_ERR_SHAPE if m_rows is out of range. */
+q4_status q4_chain_encode_rows(const q4_chain_stage* stages, int32_t num_stages,
+                               const q4_chain_matrix* matrices, int32_t num_matrices, int32_t m_rows,
+                               q4_out_dtype y_dtype, void* host_plan, int64_t plan_bytes);
+
+/* Run a plan encoded by q4_chain_encode_rows with the same m_rows (a plan
+ * encoded for another row count makes the kernel report status 2). */
+q4_status q4_chain_run_rows(const void* device_plan, int32_t m_rows, q4_out_dtype y_dtype,
+                            void* workspace, void* stream);
 
 #ifdef __cplusplus
 }

@@ -159,6 +159,58 @@ def test_chain_encode_validation_and_layout():
     assert lib.q4_chain_encode(ctypes.byref(s8), 2, ctypes.byref(m8), 2, 0, ctypes.byref(buf), nb) == q4.Q4_ERR_UNSUPPORTED
 
 
+def test_chain_encode_rows_validation():
+    """Several activation rows: the row count is checked and stored in the
+    plan's header (int32 at byte 20), the executor's lower limits for 2..4
+    rows are enforced, and buffer overlap is judged on m_rows rows."""
+    lib = q4.load()
+    nb = lib.q4_chain_plan_bytes(2, 2)
+    buf = (ctypes.c_uint8 * nb)()
+
+    def enc(stages, mats, m, ns=2, b=buf, size=nb):
+        return lib.q4_chain_encode_rows(ctypes.byref(stages), ns, ctypes.byref(mats), ns, m, 0, ctypes.byref(b), size)
+
+    stages, mats = _chain()
+    for m in (0, 5, -1):
+        assert enc(stages, mats, m) == q4.Q4_ERR_SHAPE
+    for m in (1, 2, 3, 4):
+        assert enc(stages, mats, m) == q4.Q4_OK
+        assert int.from_bytes(bytes(buf[20:24]), "little") == m
+    s1, m1 = _chain(k=11264, n=64)
+    assert enc(s1, m1, 4) == q4.Q4_OK
+    s2, m2 = _chain(k=11264 + 32, n=64)  # wider than the multi-row activation buffer
+    assert enc(s2, m2, 2) == q4.Q4_ERR_UNSUPPORTED
+    assert enc(s2, m2, 1) == q4.Q4_OK
+    # y starts one bf16 row of x past x: disjoint for one row, overlapping for two
+    s3, m3 = _chain(k=256, n=16, y=A16 + 2 * 256)
+    assert enc(s3, m3, 1) == q4.Q4_OK
+    assert enc(s3, m3, 2) == q4.Q4_ERR_UNSUPPORTED
+    # the LDS plan tables hold 128 stages for several rows (384 for one)
+    n129 = lib.q4_chain_plan_bytes(129, 129)
+    b129 = (ctypes.c_uint8 * n129)()
+    s4, m4 = _chain(n_stages=129)
+    assert enc(s4, m4, 2, 129, b129, n129) == q4.Q4_ERR_UNSUPPORTED
+    assert enc(s4, m4, 1, 129, b129, n129) == q4.Q4_OK
+    n128 = lib.q4_chain_plan_bytes(128, 128)
+    b128 = (ctypes.c_uint8 * n128)()
+    s5, m5 = _chain(n_stages=128)
+    assert enc(s5, m5, 4, 128, b128, n128) == q4.Q4_OK
+    # 32 units of 4 rows per block: n up to 32 * 4 * 256 compute units
+    s6, m6 = _chain(n=32 * 4 * 256)
+    assert enc(s6, m6, 2) == q4.Q4_OK
+    s7, m7 = _chain(n=32 * 4 * 256 + 4)
+    assert enc(s7, m7, 2) == q4.Q4_ERR_UNSUPPORTED
+    assert enc(s7, m7, 1) == q4.Q4_OK
+
+
+def test_chain_run_rows_validation():
+    lib = q4.load()
+    for m in (0, 5):
+        assert lib.q4_chain_run_rows(_p(A16), m, 0, _p(A16), None) == q4.Q4_ERR_SHAPE
+    assert lib.q4_chain_run_rows(None, 2, 0, _p(A16), None) == q4.Q4_ERR_NULL
+    assert lib.q4_chain_run_rows(_p(A16), 2, 3, _p(A16), None) == q4.Q4_ERR_SHAPE
+
+
 def test_chain_stage_geometry_and_dependencies():
     """Lanes per row and chunk count per stage, and the dependency flags the
     encoder derives from buffer overlap: stage 1 reads stage 0's output."""
