@@ -227,6 +227,8 @@ struct ChainFlags {
   float out[kMaxMatsPerStage][S::kStageUnits][kUnitRows][MV];  // the stage's finished rows
   uint32_t done_total;               // stage completions of all compute waves
   int32_t x_stage;                   // last stage whose activations are in LDS
+  int32_t x_fill;                    // stage whose activations the compute waves stage together
+  uint32_t x_filled;                 // compute-wave shares of such stagings done so far
   uint32_t abort;
   uint32_t go;
   uint32_t misfit;                   // a matrix has more units per block than the row staging holds
@@ -442,6 +444,10 @@ __device__ __forceinline__ bool build_stage_rec(StageRec& r, const ChainStageDes
   return fits;
 }
 template <int MV>
+__device__ __forceinline__ int stage_flags(const ChainLds<MV>& L, int s) { return ufl(L.st[s].flags); }
+template <int MV>
+__device__ __forceinline__ const uint16_t* stage_x(const ChainLds<MV>& L, int s) { return ufl_ptr(L.st[s].x); }
+template <int MV>
 __device__ __forceinline__ void stage_info(StageInfo& si, const ChainLds<MV>& L, int s) {
   const StageRec& r = L.st[s];
   si.s = s;
@@ -478,6 +484,9 @@ __device__ __forceinline__ void decode_item(const StageInfo& si, int i, Item& it
 
 // Buffer descriptor of a raw byte range: loads at offsets at or past nbytes
 // return zero without touching memory.
+// cache-policy bits of a buffer load: sc1, the device-coherent load (as the
+// agent-scope atomic loads above are issued)
+constexpr int kAuxSc1 = 16;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(const void* base, uint32_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)nbytes, 0x00020000);
 }
@@ -582,6 +591,59 @@ __device__ __forceinline__ void lc_load(LoadCursor& lc, Slot& d, int lane, const
   if (lc.left == 0) lc_next_item(lc, L, F, num_stages, cw, lane);
 }
 
+// One compute wave's share of staging stage t's activations (the layout
+// service_load_x writes): group e of the MV rows' 16 CH padded groups goes to
+// wave e / 64 mod kComputeWaves. Used where the waves would otherwise wait
+// for one wave to stage them alone: with one activation buffer (several
+// rows), and for activations an earlier stage wrote (loaded after the grid
+// barrier, COH: device-coherent loads). Every load goes through a range-checked
+// buffer descriptor (groups past G read zero), so that all of them are in flight together.
+template <int MV, bool COH>
+__device__ __forceinline__ void fill_x_share(const Geo& g, const void* x, uint32_t* buf, int cw, int lane) {
+  constexpr int kPer = 2;  // groups per lane in flight
+  constexpr int kSpan = kComputeWaves * 64;
+  const int gpad = kChunkGroups * g.CH;
+  const int total = MV * gpad;
+  const __amdgpu_buffer_rsrc_t rx = byte_range(x, (uint32_t)(MV * g.G * 64));
+  for (int base = cw * 64; base < total; base += kPer * kSpan) {
+    q4_u32x4 q[kPer][4];
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+      const int e = base + p * kSpan + lane;
+      int v = 0;
+#pragma unroll
+      for (int r = 1; r < MV; ++r) v += e >= r * gpad ? 1 : 0;
+      const int grp = e - v * gpad;
+      const uint32_t off = (e < total && grp < g.G) ? (uint32_t)((v * g.G + grp) * 64) : 0xFFFFFF00u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        q[p][j] = __builtin_bit_cast(q4_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(off + 16 * j), 0,
+                                                                                     COH ? kAuxSc1 : 0));
+    }
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+      const int e = base + p * kSpan + lane;
+      int v = 0;
+#pragma unroll
+      for (int r = 1; r < MV; ++r) v += e >= r * gpad ? 1 : 0;
+      const int grp = e - v * gpad;
+      if (e < total) {
+        uint32_t* dst = buf + v * ChainShape<MV>::kVecWords + grp * kXWordsPerGroup;
+        float xs = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint4 e4 = make_uint4(q[p][j].x, q[p][j].y, q[p][j].z, q[p][j].w);
+          uint32_t p02, p46, p13, p57;
+          x_to_pairs(e4, p02, p46, p13, p57);
+          *reinterpret_cast<uint4*>(dst + 4 * j) = make_uint4(p02, p46, p13, p57);
+          xs += x_sum8(e4);
+        }
+        dst[16] = __float_as_uint(xs);
+      }
+    }
+  }
+}
+
 template <int MV, bool OUT_F32>
 __device__ __forceinline__ void compute_body(int num_stages, int cw, ChainLds<MV>& L, ChainFlags<MV>& F,
                                              uint32_t* ws) {
@@ -616,7 +678,23 @@ __device__ __forceinline__ void compute_body(int num_stages, int cw, ChainLds<MV
   // grid has finished the stages before it)
   auto enter_stage = [&]() {
     uint32_t spins = 0;
+    bool filled = false;
     while (!stop && lds_geti(&F.x_stage) < si.s) {
+      if (!filled && lds_geti(&F.x_fill) == si.s) {
+        // the service wave asks the compute waves to stage these activations
+        compiler_fence();
+        const Geo g = geo_of(L.st[si.s]);
+        uint32_t* buf = L.x[S::kXBuffers == 2 ? si.s & 1 : 0];
+        if (stage_flags(L, si.s) & kStageXInternal)
+          fill_x_share<MV, true>(g, stage_x(L, si.s), buf, cw, lane);
+        else
+          fill_x_share<MV, false>(g, stage_x(L, si.s), buf, cw, lane);
+        compiler_fence();
+        if (lane == 0) lds_add(&F.x_filled, 1u);
+        wake_block();
+        filled = true;
+        continue;
+      }
       nap();
       stop = lds_get(&F.abort) != 0u || ++spins > kSpinLimit;
     }
@@ -907,10 +985,6 @@ __device__ __forceinline__ void service_store(const ChainLds<MV>& L, int s, Chai
   }
 }
 
-template <int MV>
-__device__ __forceinline__ int stage_flags(const ChainLds<MV>& L, int s) { return ufl(L.st[s].flags); }
-template <int MV>
-__device__ __forceinline__ const uint16_t* stage_x(const ChainLds<MV>& L, int s) { return ufl_ptr(L.st[s].x); }
 
 template <int MV, bool OUT_F32>
 __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, ChainFlags<MV>& F, uint32_t* ws,
@@ -924,6 +998,7 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, Cha
   wake_block();
   if (kDouble && num_stages > 1 && !(stage_flags(L, 1) & kStageXInternal))
     service_load_x<MV>(geo_of(L.st[1]), stage_x(L, 1), false, L.x[kDouble ? 1 : 0]);
+  int fills = 0;  // stagings shared with the compute waves so far
   for (int s = 0; s < num_stages; ++s) {
     uint32_t spins = 0;
     while ((int)(lds_get(&F.done_total) - (uint32_t)(kComputeWaves * (s + 1))) < 0) {
@@ -949,13 +1024,33 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, Cha
       service_arrive(ws, gs);
       service_store<MV, OUT_F32>(L, s, F);
     }
-    // with one buffer, the block's compute waves have all finished stage s,
-    // so activations no stage writes are fetched during the wait
-    if (!kDouble && !(stage_flags(L, s + 1) & kStageXInternal))
-      service_load_x<MV>(geo_of(L.st[s + 1]), stage_x(L, s + 1), false, L.x[0]);
+    // The compute waves stage the next activations together where they would
+    // otherwise wait for this wave to do it alone: with one buffer (the
+    // block's compute waves have all finished stage s, so it is free; the
+    // activations no stage writes are staged during the barrier), and for
+    // activations written in the chain (after the barrier).
+    const bool internal = (stage_flags(L, s + 1) & kStageXInternal) != 0;
+    const bool shared_fill = !kDouble || internal;
+    if (shared_fill && !internal) {
+      if ((threadIdx.x & 63) == 0) lds_puti(&F.x_fill, s + 1);
+      wake_block();
+    }
     if (!service_wait(ws, F, gs)) return;
-    if (stage_flags(L, s + 1) & kStageXInternal)
-      service_load_x<MV>(geo_of(L.st[s + 1]), stage_x(L, s + 1), true, L.x[kDouble ? (s + 1) & 1 : 0]);
+    if (shared_fill) {
+      if (internal) {
+        if ((threadIdx.x & 63) == 0) lds_puti(&F.x_fill, s + 1);
+        wake_block();
+      }
+      ++fills;
+      uint32_t fspins = 0;
+      while ((int)(lds_get(&F.x_filled) - (uint32_t)(kComputeWaves * fills)) < 0) {
+        nap();
+        if (lds_get(&F.abort) != 0u || ++fspins > kSpinLimit) {
+          service_fail(ws, F, 1u);
+          return;
+        }
+      }
+    }
     compiler_fence();
     if ((threadIdx.x & 63) == 0) lds_puti(&F.x_stage, s + 1);
     wake_block();
@@ -982,6 +1077,8 @@ chain_kernel(const ChainHeader* __restrict__ plan, uint32_t* __restrict__ ws, ui
   if (threadIdx.x == 0) {
     F.done_total = 0u;
     F.x_stage = -1;
+    F.x_fill = -1;
+    F.x_filled = 0u;
     F.abort = 0u;
     F.misfit = 0u;
     // the plan must be one this library encoded, and fit the LDS tables
