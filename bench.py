@@ -40,13 +40,13 @@ HBM_PEAK_GBS = 8000.0
 # HBM traffic of one chain_kernel launch over the full step, from two rocprofv3
 # --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch),
 # each scaled by what the same counter reads for a plain 1 GiB copy
-# (``--calibrate-copy 1024``: FETCH_SIZE reads 524301.8 KiB for 1 GiB fetched,
+# (``--calibrate-copy 1024``: FETCH_SIZE reads 524301.7 KiB for 1 GiB fetched,
 # WRITE_SIZE 1048576.0 KiB for 1 GiB written). Valid only for the kernel sources
 # whose hash is recorded: any change to them reports traffic as null until the
 # counters are taken again (profiles/chain_kernel_temporal_step_m1_pmc.md).
 CHAIN_TRAFFIC = {
-    "sources_sha256_16": "42615515ed6af7d7",
-    "fetch_kib": 2049826.7, "fetch_scale": 1048576.0 / 524301.8,
+    "sources_sha256_16": "c87a9cd1de4bac05",
+    "fetch_kib": 2048416.3, "fetch_scale": 1048576.0 / 524301.7,
     "write_kib": 4119.8, "write_scale": 1048576.0 / 1048576.0,
 }
 KERNEL_SOURCES = ("q4_chain.h", "q4_kernels.h", "q4_api.hip")
@@ -115,6 +115,28 @@ def make_temporal_chain(seed: int = 0, layers: int = workloads.TEMPORAL_LAYERS,
             log(f"[bench] built {layer + 1}/{layers} layers ({time.time() - t0:.1f}s)")
     torch.cuda.synchronize()
     return Chain(stages, out_dtype)
+
+
+def make_small_gemm(chain, m: int, seed: int = 0, device=None):
+    """The small-GEMM workload: every stage of the temporal step (its packed
+    matrices reused) against m activation rows, drawn per layer and stage on the
+    host (seeded) as for the step. Returns the stages, x [m, k] and outputs
+    [m, n] bf16 on the device."""
+    import torch
+
+    from bit_group_quantized_amd.step import Stage
+
+    device = device or torch.device("cuda:0")
+    keys = sorted({li.stage for li in workloads.temporal_layer()})
+    stages = []
+    for si, st in enumerate(chain.stages):
+        layer, key = si // len(keys), keys[si % len(keys)]
+        k = st.x.shape[-1]
+        x = workloads.activations(seed, workloads.CFG_SMALL_GEMM, layer, 100 + key, m, k)
+        xt = torch.from_numpy(x.view(np.int16)).to(device).view(torch.bfloat16)
+        outs = [torch.empty((m, mt.n), dtype=torch.bfloat16, device=device) for mt in st.mats]
+        stages.append(Stage(xt, st.mats, outs))
+    return stages
 
 
 def make_depformer(seed: int = 0, device=None):
@@ -461,27 +483,18 @@ def bench_other(args, dev) -> int:
         if not 1 <= args.m <= 16:
             print("--m must be in 1..16", file=sys.stderr)
             return 2
+        from bit_group_quantized_amd.step import Chain
+
         chain = make_temporal_chain(args.seed, args.layers, device=dev)
         wbytes = chain.weight_bytes()
-        xs = [torch.randn((args.m, st.x.numel()), device=dev, generator=torch.Generator(device=dev).manual_seed(si))
-              .to(torch.bfloat16) for si, st in enumerate(chain.stages)]
-        outs = [[torch.empty((args.m, mt.n), dtype=torch.bfloat16, device=dev) for mt in st.mats] for st in chain.stages]
-
+        rows_chain = Chain(make_small_gemm(chain, args.m, args.seed, dev))
         use_chain = args.mode == "chain" and args.m <= 4
         if use_chain:
-            # the same weights and activation rows through one persistent launch
-            from bit_group_quantized_amd.step import Chain, Stage
-
-            rows_chain = Chain([Stage(x, st.mats, ys) for x, st, ys in zip(xs, chain.stages, outs)])
+            # the step's weights and the m activation rows through one persistent launch
             rows_chain.prepare_chain()
             run, launches, kernel = rows_chain.run_chain, 1, "chain_kernel"
         else:
-            def calls():
-                for x, st, ys in zip(xs, chain.stages, outs):
-                    for mt, y in zip(st.mats, ys):
-                        q4.q4_gemm_small(x, mt.packed, mt.scales, mt.biases, out=y)
-
-            g = graph_of(calls)
+            g = graph_of(rows_chain.run_launches)
             run, launches = g.replay, chain.num_matrices()
             kernel = "gemv_kernel" if args.m <= 4 else "gemm_mfma_kernel"
         ms, per = time_replays(run, args.steps, args.warmup)

@@ -482,11 +482,11 @@ __device__ __forceinline__ void decode_item(const StageInfo& si, int i, Item& it
   it.cb = ufl((int)(((uint32_t)((it.p + 1) * si.CH) * si.inv_p) >> 16));
 }
 
-// Buffer descriptor of a raw byte range: loads at offsets at or past nbytes
-// return zero without touching memory.
 // cache-policy bits of a buffer load: sc1, the device-coherent load (as the
 // agent-scope atomic loads above are issued)
 constexpr int kAuxSc1 = 16;
+// Buffer descriptor of a raw byte range: loads at offsets at or past nbytes
+// return zero without touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(const void* base, uint32_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)nbytes, 0x00020000);
 }

@@ -5,7 +5,9 @@ conversations sharing every weight stream) against the CPU oracle.
 * a dependent chain where each stage's [m, k] activation IS the previous
   stage's bf16 [m, n] output, outputs pre-filled with a poison value;
 * the chain against one q4_gemm_small launch per matrix on the same inputs;
-* a plan encoded for one row count run with another is refused by the kernel.
+* a plan encoded for one row count run with another is refused by the kernel;
+* the small-GEMM step at m=4 (chain) and m=16 (per-matrix launches) exactly as
+  the benchmark builds and runs it, sampled layers against the oracle.
 """
 import numpy as np
 import pytest
@@ -154,3 +156,52 @@ def test_plan_row_count_mismatch_is_refused():
     torch.cuda.synchronize()
     assert chain.chain_status() == 0
     assert oracle.floored_rel_err(out_np(y), oracle.matmul(x, P, S, B, k)) <= TOL_F32
+
+
+_STEP_QUANT = {}
+
+
+def _step_weights(seed, layer, li):
+    key = (seed, layer, li.item)
+    if key not in _STEP_QUANT:
+        w = workloads.weights(seed, workloads.CFG_STEP, layer, li.item, li.n, li.k)
+        _STEP_QUANT[key] = oracle.quantize(w)
+    return _STEP_QUANT[key]
+
+
+@pytest.mark.parametrize("m", [4, 16])
+def test_small_gemm_step_sampled_layers(m):
+    """The small-GEMM step as the benchmark runs it: the temporal step's 224
+    packed matrices against m activation rows per stage, in one chain launch
+    for m=4 and one q4_gemm_small launch per matrix for m=16. Layers 0, 17 and
+    31 are checked against the oracle on weights and activations rebuilt on
+    the host."""
+    import bench
+
+    seed = 0
+    dev = torch.device("cuda:0")
+    base = bench.make_temporal_chain(seed, device=dev)
+    rows = Chain(bench.make_small_gemm(base, m, seed, dev))
+    if m <= 4:
+        rows.run_chain()
+        rows.run_chain()
+    else:
+        rows.run_launches()
+    torch.cuda.synchronize()
+    if m <= 4:
+        assert rows.chain_status() == 0
+    by_stage = {}
+    for li in workloads.temporal_layer():
+        by_stage.setdefault(li.stage, []).append(li)
+    keys = sorted(by_stage)
+    assert len(rows.stages) == workloads.TEMPORAL_LAYERS * len(keys)
+    for layer in (0, 17, 31):
+        for si, key in enumerate(keys):
+            stage = rows.stages[layer * len(keys) + si]
+            k = by_stage[key][0].k
+            x = workloads.activations(seed, workloads.CFG_SMALL_GEMM, layer, 100 + key, m, k)
+            assert np.array_equal(bf16_bits_np(stage.x), x)
+            for li, y in zip(by_stage[key], stage.outs):
+                P, S, B = _step_weights(seed, layer, li)
+                ref = oracle.matmul(x, P, S, B, li.k)
+                assert oracle.floored_rel_err(out_np(y), ref) <= TOL_BF16, (m, layer, li.name)
