@@ -30,6 +30,7 @@ Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_UNSUPPORTED, Q4_ERR_HIP =
 Q4_OUT_BF16, Q4_OUT_F32 = 0, 1
 GROUP = 32
 MAX_M = 16
+MAX_K = 16384  # Q4_MAX_K
 
 _lib = None
 

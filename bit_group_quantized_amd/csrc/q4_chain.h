@@ -830,65 +830,87 @@ __device__ __forceinline__ void compute_run(int num_stages, int cw, ChainLds<MV>
 
 // ---------------------------------------------------------------- service
 
-// Load a stage's activations into an LDS buffer, re-paired, with group sums;
-// groups past G up to 16 CH are zero. Coherent loads when an earlier stage of
-// this launch wrote them.
+// A stage's activations are staged into an LDS buffer re-paired, with group
+// sums; groups past G up to 16 CH are zero. Coherent loads when an earlier
+// stage of this launch wrote them. The service wave takes kXBatch groups per
+// lane at a time: xb_issue starts a batch's loads into registers, xb_store
+// writes the batch to LDS once they are in (MV activation rows [MV][k] in
+// memory; row v goes to dst_buf + v * kVecWords).
+constexpr int kXBatch = 3;
+struct XBatch {
+  uint64_t q[kXBatch][8];
+};
 template <int MV>
-__device__ __forceinline__ void service_load_x(const Geo& g, const void* x, bool coherent, uint32_t* dst_buf) {
-  // (MV activation rows [MV][k] in memory; row v goes to dst_buf + v * kVecWords)
-  constexpr int kBatch = 3;  // groups per lane whose loads are in flight together
+__device__ __forceinline__ int xb_row(int e, int gpad) {
+  int v = 0;
+#pragma unroll
+  for (int r = 1; r < MV; ++r) v += e >= r * gpad ? 1 : 0;
+  return v;
+}
+template <int MV>
+__device__ __forceinline__ void xb_issue(const Geo& g, const void* x, bool coherent, int base, XBatch& xb) {
   const int lane = threadIdx.x & 63;
   const int gpad = kChunkGroups * g.CH;
   const int total = MV * gpad;
   const uint64_t* x64 = static_cast<const uint64_t*>(x);
-  for (int base = 0; base < total; base += 64 * kBatch) {
-    uint64_t q[kBatch][8];
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int e = base + 64 * b + lane;
-      int v = 0;
+  for (int b = 0; b < kXBatch; ++b) {
+    const int e = base + 64 * b + lane;
+    const int v = xb_row<MV>(e, gpad);
+    const int grp = e - v * gpad;
 #pragma unroll
-      for (int r = 1; r < MV; ++r) v += e >= r * gpad ? 1 : 0;
-      const int grp = e - v * gpad;
+    for (int i = 0; i < 8; ++i) xb.q[b][i] = 0u;
+    if (e < total && grp < g.G) {
+      const uint64_t* src = x64 + ((int64_t)v * g.G + grp) * 8;
+      if (coherent) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) q[b][i] = 0u;
-      if (e < total && grp < g.G) {
-        const uint64_t* src = x64 + ((int64_t)v * g.G + grp) * 8;
-        if (coherent) {
+        for (int i = 0; i < 8; ++i) xb.q[b][i] = coh_load64(src + i);
+      } else {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) q[b][i] = coh_load64(src + i);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) q[b][i] = gload(src + i);
-        }
+        for (int i = 0; i < 8; ++i) xb.q[b][i] = gload(src + i);
       }
     }
+  }
+}
+template <int MV>
+__device__ __forceinline__ void xb_store(const Geo& g, int base, const XBatch& xb, uint32_t* dst_buf) {
+  const int lane = threadIdx.x & 63;
+  const int gpad = kChunkGroups * g.CH;
+  const int total = MV * gpad;
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int e = base + 64 * b + lane;
-      int v = 0;
+  for (int b = 0; b < kXBatch; ++b) {
+    const int e = base + 64 * b + lane;
+    const int v = xb_row<MV>(e, gpad);
+    const int grp = e - v * gpad;
+    if (e < total) {
+      // (groups past G are zero)
+      uint32_t* dst = dst_buf + v * ChainShape<MV>::kVecWords + grp * kXWordsPerGroup;
+      float xs = 0.f;
 #pragma unroll
-      for (int r = 1; r < MV; ++r) v += e >= r * gpad ? 1 : 0;
-      const int grp = e - v * gpad;
-      if (e < total) {
-        // (groups past G are zero)
-        uint32_t* dst = dst_buf + v * ChainShape<MV>::kVecWords + grp * kXWordsPerGroup;
-        float xs = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint4 e4;
-          e4.x = (uint32_t)q[b][2 * j];
-          e4.y = (uint32_t)(q[b][2 * j] >> 32);
-          e4.z = (uint32_t)q[b][2 * j + 1];
-          e4.w = (uint32_t)(q[b][2 * j + 1] >> 32);
-          uint32_t p02, p46, p13, p57;
-          x_to_pairs(e4, p02, p46, p13, p57);
-          *reinterpret_cast<uint4*>(dst + 4 * j) = make_uint4(p02, p46, p13, p57);
-          xs += x_sum8(e4);
-        }
-        dst[16] = __float_as_uint(xs);
+      for (int j = 0; j < 4; ++j) {
+        uint4 e4;
+        e4.x = (uint32_t)xb.q[b][2 * j];
+        e4.y = (uint32_t)(xb.q[b][2 * j] >> 32);
+        e4.z = (uint32_t)xb.q[b][2 * j + 1];
+        e4.w = (uint32_t)(xb.q[b][2 * j + 1] >> 32);
+        uint32_t p02, p46, p13, p57;
+        x_to_pairs(e4, p02, p46, p13, p57);
+        *reinterpret_cast<uint4*>(dst + 4 * j) = make_uint4(p02, p46, p13, p57);
+        xs += x_sum8(e4);
       }
+      dst[16] = __float_as_uint(xs);
     }
+  }
+}
+// the batches from group index `from` on, then wait for the LDS writes
+template <int MV>
+__device__ __forceinline__ void service_load_x(const Geo& g, const void* x, bool coherent, uint32_t* dst_buf,
+                                               int from = 0) {
+  const int total = MV * kChunkGroups * g.CH;
+  for (int base = from; base < total; base += 64 * kXBatch) {
+    XBatch xb;
+    xb_issue<MV>(g, x, coherent, base, xb);
+    xb_store<MV>(g, base, xb, dst_buf);
   }
   lds_wait();
 }
@@ -1024,6 +1046,15 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, Cha
       service_arrive(ws, gs);
       service_store<MV, OUT_F32>(L, s, F);
     }
+    // Activations no stage writes, for stage s + 2, go to the buffer stage s
+    // used (every compute wave has finished stage s): the loads of their first
+    // batch are issued now and arrive during the barrier; the batch is written
+    // and the rest fetched once stage s + 1 is published. (Loading them only
+    // after publishing would hold back this wave's next arrival whenever stage
+    // s + 1 is shorter than the load.)
+    const bool prefetch = kDouble && s + 2 < num_stages && !(stage_flags(L, s + 2) & kStageXInternal);
+    XBatch xb;
+    if (prefetch) xb_issue<MV>(geo_of(L.st[s + 2]), stage_x(L, s + 2), false, 0, xb);
     // The compute waves stage the next activations together where they would
     // otherwise wait for this wave to do it alone: with one buffer (the
     // block's compute waves have all finished stage s, so it is free; the
@@ -1054,10 +1085,11 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, Cha
     compiler_fence();
     if ((threadIdx.x & 63) == 0) lds_puti(&F.x_stage, s + 1);
     wake_block();
-    // every compute wave has finished stage s, so its buffer is free:
-    // activations no stage writes are fetched while stage s + 1 runs
-    if (kDouble && s + 2 < num_stages && !(stage_flags(L, s + 2) & kStageXInternal))
-      service_load_x<MV>(geo_of(L.st[s + 2]), stage_x(L, s + 2), false, L.x[s & 1]);
+    if (prefetch) {
+      const Geo g2 = geo_of(L.st[s + 2]);
+      xb_store<MV>(g2, 0, xb, L.x[s & 1]);
+      service_load_x<MV>(g2, stage_x(L, s + 2), false, L.x[s & 1], 64 * kXBatch);
+    }
   }
 }
 

@@ -62,6 +62,7 @@ def _p(v):
     (dict(scales=ODD), q4.Q4_ERR_ALIGN),
     (dict(y=ODD), q4.Q4_ERR_ALIGN),
     (dict(k=32 * 1024), q4.Q4_ERR_UNSUPPORTED),
+    (dict(k=q4.MAX_K + 32), q4.Q4_ERR_UNSUPPORTED),  # one group past the widest supported row
 ])
 def test_gemv_validation(case, want):
     a = dict(x=A16, packed=A16, scales=A16, biases=A16, n=16, k=64, y=A16, dtype=0)

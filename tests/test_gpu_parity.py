@@ -164,6 +164,23 @@ def test_gemm_rows_equal_gemv():
         assert oracle.floored_rel_err(out_np(Y[i]), out_np(y)) <= 2 * TOL_F32
 
 
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_widest_k(m):
+    """k at the library's limit (16384: 512 groups, the MFMA kernel's 32 groups
+    per wave times 16 waves), with a ragged row count."""
+    n, k = 100, q4.MAX_K
+    P, S, B = oracle.quantize(_w(n, k, seed=31))
+    x = _x(m, k, seed=32 + m)
+    gx = to_gpu_bf16_bits(x if m > 1 else x[0])
+    if m == 1:
+        y = q4.q4_gemv(gx, *upload_quantized(P, S, B), out_dtype=torch.float32)
+    else:
+        y = q4.q4_gemm_small(gx, *upload_quantized(P, S, B), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.matmul(x, P, S, B, k)
+    _check(y, ref[0] if m == 1 else ref, torch.float32)
+
+
 def test_deterministic():
     n, k = 11264, 4096
     w = _w(n, k, seed=23)
