@@ -165,9 +165,6 @@ __device__ __forceinline__ T gload_off(const unsigned char* base, uint32_t off) 
 __device__ __forceinline__ uint32_t coh_load(const uint32_t* p) {
   return __hip_atomic_load((const Q4_GLOBAL uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint64_t coh_load64(const uint64_t* p) {
-  return __hip_atomic_load((const Q4_GLOBAL uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ void coh_store(uint32_t* p, uint32_t v) {
   __hip_atomic_store((Q4_GLOBAL uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -831,9 +828,9 @@ __device__ __forceinline__ void compute_run(int num_stages, int cw, ChainLds<MV>
 // ---------------------------------------------------------------- service
 
 // A stage's activations are staged into an LDS buffer re-paired, with group
-// sums; groups past G up to 16 CH are zero. Coherent loads when an earlier
-// stage of this launch wrote them. The service wave takes kXBatch groups per
-// lane at a time: xb_issue starts a batch's loads into registers, xb_store
+// sums; groups past G up to 16 CH are zero. The service wave stages
+// activations no stage writes (the compute waves stage the others, after the
+// barrier: fill_x_share), kXBatch groups per lane at a time: xb_issue starts a batch's loads into registers, xb_store
 // writes the batch to LDS once they are in (MV activation rows [MV][k] in
 // memory; row v goes to dst_buf + v * kVecWords).
 constexpr int kXBatch = 3;
@@ -848,7 +845,7 @@ __device__ __forceinline__ int xb_row(int e, int gpad) {
   return v;
 }
 template <int MV>
-__device__ __forceinline__ void xb_issue(const Geo& g, const void* x, bool coherent, int base, XBatch& xb) {
+__device__ __forceinline__ void xb_issue(const Geo& g, const void* x, int base, XBatch& xb) {
   const int lane = threadIdx.x & 63;
   const int gpad = kChunkGroups * g.CH;
   const int total = MV * gpad;
@@ -862,13 +859,8 @@ __device__ __forceinline__ void xb_issue(const Geo& g, const void* x, bool coher
     for (int i = 0; i < 8; ++i) xb.q[b][i] = 0u;
     if (e < total && grp < g.G) {
       const uint64_t* src = x64 + ((int64_t)v * g.G + grp) * 8;
-      if (coherent) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xb.q[b][i] = coh_load64(src + i);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xb.q[b][i] = gload(src + i);
-      }
+      for (int i = 0; i < 8; ++i) xb.q[b][i] = gload(src + i);
     }
   }
 }
@@ -904,12 +896,11 @@ __device__ __forceinline__ void xb_store(const Geo& g, int base, const XBatch& x
 }
 // the batches from group index `from` on, then wait for the LDS writes
 template <int MV>
-__device__ __forceinline__ void service_load_x(const Geo& g, const void* x, bool coherent, uint32_t* dst_buf,
-                                               int from = 0) {
+__device__ __forceinline__ void service_load_x(const Geo& g, const void* x, uint32_t* dst_buf, int from = 0) {
   const int total = MV * kChunkGroups * g.CH;
   for (int base = from; base < total; base += 64 * kXBatch) {
     XBatch xb;
-    xb_issue<MV>(g, x, coherent, base, xb);
+    xb_issue<MV>(g, x, base, xb);
     xb_store<MV>(g, base, xb, dst_buf);
   }
   lds_wait();
@@ -1014,12 +1005,12 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, Cha
   constexpr bool kDouble = ChainShape<MV>::kXBuffers == 2;
   GridSync gs;
   if (!service_start(ws, F, gs, nxcc)) return;
-  service_load_x<MV>(geo_of(L.st[0]), stage_x(L, 0), false, L.x[0]);
+  service_load_x<MV>(geo_of(L.st[0]), stage_x(L, 0), L.x[0]);
   compiler_fence();
   if ((threadIdx.x & 63) == 0) lds_puti(&F.x_stage, 0);
   wake_block();
   if (kDouble && num_stages > 1 && !(stage_flags(L, 1) & kStageXInternal))
-    service_load_x<MV>(geo_of(L.st[1]), stage_x(L, 1), false, L.x[kDouble ? 1 : 0]);
+    service_load_x<MV>(geo_of(L.st[1]), stage_x(L, 1), L.x[kDouble ? 1 : 0]);
   int fills = 0;  // stagings shared with the compute waves so far
   for (int s = 0; s < num_stages; ++s) {
     uint32_t spins = 0;
@@ -1054,7 +1045,7 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, Cha
     // s + 1 is shorter than the load.)
     const bool prefetch = kDouble && s + 2 < num_stages && !(stage_flags(L, s + 2) & kStageXInternal);
     XBatch xb;
-    if (prefetch) xb_issue<MV>(geo_of(L.st[s + 2]), stage_x(L, s + 2), false, 0, xb);
+    if (prefetch) xb_issue<MV>(geo_of(L.st[s + 2]), stage_x(L, s + 2), 0, xb);
     // The compute waves stage the next activations together where they would
     // otherwise wait for this wave to do it alone: with one buffer (the
     // block's compute waves have all finished stage s, so it is free; the
@@ -1088,7 +1079,7 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, Cha
     if (prefetch) {
       const Geo g2 = geo_of(L.st[s + 2]);
       xb_store<MV>(g2, 0, xb, L.x[s & 1]);
-      service_load_x<MV>(g2, stage_x(L, s + 2), false, L.x[s & 1], 64 * kXBatch);
+      service_load_x<MV>(g2, stage_x(L, s + 2), L.x[s & 1], 64 * kXBatch);
     }
   }
 }
