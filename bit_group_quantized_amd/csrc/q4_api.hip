@@ -127,11 +127,19 @@ void launch_gemm_gs(int waves, bool f32, const uint16_t* x, int m, const uint32_
   constexpr int KB = 4;
   const size_t shmem = static_cast<size_t>(waves) * T * 256 * sizeof(float) +
                        static_cast<size_t>(waves) * 2 * T * 16 * (KB * 4 + 4) * sizeof(uint32_t);
-  if (f32)
-    hipLaunchKernelGGL((q4k::gemm_mfma_kernel<GS, T, true>), grid, block, shmem, st, x, m, packed,
+  // (16-byte runs of scales per row when every row's run is 16-byte aligned)
+  const bool sb16 = G % 8 == 0 && aligned(scales, 16) && aligned(biases, 16);
+  if (f32 && sb16)
+    hipLaunchKernelGGL((q4k::gemm_mfma_kernel<GS, T, true, true>), grid, block, shmem, st, x, m, packed,
+                       scales, biases, n, G, y);
+  else if (f32)
+    hipLaunchKernelGGL((q4k::gemm_mfma_kernel<GS, T, true, false>), grid, block, shmem, st, x, m, packed,
+                       scales, biases, n, G, y);
+  else if (sb16)
+    hipLaunchKernelGGL((q4k::gemm_mfma_kernel<GS, T, false, true>), grid, block, shmem, st, x, m, packed,
                        scales, biases, n, G, y);
   else
-    hipLaunchKernelGGL((q4k::gemm_mfma_kernel<GS, T, false>), grid, block, shmem, st, x, m, packed,
+    hipLaunchKernelGGL((q4k::gemm_mfma_kernel<GS, T, false, false>), grid, block, shmem, st, x, m, packed,
                        scales, biases, n, G, y);
 }
 

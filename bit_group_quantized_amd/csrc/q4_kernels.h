@@ -336,7 +336,11 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const uint16_t* __restrict__
 // A block has S waves; wave w owns groups [w*GS, (w+1)*GS) and keeps its
 // activation tile in registers; the block walks T tiles of 16 weight rows and
 // the S waves' tiles are summed in fixed order through LDS.
-template <int GS, int T, bool OUT_F32>
+// SB16: G is a multiple of 8, so a row's scales (and biases) of the wave's GS
+// groups are 16-byte aligned runs, loaded once per row with 16-byte loads
+// (GS / 8 per row) instead of one 2-byte load per group and batch: 16 rows
+// per load either way, so that cuts the cache lines looked up per wave by 8.
+template <int GS, int T, bool OUT_F32, bool SB16>
 __global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restrict__ x, int m,
                                                           const uint32_t* __restrict__ packed,
                                                           const uint16_t* __restrict__ scales,
@@ -406,20 +410,37 @@ __global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restr
   constexpr int kRowWords = KB * 4 + 4;
   uint32_t* stage = reinterpret_cast<uint32_t*>(red_dyn + nwaves * T * 256) + wave * (2 * T * 16 * kRowWords);
   u32x4_t wq[2][T][kPerLane];
-  uint32_t sb[2][T][KB], bb[2][T][KB];
+  uint32_t sb[2][T][SB16 ? 1 : KB], bb[2][T][SB16 ? 1 : KB];
+  constexpr int kSW = SB16 ? GS / 8 : 1;  // 16-byte runs of scales per row and wave
+  u32x4_t sw[T][kSW], bw[T][kSW];
+  if constexpr (SB16) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+#pragma unroll
+      for (int c = 0; c < kSW; ++c) {
+        // (past the wave's groups or the row tile: zeros, or groups weighed zero below)
+        const int lr = 16 * t + r16;
+        const uint32_t os = g0 + 8 * c < G ? (uint32_t)((lr * G + g0 + 8 * c) * 2) : 0xFFFFFFF0u;
+        sw[t][c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)os, 0, 0));
+        bw[t][c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, (int)os, 0, 0));
+      }
+    }
+  }
   u32x4_t xb[2][kXReg ? 1 : KB];
   auto load_batch = [&](int i0, int buf) {
 #pragma unroll
     for (int ii = 0; ii < KB; ++ii) {
       if constexpr (!kXReg) xb[buf][ii] = x_load(i0 + ii);
-      const bool gok = i0 + ii < gcount;
-      const int g = g0 + i0 + ii;
+      if constexpr (!SB16) {
+        const bool gok = i0 + ii < gcount;
+        const int g = g0 + i0 + ii;
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const int lr = 16 * t + r16;  // row within the tile (the range ends at n)
-        const uint32_t os = gok ? (uint32_t)((lr * G + g) * 2) : 0xFFFFFFF0u;
-        sb[buf][t][ii] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)os, 0, 0);
-        bb[buf][t][ii] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, (int)os, 0, 0);
+        for (int t = 0; t < T; ++t) {
+          const int lr = 16 * t + r16;  // row within the tile (the range ends at n)
+          const uint32_t os = gok ? (uint32_t)((lr * G + g) * 2) : 0xFFFFFFF0u;
+          sb[buf][t][ii] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)os, 0, 0);
+          bb[buf][t][ii] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, (int)os, 0, 0);
+        }
       }
     }
 #pragma unroll
@@ -467,8 +488,19 @@ __global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restr
         word_to_bf16_pairs(sbuf[(t * 16 + r16) * kRowWords + ii * 4 + kb], q02, q46, q13, q57);
         const u32x4_t bq = u32x4_t{q02, q46, q13, q57};
         const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bq), zero, 0, 0, 0);
-        const float s = bf16_to_f32(sb[buf][t][ii]);
-        const float b = bf16_to_f32(bb[buf][t][ii]);
+        float s, b;
+        if constexpr (SB16) {
+          // group gi of the wave: half gi % 2 of word (gi % 8) / 2 of run gi / 8;
+          // groups past the wave's share weigh zero
+          const int gi = i0 + ii;
+          const uint32_t ws = sw[t][gi / 8][(gi % 8) / 2], wb = bw[t][gi / 8][(gi % 8) / 2];
+          const bool gok = gi < gcount;
+          s = gok ? __uint_as_float(gi % 2 ? ws & 0xFFFF0000u : ws << 16) : 0.f;
+          b = gok ? __uint_as_float(gi % 2 ? wb & 0xFFFF0000u : wb << 16) : 0.f;
+        } else {
+          s = bf16_to_f32(sb[buf][t][ii]);
+          b = bf16_to_f32(bb[buf][t][ii]);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[t][j] = fmaf(s, d[j], fmaf(b, xg[j], acc[t][j]));
       }
