@@ -124,7 +124,7 @@ void launch_gemm_gs(int waves, bool f32, const uint16_t* x, int m, const uint32_
   const dim3 grid(static_cast<unsigned>(ceil_div(n, 16 * T))), block(64 * waves);
   // the waves' partial tiles, then each wave's code staging (2 batches of
   // KB groups x 16 rows per row tile, rows padded by 16 bytes)
-  constexpr int KB = 4;
+  constexpr int KB = q4k::kGemmKB;
   const size_t shmem = static_cast<size_t>(waves) * T * 256 * sizeof(float) +
                        static_cast<size_t>(waves) * 2 * T * 16 * (KB * 4 + 4) * sizeof(uint32_t);
   // (16-byte runs of scales per row when every row's run is 16-byte aligned)

@@ -321,6 +321,12 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const uint16_t* __restrict__
   }
 }
 
+// groups per batch of weight loads in the small-GEMM MFMA kernel
+#ifndef Q4_GEMM_KB
+#define Q4_GEMM_KB 4
+#endif
+constexpr int kGemmKB = Q4_GEMM_KB;
+
 // ---------------------------------------------------------------------------
 // Small GEMM, M in [5, 16] activation rows, on MFMA.
 //
@@ -398,7 +404,7 @@ __global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restr
   // Weight loads in batches of KB groups, one batch ahead of the arithmetic
   // (written out so that every wait is for exactly the batch in use); groups
   // past this wave's share read zeros (scale and bias 0: no term).
-  constexpr int KB = 4;
+  constexpr int KB = kGemmKB;
   static_assert(GS % KB == 0, "group batches");
   // Codes are loaded 16 bytes (one group of one row) per lane, lanes along a
   // row's consecutive groups, and passed through a per-wave LDS staging area
