@@ -382,9 +382,23 @@ __global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restr
   // (holding 24 or 32 tiles would spill).
   constexpr bool kXReg = GS <= 16;
   u32x4_t a[kXReg ? GS : 1];
+  // The register tile is loaded whole cache lines at a time: load j covers
+  // rows 8 (j % 2) .. + 8 and the wave's groups 2 (j / 2), + 1 (128
+  // contiguous bytes per row, 8 lines per load instead of 16), and passes
+  // through the LDS staging area into the MFMA layout before the first batch.
+  constexpr int kXLoads = kXReg ? GS : 1;
+  u32x4_t xr[kXLoads];
   if constexpr (kXReg) {
 #pragma unroll
-    for (int i = 0; i < GS; ++i) a[i] = x_pairs(x_load(i));
+    for (int j = 0; j < kXLoads; ++j) {
+      const int row = 8 * (j & 1) + (lane >> 3);
+      const int seg = lane & 7;  // 16 bytes: group 2 (j / 2) + seg / 4, inputs 8 (seg % 4) ..
+      const int gi = 2 * (j >> 1) + (seg >> 2);
+      const bool ok = gi < gcount && row < m;
+      const uint32_t off = ok ? (uint32_t)(((int64_t)row * K + (int64_t)(g0 + gi) * 32 + 8 * (seg & 3)) * 2)
+                              : 0xFFFFFFF0u;
+      xr[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0));
+    }
   }
   const u32x4_t ones = u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const f32x4_t zero = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -466,6 +480,20 @@ __global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restr
   for (int i0 = 0; i0 < GS; i0 += KB) {
     const int buf = (i0 / KB) & 1;
     if (i0 + KB < GS) load_batch(i0 + KB, buf ^ 1);
+    if (kXReg && i0 == 0) {
+      // the activation tile: rows of 8 segments (two groups) padded to 36 words
+      constexpr int kXRow = 36;
+      static_assert(16 * kXRow <= 2 * T * 16 * kRowWords, "the tile fits the staging area");
+#pragma unroll
+      for (int p = 0; p < kXLoads / 2; ++p) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          *reinterpret_cast<u32x4_t*>(stage + (8 * h + (lane >> 3)) * kXRow + (lane & 7) * 4) = xr[2 * p + h];
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          a[2 * p + q] = x_pairs(*reinterpret_cast<const u32x4_t*>(stage + r16 * kXRow + (4 * q + kb) * 4));
+      }
+    }
     // this batch's codes into the staging area, then each lane's words out
     // (a wave's LDS accesses complete in order)
     uint32_t* sbuf = stage + buf * (T * 16 * kRowWords);
