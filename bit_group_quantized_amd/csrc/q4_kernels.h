@@ -367,9 +367,18 @@ __global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restr
   // and the compiler can keep many in flight.
   const __amdgpu_buffer_rsrc_t rx =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, (int)(m * K * 2), 0x00020000);
-  auto x_load = [&](int i) {
-    const bool ok = i < gcount && r16 < m;
-    const uint32_t off = ok ? (uint32_t)(((int64_t)r16 * K + (int64_t)(g0 + i) * 32 + 8 * kb) * 2) : 0xFFFFFFF0u;
+  // Activations are loaded a whole cache line per row: the load for the
+  // wave's groups gi, gi + 1 and half h covers rows 8 h .. 8 h + 7, 128
+  // contiguous bytes each (8 lines per load instead of 16 for one group of
+  // all 16 rows), and passes through the LDS staging area into the MFMA
+  // layout (x_unpack, below).
+  auto x_line = [&](int gi, int h) {
+    const int row = 8 * h + (lane >> 3);
+    const int seg = lane & 7;  // 16 bytes: group gi + seg / 4, inputs 8 (seg % 4) ..
+    const int g = gi + (seg >> 2);
+    const bool ok = g < gcount && row < m;
+    const uint32_t off = ok ? (uint32_t)(((int64_t)row * K + (int64_t)(g0 + g) * 32 + 8 * (seg & 3)) * 2)
+                            : 0xFFFFFFF0u;
     return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0));
   };
   auto x_pairs = [](const u32x4_t e4) {
@@ -382,23 +391,13 @@ __global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restr
   // (holding 24 or 32 tiles would spill).
   constexpr bool kXReg = GS <= 16;
   u32x4_t a[kXReg ? GS : 1];
-  // The register tile is loaded whole cache lines at a time: load j covers
-  // rows 8 (j % 2) .. + 8 and the wave's groups 2 (j / 2), + 1 (128
-  // contiguous bytes per row, 8 lines per load instead of 16), and passes
-  // through the LDS staging area into the MFMA layout before the first batch.
+  // (the register tile's loads: j covers groups 2 (j / 2), + 1, half j % 2;
+  // unpacked before the first batch)
   constexpr int kXLoads = kXReg ? GS : 1;
   u32x4_t xr[kXLoads];
   if constexpr (kXReg) {
 #pragma unroll
-    for (int j = 0; j < kXLoads; ++j) {
-      const int row = 8 * (j & 1) + (lane >> 3);
-      const int seg = lane & 7;  // 16 bytes: group 2 (j / 2) + seg / 4, inputs 8 (seg % 4) ..
-      const int gi = 2 * (j >> 1) + (seg >> 2);
-      const bool ok = gi < gcount && row < m;
-      const uint32_t off = ok ? (uint32_t)(((int64_t)row * K + (int64_t)(g0 + gi) * 32 + 8 * (seg & 3)) * 2)
-                              : 0xFFFFFFF0u;
-      xr[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0));
-    }
+    for (int j = 0; j < kXLoads; ++j) xr[j] = x_line(2 * (j >> 1), j & 1);
   }
   const u32x4_t ones = u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const f32x4_t zero = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -446,11 +445,22 @@ __global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restr
       }
     }
   }
+  // two groups' activations of 16 rows (the loads of halves 0 and 1) into
+  // the MFMA layout, re-paired: rows of 8 segments padded to 36 words
+  auto x_unpack = [&](const u32x4_t lo, const u32x4_t hi, u32x4_t& a0, u32x4_t& a1) {
+    constexpr int kXRow = 36;
+    static_assert(16 * kXRow <= 2 * T * 16 * kRowWords, "two groups fit the staging area");
+    *reinterpret_cast<u32x4_t*>(stage + (lane >> 3) * kXRow + (lane & 7) * 4) = lo;
+    *reinterpret_cast<u32x4_t*>(stage + (8 + (lane >> 3)) * kXRow + (lane & 7) * 4) = hi;
+    a0 = x_pairs(*reinterpret_cast<const u32x4_t*>(stage + r16 * kXRow + kb * 4));
+    a1 = x_pairs(*reinterpret_cast<const u32x4_t*>(stage + r16 * kXRow + (4 + kb) * 4));
+  };
+  static_assert(KB % 2 == 0 && GS % 2 == 0, "activations go in pairs of groups");
   u32x4_t xb[2][kXReg ? 1 : KB];
   auto load_batch = [&](int i0, int buf) {
 #pragma unroll
     for (int ii = 0; ii < KB; ++ii) {
-      if constexpr (!kXReg) xb[buf][ii] = x_load(i0 + ii);
+      if constexpr (!kXReg) xb[buf][ii] = x_line(i0 + 2 * (ii >> 1), ii & 1);
       if constexpr (!SB16) {
         const bool gok = i0 + ii < gcount;
         const int g = g0 + i0 + ii;
@@ -480,19 +490,16 @@ __global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restr
   for (int i0 = 0; i0 < GS; i0 += KB) {
     const int buf = (i0 / KB) & 1;
     if (i0 + KB < GS) load_batch(i0 + KB, buf ^ 1);
+    // (the staging area is free here: the batch's codes go in below, and a
+    // wave's LDS accesses complete in order)
     if (kXReg && i0 == 0) {
-      // the activation tile: rows of 8 segments (two groups) padded to 36 words
-      constexpr int kXRow = 36;
-      static_assert(16 * kXRow <= 2 * T * 16 * kRowWords, "the tile fits the staging area");
 #pragma unroll
-      for (int p = 0; p < kXLoads / 2; ++p) {
+      for (int p = 0; p < kXLoads / 2; ++p) x_unpack(xr[2 * p], xr[2 * p + 1], a[2 * p], a[2 * p + 1]);
+    }
+    u32x4_t ab[kXReg ? 1 : KB];
+    if constexpr (!kXReg) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          *reinterpret_cast<u32x4_t*>(stage + (8 * h + (lane >> 3)) * kXRow + (lane & 7) * 4) = xr[2 * p + h];
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-          a[2 * p + q] = x_pairs(*reinterpret_cast<const u32x4_t*>(stage + r16 * kXRow + (4 * q + kb) * 4));
-      }
+      for (int p = 0; p < KB / 2; ++p) x_unpack(xb[buf][2 * p], xb[buf][2 * p + 1], ab[2 * p], ab[2 * p + 1]);
     }
     // this batch's codes into the staging area, then each lane's words out
     // (a wave's LDS accesses complete in order)
@@ -512,7 +519,7 @@ __global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restr
       if constexpr (kXReg) {
         ai = a[i0 + ii];
       } else {
-        ai = x_pairs(xb[buf][ii]);
+        ai = ab[ii];
       }
       const bf16x8_t av = __builtin_bit_cast(bf16x8_t, ai);
       const f32x4_t xg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, ones), zero, 0, 0, 0);
