@@ -545,6 +545,8 @@ __device__ __forceinline__ void lc_next_item(LoadCursor& lc, const ChainLds<MV>&
     uint32_t item = (uint32_t)cw;
     if (lc.fresh) {
       lc.fresh = false;
+    } else if (lc.si.total <= kComputeWaves) {
+      item = (uint32_t)lc.si.total;  // every item of the stage is some wave's own: none to claim
     } else {
       if (lane == 0) item = lds_add_rtn(&F.claim[lc.si.s], 1u);
       item = kComputeWaves + (uint32_t)ufl((int)item);
