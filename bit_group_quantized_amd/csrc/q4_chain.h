@@ -194,6 +194,7 @@ struct StageRec {
   uint32_t inv_p;             // ceil(2^16 / P): i / P == (i * inv_p) >> 16 for the small i here
   int32_t flags;              // 1 ragged (16 CH > G), 2 x written in the chain, 4 outputs read in the chain
   int32_t U[kMaxMatsPerStage];  // the block's units of each matrix
+  int32_t U0[kMaxMatsPerStage];  // the first of them
   const uint16_t* x;
   int32_t pad[2];
 };
@@ -204,7 +205,7 @@ struct MatRec {
   void* y;
   int32_t n, pad[3];
 };
-static_assert(sizeof(StageRec) == 64 && sizeof(MatRec) == 48, "table records");
+static_assert(sizeof(StageRec) == 80 && sizeof(MatRec) == 48, "table records");
 constexpr int kStageRagged = 1, kStageXInternal = 2, kStageSyncOut = 4;
 
 // Shared memory: activations and the plan tables (dynamic LDS), and the words
@@ -425,7 +426,10 @@ __device__ __forceinline__ bool build_stage_rec(StageRec& r, const ChainStageDes
   bool fits = true;
   for (int mi = 0; mi < kMaxMatsPerStage; ++mi) {
     const int nunits = mi < r.nm ? (mats[r.mat_begin + mi].n + kUnitRows - 1) / kUnitRows : 0;
-    r.U[mi] = block_range(nunits).count;
+    const BlockRange br = block_range(nunits);
+    r.U[mi] = br.count;
+    r.U0[mi] = br.u0;
+    r.pad[0] = r.pad[1] = 0;
     // (block 0 has the most units; every block takes the same decision)
     fits = fits && (nunits + (int)gridDim.x - 1) / (int)gridDim.x <= ChainShape<MV>::kStageUnits;
     units += r.U[mi];
@@ -437,7 +441,6 @@ __device__ __forceinline__ bool build_stage_rec(StageRec& r, const ChainStageDes
   r.P = P;
   r.inv_p = (65536u + (uint32_t)P - 1u) / (uint32_t)P;
   r.total = units * P;
-  r.pad[0] = r.pad[1] = 0;
   return fits;
 }
 template <int MV>
@@ -524,7 +527,7 @@ __device__ __forceinline__ void lc_item(LoadCursor& lc, const ChainLds<MV>& L) {
   decode_item(lc.si, lc.i, it);
   const MatRec& mr = L.mt[lc.si.mat_begin + it.mi];
   const int n = ufl(mr.n);
-  const int gu = unit_of(block_range((n + kUnitRows - 1) / kUnitRows), it.u);
+  const int gu = ufl(L.st[lc.si.s].U0[it.mi]) + it.u;  // (the block's units are consecutive)
   const uint32_t rows = (uint32_t)min(kUnitRows, n - gu * kUnitRows);
   const uint32_t row_w = (uint32_t)lc.si.G * 16u, row_s = (uint32_t)lc.si.G * 2u;
   lc.rw = byte_range(reinterpret_cast<const unsigned char*>(ufl_ptr(mr.packed)) + (uint64_t)gu * kUnitRows * row_w, rows * row_w);
