@@ -50,6 +50,7 @@ constexpr int kChainWaves = 1 + kComputeWaves;
 constexpr int kMaxMatsPerStage = 4;
 constexpr int kUnitRows = 4;      // rows per unit
 constexpr int kMaxPieces = 8;     // pieces a unit's chunks may be cut into
+constexpr int kMinPieceChunks = 4;  // chunks a piece keeps at least (shorter pieces cost more to close than they balance)
 #ifndef Q4_CHAIN_SPLIT_UNITS
 #define Q4_CHAIN_SPLIT_UNITS 8
 #endif
@@ -437,7 +438,7 @@ __device__ __forceinline__ bool build_stage_rec(StageRec& r, const ChainStageDes
   int P = 1;
   // (a cut stage has fewer than kSplitUnits units and, since P stops growing
   // once units * P reaches kSplitUnits, fewer than 2 kSplitUnits items)
-  while (P < kMaxPieces && P < r.CH && units * P < kSplitUnits) ++P;
+  while (P < kMaxPieces && r.CH >= kMinPieceChunks * (P + 1) && units * P < kSplitUnits) ++P;
   r.P = P;
   r.inv_p = (65536u + (uint32_t)P - 1u) / (uint32_t)P;
   r.total = units * P;
