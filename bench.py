@@ -40,13 +40,13 @@ HBM_PEAK_GBS = 8000.0
 # HBM traffic of one chain_kernel launch over the full step, from two rocprofv3
 # --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch),
 # each scaled by what the same counter reads for a plain 1 GiB copy
-# (``--calibrate-copy 1024``: FETCH_SIZE reads 524301.6 KiB for 1 GiB fetched,
+# (``--calibrate-copy 1024``: FETCH_SIZE reads 524302.9 KiB for 1 GiB fetched,
 # WRITE_SIZE 1048576.0 KiB for 1 GiB written). Valid only for the kernel sources
 # whose hash is recorded: any change to them reports traffic as null until the
 # counters are taken again (profiles/chain_kernel_temporal_step_m1_pmc.md).
 CHAIN_TRAFFIC = {
-    "sources_sha256_16": "387405ccb75201ba",
-    "fetch_kib": 2052655.6, "fetch_scale": 1048576.0 / 524301.6,
+    "sources_sha256_16": "b8050602354b952c",
+    "fetch_kib": 2052827.2, "fetch_scale": 1048576.0 / 524302.9,
     "write_kib": 4119.8, "write_scale": 1048576.0 / 1048576.0,
 }
 KERNEL_SOURCES = ("q4_chain.h", "q4_kernels.h", "q4_api.hip")
