@@ -45,7 +45,7 @@ HBM_PEAK_GBS = 8000.0
 # whose hash is recorded: any change to them reports traffic as null until the
 # counters are taken again (profiles/chain_kernel_temporal_step_m1_pmc.md).
 CHAIN_TRAFFIC = {
-    "sources_sha256_16": "b8050602354b952c",
+    "sources_sha256_16": "7f82a47239a9a4ac",
     "fetch_kib": 2052827.2, "fetch_scale": 1048576.0 / 524302.9,
     "write_kib": 4119.8, "write_scale": 1048576.0 / 1048576.0,
 }
@@ -63,12 +63,17 @@ def packed_bytes(n: int, k: int) -> int:
 
 
 def kernel_sources_hash() -> str:
+    """sha256[:16] of the kernel sources with // comments and blank space
+    removed (an edit to a comment does not change the kernels)."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "bit_group_quantized_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "bit_group_quantized_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        code = [re.sub(r"//.*$", "", line).strip() for line in text.splitlines()]
+        h.update("\n".join(line for line in code if line).encode())
     return h.hexdigest()[:16]
 
 

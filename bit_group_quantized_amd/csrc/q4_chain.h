@@ -27,9 +27,11 @@
 //    against the stage's activations in LDS; finished rows go to LDS.
 //  - wave 0, the service wave, waits for the block's compute waves to finish
 //    a stage, stores the stage's rows, synchronises the grid between stages,
-//    and stages activations into LDS (double buffered: the next stage's
-//    activations are fetched during the current stage unless an earlier
-//    stage of the chain writes them).
+//    and stages activations into LDS (with one activation row, double
+//    buffered: activations no stage writes are fetched a stage ahead).
+//    Activations an earlier stage writes, and every stage's with several
+//    activation rows (one buffer), are staged by all compute waves together
+//    once the buffer is free (after the barrier for the former).
 //
 // Grid synchronisation is two-level: blocks on one XCD (which share an L2)
 // count arrivals with L2 atomics; the last arrival of each XCD raises the
