@@ -180,9 +180,19 @@ def floored_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     """Max over outputs of |got - ref| / max(|ref|, 1e-3 * rms(ref)), per output row.
 
     "Max relative error" is ill-posed where the exact output is near zero; the
-    floor of 1e-3 of the row's RMS is the reading used for the tolerances."""
+    floor of 1e-3 of the row's RMS is the reading used for the tolerances. The
+    RMS is taken over each output row (one activation row's outputs) on its
+    own, and every element is divided by its own |ref| (or the floor). An
+    output that is not finite where the exact value is finite scores inf, so a
+    NaN or inf can never pass a tolerance. Shapes must match."""
     got = np.atleast_2d(np.asarray(got, dtype=np.float64))
     ref = np.atleast_2d(np.asarray(ref, dtype=np.float64))
+    if got.shape != ref.shape:
+        raise ValueError(f"shape mismatch: got {got.shape}, ref {ref.shape}")
+    if not np.all(np.isfinite(ref)):
+        raise ValueError("reference values must be finite")
+    if not np.all(np.isfinite(got)):
+        return float("inf")
     worst = 0.0
     for g, r in zip(got, ref):
         if r.size == 0:

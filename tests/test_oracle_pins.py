@@ -391,3 +391,54 @@ def test_rejects_bad_arguments():
     x[0, 0] = 0x7F80  # +inf
     with pytest.raises(ValueError):
         oracle.matmul(x, p, s, b, 32)
+
+
+# ---------------------------------------------------------------- tolerance yardstick
+# floored_rel_err is the measure every parity tolerance is stated in: per output
+# row, max_n |got_n - ref_n| / max(|ref_n|, 1e-3 * rms(ref row)). Each case below is
+# worked by hand and fails for one plausible slip in it.
+
+def test_floored_rel_err_exact_match_is_zero():
+    ref = np.array([[1.5, -2.25, 0.0, 3.0]])
+    assert oracle.floored_rel_err(ref.copy(), ref) == 0.0
+
+
+def test_floored_rel_err_divides_each_element_by_its_own_magnitude():
+    # |1.01 - 1| / 1 = 0.01; dividing by max|ref| (100) instead would give 1e-4
+    got = np.array([1.01, 100.0])
+    ref = np.array([1.0, 100.0])
+    assert oracle.floored_rel_err(got, ref) == pytest.approx(0.01, rel=1e-9)
+
+
+def test_floored_rel_err_floor_applies_near_zero():
+    # rms of [1e-9, 2, -2] is sqrt(8/3) (the 1e-18 term is below double precision
+    # there), floor = 1e-3 * 1.6329931618554521; an error of 1e-5 at the
+    # near-zero output scores 1e-5 / 1.6329931618554521e-3 = 0.0061237243569579
+    # (without the floor it would be 1e4)
+    ref = np.array([1e-9, 2.0, -2.0])
+    got = ref + np.array([1e-5, 0.0, 0.0])
+    assert oracle.floored_rel_err(got, ref) == pytest.approx(0.0061237243569579, rel=1e-9)
+
+
+def test_floored_rel_err_rms_is_per_output_row():
+    # row 1's rms is sqrt(2e-6 / 3) = 8.16496580927726e-4, so its floor is
+    # 8.16496580927726e-7 and an error of 1e-8 at its zero output scores
+    # 0.012247448713915890; an rms over both rows (~816) would score ~1.2e-11
+    ref = np.array([[1000.0, -1000.0, 500.0], [1e-3, -1e-3, 0.0]])
+    got = ref.copy()
+    got[1, 2] = 1e-8
+    assert oracle.floored_rel_err(got, ref) == pytest.approx(0.01224744871391589, rel=1e-9)
+    # the worst row decides: an error of 1% in row 0 on top
+    got[0, 0] = 1010.0
+    assert oracle.floored_rel_err(got, ref) == pytest.approx(0.01224744871391589, rel=1e-9)
+    got[0, 0] = 1020.0
+    assert oracle.floored_rel_err(got, ref) == pytest.approx(0.02, rel=1e-9)
+
+
+def test_floored_rel_err_non_finite_output_fails():
+    ref = np.array([[1.0, 2.0, 3.0]])
+    assert oracle.floored_rel_err(np.full((1, 3), np.nan), ref) == float("inf")
+    assert oracle.floored_rel_err(np.array([[1.0, np.inf, 3.0]]), ref) == float("inf")
+    assert oracle.floored_rel_err(np.array([[1.0, 2.0, -np.inf]]), ref) == float("inf")
+    with pytest.raises(ValueError):
+        oracle.floored_rel_err(np.zeros((1, 2)), ref)
