@@ -139,13 +139,23 @@ def q4_status_str(status: int) -> str:
 
 def q4_pack(w: torch.Tensor, packed: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
             biases: Optional[torch.Tensor] = None):
-    """Quantize fp32 W [n, k] on the GPU -> (packed int32 [n, k/8], scales bf16, biases bf16)."""
-    _need(w, "w", torch.float32)
-    if w.dim() != 2:
-        raise ValueError("w must be [n, k]")
+    """Quantize fp32 W [n, k] on the GPU -> (packed int32 [n, k/8], scales bf16, biases bf16).
+
+    Outputs given by the caller must have exactly those shapes and sit on w's
+    device (the library takes n and k from w and writes that many words)."""
+    if not isinstance(w, torch.Tensor) or w.dim() != 2:
+        raise ValueError("w must be a tensor [n, k]")
     n, k = w.shape
     if k % GROUP:
         raise ValueError("k must be a multiple of 32")
+    for t, name, shape in ((packed, "packed", (n, k // 8)), (scales, "scales", (n, k // GROUP)),
+                           (biases, "biases", (n, k // GROUP))):
+        if t is not None:
+            if not isinstance(t, torch.Tensor) or tuple(t.shape) != shape:
+                raise ValueError(f"{name} must be [{shape[0]}, {shape[1]}] for w of shape [{n}, {k}]")
+            if t.device != w.device:
+                raise ValueError(f"{name} must be on w's device ({w.device})")
+    _need(w, "w", torch.float32)
     dev = w.device
     packed = torch.empty((n, k // 8), dtype=torch.int32, device=dev) if packed is None else packed
     scales = torch.empty((n, k // GROUP), dtype=torch.bfloat16, device=dev) if scales is None else scales
@@ -171,7 +181,15 @@ def _check_matrix(packed, scales, biases):
     k = k8 * 8
     if scales.shape != (n, k // GROUP) or biases.shape != (n, k // GROUP):
         raise ValueError("scales/biases must be [n, k/32]")
+    if scales.device != packed.device or biases.device != packed.device:
+        raise ValueError("packed, scales and biases must be on one device")
     return n, k
+
+
+def _same_device(ref: torch.Tensor, *ts) -> None:
+    for t in ts:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"every tensor of a call must be on {ref.device} (got {t.device})")
 
 
 def q4_unpack(packed: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, want_codes: bool = True,
@@ -199,6 +217,7 @@ def q4_gemv(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, biases:
     _need(out, "out", out.dtype)
     if out.numel() != n:
         raise ValueError("out must hold n elements")
+    _same_device(packed, x, out)
     _check("q4_gemv", load().q4_gemv(_ptr(x), _ptr(packed), _ptr(scales), _ptr(biases), n, k, _ptr(out), code,
                                      _ptr_stream(x)))
     return out
@@ -218,6 +237,7 @@ def q4_gemm_small(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, b
     _need(out, "out", out.dtype)
     if out.numel() != m * n:
         raise ValueError("out must hold m*n elements")
+    _same_device(packed, x, out)
     _check("q4_gemm_small", load().q4_gemm_small(_ptr(x), m, _ptr(packed), _ptr(scales), _ptr(biases), n, k,
                                                  _ptr(out), code, _ptr_stream(x)))
     return out
@@ -242,6 +262,7 @@ def q4_multilinear_step(x: torch.Tensor, packed: torch.Tensor, scales: torch.Ten
     _need(out, "out", out.dtype)
     if out.numel() != m * out_rows:
         raise ValueError("out must hold m*out elements")
+    _same_device(packed, x2, out)
     _check("q4_multilinear_step",
            load().q4_multilinear_step(_ptr(x2), m, _ptr(packed), _ptr(scales), _ptr(biases), num_steps, out_rows,
                                       k, int(step), _ptr(out), code, _ptr_stream(x)))
@@ -275,7 +296,9 @@ def q4_chain_build(stages, out_dtype: Optional[torch.dtype] = None) -> ChainPlan
     descs = []
     keep = []
     rows = None
-    for st in stages:
+    for si, st in enumerate(stages):
+        if len(st.outs) != len(st.mats):
+            raise ValueError(f"stage {si}: {len(st.mats)} matrices but {len(st.outs)} outputs")
         _need(st.x, "x", torch.bfloat16)
         m_st = 1 if st.x.dim() == 1 else st.x.shape[0]
         if st.x.dim() > 2:
@@ -295,6 +318,7 @@ def q4_chain_build(stages, out_dtype: Optional[torch.dtype] = None) -> ChainPlan
             _need(y, "y", out_dtype)
             if y.numel() != rows * n:
                 raise ValueError("output must hold m*n elements")
+            _same_device(stages[0].x, st.x, m.packed, y)
             mats.append(_ChainMatrix(m.packed.data_ptr(), m.scales.data_ptr(), m.biases.data_ptr(), y.data_ptr(), n))
             keep += [m.packed, m.scales, m.biases, y]
         descs.append(_ChainStage(st.x.data_ptr(), k, first, len(mats) - first))

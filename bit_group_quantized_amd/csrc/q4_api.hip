@@ -3,6 +3,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "q4.h"
 #include "q4_kernels.h"
 #include "q4_chain.h"
@@ -26,11 +29,33 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-constexpr int kNumCU = 256;
+constexpr int kMaxDevices = 64;
+constexpr int kFallbackCU = 256;  // only if the device cannot be queried
+
+// Compute units of the current device, queried once per device (thread-safe).
+int device_cu_count() {
+  static std::once_flag once[kMaxDevices];
+  static std::atomic<int> cus[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return kFallbackCU;
+  }
+  std::call_once(once[dev], [dev]() {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = kFallbackCU;
+    }
+    cus[dev].store(n);
+  });
+  return cus[dev].load();
+}
 
 int grid_for_groups(int64_t n_groups) {
   const int64_t blocks = ceil_div(n_groups, 256);
-  return static_cast<int>(blocks < 8 * kNumCU * 4 ? (blocks < 1 ? 1 : blocks) : 8 * kNumCU * 4);
+  const int64_t cap = 32 * (int64_t)device_cu_count();
+  return static_cast<int>(blocks < cap ? (blocks < 1 ? 1 : blocks) : cap);
 }
 
 // ---- GEMV launch: pick the lane split C so that S = ceil(G/C) waves cover
@@ -64,7 +89,7 @@ bool plan_gemv(int64_t n, int64_t G, int mv, GemvPlan* p) {
   if (best_waste < 0) return false;
   const int rows_iter = (64 / best_c) * gemv_u(mv);
   // Aim for >= 2 blocks per CU; each block covers at least one iteration.
-  const int64_t target_blocks = 2 * kNumCU;
+  const int64_t target_blocks = 2 * (int64_t)device_cu_count();
   int64_t rpb = ceil_div(n, target_blocks);
   rpb = ceil_div(rpb, rows_iter) * rows_iter;
   if (rpb < rows_iter) rpb = rows_iter;
@@ -290,15 +315,6 @@ q4_status q4_multilinear_step(const uint16_t* x, int64_t m, const uint32_t* pack
 // Chain executor host side.
 namespace {
 
-int device_cu_count() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return kNumCU;
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    return kNumCU;
-  return cus;
-}
-
 // Number of XCDs (chiplets with their own L2) of the current device.
 uint32_t device_xcc_count() {
   int dev = 0, n = 0;
@@ -311,12 +327,14 @@ template <int MV>
 constexpr size_t chain_lds_bytes() { return sizeof(q4k::ChainLds<MV>); }
 
 // Per device and activation-row count: raise the dynamic-LDS limit of the
-// chain kernels once and check that one block fits per compute unit.
+// chain kernels once and check that one block fits per compute unit (once per
+// device, thread-safe; the answer is kept).
 template <int MV>
 bool chain_ready_rows(int dev) {
-  static int state[64] = {0};  // 0 unknown, 1 ready, -1 not possible
-  if (dev < 0 || dev >= 64) return false;
-  if (state[dev] == 0) {
+  static std::once_flag once[kMaxDevices];
+  static std::atomic<bool> ready[kMaxDevices];
+  if (dev < 0 || dev >= kMaxDevices) return false;
+  std::call_once(once[dev], [dev]() {
     constexpr size_t lds = chain_lds_bytes<MV>();
     bool ok = hipFuncSetAttribute(reinterpret_cast<const void*>(&q4k::chain_kernel<MV, true>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess &&
@@ -330,9 +348,9 @@ bool chain_ready_rows(int dev) {
                                                       lds) == hipSuccess &&
          a >= 1 && b >= 1;
     (void)hipGetLastError();
-    state[dev] = ok ? 1 : -1;
-  }
-  return state[dev] == 1;
+    ready[dev].store(ok);
+  });
+  return ready[dev].load();
 }
 
 template <int MV>
@@ -371,17 +389,12 @@ static_assert(q4k::ChainShape<2>::kTabStages == q4k::ChainShape<4>::kTabStages &
                   q4k::ChainShape<2>::kTabMats == q4k::ChainShape<4>::kTabMats,
               "one set of limits for several activation rows");
 
-// Lanes per row for a stage of G groups: among 64/32/16/8 lanes, the split
-// with the fewest idle lanes (ties: more lanes per row) whose padded width
-// fits the activation buffer and whose rows per unit (64/lanes) divide every
-// matrix's row count.
-// A chain stage processes units of 4 rows in chunks of 16 groups per row, so
-// its geometry depends on G only: chunks per row CH = ceil(G / 16), with the
-// activations padded to 16 * CH groups.
-bool plan_stage(int64_t G, int max_groups, int* c_log2, int* CH) {
+// A chain stage processes units of 4 rows in chunks of 16 groups per row (one
+// group per lane, 16 lanes per row), so its geometry depends on G only: chunks
+// per row CH = ceil(G / 16), with the activations padded to 16 CH groups.
+bool plan_stage(int64_t G, int max_groups, int* CH) {
   const int64_t ch = ceil_div(G, q4k::kChunkGroups);
   if (ch * q4k::kChunkGroups > max_groups) return false;
-  *c_log2 = 4;
   *CH = static_cast<int>(ch);
   return true;
 }
@@ -430,10 +443,15 @@ q4_status q4_chain_encode_rows(const q4_chain_stage* stages, int32_t num_stages,
       if (!aligned(m.scales, 16) || !aligned(m.biases, 16)) return Q4_ERR_UNSUPPORTED;
       // a stage may not write its own input
       if (ranges_overlap(st.x, 2 * st.k * m_rows, m.y, ybytes * m.n * m_rows)) return Q4_ERR_UNSUPPORTED;
+      // nor write one output range twice (its blocks store in no fixed order)
+      for (int32_t j = 0; j < i; ++j) {
+        const q4_chain_matrix& o = matrices[st.first_matrix + j];
+        if (ranges_overlap(o.y, ybytes * o.n * m_rows, m.y, ybytes * m.n * m_rows)) return Q4_ERR_UNSUPPORTED;
+      }
     }
-    int lg, ch;
+    int ch;
     if (st.num_matrices > q4k::kMaxMatsPerStage || num_matrices > lim.tab_mats || num_stages > lim.tab_stages ||
-        !plan_stage(st.k / 32, lim.max_groups, &lg, &ch))
+        !plan_stage(st.k / 32, lim.max_groups, &ch))
       return Q4_ERR_UNSUPPORTED;
   }
   if (next_matrix != num_matrices) return Q4_ERR_SHAPE;
@@ -453,26 +471,37 @@ q4_status q4_chain_encode_rows(const q4_chain_stage* stages, int32_t num_stages,
     q4k::ChainStageDesc d{};
     d.x = st.x;
     d.G = static_cast<int32_t>(st.k / 32);
-    plan_stage(d.G, lim.max_groups, &d.c_log2, &d.CH);
+    plan_stage(d.G, lim.max_groups, &d.CH);
     d.num_mats = st.num_matrices;
     d.mat_begin = st.first_matrix;
     sd[s] = d;
   }
-  // Dependencies through memory: a stage whose x overlaps an earlier stage's
-  // outputs loads it only after the preceding stage barrier (device-coherent
-  // loads), and that earlier stage makes its outputs visible before it
-  // arrives at its barrier. Activations no stage writes are prefetched.
+  // Dependencies through memory, between a stage t and a later stage s:
+  //  - s reads what t wrote (s's x overlaps t's outputs): s loads its x only
+  //    after the preceding stage barrier (device-coherent loads), and t makes
+  //    its outputs visible before it arrives at its barrier;
+  //  - s writes where t wrote (outputs overlap): t's stores are likewise
+  //    complete before its barrier, so s's stores land last.
+  // A later stage writing an earlier stage's x is harmless: every block has
+  // read that x before it arrives at the barrier that precedes the writes.
+  // Activations no stage writes are prefetched.
+  auto stage_writes = [&](int32_t t, const void* p, int64_t bytes) {
+    for (int32_t i = 0; i < stages[t].num_matrices; ++i) {
+      const q4_chain_matrix& m = matrices[stages[t].first_matrix + i];
+      if (ranges_overlap(p, bytes, m.y, ybytes * m.n * m_rows)) return true;
+    }
+    return false;
+  };
   for (int32_t s = 0; s < num_stages; ++s) {
     const q4_chain_stage& st = stages[s];
     for (int32_t t = 0; t < s; ++t) {
-      for (int32_t i = 0; i < stages[t].num_matrices; ++i) {
-        const q4_chain_matrix& m = matrices[stages[t].first_matrix + i];
-        // (a later stage writing x is harmless: x is read before that stage
-        // starts, prefetch included)
-        if (t < s && ranges_overlap(st.x, 2 * st.k * m_rows, m.y, ybytes * m.n * m_rows)) {
-          sd[s].x_internal = 1;
-          sd[t].sync_outputs = 1;
-        }
+      if (stage_writes(t, st.x, 2 * st.k * m_rows)) {
+        sd[s].x_internal = 1;
+        sd[t].sync_outputs = 1;
+      }
+      for (int32_t i = 0; i < st.num_matrices; ++i) {
+        const q4_chain_matrix& m = matrices[st.first_matrix + i];
+        if (stage_writes(t, m.y, ybytes * m.n * m_rows)) sd[t].sync_outputs = 1;
       }
     }
   }

@@ -108,13 +108,12 @@ struct alignas(16) ChainHeader {
 struct alignas(16) ChainStageDesc {
   const uint16_t* x;
   int32_t G;             // groups of 32 inputs
-  int32_t c_log2;        // lanes per row = 1 << c_log2 (always 16)
   int32_t CH;            // chunks per row: ceil(G / 16)
   int32_t num_mats;
   int32_t mat_begin;
   int32_t x_internal;    // x is written by an earlier stage of the chain
-  int32_t sync_outputs;  // a later stage reads this stage's outputs
-  int32_t pad[7];
+  int32_t sync_outputs;  // a later stage reads or overwrites this stage's outputs
+  int32_t pad[8];
 };
 struct alignas(16) ChainMatDesc {
   const uint32_t* packed;

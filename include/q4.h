@@ -94,14 +94,21 @@ int q4_last_hip_error(void);
 q4_status q4_pack(const float* w, int64_t n, int64_t k, uint32_t* packed, uint16_t* scales,
                   uint16_t* biases, void* stream);
 
-/* Unpack: recover codes and/or dequantized weights w_hat = s'*q + b' (one
- * rounding to fp32; the product s'*q is exact). Bit-exact with the oracle.
+/* Unpack ("personaplex-edge-q4" model card, Release details table: each
+ * weight is a 4-bit code with the bf16 scale and bias of its group of 32):
+ * recover codes and/or dequantized weights w_hat = s'*q + b' (one rounding to
+ * fp32; the product s'*q is exact). Bit-exact with the oracle.
  *   q_out : uint8 [n][k] or NULL;  w_out : fp32 [n][k] or NULL (at least one
  *   must be non-NULL). */
 q4_status q4_unpack(const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
                     int64_t n, int64_t k, uint8_t* q_out, float* w_out, void* stream);
 
-/* Quantized matrix-vector product, one activation row (M = 1):
+/* Quantized matrix-vector product, one activation row (M = 1): the decoding
+ * step's linear layer run straight from the packed weights ("personaplex-
+ * edge-q4" model card, introduction: weights stay packed and feed a quantized
+ * matmul; "NVIDIA PersonaPlex 7B on Apple Silicon", Depformer MultiLinear
+ * code figure: the product takes x, the packed weight, scales and biases,
+ * with the weight transposed):
  *   y[r] = sum_k w_hat[r][k] * x[k]   for r in [0, n)
  * computed per group as s'*(sum q*x) + b'*(sum x) with fp32 accumulation.
  *   x : bf16 [k] (uint16 bit patterns), y : [n] of y_dtype. */
@@ -110,7 +117,9 @@ q4_status q4_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* sca
                   void* stream);
 
 /* Small quantized GEMM for M concurrent activation rows (1 <= m <= 16), all
- * sharing one pass over the weights:
+ * sharing one pass over the weights ("A smaller voice model", Concurrency
+ * section: several conversations served together read one copy of the
+ * weights, so their frames cost little more than one):
  *   y[i][r] = sum_k w_hat[r][k] * x[i][k]
  *   x : bf16 [m][k] row-major, y : [m][n] row-major of y_dtype.
  * m == 1 is the same computation as q4_gemv. Supports k <= Q4_MAX_K. */
@@ -155,8 +164,11 @@ q4_status q4_multilinear_step(const uint16_t* x, int64_t m, const uint32_t* pack
  * 768 matrices per chain (the block copies the plan into LDS), at most 4
  * matrices per stage, k <= 12288, n < 2^22, at most 128
  * units of 4 rows of one matrix per block (n <= 512 x the number of compute
- * units), scales and biases 16-byte aligned, and no stage's output may
- * overlap its own input.
+ * units), scales and biases 16-byte aligned, no stage's output may overlap
+ * its own input, and no two outputs of one stage may overlap. Outputs of
+ * different stages may overlap: the later stage's values are the ones left
+ * (the encoder makes the earlier stage's stores complete before its barrier,
+ * as it does for outputs a later stage reads).
  *
  * Workspace: Q4_CHAIN_WORKSPACE_BYTES of device memory, 128-byte aligned,
  * zero-filled once by the caller before its first use; the executor leaves it

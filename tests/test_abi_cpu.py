@@ -105,8 +105,33 @@ def test_empty_calls_are_noops():
 def test_binding_refuses_cpu_tensors():
     import torch
     w = torch.zeros(4, 64)
-    with pytest.raises(ValueError):
+    with pytest.raises(ValueError, match="GPU tensor"):
         q4.q4_pack(w)
+
+
+def test_binding_checks_pack_output_shapes_before_any_call():
+    """q4_pack takes n and k from w: outputs the caller passes must have exactly
+    the shapes it writes (checked before the device, so a CPU run sees it)."""
+    import torch
+    w = torch.zeros(4, 64)
+    with pytest.raises(ValueError, match=r"packed must be \[4, 8\]"):
+        q4.q4_pack(w, packed=torch.zeros(4, 4, dtype=torch.int32))
+    with pytest.raises(ValueError, match=r"scales must be \[4, 2\]"):
+        q4.q4_pack(w, scales=torch.zeros(4, 1, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match=r"biases must be \[4, 2\]"):
+        q4.q4_pack(w, biases=torch.zeros(2, 2, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="multiple of 32"):
+        q4.q4_pack(torch.zeros(4, 40))
+
+
+def test_binding_chain_build_needs_one_output_per_matrix():
+    import torch
+    from types import SimpleNamespace
+    mat = SimpleNamespace(packed=torch.zeros(4, 8, dtype=torch.int32), scales=torch.zeros(4, 2, dtype=torch.bfloat16),
+                          biases=torch.zeros(4, 2, dtype=torch.bfloat16))
+    st = SimpleNamespace(x=torch.zeros(64, dtype=torch.bfloat16), mats=[mat, mat], outs=[torch.zeros(4)])
+    with pytest.raises(ValueError, match="2 matrices but 1 outputs"):
+        q4.q4_chain_build([st])
 
 
 def _chain(n_stages=2, k=256, n=16, x=A16, y=Y16, packed=A16):
@@ -224,13 +249,51 @@ def test_chain_stage_geometry_and_dependencies():
     mats = (q4._ChainMatrix * 3)(q4._ChainMatrix(A16, A16, A16, Y0, 11264), q4._ChainMatrix(A16, A16, A16, Y1, 4096),
                                  q4._ChainMatrix(A16, A16, A16, Y2, 1024))
     assert lib.q4_chain_encode(ctypes.byref(stages), 3, ctypes.byref(mats), 3, 0, ctypes.byref(buf), nb) == q4.Q4_OK
-    # G, c_log2, CH at byte offsets 8, 12, 16; x_internal 28, sync_outputs 32
+    # G, CH at byte offsets 8, 12; x_internal 24, sync_outputs 28
     # (16 lanes per row, chunks of 16 groups: CH = ceil(G / 16))
-    assert [_stage_field(buf, 0, o) for o in (8, 12, 16)] == [128, 4, 8]
-    assert [_stage_field(buf, 1, o) for o in (8, 12, 16)] == [352, 4, 22]
-    assert [_stage_field(buf, 2, o) for o in (8, 12, 16)] == [88, 4, 6]     # ragged last chunk
-    assert [_stage_field(buf, s, 28) for s in range(3)] == [0, 1, 0]
-    assert [_stage_field(buf, s, 32) for s in range(3)] == [1, 0, 0]
+    assert [_stage_field(buf, 0, o) for o in (8, 12)] == [128, 8]
+    assert [_stage_field(buf, 1, o) for o in (8, 12)] == [352, 22]
+    assert [_stage_field(buf, 2, o) for o in (8, 12)] == [88, 6]     # ragged last chunk
+    assert [_stage_field(buf, s, X_INTERNAL) for s in range(3)] == [0, 1, 0]
+    assert [_stage_field(buf, s, SYNC_OUT) for s in range(3)] == [1, 0, 0]
+
+
+X_INTERNAL, SYNC_OUT = 24, 28  # byte offsets in a stage record of the plan
+
+
+def test_chain_encoder_orders_overlapping_outputs():
+    """A later stage that overwrites an earlier stage's outputs makes the
+    earlier one store before its barrier (sync flag), as a later stage that
+    reads them does; two outputs of one stage may not overlap; a later stage
+    writing an earlier stage's input needs no flag."""
+    lib = q4.load()
+    nb = lib.q4_chain_plan_bytes(3, 3)
+    buf = (ctypes.c_uint8 * nb)()
+    X0, X1, X2, Y0, Y2 = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+
+    def encode(xs, ys, per_stage=(1, 1, 1)):
+        firsts = [sum(per_stage[:i]) for i in range(len(per_stage))]
+        st = (q4._ChainStage * len(xs))(*[q4._ChainStage(x, 256, f, c) for x, f, c in zip(xs, firsts, per_stage)])
+        mt = (q4._ChainMatrix * len(ys))(*[q4._ChainMatrix(A16, A16, A16, y, 16) for y in ys])
+        return lib.q4_chain_encode(ctypes.byref(st), len(xs), ctypes.byref(mt), len(ys), 0, ctypes.byref(buf), nb)
+
+    # stage 2 overwrites stage 0's outputs (bf16 [16] = 32 bytes at Y0): stage 0 syncs
+    assert encode([X0, X1, X2], [Y0, Y2, Y0 + 16]) == q4.Q4_OK
+    assert [_stage_field(buf, s, SYNC_OUT) for s in range(3)] == [1, 0, 0]
+    assert [_stage_field(buf, s, X_INTERNAL) for s in range(3)] == [0, 0, 0]
+    # disjoint outputs: no flags
+    assert encode([X0, X1, X2], [Y0, Y2, Y0 + 32]) == q4.Q4_OK
+    assert [_stage_field(buf, s, SYNC_OUT) for s in range(3)] == [0, 0, 0]
+    # stage 2 writes stage 0's input: harmless, no flags
+    assert encode([X0, X1, X2], [Y0, Y2, X0]) == q4.Q4_OK
+    assert [_stage_field(buf, s, SYNC_OUT) for s in range(3)] == [0, 0, 0]
+    # stage 1 reads stage 0's output: stage 0 syncs, stage 1's x is internal
+    assert encode([X0, Y0, X2], [Y0, Y2, Y0 + 64]) == q4.Q4_OK
+    assert [_stage_field(buf, s, SYNC_OUT) for s in range(3)] == [1, 0, 0]
+    assert [_stage_field(buf, s, X_INTERNAL) for s in range(3)] == [0, 1, 0]
+    # two matrices of one stage writing overlapping outputs are refused
+    assert encode([X0, X1], [Y0, Y0 + 30, Y2], per_stage=(2, 1)) == q4.Q4_ERR_UNSUPPORTED
+    assert encode([X0, X1], [Y0, Y0 + 32, Y2], per_stage=(2, 1)) == q4.Q4_OK
 
 
 def test_chain_run_validation():

@@ -126,47 +126,64 @@ def test_chain_matches_per_call_launches():
         assert oracle.floored_rel_err(out_np(u), out_np(v)) <= 2 * TOL_F32
 
 
-def test_full_temporal_step_sampled_layers():
+def _outputs_bits(chain):
+    return [y.view(torch.int16).clone() for st in chain.stages for y in st.outs]
+
+
+def _same_bits(a, b):
+    return all(torch.equal(u, v) for u, v in zip(a, b))
+
+
+@pytest.mark.timeout(600)
+def test_full_temporal_step_every_layer():
     """The 32-layer step as the benchmark builds and runs it (seeded weights
-    packed by q4_pack, bf16 outputs, one persistent launch); layers 0, 17 and 31
-    are rebuilt on the host, their packed weights compared bit for bit and
-    their outputs against the oracle."""
+    packed by q4_pack, bf16 outputs, one persistent launch). Every layer is
+    rebuilt on the host: its packed weights compared bit for bit and every
+    output against the oracle. A second launch gives bit-identical outputs."""
     import bench
 
     seed = 0
     chain = bench.make_temporal_chain(seed)
     chain.run_chain()
+    torch.cuda.synchronize()
+    assert chain.chain_status() == 0
+    first = _outputs_bits(chain)
     chain.run_chain()
     torch.cuda.synchronize()
     assert chain.chain_status() == 0
+    assert _same_bits(first, _outputs_bits(chain)), "a second launch changed the outputs"
     lin = workloads.temporal_layer()
     stages_per_layer = 4
-    assert len(chain.stages) == 32 * stages_per_layer
-    for layer in (0, 17, 31):
+    assert len(chain.stages) == workloads.TEMPORAL_LAYERS * stages_per_layer
+    by_stage = {}
+    for li in lin:
+        by_stage.setdefault(li.stage, []).append(li)
+    for layer in range(workloads.TEMPORAL_LAYERS):
         st0 = layer * stages_per_layer
-        by_stage = {}
-        for li in lin:
-            by_stage.setdefault(li.stage, []).append(li)
+        ws = dict(zip([li.name for li in lin],
+                      workloads.weights_many([(seed, workloads.CFG_STEP, layer, li.item, li.n, li.k) for li in lin])))
         for si, st in enumerate(sorted(by_stage)):
             stage = chain.stages[st0 + si]
             x = workloads.activations(seed, workloads.CFG_STEP, layer, 100 + st, 1, by_stage[st][0].k)
             assert np.array_equal(bf16_bits_np(stage.x), x[0])
             for li, m, y in zip(by_stage[st], stage.mats, stage.outs):
-                w = workloads.weights(seed, workloads.CFG_STEP, layer, li.item, li.n, li.k)
-                P, S, B = oracle.quantize(w)
+                P, S, B = oracle.quantize(ws[li.name])
                 assert np.array_equal(packed_np(m.packed), P)
                 assert np.array_equal(bf16_bits_np(m.scales), S)
                 assert np.array_equal(bf16_bits_np(m.biases), B)
                 ref = oracle.matmul(x, P, S, B, li.k)[0]
                 assert oracle.floored_rel_err(out_np(y), ref) <= TOL_BF16, (layer, li.name)
+        del ws
 
 
-def test_depformer_frame_chain_sampled_steps():
+@pytest.mark.timeout(600)
+def test_depformer_frame_chain_every_step():
     """One Depformer frame as the benchmark runs it: 16 codebook steps x 6
     layers x 4 stages in one persistent launch, every matrix the step's row
-    slice of its stacked packed tensor. Layers 0 and 5 are rebuilt on the host
-    for codebook steps 0, 7 and 15: the stacked weights are compared bit for
-    bit, the outputs against the oracle on the step's rows."""
+    slice of its stacked packed tensor. Every layer is rebuilt on the host (the
+    stacked weights compared bit for bit) and every output of every codebook
+    step checked against the oracle on the step's rows. A second launch gives
+    bit-identical outputs."""
     import bench
 
     seed = 0
@@ -175,21 +192,27 @@ def test_depformer_frame_chain_sampled_steps():
     chain = bench.make_depformer_frame(mats, seed, device=dev)
     assert len(chain.stages) == workloads.DEP_STEPS * workloads.DEP_LAYERS * 4
     chain.run_chain()
+    torch.cuda.synchronize()
+    assert chain.chain_status() == 0
+    first = _outputs_bits(chain)
     chain.run_chain()
     torch.cuda.synchronize()
     assert chain.chain_status() == 0
+    assert _same_bits(first, _outputs_bits(chain)), "a second launch changed the outputs"
     lin = workloads.depformer_layer()
     by_stage = {}
     for li in lin:
         by_stage.setdefault(li.stage, []).append(li)
-    for layer in (0, 5):
+    for layer in range(workloads.DEP_LAYERS):
         quant = {}
         for li in lin:
             w = workloads.weights(seed, workloads.CFG_DEPFORMER, layer, li.item, workloads.DEP_STEPS * li.n, li.k)
             quant[li.name] = oracle.quantize(w)
             m = mats[(layer, li.name)]
             assert np.array_equal(packed_np(m.packed), quant[li.name][0])
-        for step in (0, 7, 15):
+            assert np.array_equal(bf16_bits_np(m.scales), quant[li.name][1])
+            assert np.array_equal(bf16_bits_np(m.biases), quant[li.name][2])
+        for step in range(workloads.DEP_STEPS):
             for si, st in enumerate(sorted(by_stage)):
                 stage = chain.stages[(step * workloads.DEP_LAYERS + layer) * 4 + si]
                 k = by_stage[st][0].k

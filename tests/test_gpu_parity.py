@@ -129,6 +129,53 @@ def test_gemm_small_matches_oracle(n, k, m, out_dtype):
     _check(y, y_ref, out_dtype)
 
 
+# The host planner picks the kernel variant from k. The model shapes reach the
+# GEMV with 64/32 lanes per row and the MFMA kernel with 8/32 groups per wave;
+# these k reach the others: 16 lanes per row (G = 16, 48, 80 groups) and 16
+# groups per wave (G = 129, 200, 256; m <= 4 take the GEMV, also 16 lanes).
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("k", [512, 1536, 2560])
+def test_gemv_sixteen_lane_rows(k, out_dtype):
+    n = 1000
+    P, S, B = oracle.quantize(_w(n, k, seed=k + 1))
+    x = _x(1, k, seed=k + 2)
+    y = q4.q4_gemv(to_gpu_bf16_bits(x[0]), *upload_quantized(P, S, B), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    _check(y, oracle.matmul(x, P, S, B, k)[0], out_dtype)
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 7, 16])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("k", [4128, 6400, 8192])
+def test_gemm_small_sixteen_group_waves(k, m, out_dtype):
+    n = 300
+    P, S, B = oracle.quantize(_w(n, k, seed=k + 3))
+    x = _x(m, k, seed=k + m)
+    y = q4.q4_gemm_small(to_gpu_bf16_bits(x), *upload_quantized(P, S, B), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    _check(y, oracle.matmul(x, P, S, B, k), out_dtype)
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 7, 16])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_products_on_edge_weights(m, out_dtype):
+    """The pack edge cases (degenerate and exact-affine groups, exact code ties,
+    subnormal and signed-zero inputs, magnitudes near 1e30 and 1e-30) as
+    weights of a product, tiled to k = 4096 over 21 rows."""
+    w = np.tile(_edge_weights(), (3, 64))
+    k = w.shape[1]
+    P, S, B = oracle.quantize(w)
+    x = _x(m, k, seed=50 + m)
+    gx = to_gpu_bf16_bits(x if m > 1 else x[0])
+    if m == 1:
+        y = q4.q4_gemv(gx, *upload_quantized(P, S, B), out_dtype=out_dtype)
+    else:
+        y = q4.q4_gemm_small(gx, *upload_quantized(P, S, B), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ref = oracle.matmul(x, P, S, B, k)
+    _check(y, ref[0] if m == 1 else ref, out_dtype)
+
+
 @pytest.mark.parametrize("m", [1, 2, 16])
 def test_one_hot_input_gives_exact_dequantized_column(m):
     """x = e_j in one activation row: y = w_hat[:, j] exactly in fp32 (pins the
