@@ -37,7 +37,7 @@ _lib = None
 _EXPORTS = (
     "q4_layout_version", "q4_status_str", "q4_last_hip_error", "q4_pack", "q4_unpack", "q4_gemv",
     "q4_gemm_small", "q4_multilinear_step", "q4_chain_plan_bytes", "q4_chain_encode", "q4_chain_run",
-    "q4_chain_encode_rows", "q4_chain_run_rows",
+    "q4_chain_encode_rows", "q4_chain_run_rows", "q4_chain_run_rows_noalloc",
 )
 CHAIN_WORKSPACE_BYTES = 131328
 
@@ -86,8 +86,9 @@ def load():
     lib.q4_chain_run.argtypes = [P, V, P, P]
     lib.q4_chain_encode_rows.argtypes = [P, ctypes.c_int32, P, ctypes.c_int32, ctypes.c_int32, V, P, I]
     lib.q4_chain_run_rows.argtypes = [P, ctypes.c_int32, V, P, P]
+    lib.q4_chain_run_rows_noalloc.argtypes = [P, ctypes.c_int32, V, P, P]
     for f in ("q4_pack", "q4_unpack", "q4_gemv", "q4_gemm_small", "q4_multilinear_step", "q4_chain_encode",
-              "q4_chain_run", "q4_chain_encode_rows", "q4_chain_run_rows"):
+              "q4_chain_run", "q4_chain_encode_rows", "q4_chain_run_rows", "q4_chain_run_rows_noalloc"):
         getattr(lib, f).restype = V
     _lib = lib
     return lib
@@ -347,3 +348,18 @@ def q4_chain_run(plan: ChainPlan, workspace: torch.Tensor) -> None:
         raise ValueError("workspace must be a device tensor of >= %d bytes" % CHAIN_WORKSPACE_BYTES)
     _check("q4_chain_run_rows", load().q4_chain_run_rows(_ptr(plan.device_plan), plan.m, _out_code(plan.out_dtype),
                                                          _ptr(workspace), _ptr_stream(workspace)))
+
+
+def q4_chain_run_noalloc(plan: ChainPlan, status_out: Optional[torch.Tensor] = None) -> None:
+    """Run the chain on the current stream with the library's own device-global
+    workspace (no workspace argument, no allocation). status_out: optional
+    device int32 tensor of >= 1 element that receives the launch's status word
+    (0 = ok). Calls that overlap in time on one device race."""
+    if status_out is not None:
+        _need(status_out, "status_out", torch.int32)
+        if status_out.numel() < 1:
+            raise ValueError("status_out must hold one element")
+        _same_device(plan.device_plan, status_out)
+    _check("q4_chain_run_rows_noalloc",
+           load().q4_chain_run_rows_noalloc(_ptr(plan.device_plan), plan.m, _out_code(plan.out_dtype),
+                                            _ptr(status_out), _ptr_stream(plan.device_plan)))

@@ -545,3 +545,83 @@ q4_status q4_chain_run(const void* device_plan, q4_out_dtype y_dtype, void* work
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The chain without a caller workspace. Its workspace words (status, per-XCD
+// arrival counters, XCD flags: q4k::kWsWords words, enough for up to
+// q4k::kMaxXcc XCDs) live in this device-global array, one copy per device.
+// In host code `scratch` names a host-side stand-in, never the device memory:
+// the device address comes from hipGetSymbolAddress, taken once per device
+// with that device current, and only that address is passed to kernels.
+static __device__ __align__(256) uint32_t scratch[q4k::kWsWords];
+
+namespace {
+
+constexpr int kScratchWords = q4k::kWsWords;
+static_assert(kScratchWords * sizeof(uint32_t) == Q4_CHAIN_STATIC_SCRATCH_BYTES, "scratch size as declared");
+
+struct ScratchSlot {
+  std::once_flag once;
+  std::atomic<uint32_t*> ptr{nullptr};
+  std::atomic<int> err{0};
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the current device (nullptr and the
+// hipError_t in *err if it cannot be had).
+uint32_t* device_scratch(int dev, int* err) {
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&slot]() {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      slot.err.store(e != hipSuccess ? static_cast<int>(e) : static_cast<int>(hipErrorInvalidSymbol));
+      (void)hipGetLastError();
+      return;
+    }
+    slot.ptr.store(static_cast<uint32_t*>(p));
+  });
+  *err = slot.err.load();
+  return slot.ptr.load();
+}
+
+}  // namespace
+
+extern "C" q4_status q4_chain_run_rows_noalloc(const void* device_plan, int32_t m_rows, q4_out_dtype y_dtype,
+                                               uint32_t* status_out, void* stream) {
+  if (!device_plan) return Q4_ERR_NULL;
+  if (y_dtype != Q4_OUT_BF16 && y_dtype != Q4_OUT_F32) return Q4_ERR_SHAPE;
+  if (m_rows < 1 || m_rows > q4k::kMaxRows) return Q4_ERR_SHAPE;
+  if (!aligned(device_plan, 64) || (status_out && !aligned(status_out, 4))) return Q4_ERR_ALIGN;
+  // the array holds the barrier words of up to kMaxXcc XCDs
+  const uint32_t nxcc = device_xcc_count();
+  if (nxcc < 1 || nxcc > static_cast<uint32_t>(q4k::kMaxXcc)) return Q4_ERR_UNSUPPORTED;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    g_last_hip_error = static_cast<int>(hipGetLastError());
+    return Q4_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return Q4_ERR_UNSUPPORTED;
+  int err = 0;
+  uint32_t* ws = device_scratch(dev, &err);
+  if (!ws) {
+    g_last_hip_error = err;
+    return Q4_ERR_HIP;
+  }
+  const hipStream_t st = as_stream(stream);
+  // every call starts from cleared words (an earlier call on this device may
+  // have ended on a timeout and left them inconsistent)
+  hipLaunchKernelGGL(q4k::chain_ws_clear_kernel, dim3(1), dim3(256), 0, st, ws, kScratchWords);
+  q4_status s = launch_status();
+  if (s != Q4_OK) return s;
+  const q4k::ChainHeader* plan = static_cast<const q4k::ChainHeader*>(device_plan);
+  switch (m_rows) {
+    case 1: s = launch_chain<1>(plan, y_dtype, ws, st); break;
+    case 2: s = launch_chain<2>(plan, y_dtype, ws, st); break;
+    case 3: s = launch_chain<3>(plan, y_dtype, ws, st); break;
+    default: s = launch_chain<4>(plan, y_dtype, ws, st); break;
+  }
+  if (s != Q4_OK || !status_out) return s;
+  hipLaunchKernelGGL(q4k::chain_ws_status_kernel, dim3(1), dim3(64), 0, st, ws, status_out);
+  return launch_status();
+}

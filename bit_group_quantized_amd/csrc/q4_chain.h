@@ -1151,4 +1151,15 @@ chain_kernel(const ChainHeader* __restrict__ plan, uint32_t* __restrict__ ws, ui
   }
 }
 
+// Set-up and read-out of a chain workspace that lives in a device-global
+// array (the entry point for callers that cannot allocate): clear its words
+// before a launch, and copy the launch's status word out after it.
+__global__ void __launch_bounds__(256) chain_ws_clear_kernel(uint32_t* __restrict__ ws, int words) {
+  for (int i = threadIdx.x; i < words; i += blockDim.x) ws[i] = 0u;
+}
+__global__ void __launch_bounds__(64) chain_ws_status_kernel(const uint32_t* __restrict__ ws,
+                                                             uint32_t* __restrict__ status_out) {
+  if (threadIdx.x == 0) status_out[0] = coh_load(ws + kWsStatus);
+}
+
 }  // namespace q4k

@@ -236,6 +236,23 @@ q4_status q4_chain_encode_rows(const q4_chain_stage* stages, int32_t num_stages,
 q4_status q4_chain_run_rows(const void* device_plan, int32_t m_rows, q4_out_dtype y_dtype,
                             void* workspace, void* stream);
 
+/* q4_chain_run_rows without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). It performs no allocation at all: the
+ * executor's workspace words live in a device-global array of the library
+ * (Q4_CHAIN_STATIC_SCRATCH_BYTES per device, held until the process ends;
+ * enough for devices of up to 16 XCDs, Q4_ERR_UNSUPPORTED beyond). Every call
+ * clears those words, runs the chain, and, if status_out (device uint32, may
+ * be NULL) is given, writes the launch's status word there (the values of the
+ * workspace status word described above). All calls on one device share the
+ * one array: calls that overlap in time on one device race and give undefined
+ * results, and must be serialised by the caller (e.g. one stream). Same
+ * arguments otherwise as q4_chain_run_rows; the regular entry points are
+ * unchanged. */
+#define Q4_CHAIN_STATIC_SCRATCH_BYTES 2560
+q4_status q4_chain_run_rows_noalloc(const void* device_plan, int32_t m_rows, q4_out_dtype y_dtype,
+                                    uint32_t* status_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -302,3 +302,15 @@ def test_chain_run_validation():
     assert lib.q4_chain_run(_p(A16), 0, _p(A16 + 64), None) == q4.Q4_ERR_ALIGN
     assert lib.q4_chain_run(_p(A16 + 16), 0, _p(A16), None) == q4.Q4_ERR_ALIGN
     assert lib.q4_chain_run(_p(A16), 3, _p(A16), None) == q4.Q4_ERR_SHAPE
+
+
+def test_chain_run_noalloc_validation():
+    """The entry point without a workspace validates like q4_chain_run_rows
+    (every call here fails before any HIP call)."""
+    lib = q4.load()
+    assert lib.q4_chain_run_rows_noalloc(None, 1, 0, None, None) == q4.Q4_ERR_NULL
+    assert lib.q4_chain_run_rows_noalloc(_p(A16), 0, 0, None, None) == q4.Q4_ERR_SHAPE
+    assert lib.q4_chain_run_rows_noalloc(_p(A16), 5, 0, None, None) == q4.Q4_ERR_SHAPE
+    assert lib.q4_chain_run_rows_noalloc(_p(A16), 1, 2, None, None) == q4.Q4_ERR_SHAPE
+    assert lib.q4_chain_run_rows_noalloc(_p(A16 + 16), 1, 0, None, None) == q4.Q4_ERR_ALIGN
+    assert lib.q4_chain_run_rows_noalloc(_p(A16), 1, 0, _p(A16 + 2), None) == q4.Q4_ERR_ALIGN
