@@ -191,12 +191,17 @@ def make_depformer_frame(mats, seed: int = 0, out_dtype=None, device=None):
     return Chain(stages, out_dtype)
 
 
-def cpu_baseline(seed: int, budget_s: float, sample_layers: int = 2):
+def cpu_baseline(seed: int, budget_s: float, sample_layers: int = 2, threads: int = 0):
     """The oracle (plain C, OpenMP over rows) on a bounded sample of the step: the
     first ``sample_layers`` temporal layers (7 GEMVs each, M=1), quantized once
     (not timed), then their products run pass after pass until the time budget is
-    spent. Reported as packed-weight GB/s and the implied us per 32-layer step."""
+    spent. Reported as packed-weight GB/s and the implied us per 32-layer step.
+    threads > 0 sets the oracle's thread count (0: its default, one per core)."""
     import oracle
+
+    default_threads = oracle.threads()
+    if threads > 0:
+        oracle.set_threads(threads)
 
     lin = workloads.temporal_layer()
     layers = []
@@ -219,11 +224,92 @@ def cpu_baseline(seed: int, budget_s: float, sample_layers: int = 2):
         passes += 1
     gbs = bytes_done / elapsed / 1e9
     us_step = elapsed / (passes * len(layers)) * workloads.TEMPORAL_LAYERS * 1e6
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": oracle.threads(), "kind": "oracle",
+    used = oracle.threads()
+    oracle.set_threads(default_threads)
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": used, "kind": "oracle",
             "sample": f"temporal layers 0..{sample_layers - 1} of 32 (7 GEMVs each, M=1, "
                       f"{layer_bytes * len(layers) / 1e6:.0f} MB packed), {passes} passes, oracle product "
                       f"timed ({elapsed:.1f} s); quantization not timed",
             "us_per_step": round(us_step, 1)}
+
+
+def stream_ceiling(dev, nbytes: int, reps: int = 3):
+    """HBM stream-read ceiling for nbytes: a plain read-and-fold kernel
+    (libq4_ceiling.so) over a buffer of the same size as the workload's packed
+    weights, at a small sweep of launch shapes; the best median rate wins."""
+    import ctypes
+
+    import torch
+
+    from bit_group_quantized_amd import build as q4_build
+
+    lib = ctypes.CDLL(q4_build.CEILING_LIB)
+    lib.q4_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_void_p]
+    nbytes = nbytes // 16 * 16
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device=dev)
+    buf.random_()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(cus * 32, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    best = None
+    for per_cu in (4, 8, 16, 32):
+        for unroll in (2, 4, 8):
+            for nt in (0, 1):
+                blocks = cus * per_cu
+
+                def once():
+                    rc = lib.q4_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()),
+                                            blocks, unroll, nt, ctypes.c_void_p(stream.cuda_stream))
+                    if rc != 0:
+                        raise RuntimeError(f"q4_stream_read failed ({rc})")
+
+                once()
+                ts = []
+                for _ in range(reps):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    once()
+                    b.record(stream)
+                    b.synchronize()
+                    ts.append(a.elapsed_time(b))
+                gbs = nbytes / (float(np.median(ts)) * 1e-3) / 1e9
+                if best is None or gbs > best["gbs"]:
+                    best = {"gbs": round(gbs, 1), "blocks_per_cu": per_cu, "loads_in_flight_per_lane": unroll,
+                            "nontemporal": bool(nt)}
+    del buf
+    best["bytes"] = nbytes
+    best["kernel"] = "stream_read_kernel"
+    return best
+
+
+def pack_timing(dev, seed: int):
+    """q4_pack on the GPU against the oracle's quantizer on the host, on one
+    11264x4096 temporal matrix (input fp32 bytes per second)."""
+    import torch
+
+    import bit_group_quantized_amd as q4
+    import oracle
+
+    n, k = workloads.FFN, workloads.HIDDEN
+    w = workloads.weights(seed, workloads.CFG_STEP, 0, 4, n, k)
+    wt = torch.from_numpy(w).to(dev)
+    outs = q4.q4_pack(wt)
+    stream = torch.cuda.current_stream(dev)
+    reps = 20
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        q4.q4_pack(wt, *outs)
+    b.record(stream)
+    b.synchronize()
+    gpu_s = a.elapsed_time(b) * 1e-3 / reps
+    t0 = time.perf_counter()
+    oracle.quantize(w)
+    cpu_s = time.perf_counter() - t0
+    return {"matrix": f"{n}x{k} fp32 ({w.nbytes / 1e6:.0f} MB)", "q4_pack_us": round(gpu_s * 1e6, 1),
+            "q4_pack_gbs": round(w.nbytes / gpu_s / 1e9, 1), "oracle_quantize_ms": round(cpu_s * 1e3, 1),
+            "oracle_quantize_gbs": round(w.nbytes / cpu_s / 1e9, 3), "oracle_threads": oracle.threads()}
 
 
 def main(argv=None) -> int:
@@ -232,13 +318,14 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--mode", choices=("chain", "launches"), default="chain")
-    ap.add_argument("--workload", choices=("step", "depformer", "gemm", "gemv"), default="step",
+    ap.add_argument("--workload", choices=("step", "depformer", "gemm", "gemv", "layer"), default="step",
                     help="step: the 32-layer temporal step at M=1 (the headline); depformer: one "
                          "Depformer frame (16 codebook steps x 6 layers, M=1); gemm: the temporal "
                          "step's 224 matrices against X [M, k] (--m rows; one persistent chain launch for "
                          "M <= 4 in --mode chain, else one q4_gemm_small call per matrix); gemv: "
                          "one 4096x4096 GEMV, M=1, over 64 distinct matrices in turn (671 MB, past "
-                         "the 256 MB last-level cache)")
+                         "the 256 MB last-level cache); layer: one temporal layer's 7 GEMVs (4 stages), "
+                         "8 distinct layers in turn (1.03 GB, past the last-level cache)")
     ap.add_argument("--m", type=int, default=4, help="rows of X for --workload gemm")
     ap.add_argument("--dependent", action="store_true",
                     help="step: every stage's activation is the previous stage's first output (q -> o "
@@ -249,6 +336,8 @@ def main(argv=None) -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="step: skip the dependent step, the stream-read ceiling and the pack timing")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the step, run 5 plain device copies of MIB MiB (int32 "
                          "bitwise_not, MIB MiB read + MIB MiB written each) so that HBM byte "
@@ -328,6 +417,27 @@ def main(argv=None) -> int:
 
     ms_per_step = total_ms / args.steps
     gbs = wbytes / (ms_per_step * 1e-3) / 1e9
+    extra = {}
+    if args.mode == "chain" and not args.dependent and not args.no_extras:
+        # the same step with the model's data flow: every stage reads the
+        # previous stage's first output (stores before the barrier, coherent
+        # activation loads after it)
+        for prev, st in zip(chain.stages, chain.stages[1:]):
+            st.x = prev.outs[0]
+        chain._plan = None
+        chain.prepare_chain()
+        dms, dper = time_replays(chain.run_chain, args.steps, args.warmup)
+        if chain.chain_status() != 0:
+            print(f"chain executor reported status {chain.chain_status()} (dependent step)", file=sys.stderr)
+            return 1
+        extra["dependent_step"] = {"us_per_step": round(dms * 1e3, 1),
+                                   "gbs": round(wbytes / (dms * 1e-3) / 1e9, 1),
+                                   "pct_hbm_peak": round(100 * wbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                                   "step_ms_p10_p50_p90": [round(float(np.percentile(dper, q)), 4)
+                                                           for q in (10, 50, 90)]}
+        log("[bench] stream ceiling ...")
+        extra["stream_ceiling"] = stream_ceiling(dev, wbytes)
+        extra["pack"] = pack_timing(dev, args.seed)
     # dominant kernel: in chain mode the single launch per step; its duration is
     # the per-step event interval on the launch stream
     kernel_ms = ms_per_step / launches_per_step
@@ -360,11 +470,20 @@ def main(argv=None) -> int:
                      "traffic": chain_traffic_bytes(full and not args.dependent) if args.mode == "chain" else None,
                      "traffic_unit": "bytes per launch",
                      "kernel": "chain_kernel" if args.mode == "chain" else "gemv_kernel",
-                     "bytes_per_launch": wbytes // launches_per_step},
+                     "bytes_per_launch": wbytes // launches_per_step,
+                     "timing": "HIP events on the launch stream around each launch, mean over the timed steps"},
     }
+    if "stream_ceiling" in extra:
+        c = extra["stream_ceiling"]["gbs"]
+        result["roofline"]["stream_ceiling_gbs"] = c
+        result["roofline"]["frac_of_stream_ceiling"] = round(achieved / c, 4)
+    result.update(extra)
     if not args.no_cpu:
         log("[bench] cpu baseline ...")
         result["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_seconds)
+        one = cpu_baseline(args.seed, args.cpu_seconds / 2, sample_layers=1, threads=1)
+        result["cpu_baseline"]["single_thread"] = {"value": one["value"], "unit": "GB/s", "cores": one["cores"],
+                                                   "sample": one["sample"], "us_per_step": one["us_per_step"]}
     print(json.dumps(result), flush=True)
     return 0
 
@@ -443,6 +562,37 @@ def bench_other(args, dev) -> int:
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "traffic_unit": "bytes per launch",
                          "kernel": "gemv_kernel", "bytes_per_launch": wbytes // copies},
+        }
+        print(json.dumps(result), flush=True)
+        return 0
+    if args.workload == "layer":
+        rot = 8
+        chain = make_temporal_chain(args.seed, rot, config=workloads.CFG_LAYER, device=dev)
+        wbytes = chain.weight_bytes()
+        if args.mode == "chain":
+            chain.prepare_chain()
+            run, launches, kernel = chain.run_chain, 1, "chain_kernel"
+        else:
+            g = graph_of(chain.run_launches)
+            run, launches, kernel = g.replay, chain.num_matrices(), "gemv_kernel"
+        ms, per = time_replays(run, args.steps, args.warmup)
+        if args.mode == "chain" and chain.chain_status() != 0:
+            print(f"chain executor reported status {chain.chain_status()}", file=sys.stderr)
+            return 1
+        per_layer_us = ms * 1e3 / rot
+        gbs = wbytes / (ms * 1e-3) / 1e9
+        result = {
+            "metric": "packed-weight GB/s (% HBM peak) + us per temporal layer (7 GEMVs), M=1",
+            "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "us_per_layer": round(per_layer_us, 2), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "temporal_layer_m1", "hidden": workloads.HIDDEN, "ffn": workloads.FFN, "m": 1,
+                       "group": 32, "layers_in_turn": rot, "packed_bytes_per_layer": wbytes // rot,
+                       "executor": args.mode, "launches_per_layer": launches / rot, "stages_per_layer": 4},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "traffic_unit": "bytes per launch",
+                         "kernel": kernel, "bytes_per_launch": wbytes // launches,
+                         "timing": "HIP events on the launch stream, mean over the timed replays"},
         }
         print(json.dumps(result), flush=True)
         return 0

@@ -26,16 +26,28 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = ["hipcc", *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), SRC, "-o", tmp]
+# measurement support for the benchmark (a plain HBM stream-read kernel)
+CEILING_SRC = os.path.join(HERE, "csrc", "q4_stream_ceiling.hip")
+CEILING_LIB = os.path.join(HERE, "libq4_ceiling.so")
+
+
+def _hipcc(src: str, lib: str, verbose: bool) -> str:
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = ["hipcc", *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), src, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libq4.so (the library) and libq4_ceiling.so (the benchmark's
+    stream-read ceiling kernel) for gfx950."""
+    _hipcc(CEILING_SRC, CEILING_LIB, verbose)
+    return _hipcc(SRC, LIB, verbose)
 
 
 def stale() -> bool:
