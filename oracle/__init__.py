@@ -18,6 +18,9 @@ pages it follows in the C source. Summary of what is computed:
 * ``matmul(x, ...)``: ``y = x . W_hat^T`` summed in float64 (the blog
   translation's MultiLinear figure: quantized product with transpose).
 * ``multilinear_step``: the same product on rows ``[s*out, (s+1)*out)``.
+* ``embed_sum``: per frame, the sum over token streams of the dequantized
+  embedding row each token selects (the blog translation's pipeline figure:
+  17 streams summed into the step's input; embeddings stay packed).
 
 Parity status of each function is recorded in the design notes; every function
 here is pinned by ``tests/test_oracle_pins.py``.
@@ -65,10 +68,11 @@ def _load():
     lib.oracle_matmul.argtypes = [P, I, P, P, P, I, I, P]
     lib.oracle_multilinear_step.argtypes = [P, I, P, P, P, I, I, I, I, P]
     lib.oracle_bf16_round.argtypes = [P, I, P]
+    lib.oracle_embed_sum.argtypes = [P, I, I, P, P, P, P, I, P]
     lib.oracle_threads.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     for f in ("oracle_quantize", "oracle_unpack", "oracle_matmul", "oracle_multilinear_step",
-              "oracle_bf16_round"):
+              "oracle_bf16_round", "oracle_embed_sum"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -169,6 +173,37 @@ def multilinear_step(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray,
     _check(_load().oracle_multilinear_step(_ptr(x_bits), m, _ptr(packed), _ptr(scales), _ptr(biases),
                                            num_steps, out, k, step, _ptr(y)), "multilinear_step")
     return y[0] if squeeze else y
+
+
+def embed_sum(tokens: np.ndarray, tables, dim: int) -> np.ndarray:
+    """Sum over streams of the dequantized embedding rows the tokens select.
+
+    tokens: int32 [frames, streams]; tables: one (packed, scales, biases) per
+    stream, each [rows_t, dim] in the packed layout. A token outside [0, rows_t)
+    adds nothing. Returns float64 [frames, dim] (the pipeline figure of the
+    blog translation: the 17 token streams are summed into the step's input)."""
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    if tokens.ndim != 2 or tokens.shape[1] != len(tables):
+        raise ValueError("tokens must be [frames, streams] with one table per stream")
+    frames, streams = tokens.shape
+    arrs = []
+    for P, S, B in tables:
+        P = np.ascontiguousarray(P, dtype=np.uint32)
+        S = np.ascontiguousarray(S, dtype=np.uint16)
+        B = np.ascontiguousarray(B, dtype=np.uint16)
+        if P.shape[1] * 8 != dim or S.shape != (P.shape[0], dim // GROUP) or B.shape != S.shape:
+            raise ValueError("table shape mismatch")
+        arrs.append((P, S, B))
+    VP = ctypes.c_void_p * streams
+    pp = VP(*[a[0].ctypes.data for a in arrs])
+    sp = VP(*[a[1].ctypes.data for a in arrs])
+    bp = VP(*[a[2].ctypes.data for a in arrs])
+    rows = np.array([a[0].shape[0] for a in arrs], dtype=np.int64)
+    y = np.empty((frames, dim), dtype=np.float64)
+    _check(_load().oracle_embed_sum(_ptr(tokens), frames, streams, ctypes.cast(pp, ctypes.c_void_p),
+                                    ctypes.cast(sp, ctypes.c_void_p), ctypes.cast(bp, ctypes.c_void_p), _ptr(rows),
+                                    dim, _ptr(y)), "embed_sum")
+    return y
 
 
 def output_bits_bf16(y: np.ndarray) -> np.ndarray:

@@ -212,6 +212,48 @@ int oracle_multilinear_step(const uint16_t* x, int64_t m, const uint32_t* packed
                        biases + start * (k / 32), out, k, y);
 }
 
+/* --- packed-embedding gather and stream sum --- */
+
+/* The step's input is the sum of one embedding row per token stream: the
+ * text stream and the audio codebook streams are summed into one vector
+ * ("NVIDIA PersonaPlex 7B on Apple Silicon", pipeline figure: 17 streams,
+ * text plus 8 user plus 8 assistant audio, summed into the temporal
+ * transformer), and the embeddings stay packed ("personaplex-edge-q4" model
+ * card, introduction). Each stream t has its own table, stored in the packed
+ * layout above with rows[t] rows of `dim` values. For frame f:
+ *   y[f][d] = sum over t of w_hat_t[tokens[f][t]][d]
+ * where a token outside [0, rows[t]) (a stream with no token this frame)
+ * adds nothing. Each w_hat is the fp32 dequantized value (exact), summed in
+ * double in stream order. tokens: int32 [frames][streams]; y: double
+ * [frames][dim]. */
+int oracle_embed_sum(const int32_t* tokens, int64_t frames, int64_t streams, const uint32_t* const* packed,
+                     const uint16_t* const* scales, const uint16_t* const* biases, const int64_t* rows,
+                     int64_t dim, double* y) {
+  if (!tokens || !packed || !scales || !biases || !rows || !y || frames < 0 || streams < 1 || dim <= 0 ||
+      dim % 32 != 0)
+    return ORACLE_ERR_ARG;
+  for (int64_t t = 0; t < streams; ++t)
+    if (!packed[t] || !scales[t] || !biases[t] || rows[t] < 0) return ORACLE_ERR_ARG;
+  const int64_t groups = dim / 32;
+  for (int64_t f = 0; f < frames; ++f) {
+    for (int64_t d = 0; d < dim; ++d) {
+      double acc = 0.0;
+      for (int64_t t = 0; t < streams; ++t) {
+        const int64_t tok = tokens[f * streams + t];
+        if (tok < 0 || tok >= rows[t]) continue;
+        uint32_t word = packed[t][tok * (dim / 8) + d / 8];
+        uint32_t q = (word >> (4 * (d % 8))) & 0xFu;
+        float s = bf16_value(scales[t][tok * groups + d / 32]);
+        float b = bf16_value(biases[t][tok * groups + d / 32]);
+        float w_hat = s * (float)q + b;
+        acc += (double)w_hat;
+      }
+      y[f * dim + d] = acc;
+    }
+  }
+  return ORACLE_OK;
+}
+
 /* Threads the OpenMP runtime will use (1 when built without OpenMP). */
 int oracle_threads(void) {
 #ifdef _OPENMP

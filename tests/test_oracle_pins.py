@@ -442,3 +442,72 @@ def test_floored_rel_err_non_finite_output_fails():
     assert oracle.floored_rel_err(np.array([[1.0, 2.0, -np.inf]]), ref) == float("inf")
     with pytest.raises(ValueError):
         oracle.floored_rel_err(np.zeros((1, 2)), ref)
+
+
+# ---------------------------------------------------------------- embedding gather + stream sum
+# (the blog translation's pipeline figure: 17 token streams, text + 8 user + 8
+# assistant audio, summed into the temporal step's input; the model card's
+# introduction: embeddings stay packed)
+
+def _affine_table(rows, dim, a, s0, seed):
+    """A table whose every group is exactly affine: w = a + s0 * code, codes
+    drawn per element with 0 and 15 in every group (so the quantizer stores
+    exactly s0 and a). Returns (weights fp32, codes int)."""
+    r = np.random.default_rng(seed)
+    codes = r.integers(0, 16, size=(rows, dim))
+    codes[:, 0::32] = 0
+    codes[:, 1::32] = 15
+    w = (np.float64(a) + np.float64(s0) * codes).astype(np.float32)
+    assert np.all(w.astype(np.float64) == np.float64(a) + np.float64(s0) * codes)
+    return w, codes
+
+
+def test_embed_single_stream_selects_the_dequantized_row():
+    dim = 256
+    w = _gaussian(40, dim, seed=60)
+    table = oracle.quantize(w)
+    _, w_hat = oracle.unpack(*table, dim)
+    tokens = np.array([[0], [7], [39], [12]], dtype=np.int32)
+    y = oracle.embed_sum(tokens, [table], dim)
+    for f, tok in enumerate(tokens[:, 0]):
+        assert np.array_equal(y[f], w_hat[tok].astype(np.float64))
+
+
+def test_embed_sum_of_seventeen_affine_streams_closed_form():
+    """17 streams of exactly affine tables (bias a_t, step s0_t): the sum is
+    sum_t (a_t + s0_t * code_t[token_t][d]), exact in double (small dyadic
+    values), written out from the construction, not from the oracle."""
+    dim, streams = 128, 17
+    params = [(-1.5 + 0.25 * t, 2.0 ** -(t % 5), 3 if t == 0 else 2) for t in range(streams)]
+    tables, codes, rows_of = [], [], []
+    for t, (a, s0, rows_scale) in enumerate(params):
+        rows = 16 * rows_scale
+        w, c = _affine_table(rows, dim, a, s0, seed=70 + t)
+        P, S, B = oracle.quantize(w)
+        assert np.all(oracle.bf16_value(S) == np.float32(s0)) and np.all(oracle.bf16_value(B) == np.float32(a))
+        tables.append((P, S, B))
+        codes.append(c)
+        rows_of.append(rows)
+    r = np.random.default_rng(80)
+    tokens = np.stack([[r.integers(0, rows_of[t]) for t in range(streams)] for _ in range(3)]).astype(np.int32)
+    y = oracle.embed_sum(tokens, tables, dim)
+    for f in range(tokens.shape[0]):
+        want = np.zeros(dim, dtype=np.float64)
+        for t, (a, s0, _) in enumerate(params):
+            want += a + s0 * codes[t][tokens[f, t]]
+        assert np.array_equal(y[f], want)
+
+
+def test_embed_tokens_outside_a_table_add_nothing():
+    dim = 64
+    t0 = oracle.quantize(_gaussian(5, dim, seed=90))
+    t1 = oracle.quantize(_gaussian(9, dim, seed=91))
+    _, w0 = oracle.unpack(*t0, dim)
+    _, w1 = oracle.unpack(*t1, dim)
+    tokens = np.array([[-1, 3], [5, 2], [4, 9], [-7, -1], [2, 8]], dtype=np.int32)
+    y = oracle.embed_sum(tokens, [t0, t1], dim)
+    assert np.array_equal(y[0], w1[3].astype(np.float64))
+    assert np.array_equal(y[1], w1[2].astype(np.float64))      # token 5 is past table 0's 5 rows
+    assert np.array_equal(y[2], w0[4].astype(np.float64))      # token 9 is past table 1's 9 rows
+    assert not y[3].any()
+    assert np.array_equal(y[4], w0[2].astype(np.float64) + w1[8].astype(np.float64))
