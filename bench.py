@@ -318,14 +318,16 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--mode", choices=("chain", "launches"), default="chain")
-    ap.add_argument("--workload", choices=("step", "depformer", "gemm", "gemv", "layer"), default="step",
+    ap.add_argument("--workload", choices=("step", "depformer", "gemm", "gemv", "layer", "embed"), default="step",
                     help="step: the 32-layer temporal step at M=1 (the headline); depformer: one "
                          "Depformer frame (16 codebook steps x 6 layers, M=1); gemm: the temporal "
                          "step's 224 matrices against X [M, k] (--m rows; one persistent chain launch for "
                          "M <= 4 in --mode chain, else one q4_gemm_small call per matrix); gemv: "
                          "one 4096x4096 GEMV, M=1, over 64 distinct matrices in turn (671 MB, past "
                          "the 256 MB last-level cache); layer: one temporal layer's 7 GEMVs (4 stages), "
-                         "8 distinct layers in turn (1.03 GB, past the last-level cache)")
+                         "8 distinct layers in turn (1.03 GB, past the last-level cache); embed: the "
+                         "packed-embedding gather and 17-stream sum of --m frames (text table 32000 x 4096, "
+                         "16 audio tables 2048 x 4096), 64 token sets in turn")
     ap.add_argument("--m", type=int, default=4, help="rows of X for --workload gemm")
     ap.add_argument("--dependent", action="store_true",
                     help="step: every stage's activation is the previous stage's first output (q -> o "
@@ -562,6 +564,45 @@ def bench_other(args, dev) -> int:
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "traffic_unit": "bytes per launch",
                          "kernel": "gemv_kernel", "bytes_per_launch": wbytes // copies},
+        }
+        print(json.dumps(result), flush=True)
+        return 0
+    if args.workload == "embed":
+        import torch as _t
+
+        frames, sets = max(1, args.m), 64
+        shapes = [(workloads.TEXT_VOCAB, workloads.HIDDEN)] + [(workloads.AUDIO_CODEBOOK, workloads.HIDDEN)] * 16
+        tables = []
+        for t, (rows, dim) in enumerate(shapes):
+            w = workloads.weights(args.seed, 6, 1, t, rows, dim)
+            wt = _t.from_numpy(w).to(dev)
+            tables.append(q4.q4_pack(wt))
+            del wt
+        r = np.random.default_rng(args.seed)
+        toks = [_t.from_numpy(np.stack([[r.integers(0, n) for n, _ in shapes] for _ in range(frames)])
+                              .astype(np.int32)).to(dev) for _ in range(sets)]
+        ys = [_t.empty((frames, workloads.HIDDEN), dtype=_t.bfloat16, device=dev) for _ in range(sets)]
+
+        def calls():
+            for tk, y in zip(toks, ys):
+                q4.q4_embed_sum(tk, tables, out=y)
+
+        g = graph_of(calls)
+        ms, per = time_replays(g.replay, args.steps, args.warmup)
+        us = ms * 1e3 / sets
+        gathered = frames * len(shapes) * workloads.HIDDEN * 5 // 8  # packed bytes read per call
+        gbs = gathered / (us * 1e-6) / 1e9
+        result = {
+            "metric": "us per packed-embedding gather + 17-stream sum (GB/s of packed rows read)",
+            "value": round(us, 3), "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"embed_sum_{frames}_frames", "streams": len(shapes), "dim": workloads.HIDDEN,
+                       "text_rows": workloads.TEXT_VOCAB, "audio_rows": workloads.AUDIO_CODEBOOK, "frames": frames,
+                       "packed_bytes_per_call": gathered, "executor": f"graph of {sets} q4_embed_sum calls"},
+            "roofline": {"bound": "latency", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 6), "traffic": None, "kernel": "embed_sum_kernel",
+                         "bytes_per_launch": gathered,
+                         "timing": "HIP events on the launch stream around graph replays of 64 calls"},
         }
         print(json.dumps(result), flush=True)
         return 0

@@ -37,8 +37,9 @@ _lib = None
 _EXPORTS = (
     "q4_layout_version", "q4_status_str", "q4_last_hip_error", "q4_pack", "q4_unpack", "q4_gemv",
     "q4_gemm_small", "q4_multilinear_step", "q4_chain_plan_bytes", "q4_chain_encode", "q4_chain_run",
-    "q4_chain_encode_rows", "q4_chain_run_rows", "q4_chain_run_rows_noalloc",
+    "q4_chain_encode_rows", "q4_chain_run_rows", "q4_chain_run_rows_noalloc", "q4_embed_sum",
 )
+EMBED_MAX_TABLES = 32  # Q4_EMBED_MAX_TABLES
 CHAIN_WORKSPACE_BYTES = 131328
 
 
@@ -50,6 +51,11 @@ class _ChainMatrix(ctypes.Structure):
 class _ChainStage(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("k", ctypes.c_int64), ("first_matrix", ctypes.c_int32),
                 ("num_matrices", ctypes.c_int32)]
+
+
+class _EmbedTable(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
+                ("rows", ctypes.c_int64)]
 
 
 class Q4Error(RuntimeError):
@@ -87,8 +93,9 @@ def load():
     lib.q4_chain_encode_rows.argtypes = [P, ctypes.c_int32, P, ctypes.c_int32, ctypes.c_int32, V, P, I]
     lib.q4_chain_run_rows.argtypes = [P, ctypes.c_int32, V, P, P]
     lib.q4_chain_run_rows_noalloc.argtypes = [P, ctypes.c_int32, V, P, P]
+    lib.q4_embed_sum.argtypes = [P, I, P, ctypes.c_int32, I, P, V, P]
     for f in ("q4_pack", "q4_unpack", "q4_gemv", "q4_gemm_small", "q4_multilinear_step", "q4_chain_encode",
-              "q4_chain_run", "q4_chain_encode_rows", "q4_chain_run_rows", "q4_chain_run_rows_noalloc"):
+              "q4_chain_run", "q4_chain_encode_rows", "q4_chain_run_rows", "q4_chain_run_rows_noalloc", "q4_embed_sum"):
         getattr(lib, f).restype = V
     _lib = lib
     return lib
@@ -267,6 +274,40 @@ def q4_multilinear_step(x: torch.Tensor, packed: torch.Tensor, scales: torch.Ten
     _check("q4_multilinear_step",
            load().q4_multilinear_step(_ptr(x2), m, _ptr(packed), _ptr(scales), _ptr(biases), num_steps, out_rows,
                                       k, int(step), _ptr(out), code, _ptr_stream(x)))
+    return out
+
+
+def q4_embed_sum(tokens: torch.Tensor, tables, out_dtype: torch.dtype = torch.bfloat16,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y [frames, dim] = per frame, the sum over streams of the packed
+    embedding row each token selects (tokens: int32 [frames, streams] on the
+    device; tables: one (packed, scales, biases) per stream, [rows_t, dim]).
+    A token outside [0, rows_t) adds nothing."""
+    if not isinstance(tokens, torch.Tensor) or tokens.dim() != 2:
+        raise ValueError("tokens must be [frames, streams]")
+    frames, streams = tokens.shape
+    if streams != len(tables) or not 1 <= streams <= EMBED_MAX_TABLES:
+        raise ValueError(f"one table per stream (1..{EMBED_MAX_TABLES}): {streams} streams, {len(tables)} tables")
+    dims = set()
+    descs = []
+    for t, (packed, scales, biases) in enumerate(tables):
+        rows, dim = _check_matrix(packed, scales, biases)
+        dims.add(dim)
+        descs.append(_EmbedTable(packed.data_ptr(), scales.data_ptr(), biases.data_ptr(), rows))
+    if len(dims) != 1:
+        raise ValueError("every table must have the same dim")
+    dim = dims.pop()
+    _need(tokens, "tokens", torch.int32)
+    code = _out_code(out_dtype if out is None else out.dtype)
+    if out is None:
+        out = torch.empty((frames, dim), dtype=out_dtype, device=tokens.device)
+    _need(out, "out", out.dtype)
+    if out.numel() != frames * dim:
+        raise ValueError("out must hold frames*dim elements")
+    _same_device(tokens, out, *[p for tb in tables for p in tb])
+    arr = (_EmbedTable * streams)(*descs)
+    _check("q4_embed_sum", load().q4_embed_sum(_ptr(tokens), frames, ctypes.byref(arr), streams, dim, _ptr(out), code,
+                                               _ptr_stream(tokens)))
     return out
 
 

@@ -309,6 +309,43 @@ q4_status q4_multilinear_step(const uint16_t* x, int64_t m, const uint32_t* pack
                         biases + row0 * (k / 32), out, k, y, y_dtype, as_stream(stream));
 }
 
+q4_status q4_embed_sum(const int32_t* tokens, int64_t frames, const q4_embed_table* tables, int32_t num_tables,
+                       int64_t dim, void* y, q4_out_dtype y_dtype, void* stream) {
+  if (!tokens || !tables || !y) return Q4_ERR_NULL;
+  for (int32_t t = 0; t < num_tables && t < Q4_EMBED_MAX_TABLES; ++t)
+    if (!tables[t].packed || !tables[t].scales || !tables[t].biases) return Q4_ERR_NULL;
+  if (num_tables < 1 || num_tables > Q4_EMBED_MAX_TABLES || frames < 0 || dim <= 0 || dim % 32 != 0)
+    return Q4_ERR_SHAPE;
+  if (y_dtype != Q4_OUT_BF16 && y_dtype != Q4_OUT_F32) return Q4_ERR_SHAPE;
+  for (int32_t t = 0; t < num_tables; ++t)
+    if (tables[t].rows < 1) return Q4_ERR_SHAPE;
+  if (!aligned(tokens, 4) || !aligned(y, 16)) return Q4_ERR_ALIGN;
+  for (int32_t t = 0; t < num_tables; ++t)
+    if (!aligned(tables[t].packed, 16) || !aligned(tables[t].scales, 2) || !aligned(tables[t].biases, 2))
+      return Q4_ERR_ALIGN;
+  // every table is addressed through 32-bit buffer ranges
+  for (int32_t t = 0; t < num_tables; ++t)
+    if (tables[t].rows > (int64_t)INT32_MAX / (dim / 2)) return Q4_ERR_UNSUPPORTED;
+  if (frames == 0) return Q4_OK;
+  const int G = static_cast<int>(dim / 32);
+  const int tiles = static_cast<int>(ceil_div(G, 64));
+  if (frames > (int64_t)INT32_MAX / tiles) return Q4_ERR_UNSUPPORTED;
+  q4k::EmbedTables tabs{};
+  for (int32_t t = 0; t < num_tables; ++t) {
+    tabs.packed[t] = tables[t].packed;
+    tabs.scales[t] = tables[t].scales;
+    tabs.biases[t] = tables[t].biases;
+    tabs.rows[t] = static_cast<int32_t>(tables[t].rows);
+  }
+  tabs.count = num_tables;
+  const dim3 grid(static_cast<unsigned>(frames * tiles)), block(64);
+  if (y_dtype == Q4_OUT_F32)
+    hipLaunchKernelGGL((q4k::embed_sum_kernel<true>), grid, block, 0, as_stream(stream), tokens, tabs, G, tiles, y);
+  else
+    hipLaunchKernelGGL((q4k::embed_sum_kernel<false>), grid, block, 0, as_stream(stream), tokens, tabs, G, tiles, y);
+  return launch_status();
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------------------

@@ -564,4 +564,97 @@ __global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restr
   }
 }
 
+// ---------------------------------------------------------------------------
+// Packed-embedding gather and stream sum: the step's input vector is the sum
+// of one packed embedding row per token stream ("NVIDIA PersonaPlex 7B on
+// Apple Silicon", pipeline figure: 17 streams summed; "personaplex-edge-q4"
+// model card, introduction: embeddings stay packed).
+//
+// Lane g of a block owns group g of a frame's output row (32 values in
+// registers); it gathers that group of every stream's row, kEmbedBatch
+// streams' loads in flight at a time, and adds the dequantized values in
+// stream order in fp32. Every load goes through a buffer descriptor of the
+// whole table: a token outside [0, rows) gets an offset past the range and
+// reads zeros (code 0, scale 0, bias 0: nothing added).
+constexpr int kEmbedMaxTables = 32;
+constexpr int kEmbedBatch = 17;  // the model's 17 streams: one round of loads
+struct EmbedTables {
+  const uint32_t* packed[kEmbedMaxTables];
+  const uint16_t* scales[kEmbedMaxTables];
+  const uint16_t* biases[kEmbedMaxTables];
+  int32_t rows[kEmbedMaxTables];
+  int32_t count;
+};
+
+template <bool OUT_F32>
+__global__ void __launch_bounds__(64) embed_sum_kernel(const int32_t* __restrict__ tokens, EmbedTables tabs,
+                                                       int G, int tiles, void* __restrict__ y) {
+  const int f = blockIdx.x / tiles;
+  const int g = (blockIdx.x - f * tiles) * 64 + threadIdx.x;
+  const bool gv = g < G;
+  const int nt = tabs.count;
+  float acc[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) acc[i] = 0.f;
+  for (int t0 = 0; t0 < nt; t0 += kEmbedBatch) {
+    uint4 w[kEmbedBatch];
+    uint32_t sv[kEmbedBatch], bv[kEmbedBatch];
+#pragma unroll
+    for (int b = 0; b < kEmbedBatch; ++b) {
+      const int t = t0 + b;
+      int tok = -1, rows = 0;
+      const uint32_t* pk = nullptr;
+      const uint16_t* sc = nullptr;
+      const uint16_t* bi = nullptr;
+      if (t < nt) {
+        tok = tokens[(int64_t)f * nt + t];
+        rows = tabs.rows[t];
+        pk = tabs.packed[t];
+        sc = tabs.scales[t];
+        bi = tabs.biases[t];
+      }
+      const bool ok = gv && tok >= 0 && tok < rows;
+      const uint32_t e = ok ? (uint32_t)tok * (uint32_t)G + (uint32_t)g : 0u;
+      const __amdgpu_buffer_rsrc_t rw =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(pk), 0, rows * G * 16, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(sc), 0, rows * G * 2, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rb =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(bi), 0, rows * G * 2, 0x00020000);
+      const u32x4_t v = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? (int)(e * 16u) : (int)0xFFFFFFF0, 0, 0));
+      w[b] = make_uint4(v.x, v.y, v.z, v.w);
+      sv[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, ok ? (int)(e * 2u) : (int)0xFFFFFFF0, 0, 0);
+      bv[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, ok ? (int)(e * 2u) : (int)0xFFFFFFF0, 0, 0);
+    }
+#pragma unroll
+    for (int b = 0; b < kEmbedBatch; ++b) {
+      // w_hat = s * q + b: the product is exact, so the fma rounds once
+      const float sc = bf16_to_f32(sv[b]), bi = bf16_to_f32(bv[b]);
+      const uint32_t ws[4] = {w[b].x, w[b].y, w[b].z, w[b].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int n = 0; n < 8; ++n) acc[8 * j + n] += fmaf(sc, (float)((ws[j] >> (4 * n)) & 0xFu), bi);
+    }
+  }
+  if (!gv) return;
+  const int64_t base = ((int64_t)f * G + g) * 32;
+  if constexpr (OUT_F32) {
+    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(y) + base);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = make_float4(acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]);
+  } else {
+    uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + base);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t p[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        p[h] = (uint32_t)f32_to_bf16_rne(acc[8 * i + 2 * h]) | ((uint32_t)f32_to_bf16_rne(acc[8 * i + 2 * h + 1]) << 16);
+      dst[i] = make_uint4(p[0], p[1], p[2], p[3]);
+    }
+  }
+}
+
 }  // namespace q4k

@@ -138,6 +138,33 @@ q4_status q4_multilinear_step(const uint16_t* x, int64_t m, const uint32_t* pack
                               int64_t out, int64_t k, int64_t step, void* y,
                               q4_out_dtype y_dtype, void* stream);
 
+/* Packed-embedding gather and stream sum: the step's input vector is the sum
+ * of one embedding row per token stream ("NVIDIA PersonaPlex 7B on Apple
+ * Silicon", pipeline figure: 17 streams, text + 8 user + 8 assistant audio
+ * codebooks, summed into the temporal transformer; "personaplex-edge-q4"
+ * model card, introduction: the embeddings stay packed). Each stream t has
+ * its own table of `rows` rows of `dim` values in the stored layout above
+ * (rows x dim/2 bytes must stay below 2^31). For frame f:
+ *   y[f][d] = sum over t of w_hat_t[tokens[f][t]][d]
+ * with the dequantized values added in stream order in fp32 and rounded once
+ * if y is bf16. A token outside [0, rows_t) (a stream with no token this
+ * frame) adds nothing; the device reads no memory for it.
+ *   tokens : DEVICE int32 [frames][num_tables]
+ *   tables : HOST array of num_tables descriptors (1..Q4_EMBED_MAX_TABLES);
+ *            their pointers are device pointers (packed 16-byte aligned)
+ *   y      : DEVICE [frames][dim] of y_dtype, 16-byte aligned
+ * dim must be a positive multiple of 32. frames == 0 launches nothing. */
+#define Q4_EMBED_MAX_TABLES 32
+typedef struct q4_embed_table {
+  const uint32_t* packed; /* [rows][dim/8] */
+  const uint16_t* scales; /* [rows][dim/32] */
+  const uint16_t* biases; /* [rows][dim/32] */
+  int64_t rows;
+} q4_embed_table;
+
+q4_status q4_embed_sum(const int32_t* tokens, int64_t frames, const q4_embed_table* tables, int32_t num_tables,
+                       int64_t dim, void* y, q4_out_dtype y_dtype, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Chain executor: an ordered list of GEMV stages run by ONE persistent launch.
  *

@@ -314,3 +314,29 @@ def test_chain_run_noalloc_validation():
     assert lib.q4_chain_run_rows_noalloc(_p(A16), 1, 2, None, None) == q4.Q4_ERR_SHAPE
     assert lib.q4_chain_run_rows_noalloc(_p(A16 + 16), 1, 0, None, None) == q4.Q4_ERR_ALIGN
     assert lib.q4_chain_run_rows_noalloc(_p(A16), 1, 0, _p(A16 + 2), None) == q4.Q4_ERR_ALIGN
+
+
+def test_embed_sum_validation():
+    """Host checks of the gather-sum (no HIP call: each call fails first)."""
+    lib = q4.load()
+
+    def tabs(n=2, rows=8, packed=A16, scales=A16):
+        return (q4._EmbedTable * n)(*[q4._EmbedTable(packed, scales, A16, rows) for _ in range(n)])
+
+    t = tabs()
+    call = lambda tok=A16, frames=1, tb=t, n=2, dim=64, y=Y16, dt=0: lib.q4_embed_sum(
+        _p(tok), frames, ctypes.byref(tb) if tb is not None else None, n, dim, _p(y), dt, None)
+    assert call(tok=0) == q4.Q4_ERR_NULL
+    assert call(y=0) == q4.Q4_ERR_NULL
+    assert call(tb=tabs(packed=0)) == q4.Q4_ERR_NULL
+    assert call(n=0) == q4.Q4_ERR_SHAPE
+    assert call(n=33, tb=tabs(33)) == q4.Q4_ERR_SHAPE
+    assert call(dim=48) == q4.Q4_ERR_SHAPE
+    assert call(frames=-1) == q4.Q4_ERR_SHAPE
+    assert call(dt=2) == q4.Q4_ERR_SHAPE
+    assert call(tb=tabs(rows=0)) == q4.Q4_ERR_SHAPE
+    assert call(tok=A16 + 2) == q4.Q4_ERR_ALIGN
+    assert call(y=Y16 + 8) == q4.Q4_ERR_ALIGN
+    assert call(tb=tabs(packed=A16 + 4)) == q4.Q4_ERR_ALIGN
+    assert call(tb=tabs(rows=1 << 30), dim=4096) == q4.Q4_ERR_UNSUPPORTED  # past a 32-bit buffer range
+    assert call(frames=0) == q4.Q4_OK

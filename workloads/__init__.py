@@ -64,6 +64,15 @@ DEPFORMER_LINEARS: Tuple[Tuple[str, int, int, int], ...] = (
     ("down", DEP_DIM, DEP_FFN, STAGE_FFN_MID),
 )
 
+# Token streams of one frame (blog translation, pipeline figure: 17 streams,
+# text + 8 user audio + 8 assistant audio codebooks, summed into the step's
+# input). Table sizes: the text table follows the 32k SentencePiece tokenizer
+# of the ONNX bundle's file list; the pages give no audio codebook size, and
+# 2048 entries (an 11-bit code) is the reading taken.
+TEXT_VOCAB = 32000
+AUDIO_CODEBOOK = 2048
+TOKEN_STREAMS = 17
+
 # Workload ids (1-based, in the order the benchmark configurations are listed).
 CFG_GEMV, CFG_LAYER, CFG_STEP, CFG_DEPFORMER, CFG_SMALL_GEMM = 1, 2, 3, 4, 5
 
