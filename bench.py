@@ -328,7 +328,8 @@ def main(argv=None) -> int:
                          "8 distinct layers in turn (1.03 GB, past the last-level cache); embed: the "
                          "packed-embedding gather and 17-stream sum of --m frames (text table 32000 x 4096, "
                          "16 audio tables 2048 x 4096), 64 token sets in turn")
-    ap.add_argument("--m", type=int, default=4, help="rows of X for --workload gemm")
+    ap.add_argument("--m", type=int, default=4, help="rows of X for --workload gemm (1..64; 17..64: prefill), "
+                                                     "frames for --workload embed")
     ap.add_argument("--dependent", action="store_true",
                     help="step: every stage's activation is the previous stage's first output (q -> o "
                          "-> gate/up -> down -> next q): each stage stores its outputs before the "
@@ -676,8 +677,8 @@ def bench_other(args, dev) -> int:
                   "stages_per_frame": len(chain.stages)}
         unit_name = "frame"
     else:
-        if not 1 <= args.m <= 16:
-            print("--m must be in 1..16", file=sys.stderr)
+        if not 1 <= args.m <= 64:
+            print("--m must be in 1..64", file=sys.stderr)
             return 2
         from bit_group_quantized_amd.step import Chain
 

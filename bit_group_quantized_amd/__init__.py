@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(_HERE, "libq4.so")
 Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_UNSUPPORTED, Q4_ERR_HIP = range(6)
 Q4_OUT_BF16, Q4_OUT_F32 = 0, 1
 GROUP = 32
-MAX_M = 16
+MAX_M = 64  # Q4_MAX_M
 MAX_K = 16384  # Q4_MAX_K
 
 _lib = None
@@ -233,7 +233,7 @@ def q4_gemv(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, biases:
 
 def q4_gemm_small(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor,
                   out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Y [m, n] = X [m, k] . W_hat^T for 1 <= m <= 16."""
+    """Y [m, n] = X [m, k] . W_hat^T for 1 <= m <= 64 (17..64: prefill)."""
     n, k = _check_matrix(packed, scales, biases)
     _need(x, "x", torch.bfloat16)
     if x.dim() != 2 or x.shape[1] != k:

@@ -169,11 +169,24 @@ void launch_gemm_gs(int waves, bool f32, const uint16_t* x, int m, const uint32_
 }
 
 // Small GEMM: up to 4 activation rows share one pass of the GEMV kernel
-// (each loaded group dequantized once, dotted with every row); more rows go
-// to the MFMA kernel, one 16-row tile per group.
+// (each loaded group dequantized once, dotted with every row); 5..16 rows go
+// to the MFMA kernel, one 16-row tile per group. More rows (prefill, up to
+// 64) run the MFMA kernel once per 16-row tile of x: the first pass streams
+// the matrix from HBM, and the later ones find it in the 256 MB last-level
+// cache (a matrix of the model is at most 29 MB).
 q4_status run_gemm_small(const uint16_t* x, int64_t m, const uint32_t* packed,
                          const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
                          void* y, q4_out_dtype dt, hipStream_t st) {
+  if (m > 16) {
+    const int64_t ybytes = dt == Q4_OUT_F32 ? 4 : 2;
+    for (int64_t r0 = 0; r0 < m; r0 += 16) {
+      const int64_t mt = m - r0 < 16 ? m - r0 : 16;
+      const q4_status s = run_gemm_small(x + r0 * k, mt, packed, scales, biases, n, k,
+                                         static_cast<unsigned char*>(y) + r0 * n * ybytes, dt, st);
+      if (s != Q4_OK) return s;
+    }
+    return Q4_OK;
+  }
   switch (m) {
     case 1: return run_gemv_mv<1>(x, packed, scales, biases, n, k, y, dt, st);
     case 2: return run_gemv_mv<2>(x, packed, scales, biases, n, k, y, dt, st);

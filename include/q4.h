@@ -58,7 +58,7 @@ extern "C" {
 #endif
 
 #define Q4_GROUP 32
-#define Q4_MAX_M 16
+#define Q4_MAX_M 64
 #define Q4_MAX_K 16384
 
 typedef enum q4_status {
@@ -116,10 +116,13 @@ q4_status q4_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* sca
                   const uint16_t* biases, int64_t n, int64_t k, void* y, q4_out_dtype y_dtype,
                   void* stream);
 
-/* Small quantized GEMM for M concurrent activation rows (1 <= m <= 16), all
- * sharing one pass over the weights ("A smaller voice model", Concurrency
- * section: several conversations served together read one copy of the
- * weights, so their frames cost little more than one):
+/* Small quantized GEMM for M activation rows (1 <= m <= Q4_MAX_M = 64), all
+ * sharing one pass over the weights: concurrent conversations ("A smaller
+ * voice model", Concurrency section: several conversations served together
+ * read one copy of the weights, so their frames cost little more than one)
+ * and, for 17..64 rows, prefill ("NVIDIA PersonaPlex 7B on Apple Silicon",
+ * optimisation list: the 50-frame voice prompt runs as one batched forward
+ * pass instead of single steps):
  *   y[i][r] = sum_k w_hat[r][k] * x[i][k]
  *   x : bf16 [m][k] row-major, y : [m][n] row-major of y_dtype.
  * m == 1 is the same computation as q4_gemv. Supports k <= Q4_MAX_K. */

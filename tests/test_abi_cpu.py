@@ -72,7 +72,7 @@ def test_gemv_validation(case, want):
     assert st == want
 
 
-@pytest.mark.parametrize("m,want", [(0, q4.Q4_ERR_SHAPE), (17, q4.Q4_ERR_SHAPE), (-3, q4.Q4_ERR_SHAPE)])
+@pytest.mark.parametrize("m,want", [(0, q4.Q4_ERR_SHAPE), (65, q4.Q4_ERR_SHAPE), (-3, q4.Q4_ERR_SHAPE)])
 def test_gemm_small_rejects_m(m, want):
     st = q4.load().q4_gemm_small(_p(A16), m, _p(A16), _p(A16), _p(A16), 16, 64, _p(A16), 0, None)
     assert st == want

@@ -176,6 +176,38 @@ def test_products_on_edge_weights(m, out_dtype):
     _check(y, ref[0] if m == 1 else ref, out_dtype)
 
 
+# Prefill (17..64 rows): the MFMA kernel once per 16-row tile of x, ragged
+# last tile included.
+@pytest.mark.parametrize("m", [17, 24, 32, 33, 50, 64])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("n,k", [(37, 96), (300, 1056), (4096, 4096), (11264, 4096), (4096, 11264), (100, 16384)])
+def test_prefill_matches_oracle(n, k, m, out_dtype):
+    P, S, B = oracle.quantize(_w(n, k, seed=n + 5 * k))
+    x = _x(m, k, seed=m + 7 * k)
+    y = q4.q4_gemm_small(to_gpu_bf16_bits(x), *upload_quantized(P, S, B), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    _check(y, oracle.matmul(x, P, S, B, k), out_dtype)
+
+
+def test_prefill_rows_equal_single_rows():
+    """Row i of a 50-row prefill agrees with the GEMV of row i; the one-hot
+    input in the last row selects a column exactly."""
+    n, k, m = 4096, 4096, 50
+    P, S, B = oracle.quantize(_w(n, k, seed=41))
+    _, w_hat = oracle.unpack(P, S, B, k)
+    gP, gS, gB = upload_quantized(P, S, B)
+    x = _x(m, k, seed=42)
+    x[m - 1] = 0
+    x[m - 1, 777] = 0x3F80
+    Y = q4.q4_gemm_small(to_gpu_bf16_bits(x), gP, gS, gB, out_dtype=torch.float32)
+    for i in (0, 31, 32, 48):
+        y = q4.q4_gemv(to_gpu_bf16_bits(x[i]), gP, gS, gB, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert oracle.floored_rel_err(out_np(Y[i]), out_np(y)) <= 2 * TOL_F32
+    torch.cuda.synchronize()
+    assert np.array_equal(Y[m - 1].cpu().numpy(), w_hat[:, 777])
+
+
 @pytest.mark.parametrize("m", [1, 2, 16])
 def test_one_hot_input_gives_exact_dequantized_column(m):
     """x = e_j in one activation row: y = w_hat[:, j] exactly in fp32 (pins the
