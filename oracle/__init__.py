@@ -18,6 +18,8 @@ pages it follows in the C source. Summary of what is computed:
 * ``matmul(x, ...)``: ``y = x . W_hat^T`` summed in float64 (the blog
   translation's MultiLinear figure: quantized product with transpose).
 * ``multilinear_step``: the same product on rows ``[s*out, (s+1)*out)``.
+* ``rope`` / ``attn_decode``: the rotary embedding at a position (rounded to
+  bf16) and one query's attention per head over the KV cache (float64).
 * ``embed_sum``: per frame, the sum over token streams of the dequantized
   embedding row each token selects (the blog translation's pipeline figure:
   17 streams summed into the step's input; embeddings stay packed).
@@ -69,10 +71,12 @@ def _load():
     lib.oracle_multilinear_step.argtypes = [P, I, P, P, P, I, I, I, I, P]
     lib.oracle_bf16_round.argtypes = [P, I, P]
     lib.oracle_embed_sum.argtypes = [P, I, I, P, P, P, P, I, P]
+    lib.oracle_rope.argtypes = [P, I, I, I, ctypes.c_double, P]
+    lib.oracle_attn_decode.argtypes = [P, P, P, I, I, I, I, P]
     lib.oracle_threads.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     for f in ("oracle_quantize", "oracle_unpack", "oracle_matmul", "oracle_multilinear_step",
-              "oracle_bf16_round", "oracle_embed_sum"):
+              "oracle_bf16_round", "oracle_embed_sum", "oracle_rope", "oracle_attn_decode"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -204,6 +208,31 @@ def embed_sum(tokens: np.ndarray, tables, dim: int) -> np.ndarray:
                                     ctypes.cast(sp, ctypes.c_void_p), ctypes.cast(bp, ctypes.c_void_p), _ptr(rows),
                                     dim, _ptr(y)), "embed_sum")
     return y
+
+
+def rope(x_bits: np.ndarray, pos: int, theta: float = 10000.0) -> np.ndarray:
+    """Rotary embedding of bf16 x [heads, D] at position pos, rounded to bf16
+    (pairs (2i, 2i+1) turned by pos * theta^(-2i/D))."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    heads, d = x_bits.shape
+    out = np.empty_like(x_bits)
+    _check(_load().oracle_rope(_ptr(x_bits), heads, d, int(pos), float(theta), _ptr(out)), "rope")
+    return out
+
+
+def attn_decode(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, pos: int) -> np.ndarray:
+    """Single-query attention per head over cache positions 0..pos, in float64.
+    q: bf16 [heads, D] (rotated); k, v: bf16 [heads, cap, D]."""
+    q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    k_bits = np.ascontiguousarray(k_bits, dtype=np.uint16)
+    v_bits = np.ascontiguousarray(v_bits, dtype=np.uint16)
+    heads, cap, d = k_bits.shape
+    if q_bits.shape != (heads, d) or v_bits.shape != k_bits.shape:
+        raise ValueError("shape mismatch")
+    out = np.empty((heads, d), dtype=np.float64)
+    _check(_load().oracle_attn_decode(_ptr(q_bits), _ptr(k_bits), _ptr(v_bits), heads, d, cap, int(pos), _ptr(out)),
+           "attn_decode")
+    return out
 
 
 def output_bits_bf16(y: np.ndarray) -> np.ndarray:

@@ -45,6 +45,7 @@
 #include <string.h>
 #include <math.h>
 #include <stddef.h>
+#include <stdlib.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -251,6 +252,67 @@ int oracle_embed_sum(const int32_t* tokens, int64_t frames, int64_t streams, con
       y[f * dim + d] = acc;
     }
   }
+  return ORACLE_OK;
+}
+
+/* --- single-query attention over the KV cache (one decoding step) --- */
+
+/* Rotary position embedding at position pos ("NVIDIA PersonaPlex 7B on Apple
+ * Silicon", optimisation list: the RoPE offset is passed to the step as an
+ * input; the same page reuses RoPE among the model's parts). The pages do not
+ * give the form: the reading is the original rotary embedding, which turns
+ * each pair (x[2i], x[2i+1]) of a head by the angle pos * theta^(-2i/D).
+ * x: bf16 [heads][D] (D even); out: the rotated values rounded to bf16. */
+int oracle_rope(const uint16_t* x, int64_t heads, int64_t d, int64_t pos, double theta, uint16_t* out) {
+  if (!x || !out || heads < 0 || d <= 0 || d % 2 != 0 || pos < 0 || !(theta > 0.0)) return ORACLE_ERR_ARG;
+  for (int64_t h = 0; h < heads; ++h) {
+    for (int64_t i = 0; i < d / 2; ++i) {
+      const double angle = (double)pos * pow(theta, -(double)(2 * i) / (double)d);
+      const double c = cos(angle), sn = sin(angle);
+      const double x0 = (double)bf16_value(x[h * d + 2 * i]);
+      const double x1 = (double)bf16_value(x[h * d + 2 * i + 1]);
+      /* the rotated pair in double, rounded to fp32, then to bf16 */
+      out[h * d + 2 * i] = bf16_round_nearest_even((float)(x0 * c - x1 * sn));
+      out[h * d + 2 * i + 1] = bf16_round_nearest_even((float)(x0 * sn + x1 * c));
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* Attention of one query per head over positions 0..pos of the cache (the
+ * ONNX bundle's README, How to use: the step takes and returns the K and V
+ * caches [layers][1][32 heads][T][128] explicitly). For head h:
+ *   s_t = (q_h . k_h[t]) / sqrt(D) for t = 0..pos,
+ *   out_h = sum_t softmax(s)_t v_h[t],
+ * in double. q: bf16 [heads][D] (already rotated); k, v: bf16
+ * [heads][cap][D]; out: double [heads][D]. */
+int oracle_attn_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t heads, int64_t d,
+                       int64_t cap, int64_t pos, double* out) {
+  if (!q || !k || !v || !out || heads < 0 || d <= 0 || cap <= 0 || pos < 0 || pos >= cap) return ORACLE_ERR_ARG;
+  const double scale = 1.0 / sqrt((double)d);
+  double* s = (double*)malloc(sizeof(double) * (size_t)(pos + 1));
+  if (!s) return ORACLE_ERR_ARG;
+  for (int64_t h = 0; h < heads; ++h) {
+    double mx = -HUGE_VAL;
+    for (int64_t t = 0; t <= pos; ++t) {
+      double dot = 0.0;
+      for (int64_t i = 0; i < d; ++i)
+        dot += (double)bf16_value(q[h * d + i]) * (double)bf16_value(k[(h * cap + t) * d + i]);
+      s[t] = dot * scale;
+      if (s[t] > mx) mx = s[t];
+    }
+    double z = 0.0;
+    for (int64_t t = 0; t <= pos; ++t) {
+      s[t] = exp(s[t] - mx);
+      z += s[t];
+    }
+    for (int64_t i = 0; i < d; ++i) {
+      double acc = 0.0;
+      for (int64_t t = 0; t <= pos; ++t) acc += s[t] * (double)bf16_value(v[(h * cap + t) * d + i]);
+      out[h * d + i] = acc / z;
+    }
+  }
+  free(s);
   return ORACLE_OK;
 }
 

@@ -511,3 +511,88 @@ def test_embed_tokens_outside_a_table_add_nothing():
     assert np.array_equal(y[2], w0[4].astype(np.float64))      # token 9 is past table 1's 9 rows
     assert not y[3].any()
     assert np.array_equal(y[4], w0[2].astype(np.float64) + w1[8].astype(np.float64))
+
+
+# ---------------------------------------------------------------- rotary embedding + decode attention
+# (blog translation, optimisation list: the RoPE offset is a step input; ONNX
+# README, How to use: the step carries K and V caches [layers][1][32][T][128])
+
+def _bits(vals):
+    import torch
+    return torch.tensor(vals, dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_rope_position_zero_is_identity():
+    x = workloads.activations(0, 7, 0, 0, 4, 64)
+    assert np.array_equal(oracle.rope(x, 0), x)
+
+
+def test_rope_hand_values():
+    """One head of width 4, theta 10000: pair 0 turns by pos, pair 1 by
+    pos / 100 (10000^(-2/4)); the unit vectors (1, 0) become (cos a, sin a).
+    Values of cos and sin at 1, 0.01, 3, 0.03 written out."""
+    x = _bits([[1.0, 0.0, 1.0, 0.0]])
+    want1 = _bits([[0.5403023058681398, 0.8414709848078965, 0.9999500004166653, 0.009999833334166664]])
+    want3 = _bits([[-0.9899924966004454, 0.1411200080598672, 0.9995500337489875, 0.02999550020249566]])
+    assert np.array_equal(oracle.rope(x, 1), want1)
+    assert np.array_equal(oracle.rope(x, 3), want3)
+    # the second element of a pair: (0, 1) becomes (-sin a, cos a)
+    y = _bits([[0.0, 1.0, 0.0, 1.0]])
+    assert np.array_equal(oracle.rope(y, 1), _bits([[-0.8414709848078965, 0.5403023058681398,
+                                                    -0.009999833334166664, 0.9999500004166653]]))
+
+
+def test_rope_keeps_pair_norms_and_relative_positions():
+    x = workloads.activations(0, 7, 0, 1, 8, 128)
+    xv = oracle.bf16_value(x).astype(np.float64)
+    for pos in (1, 17, 4095):
+        r = oracle.bf16_value(oracle.rope(x, pos)).astype(np.float64)
+        n0 = xv[:, 0::2] ** 2 + xv[:, 1::2] ** 2
+        n1 = r[:, 0::2] ** 2 + r[:, 1::2] ** 2
+        assert np.all(np.abs(n1 - n0) <= 2 ** -7 * n0 + 1e-30)
+    # q . k after rotation depends on the distance of the positions only
+    q = workloads.activations(0, 7, 0, 2, 1, 128)
+    k = workloads.activations(0, 7, 0, 3, 1, 128)
+    dots = []
+    for shift in (0, 5, 100):
+        qr = oracle.bf16_value(oracle.rope(q, 40 + shift)).astype(np.float64)
+        kr = oracle.bf16_value(oracle.rope(k, 10 + shift)).astype(np.float64)
+        dots.append(float((qr @ kr.T)[0, 0]))
+    mag = float((np.abs(oracle.bf16_value(q)).astype(np.float64) @ np.abs(oracle.bf16_value(k)).astype(np.float64).T)[0, 0])
+    assert max(dots) - min(dots) <= 2 ** -6 * mag
+
+
+def test_attention_single_position_returns_its_value():
+    heads, d, cap = 3, 64, 8
+    q = workloads.activations(0, 7, 1, 0, heads, d)
+    k = workloads.activations(0, 7, 1, 1, heads * cap, d).reshape(heads, cap, d)
+    v = workloads.activations(0, 7, 1, 2, heads * cap, d).reshape(heads, cap, d)
+    out = oracle.attn_decode(q, k, v, 0)
+    assert np.array_equal(out, oracle.bf16_value(v[:, 0, :]).astype(np.float64))
+
+
+def test_attention_equal_keys_average_the_values():
+    heads, d, cap, pos = 2, 32, 16, 9
+    q = workloads.activations(0, 7, 2, 0, heads, d)
+    k = np.repeat(workloads.activations(0, 7, 2, 1, heads, d)[:, None, :], cap, axis=1)
+    v = workloads.activations(0, 7, 2, 2, heads * cap, d).reshape(heads, cap, d)
+    out = oracle.attn_decode(q, k, v, pos)
+    mean = oracle.bf16_value(v[:, :pos + 1, :]).astype(np.float64).sum(axis=1) / (pos + 1)
+    assert np.allclose(out, mean, rtol=1e-13, atol=1e-15)
+
+
+def test_attention_two_positions_closed_form():
+    """q = 2 e0, k0 = 0, k1 = 4 e0, D = 64: scores 0 and 2 * 4 / 8 = 1, so
+    out = (v0 + e v1) / (1 + e); positions past pos are ignored."""
+    import math
+    d, cap = 64, 5
+    q = np.zeros((1, d), np.uint16)
+    q[0, 0] = _bits([2.0])[0]
+    k = np.zeros((1, cap, d), np.uint16)
+    k[0, 1, 0] = _bits([4.0])[0]
+    k[0, 2:, 0] = _bits([100.0])[0]   # past pos: must not count
+    v = workloads.activations(0, 7, 3, 0, cap, d).reshape(1, cap, d)
+    out = oracle.attn_decode(q, k, v, 1)
+    vv = oracle.bf16_value(v).astype(np.float64)
+    want = (vv[0, 0] + math.e * vv[0, 1]) / (1.0 + math.e)
+    assert np.allclose(out[0], want, rtol=1e-14, atol=1e-16)
