@@ -318,7 +318,8 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--mode", choices=("chain", "launches"), default="chain")
-    ap.add_argument("--workload", choices=("step", "depformer", "gemm", "gemv", "layer", "embed"), default="step",
+    ap.add_argument("--workload", choices=("step", "depformer", "gemm", "gemv", "layer", "embed", "attn"),
+                    default="step",
                     help="step: the 32-layer temporal step at M=1 (the headline); depformer: one "
                          "Depformer frame (16 codebook steps x 6 layers, M=1); gemm: the temporal "
                          "step's 224 matrices against X [M, k] (--m rows; one persistent chain launch for "
@@ -327,7 +328,10 @@ def main(argv=None) -> int:
                          "the 256 MB last-level cache); layer: one temporal layer's 7 GEMVs (4 stages), "
                          "8 distinct layers in turn (1.03 GB, past the last-level cache); embed: the "
                          "packed-embedding gather and 17-stream sum of --m frames (text table 32000 x 4096, "
-                         "16 audio tables 2048 x 4096), 64 token sets in turn")
+                         "16 audio tables 2048 x 4096), 64 token sets in turn; attn: one decoding step's "
+                         "attention for the 32 layers (32 heads x 128, --ctx cached positions, bf16 caches "
+                         "of every layer in turn)")
+    ap.add_argument("--ctx", type=int, default=4096, help="cached positions for --workload attn")
     ap.add_argument("--m", type=int, default=4, help="rows of X for --workload gemm (1..64; 17..64: prefill), "
                                                      "frames for --workload embed")
     ap.add_argument("--dependent", action="store_true",
@@ -604,6 +608,44 @@ def bench_other(args, dev) -> int:
                          "frac": round(gbs / HBM_PEAK_GBS, 6), "traffic": None, "kernel": "embed_sum_kernel",
                          "bytes_per_launch": gathered,
                          "timing": "HIP events on the launch stream around graph replays of 64 calls"},
+        }
+        print(json.dumps(result), flush=True)
+        return 0
+    if args.workload == "attn":
+        import torch as _t
+
+        heads, d, npos, layers = 32, 128, max(1, args.ctx), workloads.TEMPORAL_LAYERS
+        cap, pos = npos, npos - 1
+        g = _t.Generator(device=dev)
+        g.manual_seed(args.seed)
+        ks = [(_t.randn((heads, cap, d), generator=g, device=dev)).to(_t.bfloat16) for _ in range(layers)]
+        vs = [(_t.randn((heads, cap, d), generator=g, device=dev)).to(_t.bfloat16) for _ in range(layers)]
+        qs = [(_t.randn((3, heads, d), generator=g, device=dev)).to(_t.bfloat16) for _ in range(layers)]
+        outs = [_t.empty((heads, d), dtype=_t.bfloat16, device=dev) for _ in range(layers)]
+        ws = _t.empty(q4.q4_attn_workspace_bytes(heads, d), dtype=_t.uint8, device=dev)
+
+        def calls():
+            for li in range(layers):
+                q4.q4_attn_decode(qs[li][0], qs[li][1], qs[li][2], ks[li], vs[li], pos, out=outs[li], workspace=ws)
+
+        gr = graph_of(calls)
+        ms, per = time_replays(gr.replay, args.steps, args.warmup)
+        kv = 2 * heads * npos * d * 2  # K and V bytes read per layer
+        us = ms * 1e3 / layers
+        gbs = kv / (us * 1e-6) / 1e9
+        result = {
+            "metric": "KV-cache GB/s (% HBM peak) + us per layer of decode attention, M=1",
+            "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "us_per_layer": round(us, 2), "us_per_step": round(ms * 1e3, 1),
+            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"attn_decode_{npos}_positions", "layers": layers, "heads": heads, "head_dim": d,
+                       "cached_positions": npos, "kv_bytes_per_layer": kv,
+                       "executor": f"graph of {layers} x 3 launches (rope + append, partial, combine)"},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "attn_partial_kernel",
+                         "bytes_per_launch": kv,
+                         "timing": "HIP events on the launch stream around graph replays; per layer = step / 32"},
         }
         print(json.dumps(result), flush=True)
         return 0

@@ -38,6 +38,7 @@ _EXPORTS = (
     "q4_layout_version", "q4_status_str", "q4_last_hip_error", "q4_pack", "q4_unpack", "q4_gemv",
     "q4_gemm_small", "q4_multilinear_step", "q4_chain_plan_bytes", "q4_chain_encode", "q4_chain_run",
     "q4_chain_encode_rows", "q4_chain_run_rows", "q4_chain_run_rows_noalloc", "q4_embed_sum",
+    "q4_attn_workspace_bytes", "q4_attn_decode",
 )
 EMBED_MAX_TABLES = 32  # Q4_EMBED_MAX_TABLES
 CHAIN_WORKSPACE_BYTES = 131328
@@ -94,8 +95,12 @@ def load():
     lib.q4_chain_run_rows.argtypes = [P, ctypes.c_int32, V, P, P]
     lib.q4_chain_run_rows_noalloc.argtypes = [P, ctypes.c_int32, V, P, P]
     lib.q4_embed_sum.argtypes = [P, I, P, ctypes.c_int32, I, P, V, P]
+    lib.q4_attn_workspace_bytes.argtypes = [I, I]
+    lib.q4_attn_workspace_bytes.restype = ctypes.c_int64
+    lib.q4_attn_decode.argtypes = [P, P, P, P, P, I, I, I, I, ctypes.c_double, P, V, P, I, P]
     for f in ("q4_pack", "q4_unpack", "q4_gemv", "q4_gemm_small", "q4_multilinear_step", "q4_chain_encode",
-              "q4_chain_run", "q4_chain_encode_rows", "q4_chain_run_rows", "q4_chain_run_rows_noalloc", "q4_embed_sum"):
+              "q4_chain_run", "q4_chain_encode_rows", "q4_chain_run_rows", "q4_chain_run_rows_noalloc", "q4_embed_sum",
+              "q4_attn_decode"):
         getattr(lib, f).restype = V
     _lib = lib
     return lib
@@ -308,6 +313,44 @@ def q4_embed_sum(tokens: torch.Tensor, tables, out_dtype: torch.dtype = torch.bf
     arr = (_EmbedTable * streams)(*descs)
     _check("q4_embed_sum", load().q4_embed_sum(_ptr(tokens), frames, ctypes.byref(arr), streams, dim, _ptr(out), code,
                                                _ptr_stream(tokens)))
+    return out
+
+
+def q4_attn_workspace_bytes(heads: int, head_dim: int) -> int:
+    return int(load().q4_attn_workspace_bytes(heads, head_dim))
+
+
+def q4_attn_decode(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+                   v_cache: torch.Tensor, pos: int, rope_theta: float = 10000.0,
+                   out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One layer's decode attention: RoPE on q and k_new at pos, k and v written
+    to the caches (bf16 [heads, cap, D]) at pos, then softmax(q.k/sqrt(D)).v
+    per head over positions 0..pos -> out [heads, D]."""
+    for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, nm, torch.bfloat16)
+    if k_cache.dim() != 3 or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must be [heads, cap, D]")
+    heads, cap, d = k_cache.shape
+    for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
+        if t.numel() != heads * d:
+            raise ValueError(f"{nm} must hold heads*D elements")
+    code = _out_code(out_dtype if out is None else out.dtype)
+    if out is None:
+        out = torch.empty((heads, d), dtype=out_dtype, device=q.device)
+    _need(out, "out", out.dtype)
+    if out.numel() != heads * d:
+        raise ValueError("out must hold heads*D elements")
+    need = q4_attn_workspace_bytes(heads, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must hold {need} bytes")
+    _same_device(q, k_new, v_new, k_cache, v_cache, out, workspace)
+    _check("q4_attn_decode", load().q4_attn_decode(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                                   heads, d, cap, int(pos), float(rope_theta), _ptr(out), code,
+                                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                                   _ptr_stream(q)))
     return out
 
 

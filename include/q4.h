@@ -168,6 +168,33 @@ typedef struct q4_embed_table {
 q4_status q4_embed_sum(const int32_t* tokens, int64_t frames, const q4_embed_table* tables, int32_t num_tables,
                        int64_t dim, void* y, q4_out_dtype y_dtype, void* stream);
 
+/* Decode attention for one layer: the step's one query per head attends over
+ * the layer's KV cache. The step's q, k and v (bf16 [heads][head_dim]) come
+ * from the layer's projections; q and k are turned by the rotary embedding
+ * at position pos (the RoPE offset is a step input: "NVIDIA PersonaPlex 7B on
+ * Apple Silicon", optimisation list), k and v are written to the caches at
+ * pos (the ONNX bundle's README, How to use: the step carries the K and V
+ * caches [layers][1][32][T][128] explicitly), then for each head
+ *   out_h = softmax_t(q_h . k_h[t] / sqrt(head_dim)) . v_h[t],  t = 0..pos.
+ * The rotary embedding turns each pair (x[2i], x[2i+1]) of a head by the
+ * angle pos * rope_theta^(-2i/head_dim), computed in fp64 and rounded to fp32
+ * and then to bf16 (the rotated q and k are bf16, like every activation).
+ *   q, k_new, v_new : DEVICE bf16 [heads][head_dim] (q 16-byte aligned)
+ *   k_cache, v_cache: DEVICE bf16 [heads][cap][head_dim], 16-byte aligned;
+ *                     row pos is written, rows 0..pos-1 are read
+ *   out             : DEVICE [heads][head_dim] of out_dtype
+ *   workspace       : DEVICE, 256-byte aligned, >= q4_attn_workspace_bytes()
+ *                     bytes, owned by the caller (partial results; no state
+ *                     is kept between calls; calls sharing one workspace must
+ *                     not overlap in time)
+ * head_dim must be 64 or 128 (Q4_ERR_UNSUPPORTED otherwise); 0 <= pos < cap.
+ * Three launches on `stream`; no allocation. */
+int64_t q4_attn_workspace_bytes(int64_t heads, int64_t head_dim);
+q4_status q4_attn_decode(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_cache,
+                         uint16_t* v_cache, int64_t heads, int64_t head_dim, int64_t cap, int64_t pos,
+                         double rope_theta, void* out, q4_out_dtype out_dtype, void* workspace,
+                         int64_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Chain executor: an ordered list of GEMV stages run by ONE persistent launch.
  *

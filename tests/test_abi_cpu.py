@@ -340,3 +340,23 @@ def test_embed_sum_validation():
     assert call(tb=tabs(packed=A16 + 4)) == q4.Q4_ERR_ALIGN
     assert call(tb=tabs(rows=1 << 30), dim=4096) == q4.Q4_ERR_UNSUPPORTED  # past a 32-bit buffer range
     assert call(frames=0) == q4.Q4_OK
+
+
+def test_attn_decode_validation():
+    lib = q4.load()
+    ws = lib.q4_attn_workspace_bytes(32, 128)
+    assert ws > 0 and lib.q4_attn_workspace_bytes(0, 128) < 0
+    W = 0x1000000  # a 256-byte aligned fake workspace address
+    call = lambda q=A16, heads=32, d=128, cap=64, pos=3, theta=10000.0, out=Y16, dt=0, w=W, wb=ws: \
+        lib.q4_attn_decode(_p(q), _p(A16), _p(A16), _p(A16), _p(A16), heads, d, cap, pos, theta, _p(out), dt,
+                           _p(w), wb, None)
+    assert call(q=0) == q4.Q4_ERR_NULL
+    assert call(w=0) == q4.Q4_ERR_NULL
+    assert call(pos=64) == q4.Q4_ERR_SHAPE
+    assert call(pos=-1) == q4.Q4_ERR_SHAPE
+    assert call(theta=0.0) == q4.Q4_ERR_SHAPE
+    assert call(dt=3) == q4.Q4_ERR_SHAPE
+    assert call(wb=ws - 1) == q4.Q4_ERR_SHAPE
+    assert call(d=96) == q4.Q4_ERR_UNSUPPORTED
+    assert call(q=A16 + 2) == q4.Q4_ERR_ALIGN
+    assert call(w=W + 16) == q4.Q4_ERR_ALIGN
