@@ -20,6 +20,9 @@ pages it follows in the C source. Summary of what is computed:
 * ``multilinear_step``: the same product on rows ``[s*out, (s+1)*out)``.
 * ``rope`` / ``attn_decode``: the rotary embedding at a position (rounded to
   bf16) and one query's attention per head over the KV cache (float64).
+* ``rmsnorm`` / ``silu_mul``: the normalization before a layer's products and
+  the gated FFN's product (with a residual sum, the parts fused around the
+  products).
 * ``embed_sum``: per frame, the sum over token streams of the dequantized
   embedding row each token selects (the blog translation's pipeline figure:
   17 streams summed into the step's input; embeddings stay packed).
@@ -72,11 +75,14 @@ def _load():
     lib.oracle_bf16_round.argtypes = [P, I, P]
     lib.oracle_embed_sum.argtypes = [P, I, I, P, P, P, P, I, P]
     lib.oracle_rope.argtypes = [P, I, I, I, ctypes.c_double, P]
+    lib.oracle_rmsnorm.argtypes = [P, I, I, P, ctypes.c_double, P]
+    lib.oracle_silu_mul.argtypes = [P, P, I, P]
     lib.oracle_attn_decode.argtypes = [P, P, P, I, I, I, I, P]
     lib.oracle_threads.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     for f in ("oracle_quantize", "oracle_unpack", "oracle_matmul", "oracle_multilinear_step",
-              "oracle_bf16_round", "oracle_embed_sum", "oracle_rope", "oracle_attn_decode"):
+              "oracle_bf16_round", "oracle_embed_sum", "oracle_rope", "oracle_attn_decode",
+              "oracle_rmsnorm", "oracle_silu_mul"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -232,6 +238,33 @@ def attn_decode(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, pos:
     out = np.empty((heads, d), dtype=np.float64)
     _check(_load().oracle_attn_decode(_ptr(q_bits), _ptr(k_bits), _ptr(v_bits), heads, d, cap, int(pos), _ptr(out)),
            "attn_decode")
+    return out
+
+
+def rmsnorm(x_bits: np.ndarray, g_bits: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm of each row of bf16 x [m, k] with weight g [k], in double,
+    rounded to bf16: (x * 1/sqrt(mean(x^2) + eps)) * g."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    squeeze = x_bits.ndim == 1
+    if squeeze:
+        x_bits = x_bits[None, :]
+    m, k = x_bits.shape
+    g_bits = np.ascontiguousarray(g_bits, dtype=np.uint16)
+    if g_bits.shape != (k,):
+        raise ValueError("norm weight must be [k]")
+    out = np.empty_like(x_bits)
+    _check(_load().oracle_rmsnorm(_ptr(x_bits), m, k, _ptr(g_bits), float(eps), _ptr(out)), "rmsnorm")
+    return out[0] if squeeze else out
+
+
+def silu_mul(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
+    """silu(gate) * up elementwise in double (the gated FFN's product)."""
+    gate = np.ascontiguousarray(gate, dtype=np.float64)
+    up = np.ascontiguousarray(up, dtype=np.float64)
+    if gate.shape != up.shape:
+        raise ValueError("shape mismatch")
+    out = np.empty_like(gate)
+    _check(_load().oracle_silu_mul(_ptr(gate), _ptr(up), gate.size, _ptr(out)), "silu_mul")
     return out
 
 

@@ -316,6 +316,42 @@ int oracle_attn_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
   return ORACLE_OK;
 }
 
+/* --- the parts of a decoder layer around its linear products --- */
+
+/* RMSNorm of each activation row (the GeekNews summary's audio pipeline and
+ * the blog translation's reuse of RMSNorm among the model's parts): for row
+ * i of x (bf16 [m][k]) and the norm weight g (bf16 [k]),
+ *   inv = 1 / sqrt(sum_j x_j^2 / k + eps),  out_j = bf16((x_j * inv) * g_j)
+ * with every operation in double (x_j^2 is exact), then rounded to fp32 and
+ * to bf16: the normalized row is a bf16 activation like every other. */
+int oracle_rmsnorm(const uint16_t* x, int64_t m, int64_t k, const uint16_t* g, double eps, uint16_t* out) {
+  if (!x || !g || !out || m < 0 || k <= 0 || !(eps >= 0.0)) return ORACLE_ERR_ARG;
+  for (int64_t i = 0; i < m * k; ++i)
+    if (!isfinite(bf16_value(x[i]))) return ORACLE_ERR_NONFINITE;
+  for (int64_t i = 0; i < m; ++i) {
+    double ss = 0.0;
+    for (int64_t j = 0; j < k; ++j) {
+      const double v = (double)bf16_value(x[i * k + j]);
+      ss += v * v;
+    }
+    const double inv = 1.0 / sqrt(ss / (double)k + eps);
+    for (int64_t j = 0; j < k; ++j) {
+      const double v = ((double)bf16_value(x[i * k + j]) * inv) * (double)bf16_value(g[j]);
+      out[i * k + j] = bf16_round_nearest_even((float)v);
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* The gated FFN's product (SwiGLU, reused among the model's parts per the
+ * same pages): out_j = silu(gate_j) * up_j, silu(t) = t / (1 + exp(-t)), in
+ * double on the exact (double) products. */
+int oracle_silu_mul(const double* gate, const double* up, int64_t count, double* out) {
+  if (!gate || !up || !out || count < 0) return ORACLE_ERR_ARG;
+  for (int64_t i = 0; i < count; ++i) out[i] = gate[i] / (1.0 + exp(-gate[i])) * up[i];
+  return ORACLE_OK;
+}
+
 /* Threads the OpenMP runtime will use (1 when built without OpenMP). */
 int oracle_threads(void) {
 #ifdef _OPENMP

@@ -596,3 +596,48 @@ def test_attention_two_positions_closed_form():
     vv = oracle.bf16_value(v).astype(np.float64)
     want = (vv[0, 0] + math.e * vv[0, 1]) / (1.0 + math.e)
     assert np.allclose(out[0], want, rtol=1e-14, atol=1e-16)
+
+
+# ---------------------------------------------------------------- RMSNorm and the gated product
+# (GeekNews summary, audio pipeline; blog translation: RMSNorm and SwiGLU are
+# among the model's reused parts)
+
+def test_rmsnorm_of_a_constant_vector_is_the_weight():
+    """x = c for every element: mean(x^2) = c^2, so out = g c / sqrt(c^2 + eps),
+    which rounds to g for eps far below c^2."""
+    k = 256
+    g = workloads.activations(0, 11, 0, 0, 1, k)[0]
+    for c in (1.0, -3.0, 0.125):
+        x = np.full((1, k), _bits([c])[0], dtype=np.uint16)
+        out = oracle.rmsnorm(x, g, 1e-6)
+        want = g if c > 0 else _bits(-oracle.bf16_value(g))
+        assert np.array_equal(out[0], want)
+
+
+def test_rmsnorm_hand_values_and_scale_invariance():
+    # x = (3, 4), g = 1, eps = 0: rms = sqrt(12.5); 3/sqrt(12.5) and 4/sqrt(12.5)
+    x = _bits([[3.0, 4.0]])
+    g = _bits([1.0, 1.0])
+    assert np.array_equal(oracle.rmsnorm(x, g, 0.0), _bits([[0.848528137423857, 1.131370849898476]]))
+    # scaling x by a power of two changes nothing (every step scales exactly)
+    xr = workloads.activations(0, 11, 0, 1, 4, 1024)
+    gr = workloads.activations(0, 11, 0, 2, 1, 1024)[0]
+    xs = _bits(oracle.bf16_value(xr) * 8.0)
+    assert np.array_equal(oracle.rmsnorm(xs, gr, 0.0), oracle.rmsnorm(xr, gr, 0.0))
+    # with g = 1 the rows come out with unit mean square, up to bf16 rounding
+    ones = _bits(np.ones(1024))
+    y = oracle.bf16_value(oracle.rmsnorm(xr, ones, 0.0)).astype(np.float64)
+    assert np.all(np.abs((y * y).mean(axis=1) - 1.0) < 2 ** -7)
+
+
+def test_silu_mul_closed_forms():
+    import math
+    g = np.array([0.0, 1.0, -1.0, 20.0, -20.0, 2.5])
+    u = np.array([3.0, 2.0, 2.0, 1.0, 1.0, -4.0])
+    out = oracle.silu_mul(g, u)
+    assert out[0] == 0.0
+    assert out[1] == pytest.approx(2.0 * 0.7310585786300049, rel=1e-15)   # silu(1) = 1 / (1 + 1/e)
+    assert out[2] == pytest.approx(2.0 * -0.2689414213699951, rel=1e-15)  # silu(-1) = -1 / (1 + e)
+    assert out[3] == pytest.approx(20.0, rel=1e-8)                         # silu(t) -> t
+    assert abs(out[4]) < 1e-7                                              # silu(t) -> 0
+    assert out[5] == pytest.approx(-4.0 * 2.5 / (1.0 + math.exp(-2.5)), rel=1e-15)
