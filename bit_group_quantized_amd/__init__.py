@@ -38,7 +38,7 @@ _EXPORTS = (
     "q4_layout_version", "q4_status_str", "q4_last_hip_error", "q4_pack", "q4_unpack", "q4_gemv",
     "q4_gemm_small", "q4_multilinear_step", "q4_chain_plan_bytes", "q4_chain_encode", "q4_chain_run",
     "q4_chain_encode_rows", "q4_chain_run_rows", "q4_chain_run_rows_noalloc", "q4_embed_sum",
-    "q4_attn_workspace_bytes", "q4_attn_decode",
+    "q4_attn_workspace_bytes", "q4_attn_decode", "q4_chain_encode_ex",
 )
 EMBED_MAX_TABLES = 32  # Q4_EMBED_MAX_TABLES
 CHAIN_WORKSPACE_BYTES = 131328
@@ -52,6 +52,17 @@ class _ChainMatrix(ctypes.Structure):
 class _ChainStage(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("k", ctypes.c_int64), ("first_matrix", ctypes.c_int32),
                 ("num_matrices", ctypes.c_int32)]
+
+
+class _ChainMatrixEx(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("n", ctypes.c_int64), ("residual", ctypes.c_void_p)]
+
+
+class _ChainStageEx(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("k", ctypes.c_int64), ("first_matrix", ctypes.c_int32),
+                ("num_matrices", ctypes.c_int32), ("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_double),
+                ("gated", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class _EmbedTable(ctypes.Structure):
@@ -93,6 +104,7 @@ def load():
     lib.q4_chain_run.argtypes = [P, V, P, P]
     lib.q4_chain_encode_rows.argtypes = [P, ctypes.c_int32, P, ctypes.c_int32, ctypes.c_int32, V, P, I]
     lib.q4_chain_run_rows.argtypes = [P, ctypes.c_int32, V, P, P]
+    lib.q4_chain_encode_ex.argtypes = [P, ctypes.c_int32, P, ctypes.c_int32, ctypes.c_int32, V, P, I]
     lib.q4_chain_run_rows_noalloc.argtypes = [P, ctypes.c_int32, V, P, P]
     lib.q4_embed_sum.argtypes = [P, I, P, ctypes.c_int32, I, P, V, P]
     lib.q4_attn_workspace_bytes.argtypes = [I, I]
@@ -100,7 +112,7 @@ def load():
     lib.q4_attn_decode.argtypes = [P, P, P, P, P, I, I, I, I, ctypes.c_double, P, V, P, I, P]
     for f in ("q4_pack", "q4_unpack", "q4_gemv", "q4_gemm_small", "q4_multilinear_step", "q4_chain_encode",
               "q4_chain_run", "q4_chain_encode_rows", "q4_chain_run_rows", "q4_chain_run_rows_noalloc", "q4_embed_sum",
-              "q4_attn_decode"):
+              "q4_attn_decode", "q4_chain_encode_ex"):
         getattr(lib, f).restype = V
     _lib = lib
     return lib
@@ -372,10 +384,14 @@ def q4_chain_workspace_bytes() -> int:
 
 
 def q4_chain_build(stages, out_dtype: Optional[torch.dtype] = None) -> ChainPlan:
-    """Encode stages (objects with .x, .mats (each .packed/.scales/.biases) and
-    .outs) and upload the plan. All outputs must share one dtype. Every stage's
-    x is either a vector [k] (one activation row) or a matrix [m, k] with the
-    same m (1..4) in every stage; each output then holds m*n elements."""
+    """Encode stages and upload the plan. A stage has .x, .mats (each
+    .packed/.scales/.biases) and .outs, and optionally .norm (bf16 [k] RMSNorm
+    weight) with .eps, .gated (True: two matrices gate, up; the output
+    silu(gate) * up goes to outs[0], outs[1] may be None) and .residuals (one
+    tensor or None per matrix, added to its product). All outputs and
+    residuals share one dtype. Every stage's x is either a vector [k] (one
+    activation row) or a matrix [m, k] with the same m (1..4) in every stage;
+    each output then holds m*n elements."""
     lib = load()
     mats = []
     descs = []
@@ -394,19 +410,47 @@ def q4_chain_build(stages, out_dtype: Optional[torch.dtype] = None) -> ChainPlan
             raise ValueError("every stage must have the same number of activation rows")
         first = len(mats)
         k = st.x.shape[-1]
-        for m, y in zip(st.mats, st.outs):
+        gated = bool(getattr(st, "gated", False))
+        residuals = getattr(st, "residuals", None) or [None] * len(st.mats)
+        if len(residuals) != len(st.mats):
+            raise ValueError(f"stage {si}: one residual (or None) per matrix")
+        norm = getattr(st, "norm", None)
+        eps = float(getattr(st, "eps", 0.0))
+        if norm is not None:
+            _need(norm, "norm", torch.bfloat16)
+            if norm.numel() != k:
+                raise ValueError("norm weight must hold k elements")
+            _same_device(st.x, norm)
+            keep.append(norm)
+        for i, (m, y, r) in enumerate(zip(st.mats, st.outs, residuals)):
             n, km = _check_matrix(m.packed, m.scales, m.biases)
             if km != k:
                 raise ValueError("every matrix of a stage must have the stage's k")
-            if out_dtype is None:
-                out_dtype = y.dtype
-            _need(y, "y", out_dtype)
-            if y.numel() != rows * n:
-                raise ValueError("output must hold m*n elements")
-            _same_device(stages[0].x, st.x, m.packed, y)
-            mats.append(_ChainMatrix(m.packed.data_ptr(), m.scales.data_ptr(), m.biases.data_ptr(), y.data_ptr(), n))
-            keep += [m.packed, m.scales, m.biases, y]
-        descs.append(_ChainStage(st.x.data_ptr(), k, first, len(mats) - first))
+            written = not (gated and i == 1)
+            if written:
+                if out_dtype is None:
+                    out_dtype = y.dtype
+                _need(y, "y", out_dtype)
+                if y.numel() != rows * n:
+                    raise ValueError("output must hold m*n elements")
+                _same_device(stages[0].x, st.x, m.packed, y)
+                keep.append(y)
+            elif y is not None:
+                raise ValueError("a gated stage writes only its first matrix's output")
+            if r is not None:
+                if out_dtype is None:
+                    out_dtype = r.dtype
+                _need(r, "residual", out_dtype)
+                if r.numel() != rows * n:
+                    raise ValueError("residual must hold m*n elements")
+                _same_device(st.x, r)
+                keep.append(r)
+            mats.append(_ChainMatrixEx(m.packed.data_ptr(), m.scales.data_ptr(), m.biases.data_ptr(),
+                                       y.data_ptr() if written else None, n,
+                                       None if r is None else r.data_ptr()))
+            keep += [m.packed, m.scales, m.biases]
+        descs.append(_ChainStageEx(st.x.data_ptr(), k, first, len(mats) - first,
+                                   None if norm is None else norm.data_ptr(), eps, 1 if gated else 0, 0))
         keep.append(st.x)
     code = _out_code(out_dtype)
     ns, nm = len(descs), len(mats)
@@ -414,10 +458,10 @@ def q4_chain_build(stages, out_dtype: Optional[torch.dtype] = None) -> ChainPlan
     if nbytes <= 0:
         raise ValueError("empty chain")
     host = (ctypes.c_uint8 * nbytes)()
-    sarr = (_ChainStage * ns)(*descs)
-    marr = (_ChainMatrix * nm)(*mats)
-    _check("q4_chain_encode_rows", lib.q4_chain_encode_rows(ctypes.byref(sarr), ns, ctypes.byref(marr), nm, rows,
-                                                            code, ctypes.byref(host), nbytes))
+    sarr = (_ChainStageEx * ns)(*descs)
+    marr = (_ChainMatrixEx * nm)(*mats)
+    _check("q4_chain_encode_ex", lib.q4_chain_encode_ex(ctypes.byref(sarr), ns, ctypes.byref(marr), nm, rows,
+                                                        code, ctypes.byref(host), nbytes))
     dev = stages[0].x.device
     host_t = torch.frombuffer(bytearray(host), dtype=torch.uint8)
     plan = torch.empty(nbytes, dtype=torch.uint8, device=dev)

@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <mutex>
+#include <vector>
 
 #include "q4.h"
 #include "q4_kernels.h"
@@ -545,9 +546,9 @@ int64_t q4_chain_plan_bytes(int32_t num_stages, int32_t num_matrices) {
          static_cast<int64_t>(num_matrices) * sizeof(q4k::ChainMatDesc);
 }
 
-q4_status q4_chain_encode_rows(const q4_chain_stage* stages, int32_t num_stages,
-                               const q4_chain_matrix* matrices, int32_t num_matrices, int32_t m_rows,
-                               q4_out_dtype y_dtype, void* host_plan, int64_t plan_bytes) {
+q4_status q4_chain_encode_ex(const q4_chain_stage_ex* stages, int32_t num_stages,
+                             const q4_chain_matrix_ex* matrices, int32_t num_matrices, int32_t m_rows,
+                             q4_out_dtype y_dtype, void* host_plan, int64_t plan_bytes) {
   if (!stages || !matrices || !host_plan) return Q4_ERR_NULL;
   if (num_stages <= 0 || num_matrices <= 0) return Q4_ERR_SHAPE;
   if (m_rows < 1 || m_rows > q4k::kMaxRows) return Q4_ERR_SHAPE;
@@ -556,27 +557,47 @@ q4_status q4_chain_encode_rows(const q4_chain_stage* stages, int32_t num_stages,
   const int64_t need = q4_chain_plan_bytes(num_stages, num_matrices);
   if (plan_bytes < need) return Q4_ERR_SHAPE;
   const int64_t ybytes = y_dtype == Q4_OUT_F32 ? 4 : 2;
+  // (a gated stage's matrix 1 writes nothing)
+  auto writes = [&](const q4_chain_stage_ex& st, int32_t i) { return !(st.gated && i == 1); };
   int32_t next_matrix = 0;
   for (int32_t s = 0; s < num_stages; ++s) {
-    const q4_chain_stage& st = stages[s];
+    const q4_chain_stage_ex& st = stages[s];
     if (st.num_matrices <= 0 || st.first_matrix != next_matrix ||
         st.first_matrix + (int64_t)st.num_matrices > num_matrices)
       return Q4_ERR_SHAPE;
     next_matrix += st.num_matrices;
+    if (st.gated != 0 && st.gated != 1) return Q4_ERR_SHAPE;
+    if (st.gated && (st.num_matrices != 2 || matrices[st.first_matrix].n != matrices[st.first_matrix + 1].n))
+      return Q4_ERR_SHAPE;
+    if (st.norm_weight) {
+      if (!(st.norm_eps >= 0.0)) return Q4_ERR_SHAPE;
+      if (!aligned(st.norm_weight, 16)) return Q4_ERR_ALIGN;
+      if (m_rows != 1) return Q4_ERR_UNSUPPORTED;
+    }
     for (int32_t i = 0; i < st.num_matrices; ++i) {
-      const q4_chain_matrix& m = matrices[st.first_matrix + i];
-      const q4_status c = check_product(st.x, m_rows, m.packed, m.scales, m.biases, m.n, st.k, m.y, y_dtype);
+      const q4_chain_matrix_ex& m = matrices[st.first_matrix + i];
+      // (matrix 1 of a gated stage has no output: any valid address stands in
+      // for its y in the shared checks)
+      void* y = writes(st, i) ? m.y : matrices[st.first_matrix].y;
+      const q4_status c = check_product(st.x, m_rows, m.packed, m.scales, m.biases, m.n, st.k, y, y_dtype);
       if (c != Q4_OK) return c;
+      if (m.residual && !writes(st, i)) return Q4_ERR_SHAPE;
+      if (m.residual && !aligned(m.residual, ybytes)) return Q4_ERR_ALIGN;
       if (m.n >= (1 << 22)) return Q4_ERR_UNSUPPORTED;
       // each block stages its rows of a matrix in LDS
       if (ceil_div(ceil_div(m.n, q4k::kUnitRows), device_cu_count()) > lim.stage_units) return Q4_ERR_UNSUPPORTED;
       if (!aligned(m.scales, 16) || !aligned(m.biases, 16)) return Q4_ERR_UNSUPPORTED;
-      // a stage may not write its own input
+      if (!writes(st, i)) continue;
+      // a stage may not write its own input (nor its norm weight)
       if (ranges_overlap(st.x, 2 * st.k * m_rows, m.y, ybytes * m.n * m_rows)) return Q4_ERR_UNSUPPORTED;
-      // nor write one output range twice (its blocks store in no fixed order)
-      for (int32_t j = 0; j < i; ++j) {
-        const q4_chain_matrix& o = matrices[st.first_matrix + j];
-        if (ranges_overlap(o.y, ybytes * o.n * m_rows, m.y, ybytes * m.n * m_rows)) return Q4_ERR_UNSUPPORTED;
+      // nor write one output range twice (its blocks store in no fixed order),
+      // nor write another matrix's residual
+      for (int32_t j = 0; j < st.num_matrices; ++j) {
+        if (j == i || !writes(st, j)) continue;
+        const q4_chain_matrix_ex& o = matrices[st.first_matrix + j];
+        if (j < i && ranges_overlap(o.y, ybytes * o.n * m_rows, m.y, ybytes * m.n * m_rows)) return Q4_ERR_UNSUPPORTED;
+        if (o.residual && ranges_overlap(o.residual, ybytes * o.n * m_rows, m.y, ybytes * m.n * m_rows))
+          return Q4_ERR_UNSUPPORTED;
       }
     }
     int ch;
@@ -585,6 +606,16 @@ q4_status q4_chain_encode_rows(const q4_chain_stage* stages, int32_t num_stages,
       return Q4_ERR_UNSUPPORTED;
   }
   if (next_matrix != num_matrices) return Q4_ERR_SHAPE;
+  // no stage may write a norm weight
+  for (int32_t s = 0; s < num_stages; ++s) {
+    if (!stages[s].norm_weight) continue;
+    for (int32_t t = 0; t < num_stages; ++t)
+      for (int32_t i = 0; i < stages[t].num_matrices; ++i) {
+        const q4_chain_matrix_ex& m = matrices[stages[t].first_matrix + i];
+        if (writes(stages[t], i) && ranges_overlap(stages[s].norm_weight, 2 * stages[s].k, m.y, ybytes * m.n * m_rows))
+          return Q4_ERR_UNSUPPORTED;
+      }
+  }
 
   unsigned char* out = static_cast<unsigned char*>(host_plan);
   auto* hdr = reinterpret_cast<q4k::ChainHeader*>(out);
@@ -597,41 +628,52 @@ q4_status q4_chain_encode_rows(const q4_chain_stage* stages, int32_t num_stages,
   hdr->rows = m_rows;
   auto* sd = reinterpret_cast<q4k::ChainStageDesc*>(hdr + 1);
   for (int32_t s = 0; s < num_stages; ++s) {
-    const q4_chain_stage& st = stages[s];
+    const q4_chain_stage_ex& st = stages[s];
     q4k::ChainStageDesc d{};
     d.x = st.x;
     d.G = static_cast<int32_t>(st.k / 32);
     plan_stage(d.G, lim.max_groups, &d.CH);
     d.num_mats = st.num_matrices;
     d.mat_begin = st.first_matrix;
+    d.norm = st.norm_weight;
+    d.norm_eps = st.norm_eps;
+    d.gated = st.gated;
     sd[s] = d;
   }
   // Dependencies through memory, between a stage t and a later stage s:
-  //  - s reads what t wrote (s's x overlaps t's outputs): s loads its x only
-  //    after the preceding stage barrier (device-coherent loads), and t makes
-  //    its outputs visible before it arrives at its barrier;
+  //  - s reads what t wrote (s's x or a residual of s overlaps t's outputs):
+  //    t makes its outputs visible before it arrives at its barrier; s loads
+  //    its x only after the preceding stage barrier (device-coherent loads;
+  //    residuals are always read that way, after s's products);
   //  - s writes where t wrote (outputs overlap): t's stores are likewise
-  //    complete before its barrier, so s's stores land last.
+  //    complete before its barrier, so s's stores land last;
+  //  - s writes where t reads a residual: t's residual reads (and stores)
+  //    complete before its barrier.
   // A later stage writing an earlier stage's x is harmless: every block has
   // read that x before it arrives at the barrier that precedes the writes.
   // Activations no stage writes are prefetched.
   auto stage_writes = [&](int32_t t, const void* p, int64_t bytes) {
     for (int32_t i = 0; i < stages[t].num_matrices; ++i) {
-      const q4_chain_matrix& m = matrices[stages[t].first_matrix + i];
-      if (ranges_overlap(p, bytes, m.y, ybytes * m.n * m_rows)) return true;
+      const q4_chain_matrix_ex& m = matrices[stages[t].first_matrix + i];
+      if (writes(stages[t], i) && ranges_overlap(p, bytes, m.y, ybytes * m.n * m_rows)) return true;
     }
     return false;
   };
   for (int32_t s = 0; s < num_stages; ++s) {
-    const q4_chain_stage& st = stages[s];
+    const q4_chain_stage_ex& st = stages[s];
     for (int32_t t = 0; t < s; ++t) {
       if (stage_writes(t, st.x, 2 * st.k * m_rows)) {
         sd[s].x_internal = 1;
         sd[t].sync_outputs = 1;
       }
       for (int32_t i = 0; i < st.num_matrices; ++i) {
-        const q4_chain_matrix& m = matrices[st.first_matrix + i];
-        if (stage_writes(t, m.y, ybytes * m.n * m_rows)) sd[t].sync_outputs = 1;
+        const q4_chain_matrix_ex& m = matrices[st.first_matrix + i];
+        if (writes(st, i) && stage_writes(t, m.y, ybytes * m.n * m_rows)) sd[t].sync_outputs = 1;
+        if (m.residual && stage_writes(t, m.residual, ybytes * m.n * m_rows)) sd[t].sync_outputs = 1;
+      }
+      for (int32_t i = 0; i < stages[t].num_matrices; ++i) {
+        const q4_chain_matrix_ex& m = matrices[stages[t].first_matrix + i];
+        if (m.residual && stage_writes(s, m.residual, ybytes * m.n * m_rows)) sd[t].sync_outputs = 1;
       }
     }
   }
@@ -643,9 +685,32 @@ q4_status q4_chain_encode_rows(const q4_chain_stage* stages, int32_t num_stages,
     d.biases = matrices[i].biases;
     d.y = matrices[i].y;
     d.n = static_cast<int32_t>(matrices[i].n);
+    d.residual = matrices[i].residual;
     md[i] = d;
   }
   return Q4_OK;
+}
+
+q4_status q4_chain_encode_rows(const q4_chain_stage* stages, int32_t num_stages,
+                               const q4_chain_matrix* matrices, int32_t num_matrices, int32_t m_rows,
+                               q4_out_dtype y_dtype, void* host_plan, int64_t plan_bytes) {
+  if (!stages || !matrices || !host_plan) return Q4_ERR_NULL;
+  if (num_stages <= 0 || num_matrices <= 0) return Q4_ERR_SHAPE;
+  std::vector<q4_chain_stage_ex> se, me_dummy;
+  std::vector<q4_chain_matrix_ex> me;
+  try {
+    se.resize(static_cast<size_t>(num_stages));
+    me.resize(static_cast<size_t>(num_matrices));
+  } catch (...) {
+    return Q4_ERR_UNSUPPORTED;  // (no exception crosses the interface)
+  }
+  for (int32_t s = 0; s < num_stages; ++s)
+    se[s] = q4_chain_stage_ex{stages[s].x, stages[s].k, stages[s].first_matrix, stages[s].num_matrices, nullptr, 0.0,
+                              0, 0};
+  for (int32_t i = 0; i < num_matrices; ++i)
+    me[i] = q4_chain_matrix_ex{matrices[i].packed, matrices[i].scales, matrices[i].biases, matrices[i].y,
+                               matrices[i].n, nullptr};
+  return q4_chain_encode_ex(se.data(), num_stages, me.data(), num_matrices, m_rows, y_dtype, host_plan, plan_bytes);
 }
 
 q4_status q4_chain_encode(const q4_chain_stage* stages, int32_t num_stages,

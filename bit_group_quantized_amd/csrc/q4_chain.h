@@ -112,8 +112,11 @@ struct alignas(16) ChainStageDesc {
   int32_t num_mats;
   int32_t mat_begin;
   int32_t x_internal;    // x is written by an earlier stage of the chain
-  int32_t sync_outputs;  // a later stage reads or overwrites this stage's outputs
-  int32_t pad[8];
+  int32_t sync_outputs;  // a later stage reads or overwrites this stage's outputs (or a residual it reads)
+  const uint16_t* norm;  // RMSNorm weight of x, or null
+  double norm_eps;
+  int32_t gated;         // outputs silu(matrix 0) * matrix 1, to matrix 0's y
+  int32_t pad[3];
 };
 struct alignas(16) ChainMatDesc {
   const uint32_t* packed;
@@ -121,7 +124,8 @@ struct alignas(16) ChainMatDesc {
   const uint16_t* biases;
   void* y;
   int32_t n;
-  int32_t pad[3];
+  int32_t pad;
+  const void* residual;  // added to the product before the rounding, or null
 };
 static_assert(sizeof(ChainHeader) == 64 && sizeof(ChainStageDesc) == 64 && sizeof(ChainMatDesc) == 48,
               "descriptor sizes");
@@ -167,6 +171,9 @@ __device__ __forceinline__ T gload_off(const unsigned char* base, uint32_t off) 
 __device__ __forceinline__ uint32_t coh_load(const uint32_t* p) {
   return __hip_atomic_load((const Q4_GLOBAL uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint16_t coh_load16(const uint16_t* p) {
+  return __hip_atomic_load((const Q4_GLOBAL uint16_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void coh_store(uint32_t* p, uint32_t v) {
   __hip_atomic_store((Q4_GLOBAL uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -194,10 +201,13 @@ struct StageRec {
   int32_t G, CH, nm, mat_begin;
   int32_t P, total;           // pieces per unit, items of the block
   uint32_t inv_p;             // ceil(2^16 / P): i / P == (i * inv_p) >> 16 for the small i here
-  int32_t flags;              // 1 ragged (16 CH > G), 2 x written in the chain, 4 outputs read in the chain
+  int32_t flags;              // 1 ragged (16 CH > G), 2 x written in the chain, 4 outputs read in the chain,
+                              // 8 x normalized (RMSNorm), 16 gated output
   int32_t U[kMaxMatsPerStage];  // the block's units of each matrix
   int32_t U0[kMaxMatsPerStage];  // the first of them
   const uint16_t* x;
+  const uint16_t* norm;       // RMSNorm weight (flag 8)
+  double norm_eps;
   int32_t pad[2];
 };
 struct MatRec {
@@ -205,10 +215,11 @@ struct MatRec {
   const uint16_t* scales;
   const uint16_t* biases;
   void* y;
-  int32_t n, pad[3];
+  int32_t n, pad;
+  const void* residual;
 };
-static_assert(sizeof(StageRec) == 80 && sizeof(MatRec) == 48, "table records");
-constexpr int kStageRagged = 1, kStageXInternal = 2, kStageSyncOut = 4;
+static_assert(sizeof(StageRec) == 96 && sizeof(MatRec) == 48, "table records");
+constexpr int kStageRagged = 1, kStageXInternal = 2, kStageSyncOut = 4, kStageNorm = 8, kStageGated = 16;
 
 // Shared memory: activations and the plan tables (dynamic LDS), and the words
 // that connect the roles (a separate static object).
@@ -234,6 +245,8 @@ struct ChainFlags {
   uint32_t misfit;                   // a matrix has more units per block than the row staging holds
   uint32_t claim[S::kTabStages];     // items of each stage claimed so far by the block's waves
   uint32_t queue[kComputeWaves][kQueueLen];  // each wave's claimed items, oldest first
+  double norm_part[kComputeWaves];   // each compute wave's share of a normalized stage's sum of squares
+  uint32_t norm_cnt;                 // shares written so far
 };
 
 // LDS flag words, accessed through explicit LDS pointers (a volatile access
@@ -423,7 +436,10 @@ __device__ __forceinline__ bool build_stage_rec(StageRec& r, const ChainStageDes
   r.mat_begin = sd->mat_begin;
   r.x = sd->x;
   r.flags = (r.CH * kChunkGroups != r.G ? kStageRagged : 0) | (sd->x_internal ? kStageXInternal : 0) |
-            (sd->sync_outputs ? kStageSyncOut : 0);
+            (sd->sync_outputs ? kStageSyncOut : 0) | (sd->norm ? kStageNorm : 0) | (sd->gated ? kStageGated : 0);
+  r.norm = sd->norm;
+  r.norm_eps = sd->norm_eps;
+  r.pad[0] = r.pad[1] = 0;
   int units = 0;
   bool fits = true;
   for (int mi = 0; mi < kMaxMatsPerStage; ++mi) {
@@ -657,6 +673,108 @@ __device__ __forceinline__ void fill_x_share(const Geo& g, const void* x, uint32
   }
 }
 
+// One compute wave's share of staging a normalized stage's activations (one
+// activation row; RMSNorm in front of the products, the normalization of the
+// model's layers). Two lanes share a group: lane (cw, lane) takes half
+// (64 cw + lane) & 1 of group (64 cw + lane) >> 1, 16 values; every group of
+// the padded row has its lanes (2 * 16 CH <= 768 < 64 kComputeWaves).
+//  1. The lane's values are loaded, their squares summed in fp64 (each square
+//     is exact), and the raw values parked in their LDS slot. The wave's sum
+//     goes to LDS; once all kComputeWaves shares are there, every wave adds
+//     them in wave order, so every block forms the same total.
+//  2. inv = 1 / sqrt(total / k + eps); each value becomes (x * inv) * gamma in
+//     fp64 with explicit rounding, then fp32, then bf16 (the normalized row is
+//     a bf16 activation), re-paired in place. The group sum adds the four
+//     8-value sums in the order the plain staging adds them. gamma was staged
+//     raw, group by group, in the other activation buffer by the service wave
+//     before it released this staging.
+// Groups past G stay zero. nfill counts the normalized stagings this wave
+// has taken part in (the LDS count of shares runs on across stages). Returns
+// false if the wait for the other waves' shares timed out or the block is
+// aborting. Only phase 1 holds loaded registers; the spin between holds none.
+template <bool COH>
+__device__ __forceinline__ bool fill_x_norm(const Geo& g, const void* x, double eps, uint32_t* buf,
+                                            const uint32_t* gbuf, int cw, int lane, ChainFlags<1>& F,
+                                            uint32_t& nfill) {
+  const int gpad = kChunkGroups * g.CH;
+  const int grp = (cw * 64 + lane) >> 1;
+  const int half = lane & 1;
+  const bool live = grp < g.G;
+  const bool slot = grp < gpad;
+  uint32_t* dst = buf + grp * kXWordsPerGroup + 8 * half;
+  {
+    const __amdgpu_buffer_rsrc_t rx = byte_range(x, (uint32_t)(g.G * 64));
+    const uint32_t off = live ? (uint32_t)(grp * 64 + 32 * half) : 0xFFFFFF00u;
+    q4_u32x4 q[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      q[j] = __builtin_bit_cast(q4_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(off + 16 * j), 0,
+                                                                                COH ? kAuxSc1 : 0));
+    double ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t w4[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const double lo = (double)bf16_to_f32(w4[h] & 0xFFFFu), hi = (double)bf16_to_f32(w4[h] >> 16);
+        ss = __dadd_rn(ss, __dmul_rn(lo, lo));
+        ss = __dadd_rn(ss, __dmul_rn(hi, hi));
+      }
+    }
+    if (slot) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) *reinterpret_cast<uint4*>(dst + 4 * j) = make_uint4(q[j].x, q[j].y, q[j].z, q[j].w);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss = __dadd_rn(ss, __shfl_xor(ss, o, 64));
+    if (lane == 0) *(volatile Q4_LDS double*)&F.norm_part[cw] = ss;
+  }
+  compiler_fence();
+  lds_wait();
+  if (lane == 0) lds_add(&F.norm_cnt, 1u);
+  wake_block();
+  ++nfill;
+  uint32_t spins = 0;
+  while ((int)(lds_get(&F.norm_cnt) - (uint32_t)kComputeWaves * nfill) < 0) {
+    nap();
+    if (lds_get(&F.abort) != 0u || ++spins > kSpinLimit) return false;
+  }
+  compiler_fence();
+  double tot = 0.0;
+  for (int w = 0; w < kComputeWaves; ++w) tot = __dadd_rn(tot, *(volatile Q4_LDS double*)&F.norm_part[w]);
+  const double inv = __ddiv_rn(1.0, __dsqrt_rn(__dadd_rn(__ddiv_rn(tot, (double)(g.G * 32)), eps)));
+  float part[2] = {0.f, 0.f};
+  if (slot) {
+    const uint32_t* gsrc = gbuf + grp * kXWordsPerGroup + 8 * half;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint4 xw = *reinterpret_cast<const uint4*>(dst + 4 * j);
+      const uint4 gw = *reinterpret_cast<const uint4*>(gsrc + 4 * j);
+      const uint32_t w4[4] = {xw.x, xw.y, xw.z, xw.w};
+      const uint32_t g4[4] = {gw.x, gw.y, gw.z, gw.w};
+      uint32_t nv[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const double lo = __dmul_rn(__dmul_rn((double)bf16_to_f32(w4[h] & 0xFFFFu), inv),
+                                    (double)bf16_to_f32(g4[h] & 0xFFFFu));
+        const double hi = __dmul_rn(__dmul_rn((double)bf16_to_f32(w4[h] >> 16), inv), (double)bf16_to_f32(g4[h] >> 16));
+        nv[h] = live ? ((uint32_t)f32_to_bf16_rne(__double2float_rn(lo)) |
+                        ((uint32_t)f32_to_bf16_rne(__double2float_rn(hi)) << 16))
+                     : 0u;
+      }
+      const uint4 e4 = make_uint4(nv[0], nv[1], nv[2], nv[3]);
+      uint32_t p02, p46, p13, p57;
+      x_to_pairs(e4, p02, p46, p13, p57);
+      *reinterpret_cast<uint4*>(dst + 4 * j) = make_uint4(p02, p46, p13, p57);
+      part[j] = x_sum8(e4);
+    }
+  }
+  // group sum ((s0 + s1) + s2) + s3, s2 and s3 from the odd lane of the pair
+  const float s2 = __shfl_xor(part[0], 1, 64), s3 = __shfl_xor(part[1], 1, 64);
+  if (slot && half == 0) dst[16] = __float_as_uint(((part[0] + part[1]) + s2) + s3);
+  return true;
+}
+
 template <int MV, bool OUT_F32>
 __device__ __forceinline__ void compute_body(int num_stages, int cw, ChainLds<MV>& L, ChainFlags<MV>& F,
                                              uint32_t* ws) {
@@ -686,6 +804,7 @@ __device__ __forceinline__ void compute_body(int num_stages, int cw, ChainLds<MV
 #pragma unroll
   for (int v = 0; v < MV; ++v) acc[v] = 0.f;
   bool stop = false;  // a wait timed out or another wave failed: finish without waiting
+  uint32_t nfill = 0;  // normalized stagings this wave has taken part in
 
   // stage si.s may start once its activations are in LDS (every wave of the
   // grid has finished the stages before it)
@@ -698,10 +817,26 @@ __device__ __forceinline__ void compute_body(int num_stages, int cw, ChainLds<MV
         compiler_fence();
         const Geo g = geo_of(L.st[si.s]);
         uint32_t* buf = L.x[S::kXBuffers == 2 ? si.s & 1 : 0];
-        if (stage_flags(L, si.s) & kStageXInternal)
-          fill_x_share<MV, true>(g, stage_x(L, si.s), buf, cw, lane);
-        else
-          fill_x_share<MV, false>(g, stage_x(L, si.s), buf, cw, lane);
+        const int fl = stage_flags(L, si.s);
+        if constexpr (MV == 1) {
+          if (fl & kStageNorm) {
+            const double eps = L.st[si.s].norm_eps;
+            const uint32_t* gbuf = L.x[(si.s & 1) ^ 1];
+            const bool ok = (fl & kStageXInternal)
+                                ? fill_x_norm<true>(g, stage_x(L, si.s), eps, buf, gbuf, cw, lane, F, nfill)
+                                : fill_x_norm<false>(g, stage_x(L, si.s), eps, buf, gbuf, cw, lane, F, nfill);
+            if (!ok) stop = true;
+          } else if (fl & kStageXInternal) {
+            fill_x_share<MV, true>(g, stage_x(L, si.s), buf, cw, lane);
+          } else {
+            fill_x_share<MV, false>(g, stage_x(L, si.s), buf, cw, lane);
+          }
+        } else {
+          if (fl & kStageXInternal)
+            fill_x_share<MV, true>(g, stage_x(L, si.s), buf, cw, lane);
+          else
+            fill_x_share<MV, false>(g, stage_x(L, si.s), buf, cw, lane);
+        }
         compiler_fence();
         if (lane == 0) lds_add(&F.x_filled, 1u);
         wake_block();
@@ -899,7 +1034,7 @@ __device__ __forceinline__ void compute_run(int num_stages, int cw, ChainLds<MV>
 // memory; row v goes to dst_buf + v * kVecWords).
 constexpr int kXBatch = 3;
 struct XBatch {
-  uint64_t q[kXBatch][8];
+  q4_u32x4 q[kXBatch][4];
 };
 template <int MV>
 __device__ __forceinline__ int xb_row(int e, int gpad) {
@@ -908,24 +1043,23 @@ __device__ __forceinline__ int xb_row(int e, int gpad) {
   for (int r = 1; r < MV; ++r) v += e >= r * gpad ? 1 : 0;
   return v;
 }
+// Buffer loads with 32-bit offsets (the base stays in scalar registers); a
+// lane past the rows' groups reads zeros.
 template <int MV>
 __device__ __forceinline__ void xb_issue(const Geo& g, const void* x, int base, XBatch& xb) {
   const int lane = threadIdx.x & 63;
   const int gpad = kChunkGroups * g.CH;
   const int total = MV * gpad;
-  const uint64_t* x64 = static_cast<const uint64_t*>(x);
+  const __amdgpu_buffer_rsrc_t rx = byte_range(x, (uint32_t)(MV * g.G * 64));
 #pragma unroll
   for (int b = 0; b < kXBatch; ++b) {
     const int e = base + 64 * b + lane;
     const int v = xb_row<MV>(e, gpad);
     const int grp = e - v * gpad;
+    const uint32_t off = (e < total && grp < g.G) ? (uint32_t)((v * g.G + grp) * 64) : 0xFFFFFF00u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xb.q[b][i] = 0u;
-    if (e < total && grp < g.G) {
-      const uint64_t* src = x64 + ((int64_t)v * g.G + grp) * 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xb.q[b][i] = gload(src + i);
-    }
+    for (int j = 0; j < 4; ++j)
+      xb.q[b][j] = __builtin_bit_cast(q4_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(off + 16 * j), 0, 0));
   }
 }
 template <int MV>
@@ -944,11 +1078,7 @@ __device__ __forceinline__ void xb_store(const Geo& g, int base, const XBatch& x
       float xs = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint4 e4;
-        e4.x = (uint32_t)xb.q[b][2 * j];
-        e4.y = (uint32_t)(xb.q[b][2 * j] >> 32);
-        e4.z = (uint32_t)xb.q[b][2 * j + 1];
-        e4.w = (uint32_t)(xb.q[b][2 * j + 1] >> 32);
+        const uint4 e4 = make_uint4(xb.q[b][j].x, xb.q[b][j].y, xb.q[b][j].z, xb.q[b][j].w);
         uint32_t p02, p46, p13, p57;
         x_to_pairs(e4, p02, p46, p13, p57);
         *reinterpret_cast<uint4*>(dst + 4 * j) = make_uint4(p02, p46, p13, p57);
@@ -966,6 +1096,38 @@ __device__ __forceinline__ void service_load_x(const Geo& g, const void* x, uint
     XBatch xb;
     xb_issue<MV>(g, x, base, xb);
     xb_store<MV>(g, base, xb, dst_buf);
+  }
+  lds_wait();
+}
+
+// The RMSNorm weight of a normalized stage, raw, group by group (the
+// activation buffers' group stride), into the activation buffer the stage
+// does not use; groups past G get zeros. The compute waves read it while
+// they normalize.
+__device__ __forceinline__ void service_load_gamma(const Geo& g, const uint16_t* gamma, uint32_t* dst_buf) {
+  const int lane = threadIdx.x & 63;
+  const int gpad = kChunkGroups * g.CH;
+  const __amdgpu_buffer_rsrc_t rg = byte_range(gamma, (uint32_t)(g.G * 64));
+  for (int base = 0; base < gpad; base += 128) {
+    q4_u32x4 q[2][4];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int e = base + 64 * p + lane;
+      const uint32_t off = e < g.G ? (uint32_t)(e * 64) : 0xFFFFFF00u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        q[p][j] = __builtin_bit_cast(q4_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, (int)(off + 16 * j), 0, 0));
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int e = base + 64 * p + lane;
+      if (e < gpad) {
+        uint32_t* dst = dst_buf + e * kXWordsPerGroup;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<uint4*>(dst + 4 * j) = make_uint4(q[p][j].x, q[p][j].y, q[p][j].z, q[p][j].w);
+      }
+    }
   }
   lds_wait();
 }
@@ -1035,22 +1197,37 @@ __device__ __forceinline__ bool service_wait(uint32_t* ws, ChainFlags<MV>& F, Gr
 // Store stage s's rows from LDS: entry (mi, u, r) is row 4 unit + r of the
 // stage's matrix mi, for the block's local unit u.
 // With MV activation rows the outputs are [MV][n].
+// A gated stage stores silu(matrix 0) * matrix 1 as matrix 0's output; a
+// matrix with a residual adds it (a device-coherent load: an earlier stage may
+// have written it) before the one rounding.
 template <int MV, bool OUT_F32>
 __device__ __forceinline__ void service_store(const ChainLds<MV>& L, int s, ChainFlags<MV>& F) {
   const int lane = threadIdx.x & 63;
   const Geo g = geo_of(L.st[s]);
-  for (int mi = 0; mi < g.num_mats; ++mi) {
+  const bool gated = (stage_flags(L, s) & kStageGated) != 0;
+  for (int mi = 0; mi < (gated ? 1 : g.num_mats); ++mi) {
     const MatRec& mr = L.mt[g.mat_begin + mi];
     const int n = ufl(mr.n);
     const BlockRange br = block_range((n + kUnitRows - 1) / kUnitRows);
     void* y = ufl_ptr(mr.y);
+    const void* res = ufl_ptr(mr.residual);
     for (int e = lane; e < br.count * kUnitRows; e += 64) {
       const int u = e >> 2, r = e & 3;
       const int orow = unit_of(br, u) * kUnitRows + r;
       if (orow < n) {
 #pragma unroll
         for (int v = 0; v < MV; ++v) {
-          const float val = *(volatile Q4_LDS float*)&F.out[mi][u][r][v];
+          float val = *(volatile Q4_LDS float*)&F.out[mi][u][r][v];
+          if (gated) {
+            const float up = *(volatile Q4_LDS float*)&F.out[1][u][r][v];
+            val = val / (1.0f + expf(-val)) * up;
+          }
+          if (res) {
+            if constexpr (OUT_F32)
+              val += __uint_as_float(coh_load(static_cast<const uint32_t*>(res) + (int64_t)v * n + orow));
+            else
+              val += bf16_to_f32(coh_load16(static_cast<const uint16_t*>(res) + (int64_t)v * n + orow));
+          }
           if constexpr (OUT_F32) {
             coh_store(static_cast<uint32_t*>(y) + (int64_t)v * n + orow, __float_as_uint(val));
           } else {
@@ -1069,13 +1246,35 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, Cha
   constexpr bool kDouble = ChainShape<MV>::kXBuffers == 2;
   GridSync gs;
   if (!service_start(ws, F, gs, nxcc)) return;
-  service_load_x<MV>(geo_of(L.st[0]), stage_x(L, 0), L.x[0]);
+  int fills = 0;  // stagings shared with the compute waves so far
+  // (a normalized stage's activations are always staged by the compute
+  // waves together: the norm needs every group's sum of squares)
+  auto wait_filled = [&]() {
+    uint32_t fspins = 0;
+    while ((int)(lds_get(&F.x_filled) - (uint32_t)(kComputeWaves * fills)) < 0) {
+      nap();
+      if (lds_get(&F.abort) != 0u || ++fspins > kSpinLimit) {
+        service_fail(ws, F, 1u);
+        return false;
+      }
+    }
+    return true;
+  };
+  if (stage_flags(L, 0) & kStageNorm) {
+    if constexpr (kDouble) service_load_gamma(geo_of(L.st[0]), ufl_ptr(L.st[0].norm), L.x[1]);
+    compiler_fence();
+    if ((threadIdx.x & 63) == 0) lds_puti(&F.x_fill, 0);
+    wake_block();
+    ++fills;
+    if (!wait_filled()) return;
+  } else {
+    service_load_x<MV>(geo_of(L.st[0]), stage_x(L, 0), L.x[0]);
+  }
   compiler_fence();
   if ((threadIdx.x & 63) == 0) lds_puti(&F.x_stage, 0);
   wake_block();
-  if (kDouble && num_stages > 1 && !(stage_flags(L, 1) & kStageXInternal))
+  if (kDouble && num_stages > 1 && !(stage_flags(L, 1) & (kStageXInternal | kStageNorm)))
     service_load_x<MV>(geo_of(L.st[1]), stage_x(L, 1), L.x[kDouble ? 1 : 0]);
-  int fills = 0;  // stagings shared with the compute waves so far
   for (int s = 0; s < num_stages; ++s) {
     uint32_t spins = 0;
     while ((int)(lds_get(&F.done_total) - (uint32_t)(kComputeWaves * (s + 1))) < 0) {
@@ -1107,7 +1306,16 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, Cha
     // and the rest fetched once stage s + 1 is published. (Loading them only
     // after publishing would hold back this wave's next arrival whenever stage
     // s + 1 is shorter than the load.)
-    const bool prefetch = kDouble && s + 2 < num_stages && !(stage_flags(L, s + 2) & kStageXInternal);
+    const bool internal = (stage_flags(L, s + 1) & kStageXInternal) != 0;
+    const bool norm = (stage_flags(L, s + 1) & kStageNorm) != 0;
+    if constexpr (kDouble) {
+      // A normalized stage s + 1 reads its RMSNorm weight from the buffer
+      // stage s used (free until that staging is done: the prefetch below
+      // writes it only after). Staged before the prefetch's loads are issued,
+      // so the two never hold registers together.
+      if (norm) service_load_gamma(geo_of(L.st[s + 1]), ufl_ptr(L.st[s + 1].norm), L.x[s & 1]);
+    }
+    const bool prefetch = kDouble && s + 2 < num_stages && !(stage_flags(L, s + 2) & (kStageXInternal | kStageNorm));
     XBatch xb;
     if (prefetch) xb_issue<MV>(geo_of(L.st[s + 2]), stage_x(L, s + 2), 0, xb);
     // The compute waves stage the next activations together where they would
@@ -1115,8 +1323,8 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, Cha
     // block's compute waves have all finished stage s, so it is free; the
     // activations no stage writes are staged during the barrier), and for
     // activations written in the chain (after the barrier).
-    const bool internal = (stage_flags(L, s + 1) & kStageXInternal) != 0;
-    const bool shared_fill = !kDouble || internal;
+    const bool shared_fill = !kDouble || internal || norm;
+    compiler_fence();
     if (shared_fill && !internal) {
       if ((threadIdx.x & 63) == 0) lds_puti(&F.x_fill, s + 1);
       wake_block();
@@ -1128,14 +1336,7 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, Cha
         wake_block();
       }
       ++fills;
-      uint32_t fspins = 0;
-      while ((int)(lds_get(&F.x_filled) - (uint32_t)(kComputeWaves * fills)) < 0) {
-        nap();
-        if (lds_get(&F.abort) != 0u || ++fspins > kSpinLimit) {
-          service_fail(ws, F, 1u);
-          return;
-        }
-      }
+      if (!wait_filled()) return;
     }
     compiler_fence();
     if ((threadIdx.x & 63) == 0) lds_puti(&F.x_stage, s + 1);
@@ -1168,6 +1369,7 @@ chain_kernel(const ChainHeader* __restrict__ plan, uint32_t* __restrict__ ws, ui
     F.x_filled = 0u;
     F.abort = 0u;
     F.misfit = 0u;
+    F.norm_cnt = 0u;
     // the plan must be one this library encoded, and fit the LDS tables
     const int ns = cload(&plan->num_stages), nm = cload(&plan->num_mats);
     const bool ok = coh_load(ws + kWsStatus) == 0u && cload(&plan->magic) == kChainMagic && ns > 0 &&
@@ -1192,7 +1394,8 @@ chain_kernel(const ChainHeader* __restrict__ plan, uint32_t* __restrict__ ws, ui
     r.biases = mats[m].biases;
     r.y = mats[m].y;
     r.n = mats[m].n;
-    r.pad[0] = r.pad[1] = r.pad[2] = 0;
+    r.pad = 0;
+    r.residual = mats[m].residual;
     L.mt[m] = r;
   }
   __syncthreads();

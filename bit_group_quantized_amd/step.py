@@ -52,7 +52,15 @@ class Q4Matrix:
 class Stage:
     x: torch.Tensor                     # bf16 [k], or [m, k] for m activation rows
     mats: List[Q4Matrix]
-    outs: List[torch.Tensor] = field(default_factory=list)
+    outs: List[Optional[torch.Tensor]] = field(default_factory=list)
+    # Parts of a decoder layer fused into the chain (persistent executor only):
+    norm: Optional[torch.Tensor] = None   # RMSNorm weight bf16 [k]: x is normalized first (one row)
+    eps: float = 0.0
+    gated: bool = False                   # two matrices (gate, up): outs[0] = silu(gate) * up
+    residuals: Optional[List[Optional[torch.Tensor]]] = None  # added to each product (may be its out)
+
+    def fused(self) -> bool:
+        return self.norm is not None or self.gated or any(r is not None for r in (self.residuals or []))
 
 
 class Chain:
@@ -63,7 +71,8 @@ class Chain:
         for st in stages:
             if not st.outs:
                 shape = (st.x.shape[0],) if st.x.dim() == 2 else ()
-                st.outs = [torch.empty(shape + (m.n,), dtype=out_dtype, device=dev) for m in st.mats]
+                st.outs = [None if (st.gated and i == 1) else torch.empty(shape + (m.n,), dtype=out_dtype, device=dev)
+                           for i, m in enumerate(st.mats)]
         self._plan = None
         self._ws: Optional[torch.Tensor] = None
         self.device = dev
@@ -76,6 +85,8 @@ class Chain:
 
     # ---- executor 1: one launch per matrix
     def run_launches(self) -> None:
+        if any(st.fused() for st in self.stages):
+            raise ValueError("norm, gate and residual are fused in the persistent executor only")
         for st in self.stages:
             for m, y in zip(st.mats, st.outs):
                 if st.x.dim() == 1:

@@ -264,6 +264,49 @@ q4_status q4_chain_encode(const q4_chain_stage* stages, int32_t num_stages,
                           const q4_chain_matrix* matrices, int32_t num_matrices,
                           q4_out_dtype y_dtype, void* host_plan, int64_t plan_bytes);
 
+/* The chain with the parts of a decoder layer fused around its products
+ * (RMSNorm, the SwiGLU gate and the residual sum are reused parts of the
+ * model: GeekNews summary, audio pipeline; "NVIDIA PersonaPlex 7B on Apple
+ * Silicon", Mimi reuse section). Each is optional per stage or matrix:
+ *  - norm_weight (bf16 [k], may be NULL): the stage's x is replaced by its
+ *    RMSNorm before the products: inv = 1/sqrt(sum x^2 / k + norm_eps),
+ *    x_j -> bf16((x_j * inv) * norm_weight_j), the sum and scaling in fp64
+ *    (one activation row only: m_rows == 1);
+ *  - gated (0 or 1): a stage of exactly two matrices of equal n (gate, up);
+ *    its output is silu(gate) * up, silu(t) = t / (1 + exp(-t)), computed in
+ *    fp32 from the two fp32 products and written to matrix 0's y (matrix 1's
+ *    y is not written and may be NULL);
+ *  - residual (per matrix, may be NULL): [m_rows][n] of the chain's output
+ *    dtype, added to the matrix's product (after the gate, on a gated stage's
+ *    matrix 0) before its one rounding; it may be y itself (in place) and may
+ *    be written by an earlier stage of the chain.
+ * Every other rule is q4_chain_encode_rows's; in addition a norm weight may
+ * not overlap any stage's output, a residual may not overlap another output
+ * of its own stage, and a gated stage's matrix 1 takes no residual. */
+typedef struct q4_chain_stage_ex {
+  const uint16_t* x;           /* bf16 [m_rows][k], 16-byte aligned */
+  int64_t k;
+  int32_t first_matrix;
+  int32_t num_matrices;
+  const uint16_t* norm_weight; /* bf16 [k] or NULL, 16-byte aligned */
+  double norm_eps;
+  int32_t gated;
+  int32_t reserved;            /* 0 */
+} q4_chain_stage_ex;
+
+typedef struct q4_chain_matrix_ex {
+  const uint32_t* packed;
+  const uint16_t* scales;
+  const uint16_t* biases;
+  void* y;
+  int64_t n;
+  const void* residual;        /* [m_rows][n] of the output dtype, or NULL */
+} q4_chain_matrix_ex;
+
+q4_status q4_chain_encode_ex(const q4_chain_stage_ex* stages, int32_t num_stages,
+                             const q4_chain_matrix_ex* matrices, int32_t num_matrices, int32_t m_rows,
+                             q4_out_dtype y_dtype, void* host_plan, int64_t plan_bytes);
+
 /* Run an encoded chain (device copy of the plan) on `stream`: one launch of one
  * 960-thread block per compute unit, all resident at once (the stage
  * barrier needs that; Q4_ERR_UNSUPPORTED if the kernel cannot fit one block

@@ -4,6 +4,7 @@ call here fails validation, so no HIP call is made)."""
 import ctypes
 import os
 import re
+import struct
 
 import pytest
 
@@ -360,3 +361,119 @@ def test_attn_decode_validation():
     assert call(d=96) == q4.Q4_ERR_UNSUPPORTED
     assert call(q=A16 + 2) == q4.Q4_ERR_ALIGN
     assert call(w=W + 16) == q4.Q4_ERR_ALIGN
+
+
+NORM_PTR, NORM_EPS, GATED = 32, 40, 48  # byte offsets in a stage record of the plan
+
+
+def _stage_u64(buf, s, off):
+    base = 64 + 64 * s
+    return int.from_bytes(bytes(buf[base + off:base + off + 8]), "little")
+
+
+def _encode_ex(stages, mats, rows=1, dtype=0):
+    lib = q4.load()
+    nb = lib.q4_chain_plan_bytes(len(stages), len(mats))
+    buf = (ctypes.c_uint8 * nb)()
+    st = (q4._ChainStageEx * len(stages))(*stages)
+    mt = (q4._ChainMatrixEx * len(mats))(*mats)
+    rc = lib.q4_chain_encode_ex(ctypes.byref(st), len(stages), ctypes.byref(mt), len(mats), rows, dtype,
+                                ctypes.byref(buf), nb)
+    return rc, buf
+
+
+def _sx(x, k, first, count, norm=None, eps=1e-5, gated=0):
+    return q4._ChainStageEx(x, k, first, count, norm, eps, gated, 0)
+
+
+def _mx(y, n, residual=None):
+    return q4._ChainMatrixEx(A16, A16, A16, y, n, residual)
+
+
+def test_chain_encode_ex_records_the_fused_parts():
+    """The norm weight, eps and gate flag land in the stage record; a gated
+    stage's second matrix needs no output."""
+    X0, G0, Y0, Y1, Y2 = 0x100000, 0x180000, 0x400000, 0x500000, 0x600000
+    rc, buf = _encode_ex([_sx(X0, 256, 0, 1, norm=G0, eps=0.25), _sx(X0, 256, 1, 2, gated=1)],
+                         [_mx(Y0, 64), _mx(Y1, 32), _mx(None, 32)])
+    assert rc == q4.Q4_OK
+    assert _stage_u64(buf, 0, NORM_PTR) == G0 and _stage_u64(buf, 1, NORM_PTR) == 0
+    assert struct.unpack("<d", bytes(buf[64 + NORM_EPS:64 + NORM_EPS + 8]))[0] == 0.25
+    assert [_stage_field(buf, s, GATED) for s in range(2)] == [0, 1]
+    # q4_chain_encode_rows writes the same plan as the extended encoder without fused parts
+    lib = q4.load()
+    nb = lib.q4_chain_plan_bytes(2, 2)
+    plain = (ctypes.c_uint8 * nb)()
+    st = (q4._ChainStage * 2)(q4._ChainStage(X0, 256, 0, 1), q4._ChainStage(Y0, 64, 1, 1))
+    mt = (q4._ChainMatrix * 2)(q4._ChainMatrix(A16, A16, A16, Y1, 64), q4._ChainMatrix(A16, A16, A16, Y2, 32))
+    assert lib.q4_chain_encode_rows(ctypes.byref(st), 2, ctypes.byref(mt), 2, 1, 0, ctypes.byref(plain), nb) == 0
+    rc, ex = _encode_ex([_sx(X0, 256, 0, 1, eps=0.0), _sx(Y0, 64, 1, 1, eps=0.0)], [_mx(Y1, 64), _mx(Y2, 32)])
+    assert rc == q4.Q4_OK and bytes(ex) == bytes(plain)
+
+
+@pytest.mark.parametrize("case,want", [
+    ("gate_one_matrix", q4.Q4_ERR_SHAPE),
+    ("gate_unequal_n", q4.Q4_ERR_SHAPE),
+    ("gate_flag_2", q4.Q4_ERR_SHAPE),
+    ("gate_residual_on_up", q4.Q4_ERR_SHAPE),
+    ("norm_two_rows", q4.Q4_ERR_UNSUPPORTED),
+    ("norm_misaligned", q4.Q4_ERR_ALIGN),
+    ("eps_negative", q4.Q4_ERR_SHAPE),
+    ("eps_nan", q4.Q4_ERR_SHAPE),
+    ("residual_misaligned", q4.Q4_ERR_ALIGN),
+    ("residual_is_other_output", q4.Q4_ERR_UNSUPPORTED),
+    ("output_over_norm", q4.Q4_ERR_UNSUPPORTED),
+    ("residual_in_place", q4.Q4_OK),
+])
+def test_chain_encode_ex_validation(case, want):
+    X0, G0, Y0, Y1 = 0x100000, 0x180000, 0x400000, 0x500000
+    stages = [_sx(X0, 256, 0, 2)]
+    mats = [_mx(Y0, 32), _mx(Y1, 32)]
+    rows = 1
+    if case == "gate_one_matrix":
+        stages = [_sx(X0, 256, 0, 1, gated=1)]
+        mats = mats[:1]
+    elif case == "gate_unequal_n":
+        stages = [_sx(X0, 256, 0, 2, gated=1)]
+        mats = [_mx(Y0, 32), _mx(None, 64)]
+    elif case == "gate_flag_2":
+        stages = [_sx(X0, 256, 0, 2, gated=2)]
+    elif case == "gate_residual_on_up":
+        stages = [_sx(X0, 256, 0, 2, gated=1)]
+        mats = [_mx(Y0, 32), _mx(None, 32, residual=Y1)]
+    elif case == "norm_two_rows":
+        stages = [_sx(X0, 256, 0, 2, norm=G0)]
+        rows = 2
+    elif case == "norm_misaligned":
+        stages = [_sx(X0, 256, 0, 2, norm=G0 + 2)]
+    elif case == "eps_negative":
+        stages = [_sx(X0, 256, 0, 2, norm=G0, eps=-1e-6)]
+    elif case == "eps_nan":
+        stages = [_sx(X0, 256, 0, 2, norm=G0, eps=float("nan"))]
+    elif case == "residual_misaligned":
+        mats = [_mx(Y0, 32, residual=Y1 + 1), _mx(Y1 + 64, 32)]
+    elif case == "residual_is_other_output":
+        mats = [_mx(Y0, 32, residual=Y1), _mx(Y1, 32)]
+    elif case == "output_over_norm":
+        stages = [_sx(X0, 256, 0, 2, norm=Y1)]
+    elif case == "residual_in_place":
+        mats = [_mx(Y0, 32, residual=Y0), _mx(Y1, 32, residual=Y1)]
+    rc, _ = _encode_ex(stages, mats, rows=rows)
+    assert rc == want
+
+
+def test_chain_encode_ex_residual_dependencies():
+    """A residual written by an earlier stage makes that stage store before its
+    barrier; so does a later stage overwriting a residual an earlier stage
+    reads. A residual no stage writes needs no flag."""
+    X0, X1, R, Y0, Y1 = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+    rc, buf = _encode_ex([_sx(X0, 256, 0, 1), _sx(X1, 256, 1, 1)], [_mx(Y0, 32), _mx(Y1, 32, residual=Y0)])
+    assert rc == q4.Q4_OK
+    assert [_stage_field(buf, s, SYNC_OUT) for s in range(2)] == [1, 0]
+    assert [_stage_field(buf, s, X_INTERNAL) for s in range(2)] == [0, 0]
+    rc, buf = _encode_ex([_sx(X0, 256, 0, 1), _sx(X1, 256, 1, 1)], [_mx(Y0, 32, residual=R), _mx(R, 32)])
+    assert rc == q4.Q4_OK
+    assert [_stage_field(buf, s, SYNC_OUT) for s in range(2)] == [1, 0]
+    rc, buf = _encode_ex([_sx(X0, 256, 0, 1), _sx(X1, 256, 1, 1)], [_mx(Y0, 32, residual=R), _mx(Y1, 32, residual=R)])
+    assert rc == q4.Q4_OK
+    assert [_stage_field(buf, s, SYNC_OUT) for s in range(2)] == [0, 0]
