@@ -122,6 +122,39 @@ def make_temporal_chain(seed: int = 0, layers: int = workloads.TEMPORAL_LAYERS,
     return Chain(stages, out_dtype)
 
 
+def fused_stages(chain, seed: int = 0):
+    """The temporal step's stages with the model's data flow and the decoder
+    layer's parts fused in, on the same matrices: per layer
+      norm(h) -> q, k, v;   o(q) + h -> h;   norm(h) -> silu(gate) * up -> mid;
+      down(mid) + h -> h
+    (h: the bf16 hidden state, updated in place; q stands in for the attention
+    output, which this chain does not compute). RMSNorm weights are drawn
+    around 1 (seeded), eps 1e-5."""
+    import torch
+
+    from bit_group_quantized_amd.step import Stage
+
+    dev = chain.stages[0].x.device
+    d, f = workloads.HIDDEN, workloads.FFN
+    h = torch.from_numpy(workloads.activations(seed, workloads.CFG_STEP, 0, 200, 1, d)[0].view(np.int16)).to(dev)
+    h = h.view(torch.bfloat16)
+    out = []
+    for layer in range(len(chain.stages) // 4):
+        qkv, o, gu, down = chain.stages[4 * layer:4 * layer + 4]
+        r = np.random.default_rng([seed, layer, 7])
+        gam = [torch.from_numpy(workloads.bf16_bits_rne((1 + 0.1 * r.standard_normal(d)).astype(np.float32))
+                                .view(np.int16)).to(dev).view(torch.bfloat16) for _ in range(2)]
+        q = torch.empty(d, dtype=torch.bfloat16, device=dev)
+        kk = torch.empty(d, dtype=torch.bfloat16, device=dev)
+        v = torch.empty(d, dtype=torch.bfloat16, device=dev)
+        mid = torch.empty(f, dtype=torch.bfloat16, device=dev)
+        out += [Stage(h, qkv.mats, [q, kk, v], norm=gam[0], eps=1e-5),
+                Stage(q, o.mats, [h], residuals=[h]),
+                Stage(h, gu.mats, [mid, None], norm=gam[1], eps=1e-5, gated=True),
+                Stage(mid, down.mats, [h], residuals=[h])]
+    return out, h
+
+
 def make_small_gemm(chain, m: int, seed: int = 0, device=None):
     """The small-GEMM workload: every stage of the temporal step (its packed
     matrices reused) against m activation rows, drawn per layer and stage on the
@@ -442,6 +475,25 @@ def main(argv=None) -> int:
                                    "pct_hbm_peak": round(100 * wbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                                    "step_ms_p10_p50_p90": [round(float(np.percentile(dper, q)), 4)
                                                            for q in (10, 50, 90)]}
+        # and with the decoder layer's RMSNorm, SwiGLU gate and residual sums
+        # fused in (the hidden state updated in place)
+        from bit_group_quantized_amd.step import Chain
+        # (h keeps accumulating over the replays: a random walk of O(1) terms
+        # that stays far from the bf16 range over any run length used here)
+        fst, _ = fused_stages(chain, args.seed)
+        fchain = Chain(fst, torch.bfloat16)
+        fchain.prepare_chain()
+        fms, fper = time_replays(fchain.run_chain, args.steps, args.warmup)
+        if fchain.chain_status() != 0:
+            print(f"chain executor reported status {fchain.chain_status()} (fused step)", file=sys.stderr)
+            return 1
+        extra["fused_step"] = {"us_per_step": round(fms * 1e3, 1),
+                               "gbs": round(wbytes / (fms * 1e-3) / 1e9, 1),
+                               "pct_hbm_peak": round(100 * wbytes / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                               "step_ms_p10_p50_p90": [round(float(np.percentile(fper, q)), 4)
+                                                       for q in (10, 50, 90)],
+                               "stages": "per layer: norm->qkv, o+residual, norm->gate/up gated, down+residual"}
+        del fchain, fst
         log("[bench] stream ceiling ...")
         extra["stream_ceiling"] = stream_ceiling(dev, wbytes)
         extra["pack"] = pack_timing(dev, args.seed)

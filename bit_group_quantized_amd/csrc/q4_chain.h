@@ -247,6 +247,7 @@ struct ChainFlags {
   uint32_t queue[kComputeWaves][kQueueLen];  // each wave's claimed items, oldest first
   double norm_part[kComputeWaves];   // each compute wave's share of a normalized stage's sum of squares
   uint32_t norm_cnt;                 // shares written so far
+  uint32_t any_norm;                 // some stage of the plan is normalized
 };
 
 // LDS flag words, accessed through explicit LDS pointers (a volatile access
@@ -692,7 +693,6 @@ __device__ __forceinline__ void fill_x_share(const Geo& g, const void* x, uint32
 // has taken part in (the LDS count of shares runs on across stages). Returns
 // false if the wait for the other waves' shares timed out or the block is
 // aborting. Only phase 1 holds loaded registers; the spin between holds none.
-template <bool COH>
 __device__ __forceinline__ bool fill_x_norm(const Geo& g, const void* x, double eps, uint32_t* buf,
                                             const uint32_t* gbuf, int cw, int lane, ChainFlags<1>& F,
                                             uint32_t& nfill) {
@@ -708,8 +708,7 @@ __device__ __forceinline__ bool fill_x_norm(const Geo& g, const void* x, double 
     q4_u32x4 q[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      q[j] = __builtin_bit_cast(q4_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(off + 16 * j), 0,
-                                                                                COH ? kAuxSc1 : 0));
+      q[j] = __builtin_bit_cast(q4_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(off + 16 * j), 0, kAuxSc1));
     double ss = 0.0;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -775,7 +774,10 @@ __device__ __forceinline__ bool fill_x_norm(const Geo& g, const void* x, double 
   return true;
 }
 
-template <int MV, bool OUT_F32>
+// NORM: the plan has normalized stages. The staging code those need is
+// large and is inlined at every place a wave can change stage, so plans
+// without them run a body compiled without it (its code then stays small).
+template <int MV, bool OUT_F32, bool NORM>
 __device__ __forceinline__ void compute_body(int num_stages, int cw, ChainLds<MV>& L, ChainFlags<MV>& F,
                                              uint32_t* ws) {
   using S = ChainShape<MV>;
@@ -819,17 +821,15 @@ __device__ __forceinline__ void compute_body(int num_stages, int cw, ChainLds<MV
         uint32_t* buf = L.x[S::kXBuffers == 2 ? si.s & 1 : 0];
         const int fl = stage_flags(L, si.s);
         if constexpr (MV == 1) {
-          if (fl & kStageNorm) {
+          // (one activation row: the service wave stages activations no stage
+          // writes, except a normalized stage's; the compute waves stage those
+          // and the ones written in the chain, always with coherent loads)
+          if (NORM && (fl & kStageNorm)) {
             const double eps = L.st[si.s].norm_eps;
             const uint32_t* gbuf = L.x[(si.s & 1) ^ 1];
-            const bool ok = (fl & kStageXInternal)
-                                ? fill_x_norm<true>(g, stage_x(L, si.s), eps, buf, gbuf, cw, lane, F, nfill)
-                                : fill_x_norm<false>(g, stage_x(L, si.s), eps, buf, gbuf, cw, lane, F, nfill);
-            if (!ok) stop = true;
-          } else if (fl & kStageXInternal) {
-            fill_x_share<MV, true>(g, stage_x(L, si.s), buf, cw, lane);
+            if (!fill_x_norm(g, stage_x(L, si.s), eps, buf, gbuf, cw, lane, F, nfill)) stop = true;
           } else {
-            fill_x_share<MV, false>(g, stage_x(L, si.s), buf, cw, lane);
+            fill_x_share<MV, true>(g, stage_x(L, si.s), buf, cw, lane);
           }
         } else {
           if (fl & kStageXInternal)
@@ -1018,7 +1018,14 @@ __device__ __forceinline__ void compute_body(int num_stages, int cw, ChainLds<MV
 template <int MV, bool OUT_F32>
 __device__ __forceinline__ void compute_run(int num_stages, int cw, ChainLds<MV>& L, ChainFlags<MV>& F,
                                             uint32_t* ws) {
-  compute_body<MV, OUT_F32>(num_stages, cw, L, F, ws);
+  if constexpr (MV == 1) {
+    if (lds_get(&F.any_norm) != 0u)
+      compute_body<MV, OUT_F32, true>(num_stages, cw, L, F, ws);
+    else
+      compute_body<MV, OUT_F32, false>(num_stages, cw, L, F, ws);
+  } else {
+    compute_body<MV, OUT_F32, false>(num_stages, cw, L, F, ws);
+  }
   // loads still in flight (the refills past the wave's last slot, or an
   // aborted wave's) complete before the wave ends
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -1370,6 +1377,7 @@ chain_kernel(const ChainHeader* __restrict__ plan, uint32_t* __restrict__ ws, ui
     F.abort = 0u;
     F.misfit = 0u;
     F.norm_cnt = 0u;
+    F.any_norm = 0u;
     // the plan must be one this library encoded, and fit the LDS tables
     const int ns = cload(&plan->num_stages), nm = cload(&plan->num_mats);
     const bool ok = coh_load(ws + kWsStatus) == 0u && cload(&plan->magic) == kChainMagic && ns > 0 &&
@@ -1385,8 +1393,10 @@ chain_kernel(const ChainHeader* __restrict__ plan, uint32_t* __restrict__ ws, ui
   const ChainStageDesc* stages = reinterpret_cast<const ChainStageDesc*>(plan + 1);
   const ChainMatDesc* mats = reinterpret_cast<const ChainMatDesc*>(stages + num_stages);
   // the plan into LDS, one lane per stage and per matrix
-  for (int s = threadIdx.x; s < num_stages; s += blockDim.x)
+  for (int s = threadIdx.x; s < num_stages; s += blockDim.x) {
     if (!build_stage_rec<MV>(L.st[s], stages + s, mats)) lds_put(&F.misfit, 1u);
+    if (L.st[s].flags & kStageNorm) lds_put(&F.any_norm, 1u);
+  }
   for (int m = threadIdx.x; m < num_mats; m += blockDim.x) {
     MatRec r;
     r.packed = mats[m].packed;
