@@ -180,6 +180,13 @@ __device__ __forceinline__ void coh_store(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ void coh_store16(uint16_t* p, uint16_t v) {
   __hip_atomic_store((Q4_GLOBAL uint16_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint64_t coh_load64(const uint64_t* p) {
+  return __hip_atomic_load((const Q4_GLOBAL uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// device-coherent add whose result is not waited for
+__device__ __forceinline__ void coh_add64_post(uint64_t* p, uint64_t v) {
+  (void)__hip_atomic_fetch_add((Q4_GLOBAL uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
 __device__ __forceinline__ uint32_t coh_add(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add((Q4_GLOBAL uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -236,6 +243,7 @@ struct ChainFlags {
   float parts[kSplitItems][kUnitRows][MV];   // partial row sums of the pieces of a stage
   uint32_t pieces_done[kSplitUnits];         // pieces of a unit of the stage finished
   float out[kMaxMatsPerStage][S::kStageUnits][kUnitRows][MV];  // the stage's finished rows
+  float res[kMaxMatsPerStage][S::kStageUnits][kUnitRows][MV];  // residuals of those rows, loaded early
   uint32_t done_total;               // stage completions of all compute waves
   int32_t x_stage;                   // last stage whose activations are in LDS
   int32_t x_fill;                    // stage whose activations the compute waves stage together
@@ -674,27 +682,53 @@ __device__ __forceinline__ void fill_x_share(const Geo& g, const void* x, uint32
   }
 }
 
+// Sum over a wave, in fp64, in a fixed order: within each row of 16 lanes by
+// DPP rotations (every lane ends with its row's total), then the four rows'
+// totals (read from lanes 0, 16, 32, 48) as (r0 + r1) + (r2 + r3).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double lane_f64(double v, int l) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v = __dadd_rn(v, dpp_f64<0x128>(v));  // row_ror:8
+  v = __dadd_rn(v, dpp_f64<0x124>(v));  // row_ror:4
+  v = __dadd_rn(v, dpp_f64<0x122>(v));  // row_ror:2
+  v = __dadd_rn(v, dpp_f64<0x121>(v));  // row_ror:1
+  return __dadd_rn(__dadd_rn(lane_f64(v, 0), lane_f64(v, 16)), __dadd_rn(lane_f64(v, 32), lane_f64(v, 48)));
+}
+
 // One compute wave's share of staging a normalized stage's activations (one
 // activation row; RMSNorm in front of the products, the normalization of the
 // model's layers). Two lanes share a group: lane (cw, lane) takes half
 // (64 cw + lane) & 1 of group (64 cw + lane) >> 1, 16 values; every group of
 // the padded row has its lanes (2 * 16 CH <= 768 < 64 kComputeWaves).
-//  1. The lane's values are loaded, their squares summed in fp64 (each square
-//     is exact), and the raw values parked in their LDS slot. The wave's sum
-//     goes to LDS; once all kComputeWaves shares are there, every wave adds
-//     them in wave order, so every block forms the same total.
-//  2. inv = 1 / sqrt(total / k + eps); each value becomes (x * inv) * gamma in
-//     fp64 with explicit rounding, then fp32, then bf16 (the normalized row is
-//     a bf16 activation), re-paired in place. The group sum adds the four
-//     8-value sums in the order the plain staging adds them. gamma was staged
-//     raw, group by group, in the other activation buffer by the service wave
-//     before it released this staging.
-// Groups past G stay zero. nfill counts the normalized stagings this wave
-// has taken part in (the LDS count of shares runs on across stages). Returns
-// false if the wait for the other waves' shares timed out or the block is
-// aborting. Only phase 1 holds loaded registers; the spin between holds none.
-__device__ __forceinline__ bool fill_x_norm(const Geo& g, const void* x, double eps, uint32_t* buf,
-                                            const uint32_t* gbuf, int cw, int lane, ChainFlags<1>& F,
+//  1. The lane loads its 16 values and their 16 norm weights and parks both,
+//     raw, in their slots: the values in the stage's activation buffer, the
+//     weights in the other one (free: every wave of the block has finished the
+//     stage before, and the next prefetch into it waits for this staging).
+//     The squares (exact in fp32) are summed in fp64; the wave's sum goes to
+//     LDS and, once all kComputeWaves shares are there, every wave adds them
+//     in wave order, so every block forms the same total.
+//  2. inv = 1 / sqrt(total / k + eps) in fp64; each value becomes
+//     (x * gamma) * inv, the product x * gamma exact in fp32 and the scaling
+//     in fp64, rounded to fp32 and then to bf16 (the normalized row is a bf16
+//     activation), re-paired in place. The group sum adds the four 8-value
+//     sums in the order the plain staging adds them.
+// Groups past G stay zero. nfill counts the normalized stagings this wave has
+// taken part in (the LDS count of shares runs on across stages). Returns false
+// if the wait for the other waves' shares timed out or the block is aborting.
+// Only phase 1 holds loaded registers; the spin between holds none.
+__device__ __forceinline__ bool fill_x_norm(const Geo& g, const void* x, const uint16_t* gamma, double eps,
+                                            uint32_t* buf, uint32_t* gbuf, int cw, int lane, ChainFlags<1>& F,
                                             uint32_t& nfill) {
   const int gpad = kChunkGroups * g.CH;
   const int grp = (cw * 64 + lane) >> 1;
@@ -702,30 +736,36 @@ __device__ __forceinline__ bool fill_x_norm(const Geo& g, const void* x, double 
   const bool live = grp < g.G;
   const bool slot = grp < gpad;
   uint32_t* dst = buf + grp * kXWordsPerGroup + 8 * half;
+  uint32_t* gdst = gbuf + grp * kXWordsPerGroup + 8 * half;
   {
     const __amdgpu_buffer_rsrc_t rx = byte_range(x, (uint32_t)(g.G * 64));
+    const __amdgpu_buffer_rsrc_t rg = byte_range(gamma, (uint32_t)(g.G * 64));
     const uint32_t off = live ? (uint32_t)(grp * 64 + 32 * half) : 0xFFFFFF00u;
-    q4_u32x4 q[2];
+    q4_u32x4 q[2], gm[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j) {
       q[j] = __builtin_bit_cast(q4_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(off + 16 * j), 0, kAuxSc1));
+      gm[j] = __builtin_bit_cast(q4_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, (int)(off + 16 * j), 0, 0));
+    }
     double ss = 0.0;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const uint32_t w4[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        const double lo = (double)bf16_to_f32(w4[h] & 0xFFFFu), hi = (double)bf16_to_f32(w4[h] >> 16);
-        ss = __dadd_rn(ss, __dmul_rn(lo, lo));
-        ss = __dadd_rn(ss, __dmul_rn(hi, hi));
+        const float lo = bf16_to_f32(w4[h] & 0xFFFFu), hi = bf16_to_f32(w4[h] >> 16);
+        ss = __dadd_rn(ss, (double)(lo * lo));
+        ss = __dadd_rn(ss, (double)(hi * hi));
       }
     }
     if (slot) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) *reinterpret_cast<uint4*>(dst + 4 * j) = make_uint4(q[j].x, q[j].y, q[j].z, q[j].w);
+      for (int j = 0; j < 2; ++j) {
+        *reinterpret_cast<uint4*>(dst + 4 * j) = make_uint4(q[j].x, q[j].y, q[j].z, q[j].w);
+        *reinterpret_cast<uint4*>(gdst + 4 * j) = make_uint4(gm[j].x, gm[j].y, gm[j].z, gm[j].w);
+      }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) ss = __dadd_rn(ss, __shfl_xor(ss, o, 64));
+    ss = wave_sum_f64(ss);
     if (lane == 0) *(volatile Q4_LDS double*)&F.norm_part[cw] = ss;
   }
   compiler_fence();
@@ -744,21 +784,19 @@ __device__ __forceinline__ bool fill_x_norm(const Geo& g, const void* x, double 
   const double inv = __ddiv_rn(1.0, __dsqrt_rn(__dadd_rn(__ddiv_rn(tot, (double)(g.G * 32)), eps)));
   float part[2] = {0.f, 0.f};
   if (slot) {
-    const uint32_t* gsrc = gbuf + grp * kXWordsPerGroup + 8 * half;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const uint4 xw = *reinterpret_cast<const uint4*>(dst + 4 * j);
-      const uint4 gw = *reinterpret_cast<const uint4*>(gsrc + 4 * j);
+      const uint4 gw = *reinterpret_cast<const uint4*>(gdst + 4 * j);
       const uint32_t w4[4] = {xw.x, xw.y, xw.z, xw.w};
       const uint32_t g4[4] = {gw.x, gw.y, gw.z, gw.w};
       uint32_t nv[4];
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        const double lo = __dmul_rn(__dmul_rn((double)bf16_to_f32(w4[h] & 0xFFFFu), inv),
-                                    (double)bf16_to_f32(g4[h] & 0xFFFFu));
-        const double hi = __dmul_rn(__dmul_rn((double)bf16_to_f32(w4[h] >> 16), inv), (double)bf16_to_f32(g4[h] >> 16));
-        nv[h] = live ? ((uint32_t)f32_to_bf16_rne(__double2float_rn(lo)) |
-                        ((uint32_t)f32_to_bf16_rne(__double2float_rn(hi)) << 16))
+        const float tlo = bf16_to_f32(w4[h] & 0xFFFFu) * bf16_to_f32(g4[h] & 0xFFFFu);
+        const float thi = bf16_to_f32(w4[h] >> 16) * bf16_to_f32(g4[h] >> 16);
+        nv[h] = live ? ((uint32_t)f32_to_bf16_rne(__double2float_rn(__dmul_rn((double)tlo, inv))) |
+                        ((uint32_t)f32_to_bf16_rne(__double2float_rn(__dmul_rn((double)thi, inv))) << 16))
                      : 0u;
       }
       const uint4 e4 = make_uint4(nv[0], nv[1], nv[2], nv[3]);
@@ -825,9 +863,9 @@ __device__ __forceinline__ void compute_body(int num_stages, int cw, ChainLds<MV
           // writes, except a normalized stage's; the compute waves stage those
           // and the ones written in the chain, always with coherent loads)
           if (NORM && (fl & kStageNorm)) {
-            const double eps = L.st[si.s].norm_eps;
-            const uint32_t* gbuf = L.x[(si.s & 1) ^ 1];
-            if (!fill_x_norm(g, stage_x(L, si.s), eps, buf, gbuf, cw, lane, F, nfill)) stop = true;
+            if (!fill_x_norm(g, stage_x(L, si.s), ufl_ptr(L.st[si.s].norm), L.st[si.s].norm_eps, buf,
+                             L.x[(si.s & 1) ^ 1], cw, lane, F, nfill))
+              stop = true;
           } else {
             fill_x_share<MV, true>(g, stage_x(L, si.s), buf, cw, lane);
           }
@@ -1107,43 +1145,12 @@ __device__ __forceinline__ void service_load_x(const Geo& g, const void* x, uint
   lds_wait();
 }
 
-// The RMSNorm weight of a normalized stage, raw, group by group (the
-// activation buffers' group stride), into the activation buffer the stage
-// does not use; groups past G get zeros. The compute waves read it while
-// they normalize.
-__device__ __forceinline__ void service_load_gamma(const Geo& g, const uint16_t* gamma, uint32_t* dst_buf) {
-  const int lane = threadIdx.x & 63;
-  const int gpad = kChunkGroups * g.CH;
-  const __amdgpu_buffer_rsrc_t rg = byte_range(gamma, (uint32_t)(g.G * 64));
-  for (int base = 0; base < gpad; base += 128) {
-    q4_u32x4 q[2][4];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int e = base + 64 * p + lane;
-      const uint32_t off = e < g.G ? (uint32_t)(e * 64) : 0xFFFFFF00u;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        q[p][j] = __builtin_bit_cast(q4_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, (int)(off + 16 * j), 0, 0));
-    }
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int e = base + 64 * p + lane;
-      if (e < gpad) {
-        uint32_t* dst = dst_buf + e * kXWordsPerGroup;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<uint4*>(dst + 4 * j) = make_uint4(q[p][j].x, q[p][j].y, q[p][j].z, q[p][j].w);
-      }
-    }
-  }
-  lds_wait();
-}
-
 struct GridSync {
   uint32_t xcc;
   uint32_t per;      // blocks on this XCD
   uint32_t present;  // mask of XCDs that hold blocks
   uint32_t epoch;
+  uint32_t nxcc;
 };
 
 template <int MV>
@@ -1156,12 +1163,24 @@ __device__ __forceinline__ bool service_fail(uint32_t* ws, ChainFlags<MV>& F, ui
   return false;
 }
 
+#ifndef Q4_CHAIN_BARRIER
+#define Q4_CHAIN_BARRIER 1
+#endif
 // Start of a launch. The hardware deals the blocks of a launch round-robin
 // over the device's nxcc XCDs, so block b runs on XCD b % nxcc (checked: a
-// block on any other XCD reports status 3). The XCD's counters continue from
-// earlier launches: the exchange flag holds the last completed epoch, and it
-// cannot move before every block of this XCD has arrived at the first
-// barrier of this launch, so every block of the XCD reads the same value here.
+// block on any other XCD reports status 3).
+#if Q4_CHAIN_BARRIER == 2
+// Each XCD has a 64-bit arrival counter (device-coherent, in its own 128-byte
+// line) that runs on across launches: every launch on a workspace has the
+// same blocks per XCD and completes all its barriers, so at the start of a
+// launch the counter of XCD x holds per_x * E arrivals, E the barriers
+// completed so far, plus fewer than per_x arrivals of this launch's first
+// barrier (which cannot complete before this block arrives): E is the
+// counter divided by per_x.
+__device__ __forceinline__ uint64_t* xcd_counter(uint32_t* ws, uint32_t x) {
+  return reinterpret_cast<uint64_t*>(ws + kWsXcnt + 32 * x);
+}
+#endif
 template <int MV>
 __device__ __forceinline__ bool service_start(uint32_t* ws, ChainFlags<MV>& F, GridSync& gs, uint32_t nxcc) {
   const uint32_t nb = gridDim.x;
@@ -1169,12 +1188,48 @@ __device__ __forceinline__ bool service_start(uint32_t* ws, ChainFlags<MV>& F, G
   if (xcc_id() != gs.xcc) return service_fail(ws, F, 3u);
   gs.per = nb / nxcc + (gs.xcc < nb % nxcc ? 1u : 0u);
   gs.present = nxcc >= 32u ? 0xFFFFFFFFu : ((1u << (nxcc < nb ? nxcc : nb)) - 1u);
-  // (unlike an L2 atomic on one line for every block of the XCD, reading the
-  // flag does not serialise)
+#if Q4_CHAIN_BARRIER == 2
+  gs.nxcc = nxcc;
+  gs.epoch = (uint32_t)(coh_load64(xcd_counter(ws, gs.xcc)) / gs.per);
+#else
+  // The XCD's counters continue from earlier launches: the exchange flag
+  // holds the last completed epoch, and it cannot move before every block of
+  // this XCD has arrived at the first barrier of this launch, so every block
+  // of the XCD reads the same value here. (unlike an L2 atomic on one line for
+  // every block of the XCD, reading the flag does not serialise)
   gs.epoch = coh_load(ws + kWsGflag + gs.xcc);
+#endif
   return true;
 }
 
+#if Q4_CHAIN_BARRIER == 2
+// Grid barrier: arrive with a device-coherent add on this XCD's counter, not
+// waited for; every block waits until each XCD's counter has reached
+// (blocks of that XCD) x (this barrier's epoch). The waiting block reads the
+// counters with one lane per XCD.
+// (in two halves: work issued between arrive and wait overlaps the wait)
+__device__ __forceinline__ void service_arrive(uint32_t* ws, GridSync& gs) {
+  ++gs.epoch;
+  if ((threadIdx.x & 63) == 0) coh_add64_post(xcd_counter(ws, gs.xcc), 1u);
+}
+template <int MV>
+__device__ __forceinline__ bool service_wait(uint32_t* ws, ChainFlags<MV>& F, GridSync& gs) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t nb = gridDim.x;
+  const uint32_t x = (uint32_t)lane;
+  const uint64_t per_x = nb / gs.nxcc + (x < nb % gs.nxcc ? 1u : 0u);
+  const uint64_t target = per_x * (uint64_t)gs.epoch;
+  const bool watch = lane < kMaxXcc && ((gs.present >> lane) & 1u);
+  uint32_t spins = 0;
+  while (true) {
+    bool mine = true;
+    if (watch) mine = coh_load64(xcd_counter(ws, x)) >= target;
+    if (__all(mine)) break;
+    if (++spins > kSpinLimit || coh_load(ws + kWsStatus) != 0u) return service_fail(ws, F, 1u);
+  }
+  return true;
+}
+#else
 // Grid barrier: arrive on this XCD's L2 counter; the XCD's last arrival
 // publishes the XCD's flag device-wide; every block waits until all XCDs'
 // flags (one 64-byte line) carry this epoch.
@@ -1200,13 +1255,14 @@ __device__ __forceinline__ bool service_wait(uint32_t* ws, ChainFlags<MV>& F, Gr
   }
   return true;
 }
+#endif
 
 // Store stage s's rows from LDS: entry (mi, u, r) is row 4 unit + r of the
 // stage's matrix mi, for the block's local unit u.
 // With MV activation rows the outputs are [MV][n].
 // A gated stage stores silu(matrix 0) * matrix 1 as matrix 0's output; a
-// matrix with a residual adds it (a device-coherent load: an earlier stage may
-// have written it) before the one rounding.
+// matrix with a residual adds it (staged by service_load_res) before the one
+// rounding.
 template <int MV, bool OUT_F32>
 __device__ __forceinline__ void service_store(const ChainLds<MV>& L, int s, ChainFlags<MV>& F) {
   const int lane = threadIdx.x & 63;
@@ -1229,12 +1285,7 @@ __device__ __forceinline__ void service_store(const ChainLds<MV>& L, int s, Chai
             const float up = *(volatile Q4_LDS float*)&F.out[1][u][r][v];
             val = val / (1.0f + expf(-val)) * up;
           }
-          if (res) {
-            if constexpr (OUT_F32)
-              val += __uint_as_float(coh_load(static_cast<const uint32_t*>(res) + (int64_t)v * n + orow));
-            else
-              val += bf16_to_f32(coh_load16(static_cast<const uint16_t*>(res) + (int64_t)v * n + orow));
-          }
+          if (res) val += *(volatile Q4_LDS float*)&F.res[mi][u][r][v];
           if constexpr (OUT_F32) {
             coh_store(static_cast<uint32_t*>(y) + (int64_t)v * n + orow, __float_as_uint(val));
           } else {
@@ -1246,6 +1297,39 @@ __device__ __forceinline__ void service_store(const ChainLds<MV>& L, int s, Chai
   }
 }
 
+// The residuals of the rows this block stores in stage s, into LDS, as soon
+// as the stage starts (device-coherent loads: every stage before s has made
+// its outputs visible before the barrier that opened s; a later stage that
+// overwrites them waits for this stage's barrier), so that the stores at the
+// end of the stage do not wait for them.
+template <int MV, bool OUT_F32>
+__device__ __forceinline__ void service_load_res(const ChainLds<MV>& L, int s, ChainFlags<MV>& F) {
+  const int lane = threadIdx.x & 63;
+  const Geo g = geo_of(L.st[s]);
+  const bool gated = (stage_flags(L, s) & kStageGated) != 0;
+  for (int mi = 0; mi < (gated ? 1 : g.num_mats); ++mi) {
+    const MatRec& mr = L.mt[g.mat_begin + mi];
+    const void* res = ufl_ptr(mr.residual);
+    if (!res) continue;
+    const int n = ufl(mr.n);
+    const BlockRange br = block_range((n + kUnitRows - 1) / kUnitRows);
+    for (int e = lane; e < br.count * kUnitRows; e += 64) {
+      const int u = e >> 2, r = e & 3;
+      const int orow = unit_of(br, u) * kUnitRows + r;
+      if (orow < n) {
+#pragma unroll
+        for (int v = 0; v < MV; ++v) {
+          float val;
+          if constexpr (OUT_F32)
+            val = __uint_as_float(coh_load(static_cast<const uint32_t*>(res) + (int64_t)v * n + orow));
+          else
+            val = bf16_to_f32(coh_load16(static_cast<const uint16_t*>(res) + (int64_t)v * n + orow));
+          *(volatile Q4_LDS float*)&F.res[mi][u][r][v] = val;
+        }
+      }
+    }
+  }
+}
 
 template <int MV, bool OUT_F32>
 __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, ChainFlags<MV>& F, uint32_t* ws,
@@ -1268,8 +1352,6 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, Cha
     return true;
   };
   if (stage_flags(L, 0) & kStageNorm) {
-    if constexpr (kDouble) service_load_gamma(geo_of(L.st[0]), ufl_ptr(L.st[0].norm), L.x[1]);
-    compiler_fence();
     if ((threadIdx.x & 63) == 0) lds_puti(&F.x_fill, 0);
     wake_block();
     ++fills;
@@ -1280,6 +1362,7 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, Cha
   compiler_fence();
   if ((threadIdx.x & 63) == 0) lds_puti(&F.x_stage, 0);
   wake_block();
+  service_load_res<MV, OUT_F32>(L, 0, F);
   if (kDouble && num_stages > 1 && !(stage_flags(L, 1) & (kStageXInternal | kStageNorm)))
     service_load_x<MV>(geo_of(L.st[1]), stage_x(L, 1), L.x[kDouble ? 1 : 0]);
   for (int s = 0; s < num_stages; ++s) {
@@ -1315,13 +1398,8 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, Cha
     // s + 1 is shorter than the load.)
     const bool internal = (stage_flags(L, s + 1) & kStageXInternal) != 0;
     const bool norm = (stage_flags(L, s + 1) & kStageNorm) != 0;
-    if constexpr (kDouble) {
-      // A normalized stage s + 1 reads its RMSNorm weight from the buffer
-      // stage s used (free until that staging is done: the prefetch below
-      // writes it only after). Staged before the prefetch's loads are issued,
-      // so the two never hold registers together.
-      if (norm) service_load_gamma(geo_of(L.st[s + 1]), ufl_ptr(L.st[s + 1].norm), L.x[s & 1]);
-    }
+    // (a normalized stage s + 1 parks its norm weights in the buffer stage s
+    // used: the prefetch below writes that buffer only after the staging)
     const bool prefetch = kDouble && s + 2 < num_stages && !(stage_flags(L, s + 2) & (kStageXInternal | kStageNorm));
     XBatch xb;
     if (prefetch) xb_issue<MV>(geo_of(L.st[s + 2]), stage_x(L, s + 2), 0, xb);
@@ -1348,6 +1426,7 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, Cha
     compiler_fence();
     if ((threadIdx.x & 63) == 0) lds_puti(&F.x_stage, s + 1);
     wake_block();
+    service_load_res<MV, OUT_F32>(L, s + 1, F);
     if (prefetch) {
       const Geo g2 = geo_of(L.st[s + 2]);
       xb_store<MV>(g2, 0, xb, L.x[s & 1]);

@@ -270,8 +270,8 @@ q4_status q4_chain_encode(const q4_chain_stage* stages, int32_t num_stages,
  * Silicon", Mimi reuse section). Each is optional per stage or matrix:
  *  - norm_weight (bf16 [k], may be NULL): the stage's x is replaced by its
  *    RMSNorm before the products: inv = 1/sqrt(sum x^2 / k + norm_eps),
- *    x_j -> bf16((x_j * inv) * norm_weight_j), the sum and scaling in fp64
- *    (one activation row only: m_rows == 1);
+ *    x_j -> bf16((x_j * norm_weight_j) * inv), the product exact, the sum of
+ *    squares and the scaling in fp64 (one activation row only: m_rows == 1);
  *  - gated (0 or 1): a stage of exactly two matrices of equal n (gate, up);
  *    its output is silu(gate) * up, silu(t) = t / (1 + exp(-t)), computed in
  *    fp32 from the two fp32 products and written to matrix 0's y (matrix 1's

@@ -243,7 +243,7 @@ def attn_decode(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, pos:
 
 def rmsnorm(x_bits: np.ndarray, g_bits: np.ndarray, eps: float) -> np.ndarray:
     """RMSNorm of each row of bf16 x [m, k] with weight g [k], in double,
-    rounded to bf16: (x * 1/sqrt(mean(x^2) + eps)) * g."""
+    rounded to bf16: (x * g) * 1/sqrt(mean(x^2) + eps), x * g exact."""
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     squeeze = x_bits.ndim == 1
     if squeeze:

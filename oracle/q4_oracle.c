@@ -321,9 +321,11 @@ int oracle_attn_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
 /* RMSNorm of each activation row (the GeekNews summary's audio pipeline and
  * the blog translation's reuse of RMSNorm among the model's parts): for row
  * i of x (bf16 [m][k]) and the norm weight g (bf16 [k]),
- *   inv = 1 / sqrt(sum_j x_j^2 / k + eps),  out_j = bf16((x_j * inv) * g_j)
- * with every operation in double (x_j^2 is exact), then rounded to fp32 and
- * to bf16: the normalized row is a bf16 activation like every other. */
+ *   inv = 1 / sqrt(sum_j x_j^2 / k + eps),  out_j = bf16((x_j * g_j) * inv)
+ * with every operation in double (x_j^2 and x_j * g_j are exact: products of
+ * two bf16 values), then rounded to fp32 and to bf16: the normalized row is a
+ * bf16 activation like every other. The definition is exact arithmetic;
+ * taking the exact product x_j * g_j first leaves one rounding in the scaling. */
 int oracle_rmsnorm(const uint16_t* x, int64_t m, int64_t k, const uint16_t* g, double eps, uint16_t* out) {
   if (!x || !g || !out || m < 0 || k <= 0 || !(eps >= 0.0)) return ORACLE_ERR_ARG;
   for (int64_t i = 0; i < m * k; ++i)
@@ -336,7 +338,7 @@ int oracle_rmsnorm(const uint16_t* x, int64_t m, int64_t k, const uint16_t* g, d
     }
     const double inv = 1.0 / sqrt(ss / (double)k + eps);
     for (int64_t j = 0; j < k; ++j) {
-      const double v = ((double)bf16_value(x[i * k + j]) * inv) * (double)bf16_value(g[j]);
+      const double v = ((double)bf16_value(x[i * k + j]) * (double)bf16_value(g[j])) * inv;
       out[i * k + j] = bf16_round_nearest_even((float)v);
     }
   }
