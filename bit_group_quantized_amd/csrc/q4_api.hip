@@ -65,14 +65,19 @@ int grid_for_groups(int64_t n_groups) {
 struct GemvPlan {
   int c;
   int waves;
+  int u;  // weight rows each lane keeps in flight
   int rows_per_block;
   int blocks;
 };
 
-// weight rows each lane keeps in flight: 8 for one activation row; 2 when
-// up to 4 activation rows hold their slices in registers too
-constexpr int gemv_u(int mv) { return mv == 1 ? 8 : 2; }
-
+// A cold GEMV is one memory round trip per block: the launch is fastest when
+// every block loads its rows in one go and the blocks are many (measured on a
+// 4096x4096 GEMV, graph of launches: 8 rows per lane and 2 blocks per compute
+// unit 6.3 us per call, 4 rows and 4 blocks 5.5 us, 2 rows and 8 blocks
+// 5.3 us). So with one activation row each lane keeps U = 8, 4 or 2 weight
+// rows in flight, the largest that still gives >= 8 blocks per compute unit
+// (2 if none does), and a block takes one load per lane and row; with 2..4
+// activation rows, whose slices also live in registers, U = 2.
 bool plan_gemv(int64_t n, int64_t G, int mv, GemvPlan* p) {
   int best_c = 0, best_s = 0;
   int64_t best_waste = -1;
@@ -89,35 +94,52 @@ bool plan_gemv(int64_t n, int64_t G, int mv, GemvPlan* p) {
     }
   }
   if (best_waste < 0) return false;
-  const int rows_iter = (64 / best_c) * gemv_u(mv);
-  // Aim for >= 2 blocks per CU; each block covers at least one iteration.
-  const int64_t target_blocks = 2 * (int64_t)device_cu_count();
-  int64_t rpb = ceil_div(n, target_blocks);
-  rpb = ceil_div(rpb, rows_iter) * rows_iter;
-  if (rpb < rows_iter) rpb = rows_iter;
+  const int rpi = 64 / best_c;  // row slots per wave
+  const int64_t cus = device_cu_count();
+  int u = 2;
+  if (mv == 1) {
+    const int cand[3] = {8, 4, 2};
+    for (int i = 0; i < 3; ++i) {
+      if (ceil_div(n, (int64_t)rpi * cand[i]) >= 8 * cus) {
+        u = cand[i];
+        break;
+      }
+    }
+  }
+  const int64_t rows_iter = (int64_t)rpi * u;
   // a block's rows are addressed through 32-bit buffer ranges
-  const int64_t max_rpb = ((int64_t)INT32_MAX / (G * 16)) / rows_iter * rows_iter;
-  if (max_rpb < rows_iter) return false;
-  if (rpb > max_rpb) rpb = max_rpb;
+  if (rows_iter * G * 16 > (int64_t)INT32_MAX) return false;
+  const int64_t blocks = ceil_div(n, rows_iter);
+  if (blocks > (int64_t)INT32_MAX) return false;
   p->c = best_c;
   p->waves = best_s;
-  p->rows_per_block = static_cast<int>(rpb);
-  p->blocks = static_cast<int>(ceil_div(n, rpb));
+  p->u = u;
+  p->rows_per_block = static_cast<int>(rows_iter);
+  p->blocks = static_cast<int>(blocks);
   return true;
 }
 
-template <int C, int MV>
-void launch_gemv_c(const GemvPlan& p, bool f32, const uint16_t* x, int64_t k, const uint32_t* packed,
-                   const uint16_t* scales, const uint16_t* biases, int n, int G, void* y,
-                   hipStream_t st) {
+template <int C, int U, int MV>
+void launch_gemv_cu(const GemvPlan& p, bool f32, const uint16_t* x, int64_t k, const uint32_t* packed,
+                    const uint16_t* scales, const uint16_t* biases, int n, int G, void* y, hipStream_t st) {
   const dim3 grid(p.blocks), block(64 * p.waves);
-  constexpr int U = gemv_u(MV);
   if (f32)
     hipLaunchKernelGGL((q4k::gemv_kernel<C, U, MV, true>), grid, block, 0, st, x, k, packed, scales,
                        biases, n, G, p.rows_per_block, y, (int64_t)n);
   else
     hipLaunchKernelGGL((q4k::gemv_kernel<C, U, MV, false>), grid, block, 0, st, x, k, packed, scales,
                        biases, n, G, p.rows_per_block, y, (int64_t)n);
+}
+
+template <int C, int MV>
+void launch_gemv_c(const GemvPlan& p, bool f32, const uint16_t* x, int64_t k, const uint32_t* packed,
+                   const uint16_t* scales, const uint16_t* biases, int n, int G, void* y,
+                   hipStream_t st) {
+  if constexpr (MV == 1) {
+    if (p.u == 8) return launch_gemv_cu<C, 8, MV>(p, f32, x, k, packed, scales, biases, n, G, y, st);
+    if (p.u == 4) return launch_gemv_cu<C, 4, MV>(p, f32, x, k, packed, scales, biases, n, G, y, st);
+  }
+  launch_gemv_cu<C, 2, MV>(p, f32, x, k, packed, scales, biases, n, G, y, st);
 }
 
 template <int MV>

@@ -144,6 +144,21 @@ def test_gemv_sixteen_lane_rows(k, out_dtype):
     _check(y, oracle.matmul(x, P, S, B, k)[0], out_dtype)
 
 
+# With one activation row each lane keeps 8, 4 or 2 weight rows in flight,
+# the most that still gives >= 8 blocks per compute unit (k = 2048: one lane
+# per group, one row per wave): on 256 compute units 16421 rows take 8 (the
+# last block ragged), 8197 rows take 4 and 1000 rows take 2.
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("n", [16421, 8197, 1000])
+def test_gemv_rows_in_flight(n, out_dtype):
+    k = 2048
+    P, S, B = oracle.quantize(_w(n, k, seed=n + 5))
+    x = _x(1, k, seed=n + 6)
+    y = q4.q4_gemv(to_gpu_bf16_bits(x[0]), *upload_quantized(P, S, B), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    _check(y, oracle.matmul(x, P, S, B, k)[0], out_dtype)
+
+
 @pytest.mark.parametrize("m", [1, 2, 4, 7, 16])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("k", [4128, 6400, 8192])
