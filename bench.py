@@ -674,7 +674,7 @@ def bench_other(args, dev) -> int:
         vs = [(_t.randn((heads, cap, d), generator=g, device=dev)).to(_t.bfloat16) for _ in range(layers)]
         qs = [(_t.randn((3, heads, d), generator=g, device=dev)).to(_t.bfloat16) for _ in range(layers)]
         outs = [_t.empty((heads, d), dtype=_t.bfloat16, device=dev) for _ in range(layers)]
-        ws = _t.empty(q4.q4_attn_workspace_bytes(heads, d), dtype=_t.uint8, device=dev)
+        ws = _t.zeros(q4.q4_attn_workspace_bytes(heads, d), dtype=_t.uint8, device=dev)
 
         def calls():
             for li in range(layers):
@@ -695,7 +695,7 @@ def bench_other(args, dev) -> int:
                        "cached_positions": npos, "kv_bytes_per_layer": kv,
                        "executor": f"graph of {layers} x 3 launches (rope + append, partial, combine)"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "attn_partial_kernel",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "attn_decode_kernel",
                          "bytes_per_launch": kv,
                          "timing": "HIP events on the launch stream around graph replays; per layer = step / 32"},
         }

@@ -355,7 +355,7 @@ def q4_attn_decode(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_
         raise ValueError("out must hold heads*D elements")
     need = q4_attn_workspace_bytes(heads, d)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     if workspace.numel() * workspace.element_size() < need:
         raise ValueError(f"workspace must hold {need} bytes")
     _same_device(q, k_new, v_new, k_cache, v_cache, out, workspace)

@@ -393,34 +393,29 @@ namespace {
 // blocks, at least 64 positions each, at most kAttnMaxSplits
 int attn_splits(int64_t heads, int64_t npos) {
   const int64_t cus = device_cu_count();
-  int64_t splits = ceil_div(4 * cus, heads);
+  // (about two blocks per compute unit: measured against one and four, from
+  // 512 to 16384 positions)
+  int64_t splits = ceil_div(2 * cus, heads);
   const int64_t by_len = ceil_div(npos, 64);
   if (splits > by_len) splits = by_len;
   if (splits > q4k::kAttnMaxSplits) splits = q4k::kAttnMaxSplits;
   return static_cast<int>(splits < 1 ? 1 : splits);
 }
 
-int64_t attn_part_offset(int64_t heads, int64_t d) { return ceil_div(heads * d * 2, 256) * 256; }
-
 template <int D>
 q4_status launch_attn(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_cache,
                       uint16_t* v_cache, int heads, int cap, int pos, double theta, void* out, bool f32,
                       unsigned char* ws, hipStream_t st) {
-  uint16_t* q_rot = reinterpret_cast<uint16_t*>(ws);
-  float* part = reinterpret_cast<float*>(ws + attn_part_offset(heads, D));
-  hipLaunchKernelGGL((q4k::attn_rope_kernel<D>), dim3(heads), dim3(D / 2), 0, st, q, k_new, v_new, k_cache, v_cache,
-                     cap, pos, theta, q_rot);
   const int npos = pos + 1;
   const int splits = attn_splits(heads, npos);
   const int chunk = static_cast<int>(ceil_div(npos, splits));
-  constexpr int kR = q4k::kAttnThreads / (D / 8);
-  const size_t shmem = (static_cast<size_t>(chunk) + static_cast<size_t>(kR) * D) * sizeof(float);
-  hipLaunchKernelGGL((q4k::attn_partial_kernel<D>), dim3(heads, splits), dim3(q4k::kAttnThreads), shmem, st, q_rot,
-                     k_cache, v_cache, cap, npos, chunk, splits, part);
+  const dim3 grid(heads, splits), block(q4k::kAttnThreads);
   if (f32)
-    hipLaunchKernelGGL((q4k::attn_combine_kernel<D, true>), dim3(heads), dim3(D), 0, st, part, splits, out);
+    hipLaunchKernelGGL((q4k::attn_decode_kernel<D, true>), grid, block, 0, st, q, k_new, v_new, k_cache, v_cache, cap,
+                       pos, theta, chunk, splits, ws, out);
   else
-    hipLaunchKernelGGL((q4k::attn_combine_kernel<D, false>), dim3(heads), dim3(D), 0, st, part, splits, out);
+    hipLaunchKernelGGL((q4k::attn_decode_kernel<D, false>), grid, block, 0, st, q, k_new, v_new, k_cache, v_cache,
+                       cap, pos, theta, chunk, splits, ws, out);
   return launch_status();
 }
 
@@ -430,7 +425,7 @@ extern "C" {
 
 int64_t q4_attn_workspace_bytes(int64_t heads, int64_t head_dim) {
   if (heads < 1 || head_dim < 1) return -1;
-  return attn_part_offset(heads, head_dim) + heads * q4k::kAttnMaxSplits * (head_dim + 2) * 4;
+  return q4k::attn_ws_part_offset(heads, head_dim) + heads * q4k::kAttnMaxSplits * (head_dim + 2) * 4;
 }
 
 q4_status q4_attn_decode(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_cache,
@@ -449,10 +444,9 @@ q4_status q4_attn_decode(const uint16_t* q, const uint16_t* k_new, const uint16_
   // element counts per head
   if (heads > 65535 || cap > (int64_t)INT32_MAX / head_dim || heads * cap * head_dim > (int64_t)1 << 40)
     return Q4_ERR_UNSUPPORTED;
-  // (a split's scores and partial rows live in LDS: at most 12288 positions
-  // per split keeps them under the default 64 KiB)
+  // (a split's range is addressed through a 32-bit buffer range)
   const int splits = attn_splits(heads, pos + 1);
-  if (ceil_div(pos + 1, splits) > 12288) return Q4_ERR_UNSUPPORTED;
+  if (ceil_div(pos + 1, splits) * head_dim * 2 > (int64_t)INT32_MAX) return Q4_ERR_UNSUPPORTED;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   const bool f32 = out_dtype == Q4_OUT_F32;
   if (head_dim == 128)

@@ -184,11 +184,14 @@ q4_status q4_embed_sum(const int32_t* tokens, int64_t frames, const q4_embed_tab
  *                     row pos is written, rows 0..pos-1 are read
  *   out             : DEVICE [heads][head_dim] of out_dtype
  *   workspace       : DEVICE, 256-byte aligned, >= q4_attn_workspace_bytes()
- *                     bytes, owned by the caller (partial results; no state
- *                     is kept between calls; calls sharing one workspace must
- *                     not overlap in time)
+ *                     bytes, owned by the caller, zero-filled once before its
+ *                     first use (the heads' split counters, which every call
+ *                     leaves at zero; then the rotated q, bf16 [heads][D],
+ *                     and the splits' partial results); calls sharing one
+ *                     workspace must not overlap in time
  * head_dim must be 64 or 128 (Q4_ERR_UNSUPPORTED otherwise); 0 <= pos < cap.
- * Three launches on `stream`; no allocation. */
+ * One launch on `stream` (blocks of a head split the positions; the head's
+ * last block to finish adds the splits up); no allocation. */
 int64_t q4_attn_workspace_bytes(int64_t heads, int64_t head_dim);
 q4_status q4_attn_decode(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_cache,
                          uint16_t* v_cache, int64_t heads, int64_t head_dim, int64_t cap, int64_t pos,

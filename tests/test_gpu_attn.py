@@ -48,8 +48,11 @@ def test_model_heads_match_oracle(pos, out_dtype):
     others = [t for t in range(cap) if t != pos]
     assert np.array_equal(gk[:, others, :], k_cache[:, others, :])
     assert np.array_equal(gv[:, others, :], v_cache[:, others, :])
-    # the rotated query (the workspace's first heads x D bf16 words)
-    assert np.array_equal(ws[: heads * d * 2].cpu().numpy().view(np.uint16).reshape(heads, d), q_rot)
+    # the rotated query (bf16 [heads][D] in the workspace, after the heads'
+    # split counters, which the call leaves at zero)
+    off = -(-heads * 4 // 256) * 256
+    assert not ws[: heads * 4].any()
+    assert np.array_equal(ws[off: off + heads * d * 2].cpu().numpy().view(np.uint16).reshape(heads, d), q_rot)
     k_ref, v_ref = k_cache.copy(), v_cache.copy()
     k_ref[:, pos, :] = k_rot
     v_ref[:, pos, :] = v_new
@@ -88,3 +91,36 @@ def test_full_cache_last_position():
     v_ref[:, pos, :] = v_new
     ref = oracle.attn_decode(oracle.rope(q, pos), k_ref, v_ref, pos)
     assert oracle.floored_rel_err(out_np(out), ref) <= TOL_BF16
+
+
+def test_long_context_several_batches_per_split():
+    """20001 positions: each of the 32 splits of a head takes ~626 positions,
+    five batches of loads with the online softmax carried across them."""
+    heads, d, cap = 32, 128, 20001
+    pos = cap - 1
+    q, k_new, v_new, k_cache, v_cache = _case(heads, d, cap, pos, seed=21)
+    out, _, _, _ = _run(q, k_new, v_new, k_cache, v_cache, pos, torch.float32)
+    k_ref, v_ref = k_cache.copy(), v_cache.copy()
+    k_ref[:, pos, :] = oracle.rope(k_new, pos)
+    v_ref[:, pos, :] = v_new
+    ref = oracle.attn_decode(oracle.rope(q, pos), k_ref, v_ref, pos)
+    assert oracle.floored_rel_err(out_np(out), ref) <= TOL_F32
+
+
+def test_workspace_reused_across_calls():
+    """One workspace for calls with different split counts (1, 32, 2 splits per
+    head): the heads' counters come back to zero after every call."""
+    heads, d, cap = 32, 128, 4096
+    ws = torch.zeros(q4.q4_attn_workspace_bytes(heads, d), dtype=torch.uint8, device="cuda:0")
+    for i, pos in enumerate((10, 4095, 100)):
+        q, k_new, v_new, k_cache, v_cache = _case(heads, d, cap, pos, seed=30 + i)
+        gk, gv = to_gpu_bf16_bits(k_cache), to_gpu_bf16_bits(v_cache)
+        out = q4.q4_attn_decode(to_gpu_bf16_bits(q), to_gpu_bf16_bits(k_new), to_gpu_bf16_bits(v_new), gk, gv, pos,
+                                out_dtype=torch.float32, workspace=ws)
+        torch.cuda.synchronize()
+        assert not ws[: heads * 4].any(), pos
+        k_ref, v_ref = k_cache.copy(), v_cache.copy()
+        k_ref[:, pos, :] = oracle.rope(k_new, pos)
+        v_ref[:, pos, :] = v_new
+        ref = oracle.attn_decode(oracle.rope(q, pos), k_ref, v_ref, pos)
+        assert oracle.floored_rel_err(out_np(out), ref) <= TOL_F32, pos
