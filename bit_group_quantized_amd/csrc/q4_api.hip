@@ -642,6 +642,16 @@ q4_status q4_chain_encode_ex(const q4_chain_stage_ex* stages, int32_t num_stages
   hdr->out_f32 = y_dtype == Q4_OUT_F32 ? 1 : 0;
   hdr->plan_bytes = static_cast<int32_t>(need);
   hdr->rows = m_rows;
+  // The grid barrier: the one whose arrivals wait for no round trip where
+  // stages are short (below 8 MB of weights per stage on average: the
+  // Depformer's 0.7-1.8 MB stages), the L2-flag one for larger stages.
+  {
+    double bytes = 0.0;
+    for (int32_t s2 = 0; s2 < num_stages; ++s2)
+      for (int32_t i = 0; i < stages[s2].num_matrices; ++i)
+        bytes += (double)matrices[stages[s2].first_matrix + i].n * (double)stages[s2].k * 0.625;
+    hdr->barrier = bytes / num_stages < 8.0e6 ? q4k::kBarrierCounters : q4k::kBarrierL2Flags;
+  }
   auto* sd = reinterpret_cast<q4k::ChainStageDesc*>(hdr + 1);
   for (int32_t s = 0; s < num_stages; ++s) {
     const q4_chain_stage_ex& st = stages[s];

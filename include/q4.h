@@ -352,7 +352,7 @@ q4_status q4_chain_run_rows(const void* device_plan, int32_t m_rows, q4_out_dtyp
  * results, and must be serialised by the caller (e.g. one stream). Same
  * arguments otherwise as q4_chain_run_rows; the regular entry points are
  * unchanged. */
-#define Q4_CHAIN_STATIC_SCRATCH_BYTES 2560
+#define Q4_CHAIN_STATIC_SCRATCH_BYTES 4608
 q4_status q4_chain_run_rows_noalloc(const void* device_plan, int32_t m_rows, q4_out_dtype y_dtype,
                                     uint32_t* status_out, void* stream);
 

@@ -477,3 +477,15 @@ def test_chain_encode_ex_residual_dependencies():
     rc, buf = _encode_ex([_sx(X0, 256, 0, 1), _sx(X1, 256, 1, 1)], [_mx(Y0, 32, residual=R), _mx(Y1, 32, residual=R)])
     assert rc == q4.Q4_OK
     assert [_stage_field(buf, s, SYNC_OUT) for s in range(2)] == [0, 0]
+
+
+def test_chain_encoder_picks_the_barrier_by_stage_size():
+    """Plans whose stages average under 8 MB of weights use the device-counter
+    barrier (2), larger ones the L2-flag barrier (1); header word 6."""
+    def barrier(n, k, stages=4):
+        rc, buf = _encode_ex([_sx(0x100000 * (s + 1), k, s, 1) for s in range(stages)],
+                             [_mx(0x4000000 + 0x1000000 * s, n) for s in range(stages)])
+        assert rc == q4.Q4_OK
+        return int.from_bytes(bytes(buf[24:28]), "little")
+    assert barrier(11264, 4096) == 1   # 28.8 MB per stage (a temporal FFN stage)
+    assert barrier(1024, 1024) == 2    # 0.66 MB per stage (a Depformer attention stage)
