@@ -45,8 +45,8 @@ HBM_PEAK_GBS = 8000.0
 # whose hash is recorded: any change to them reports traffic as null until the
 # counters are taken again (profiles/chain_kernel_temporal_step_m1_pmc.md).
 CHAIN_TRAFFIC = {
-    "sources_sha256_16": "878cd6ac2c485552",
-    "fetch_kib": 2014262.2, "fetch_scale": 1048576.0 / 524301.4,
+    "sources_sha256_16": "68b5823c16ca16ad",
+    "fetch_kib": 2014197.9, "fetch_scale": 1048576.0 / 524301.4,
     "write_kib": 4119.8, "write_scale": 1048576.0 / 1048576.0,
 }
 KERNEL_SOURCES = ("q4_chain.h", "q4_kernels.h", "q4_api.hip")
