@@ -642,16 +642,6 @@ q4_status q4_chain_encode_ex(const q4_chain_stage_ex* stages, int32_t num_stages
   hdr->out_f32 = y_dtype == Q4_OUT_F32 ? 1 : 0;
   hdr->plan_bytes = static_cast<int32_t>(need);
   hdr->rows = m_rows;
-  // The grid barrier: the one whose arrivals wait for no round trip where
-  // stages are short (below 8 MB of weights per stage on average: the
-  // Depformer's 0.7-1.8 MB stages), the L2-flag one for larger stages.
-  {
-    double bytes = 0.0;
-    for (int32_t s2 = 0; s2 < num_stages; ++s2)
-      for (int32_t i = 0; i < stages[s2].num_matrices; ++i)
-        bytes += (double)matrices[stages[s2].first_matrix + i].n * (double)stages[s2].k * 0.625;
-    hdr->barrier = bytes / num_stages < 8.0e6 ? q4k::kBarrierCounters : q4k::kBarrierL2Flags;
-  }
   auto* sd = reinterpret_cast<q4k::ChainStageDesc*>(hdr + 1);
   for (int32_t s = 0; s < num_stages; ++s) {
     const q4_chain_stage_ex& st = stages[s];
@@ -702,6 +692,54 @@ q4_status q4_chain_encode_ex(const q4_chain_stage_ex* stages, int32_t num_stages
         if (m.residual && stage_writes(s, m.residual, ybytes * m.n * m_rows)) sd[t].sync_outputs = 1;
       }
     }
+  }
+  // Grid barriers only where a dependency needs one. Stage s starts without
+  // one when, against every stage u since the last barrier, s reads nothing u
+  // writes (its x, its residuals), and writes nothing u reads (x, residuals)
+  // or writes. Blocks then run through such stages at their own pace: a
+  // block's reads of an x or a residual all happen between the barriers that
+  // enclose its stage (an x is prefetched at most two stages ahead, and
+  // before the barrier that opens its stage completes its loads).
+  auto stage_reads = [&](int32_t u, const void* p, int64_t bytes) {
+    if (ranges_overlap(stages[u].x, 2 * stages[u].k * m_rows, p, bytes)) return true;
+    for (int32_t i = 0; i < stages[u].num_matrices; ++i) {
+      const q4_chain_matrix_ex& m = matrices[stages[u].first_matrix + i];
+      if (m.residual && ranges_overlap(m.residual, ybytes * m.n * m_rows, p, bytes)) return true;
+    }
+    return false;
+  };
+  auto depends = [&](int32_t s, int32_t u) {
+    const q4_chain_stage_ex& st = stages[s];
+    if (stage_writes(u, st.x, 2 * st.k * m_rows)) return true;
+    for (int32_t i = 0; i < st.num_matrices; ++i) {
+      const q4_chain_matrix_ex& m = matrices[st.first_matrix + i];
+      if (m.residual && stage_writes(u, m.residual, ybytes * m.n * m_rows)) return true;
+      if (writes(st, i) && (stage_reads(u, m.y, ybytes * m.n * m_rows) || stage_writes(u, m.y, ybytes * m.n * m_rows)))
+        return true;
+    }
+    return false;
+  };
+  int32_t barriers = 0;
+  for (int32_t s = 1, seg = 0; s < num_stages; ++s) {
+    bool need = false;
+    for (int32_t u = seg; u < s && !need; ++u) need = depends(s, u);
+    if (need) {
+      seg = s;
+      ++barriers;
+    } else {
+      sd[s].no_barrier = 1;
+    }
+  }
+  // The grid barrier: the one whose arrivals wait for no round trip where the
+  // stretches between barriers are short (below 8 MB of weights on average:
+  // the Depformer's 0.7-1.8 MB stages, each reading the last one's output),
+  // the L2-flag one for longer stretches.
+  {
+    double bytes = 0.0;
+    for (int32_t s2 = 0; s2 < num_stages; ++s2)
+      for (int32_t i = 0; i < stages[s2].num_matrices; ++i)
+        bytes += (double)matrices[stages[s2].first_matrix + i].n * (double)stages[s2].k * 0.625;
+    hdr->barrier = bytes / (barriers + 1) < 8.0e6 ? q4k::kBarrierCounters : q4k::kBarrierL2Flags;
   }
   auto* md = reinterpret_cast<q4k::ChainMatDesc*>(sd + num_stages);
   for (int32_t i = 0; i < num_matrices; ++i) {

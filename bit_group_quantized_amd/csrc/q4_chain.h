@@ -81,8 +81,12 @@ struct ChainShape {
   static_assert(MV >= 1 && MV <= kMaxRows, "activation rows");
   static constexpr int kTabStages = MV == 1 ? 384 : 128;  // stages of a chain (the plan is copied into LDS)
   static constexpr int kTabMats = MV == 1 ? 768 : 256;    // matrices of a chain
-  static constexpr int kStageUnits = MV == 1 ? 128 : 32;  // units of one matrix per block and stage
+  static constexpr int kStageUnits = MV == 1 ? 64 : 32;  // units of one matrix per block and stage
   static constexpr int kXBuffers = MV == 1 ? 2 : 1;
+  // With two activation buffers a block's waves may start the next stage
+  // while others finish the current one, so the rows of a stage go to one of
+  // two buffers, by the stage's parity.
+  static constexpr int kRowBufs = kXBuffers;
   static constexpr int kMaxGroups = MV == 1 ? 384 : 352;  // k <= 12288 (11264 with several rows)
   static constexpr int kVecWords = kMaxGroups * kXWordsPerGroup + (MV == 1 ? 0 : 4);  // one row (bank shift)
 };
@@ -117,7 +121,8 @@ struct alignas(16) ChainStageDesc {
   const uint16_t* norm;  // RMSNorm weight of x, or null
   double norm_eps;
   int32_t gated;         // outputs silu(matrix 0) * matrix 1, to matrix 0's y
-  int32_t pad[3];
+  int32_t no_barrier;    // no grid barrier before this stage (nothing it touches depends on the stages since the last one)
+  int32_t pad[2];
 };
 struct alignas(16) ChainMatDesc {
   const uint32_t* packed;
@@ -211,7 +216,7 @@ struct StageRec {
   int32_t P, total;           // pieces per unit, items of the block
   uint32_t inv_p;             // ceil(2^16 / P): i / P == (i * inv_p) >> 16 for the small i here
   int32_t flags;              // 1 ragged (16 CH > G), 2 x written in the chain, 4 outputs read in the chain,
-                              // 8 x normalized (RMSNorm), 16 gated output
+                              // 8 x normalized (RMSNorm), 16 gated output, 32 no grid barrier before it
   int32_t U[kMaxMatsPerStage];  // the block's units of each matrix
   int32_t U0[kMaxMatsPerStage];  // the first of them
   const uint16_t* x;
@@ -228,7 +233,8 @@ struct MatRec {
   const void* residual;
 };
 static_assert(sizeof(StageRec) == 96 && sizeof(MatRec) == 48, "table records");
-constexpr int kStageRagged = 1, kStageXInternal = 2, kStageSyncOut = 4, kStageNorm = 8, kStageGated = 16;
+constexpr int kStageRagged = 1, kStageXInternal = 2, kStageSyncOut = 4, kStageNorm = 8, kStageGated = 16,
+              kStageNoBarrier = 32;
 
 // Shared memory: activations and the plan tables (dynamic LDS), and the words
 // that connect the roles (a separate static object).
@@ -242,11 +248,12 @@ struct ChainLds {
 template <int MV>
 struct ChainFlags {
   using S = ChainShape<MV>;
-  float parts[kSplitItems][kUnitRows][MV];   // partial row sums of the pieces of a stage
-  uint32_t pieces_done[kSplitUnits];         // pieces of a unit of the stage finished
-  float out[kMaxMatsPerStage][S::kStageUnits][kUnitRows][MV];  // the stage's finished rows
-  float res[kMaxMatsPerStage][S::kStageUnits][kUnitRows][MV];  // residuals of those rows, loaded early
-  uint32_t done_total;               // stage completions of all compute waves
+  // (per stage parity, kRowBufs == 2)
+  float parts[S::kRowBufs][kSplitItems][kUnitRows][MV];   // partial row sums of the pieces of a stage
+  uint32_t pieces_done[S::kRowBufs][kSplitUnits];         // pieces of a unit of the stage finished
+  float out[S::kRowBufs][kMaxMatsPerStage][S::kStageUnits][kUnitRows][MV];  // the stage's finished rows
+  float res[S::kRowBufs][kMaxMatsPerStage][S::kStageUnits][kUnitRows][MV];  // residuals of those rows, loaded early
+  uint32_t done[2];                  // completions of the even and of the odd stages by the compute waves
   int32_t x_stage;                   // last stage whose activations are in LDS
   int32_t x_fill;                    // stage whose activations the compute waves stage together
   uint32_t x_filled;                 // compute-wave shares of such stagings done so far
@@ -406,10 +413,10 @@ __device__ __forceinline__ void slot_terms(const Slot& d, const uint32_t* xg, in
 // LDS; the service wave stores them. Compute waves issue no global stores at
 // all, so that every step of their loop issues exactly the same loads.
 template <int MV>
-__device__ __forceinline__ void stage_rows(ChainFlags<MV>& F, int mi, int u, int lane, const float (&v)[MV]) {
+__device__ __forceinline__ void stage_rows(ChainFlags<MV>& F, int s, int mi, int u, int lane, const float (&v)[MV]) {
   if (lane < kUnitRows) {
 #pragma unroll
-    for (int i = 0; i < MV; ++i) *(volatile Q4_LDS float*)&F.out[mi][u][lane][i] = v[i];
+    for (int i = 0; i < MV; ++i) *(volatile Q4_LDS float*)&F.out[s % ChainShape<MV>::kRowBufs][mi][u][lane][i] = v[i];
   }
 }
 
@@ -447,7 +454,8 @@ __device__ __forceinline__ bool build_stage_rec(StageRec& r, const ChainStageDes
   r.mat_begin = sd->mat_begin;
   r.x = sd->x;
   r.flags = (r.CH * kChunkGroups != r.G ? kStageRagged : 0) | (sd->x_internal ? kStageXInternal : 0) |
-            (sd->sync_outputs ? kStageSyncOut : 0) | (sd->norm ? kStageNorm : 0) | (sd->gated ? kStageGated : 0);
+            (sd->sync_outputs ? kStageSyncOut : 0) | (sd->norm ? kStageNorm : 0) | (sd->gated ? kStageGated : 0) |
+            (sd->no_barrier ? kStageNoBarrier : 0);
   r.norm = sd->norm;
   r.norm_eps = sd->norm_eps;
   r.pad[0] = r.pad[1] = 0;
@@ -848,8 +856,9 @@ __device__ __forceinline__ void compute_body(int num_stages, int cw, ChainLds<MV
   bool stop = false;  // a wait timed out or another wave failed: finish without waiting
   uint32_t nfill = 0;  // normalized stagings this wave has taken part in
 
-  // stage si.s may start once its activations are in LDS (every wave of the
-  // grid has finished the stages before it)
+  // stage si.s may start once the service wave has published it: its
+  // activations are in LDS, and every wave of the grid has finished the
+  // stages it depends on
   auto enter_stage = [&]() {
     uint32_t spins = 0;
     bool filled = false;
@@ -902,7 +911,7 @@ __device__ __forceinline__ void compute_body(int num_stages, int cw, ChainLds<MV
     while (si.s < s_next) {
       if (!left_counted) {
         compiler_fence();
-        if (lane == 0) lds_add(&F.done_total, 1u);
+        if (lane == 0) lds_add(&F.done[si.s & 1], 1u);
         wake_block();
       }
       left_counted = false;
@@ -926,7 +935,7 @@ __device__ __forceinline__ void compute_body(int num_stages, int cw, ChainLds<MV
     const int s_next = code == kQueueEnd ? num_stages : (int)(code >> 16);
     if (si.s < s_next) {
       compiler_fence();
-      if (lane == 0) lds_add(&F.done_total, 1u);
+      if (lane == 0) lds_add(&F.done[si.s & 1], 1u);
       wake_block();
     }
     return s_next;
@@ -942,18 +951,19 @@ __device__ __forceinline__ void compute_body(int num_stages, int cw, ChainLds<MV
       acc[v] = 0.f;
     }
     if (si.P == 1) {
-      stage_rows(F, it.mi, it.u, lane, tot);
+      stage_rows(F, si.s, it.mi, it.u, lane, tot);
       return;
     }
     // pieces of unit j of the stage are items j P .. j P + P - 1
     const int j = ufl((int)(((uint32_t)i * si.inv_p) >> 16));
+    const int rb = si.s % S::kRowBufs;
     if (lane < kUnitRows) {
 #pragma unroll
-      for (int v = 0; v < MV; ++v) *(volatile Q4_LDS float*)&F.parts[i][lane][v] = tot[v];
+      for (int v = 0; v < MV; ++v) *(volatile Q4_LDS float*)&F.parts[rb][i][lane][v] = tot[v];
     }
     compiler_fence();
     uint32_t old = 0;
-    if (lane == 0) old = lds_add_rtn(&F.pieces_done[j], 1u);
+    if (lane == 0) old = lds_add_rtn(&F.pieces_done[rb][j], 1u);
     old = (uint32_t)__builtin_amdgcn_readfirstlane((int)old);
     if (old == (uint32_t)si.P - 1u) {
       compiler_fence();
@@ -962,10 +972,10 @@ __device__ __forceinline__ void compute_body(int num_stages, int cw, ChainLds<MV
       for (int v = 0; v < MV; ++v) sum[v] = 0.f;
       for (int p = 0; p < si.P; ++p) {
 #pragma unroll
-        for (int v = 0; v < MV; ++v) sum[v] += *(volatile Q4_LDS float*)&F.parts[j * si.P + p][lane & 3][v];
+        for (int v = 0; v < MV; ++v) sum[v] += *(volatile Q4_LDS float*)&F.parts[rb][j * si.P + p][lane & 3][v];
       }
-      stage_rows(F, it.mi, it.u, lane, sum);
-      if (lane == 0) lds_put(&F.pieces_done[j], 0u);
+      stage_rows(F, si.s, it.mi, it.u, lane, sum);
+      if (lane == 0) lds_put(&F.pieces_done[rb][j], 0u);
     }
   };
   // consume the slot in d (the current item's next chunk), then refill d
@@ -1004,7 +1014,7 @@ __device__ __forceinline__ void compute_body(int num_stages, int cw, ChainLds<MV
     // (stages before the wave's first item: entered and counted done in turn)
     while (si.s < s_next) {
       compiler_fence();
-      if (lane == 0) lds_add(&F.done_total, 1u);
+      if (lane == 0) lds_add(&F.done[si.s & 1], 1u);
       wake_block();
       if (si.s + 1 >= num_stages) {
         si.s = num_stages;
@@ -1270,12 +1280,12 @@ __device__ __forceinline__ void service_store(const ChainLds<MV>& L, int s, Chai
       if (orow < n) {
 #pragma unroll
         for (int v = 0; v < MV; ++v) {
-          float val = *(volatile Q4_LDS float*)&F.out[mi][u][r][v];
+          float val = *(volatile Q4_LDS float*)&F.out[s % ChainShape<MV>::kRowBufs][mi][u][r][v];
           if (gated) {
-            const float up = *(volatile Q4_LDS float*)&F.out[1][u][r][v];
+            const float up = *(volatile Q4_LDS float*)&F.out[s % ChainShape<MV>::kRowBufs][1][u][r][v];
             val = val / (1.0f + expf(-val)) * up;
           }
-          if (res) val += *(volatile Q4_LDS float*)&F.res[mi][u][r][v];
+          if (res) val += *(volatile Q4_LDS float*)&F.res[s % ChainShape<MV>::kRowBufs][mi][u][r][v];
           if constexpr (OUT_F32) {
             coh_store(static_cast<uint32_t*>(y) + (int64_t)v * n + orow, __float_as_uint(val));
           } else {
@@ -1288,10 +1298,10 @@ __device__ __forceinline__ void service_store(const ChainLds<MV>& L, int s, Chai
 }
 
 // The residuals of the rows this block stores in stage s, into LDS, as soon
-// as the stage starts (device-coherent loads: every stage before s has made
-// its outputs visible before the barrier that opened s; a later stage that
-// overwrites them waits for this stage's barrier), so that the stores at the
-// end of the stage do not wait for them.
+// as the stage starts (device-coherent loads: a stage before s that writes
+// them has made its outputs visible before a grid barrier that precedes s; a
+// later stage that overwrites them is separated from s by a barrier), so that
+// the stores at the end of the stage do not wait for them.
 template <int MV, bool OUT_F32>
 __device__ __forceinline__ void service_load_res(const ChainLds<MV>& L, int s, ChainFlags<MV>& F) {
   const int lane = threadIdx.x & 63;
@@ -1314,7 +1324,7 @@ __device__ __forceinline__ void service_load_res(const ChainLds<MV>& L, int s, C
             val = __uint_as_float(coh_load(static_cast<const uint32_t*>(res) + (int64_t)v * n + orow));
           else
             val = bf16_to_f32(coh_load16(static_cast<const uint16_t*>(res) + (int64_t)v * n + orow));
-          *(volatile Q4_LDS float*)&F.res[mi][u][r][v] = val;
+          *(volatile Q4_LDS float*)&F.res[s % ChainShape<MV>::kRowBufs][mi][u][r][v] = val;
         }
       }
     }
@@ -1353,11 +1363,35 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, Cha
   if ((threadIdx.x & 63) == 0) lds_puti(&F.x_stage, 0);
   wake_block();
   service_load_res<MV, OUT_F32>(L, 0, F);
-  if (kDouble && num_stages > 1 && !(stage_flags(L, 1) & (kStageXInternal | kStageNorm)))
+  // Activations no stage writes are staged by this wave into the buffer two
+  // stages back (prefetchable). A stage that needs no grid barrier and whose
+  // activations this wave stages is published as soon as they are in LDS
+  // (early): the block's waves that have finished the stage before it go on
+  // at once, while the others finish.
+  auto prefetchable = [&](int t) {
+    return kDouble && t < num_stages && !(stage_flags(L, t) & (kStageXInternal | kStageNorm));
+  };
+  auto early = [&](int t) { return prefetchable(t) && (stage_flags(L, t) & kStageNoBarrier) != 0; };
+  auto publish = [&](int t) {
+    compiler_fence();
+    if ((threadIdx.x & 63) == 0) lds_puti(&F.x_stage, t);
+    wake_block();
+    service_load_res<MV, OUT_F32>(L, t, F);
+  };
+  int published = 0;  // the last stage published
+  if (prefetchable(1)) {
     service_load_x<MV>(geo_of(L.st[1]), stage_x(L, 1), L.x[kDouble ? 1 : 0]);
+    if (early(1)) publish(published = 1);
+  }
+  // Outputs a later stage reads, stored since the last grid barrier: the next
+  // barrier waits for their stores before arriving.
+  bool unsynced = false;
   for (int s = 0; s < num_stages; ++s) {
     uint32_t spins = 0;
-    while ((int)(lds_get(&F.done_total) - (uint32_t)(kComputeWaves * (s + 1))) < 0) {
+    // every compute wave has finished stage s (a wave can be at most one
+    // stage ahead of the block's slowest, so the count of stage s's parity
+    // holds no completions of stage s + 2 yet)
+    while ((int)(lds_get(&F.done[s & 1]) - (uint32_t)(kComputeWaves * (s / 2 + 1))) < 0) {
       nap();
       if (lds_get(&F.abort) != 0u || ++spins > kSpinLimit) {
         service_fail(ws, F, 1u);
@@ -1369,11 +1403,23 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, Cha
       service_store<MV, OUT_F32>(L, s, F);
       break;
     }
-    if (stage_flags(L, s) & kStageSyncOut) {
+    const bool sync_out = (stage_flags(L, s) & kStageSyncOut) != 0;
+    // Stage s + 1 runs already (published early: no barrier between), or it
+    // waits for this transition: a grid barrier, or activations staged by the
+    // compute waves together. Stage s + 1 needs no grid barrier where nothing
+    // it reads or writes depends on the stages since the last one (the
+    // encoder checks).
+    const bool ahead = published > s;
+    const bool barrier = !ahead && (stage_flags(L, s + 1) & kStageNoBarrier) == 0;
+    if (!barrier) {
+      service_store<MV, OUT_F32>(L, s, F);
+      unsynced = unsynced || sync_out;
+    } else if (sync_out || unsynced) {
       // outputs read by a later stage must be visible before the barrier
       service_store<MV, OUT_F32>(L, s, F);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       service_arrive<BAR>(ws, gs);
+      unsynced = false;
     } else {
       // arrive first: the stores then overlap the wait instead of delaying
       // the arrival
@@ -1382,45 +1428,45 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, Cha
     }
     // Activations no stage writes, for stage s + 2, go to the buffer stage s
     // used (every compute wave has finished stage s): the loads of their first
-    // batch are issued now and arrive during the barrier; the batch is written
-    // and the rest fetched once stage s + 1 is published. (Loading them only
-    // after publishing would hold back this wave's next arrival whenever stage
-    // s + 1 is shorter than the load.)
-    const bool internal = (stage_flags(L, s + 1) & kStageXInternal) != 0;
-    const bool norm = (stage_flags(L, s + 1) & kStageNorm) != 0;
-    // (a normalized stage s + 1 parks its norm weights in the buffer stage s
-    // used: the prefetch below writes that buffer only after the staging)
-    const bool prefetch = kDouble && s + 2 < num_stages && !(stage_flags(L, s + 2) & (kStageXInternal | kStageNorm));
+    // batch are issued now and arrive during the barrier, if any; the batch is
+    // written and the rest fetched once stage s + 1 is published. (Loading
+    // them only after publishing would hold back this wave's next arrival
+    // whenever stage s + 1 is shorter than the load.)
+    const bool prefetch = prefetchable(s + 2);
     XBatch xb;
     if (prefetch) xb_issue<MV>(geo_of(L.st[s + 2]), stage_x(L, s + 2), 0, xb);
-    // The compute waves stage the next activations together where they would
-    // otherwise wait for this wave to do it alone: with one buffer (the
-    // block's compute waves have all finished stage s, so it is free; the
-    // activations no stage writes are staged during the barrier), and for
-    // activations written in the chain (after the barrier).
-    const bool shared_fill = !kDouble || internal || norm;
-    compiler_fence();
-    if (shared_fill && !internal) {
-      if ((threadIdx.x & 63) == 0) lds_puti(&F.x_fill, s + 1);
-      wake_block();
-    }
-    if (!service_wait<BAR>(ws, F, gs)) return;
-    if (shared_fill) {
-      if (internal) {
+    if (!ahead) {
+      const bool internal = (stage_flags(L, s + 1) & kStageXInternal) != 0;
+      const bool norm = (stage_flags(L, s + 1) & kStageNorm) != 0;
+      // (a normalized stage s + 1 parks its norm weights in the buffer stage
+      // s used: the prefetch writes that buffer only after the staging)
+      // The compute waves stage the next activations together where they
+      // would otherwise wait for this wave to do it alone: with one buffer
+      // (the block's compute waves have all finished stage s, so it is free;
+      // the activations no stage writes are staged during the barrier), and
+      // for activations written in the chain (after the barrier).
+      const bool shared_fill = !kDouble || internal || norm;
+      compiler_fence();
+      if (shared_fill && !internal) {
         if ((threadIdx.x & 63) == 0) lds_puti(&F.x_fill, s + 1);
         wake_block();
       }
-      ++fills;
-      if (!wait_filled()) return;
+      if (barrier && !service_wait<BAR>(ws, F, gs)) return;
+      if (shared_fill) {
+        if (internal) {
+          if ((threadIdx.x & 63) == 0) lds_puti(&F.x_fill, s + 1);
+          wake_block();
+        }
+        ++fills;
+        if (!wait_filled()) return;
+      }
+      publish(published = s + 1);
     }
-    compiler_fence();
-    if ((threadIdx.x & 63) == 0) lds_puti(&F.x_stage, s + 1);
-    wake_block();
-    service_load_res<MV, OUT_F32>(L, s + 1, F);
     if (prefetch) {
       const Geo g2 = geo_of(L.st[s + 2]);
       xb_store<MV>(g2, 0, xb, L.x[s & 1]);
       service_load_x<MV>(g2, stage_x(L, s + 2), L.x[s & 1], 64 * kXBatch);
+      if (early(s + 2)) publish(published = s + 2);
     }
   }
 }
@@ -1436,10 +1482,10 @@ chain_kernel(const ChainHeader* __restrict__ plan, uint32_t* __restrict__ ws, ui
   ChainLds<MV>& L = *reinterpret_cast<ChainLds<MV>*>(lds_raw);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  if (threadIdx.x < kSplitUnits) F.pieces_done[threadIdx.x] = 0u;
+  if (threadIdx.x < ChainShape<MV>::kRowBufs * kSplitUnits) (&F.pieces_done[0][0])[threadIdx.x] = 0u;
   for (int e = threadIdx.x; e < S::kTabStages; e += blockDim.x) F.claim[e] = 0u;
   if (threadIdx.x == 0) {
-    F.done_total = 0u;
+    F.done[0] = F.done[1] = 0u;
     F.x_stage = -1;
     F.x_fill = -1;
     F.x_filled = 0u;

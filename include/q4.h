@@ -209,10 +209,15 @@ q4_status q4_attn_decode(const uint16_t* q, const uint16_t* k_new, const uint16_
  * up, and the gated product feeds down. A stage is one activation vector x
  * (bf16 [k]) multiplied by one or more matrices that share it:
  *   y_i[r] = sum_k w_hat_i[r][k] * x[k]   for every matrix i of the stage.
- * Stages run in order: no product of stage s+1 starts before every output of
- * stage s is written and visible, so a stage's x may be (the bf16 output of)
- * an earlier stage. Weight bytes of later stages are fetched ahead of that
- * point (weights never depend on activations).
+ * Stages run in order as far as memory can tell: a stage that reads what an
+ * earlier stage writes (its x, a residual), or writes what an earlier stage
+ * reads or writes, starts only after that stage's outputs are written and
+ * visible everywhere (a grid barrier, placed by the encoder), so a stage's x
+ * may be (the bf16 output of) an earlier stage. Stages with no such
+ * dependency run without a barrier between them: each block goes on to its
+ * share of the next stage as soon as it has finished its share of the last.
+ * Weight bytes of later stages are fetched ahead of either point (weights
+ * never depend on activations).
  *
  * Use: describe the chain with host arrays, q4_chain_encode() it into a host
  * buffer of q4_chain_plan_bytes(), copy that buffer to device memory
@@ -222,8 +227,8 @@ q4_status q4_attn_decode(const uint16_t* q, const uint16_t* k_new, const uint16_
  * stage needs >= 1 matrix, all of that stage's k. Limits of the executor
  * (Q4_ERR_UNSUPPORTED from q4_chain_encode otherwise): at most 384 stages and
  * 768 matrices per chain (the block copies the plan into LDS), at most 4
- * matrices per stage, k <= 12288, n < 2^22, at most 128
- * units of 4 rows of one matrix per block (n <= 512 x the number of compute
+ * matrices per stage, k <= 12288, n < 2^22, at most 64
+ * units of 4 rows of one matrix per block (n <= 256 x the number of compute
  * units), scales and biases 16-byte aligned, no stage's output may overlap
  * its own input, and no two outputs of one stage may overlap. Outputs of
  * different stages may overlap: the later stage's values are the ones left

@@ -489,3 +489,50 @@ def test_chain_encoder_picks_the_barrier_by_stage_size():
         return int.from_bytes(bytes(buf[24:28]), "little")
     assert barrier(11264, 4096) == 1   # 28.8 MB per stage (a temporal FFN stage)
     assert barrier(1024, 1024) == 2    # 0.66 MB per stage (a Depformer attention stage)
+
+
+NO_BARRIER = 52  # byte offset in a stage record of the plan
+
+
+def test_chain_encoder_places_barriers_only_at_dependencies():
+    """Stage s starts without a grid barrier unless it reads what a stage since
+    the last barrier writes (x or residual), or writes what such a stage reads
+    (x or residual) or writes. Independent stages, as in the temporal step with
+    activations drawn per stage, run with none."""
+    X0, X1, X2, X3, R, Y0, Y1, Y2, Y3 = (0x100000 * i for i in range(1, 10))
+
+    def flags(xs, ys, res=(None,) * 4):
+        rc, buf = _encode_ex([_sx(x, 256, i, 1) for i, x in enumerate(xs)],
+                             [_mx(y, 128, residual=r) for y, r in zip(ys, res)])
+        assert rc == q4.Q4_OK
+        return [_stage_field(buf, s, NO_BARRIER) for s in range(len(xs))]
+
+    # independent stages: no barrier anywhere
+    assert flags([X0, X1, X2, X3], [Y0, Y1, Y2, Y3]) == [0, 1, 1, 1]
+    # stage 2 reads stage 1's output: a barrier before stage 2 only
+    assert flags([X0, X1, Y1, X3], [Y0, Y1, Y2, Y3]) == [0, 1, 0, 1]
+    # stage 3 reads stage 0's output; a barrier before stage 2 already separates them
+    assert flags([X0, X1, Y1, Y0], [Y0, Y1, Y2, Y3]) == [0, 1, 0, 1]
+    # ... without it, stage 3 needs its own
+    assert flags([X0, X1, X2, Y0], [Y0, Y1, Y2, Y3]) == [0, 1, 1, 0]
+    # stage 2 overwrites stage 0's input (a write after a read)
+    assert flags([X0, X1, X2, X3], [Y0, Y1, X0, Y3]) == [0, 1, 0, 1]
+    # stage 3 overwrites stage 1's output (a write after a write)
+    assert flags([X0, X1, X2, X3], [Y0, Y1, Y2, Y1]) == [0, 1, 1, 0]
+    # stage 1 adds a residual stage 0 writes; stage 3 overwrites a residual stage 2 reads
+    assert flags([X0, X1, X2, X3], [Y0, Y1, Y2, R], res=(None, Y0, R, None)) == [0, 0, 1, 0]
+    # a residual no stage writes, read by two stages: no barrier
+    assert flags([X0, X1, X2, X3], [Y0, Y1, Y2, Y3], res=(R, None, R, None)) == [0, 1, 1, 1]
+
+
+def test_chain_encoder_barrier_kind_with_dependent_stages():
+    """Counted per stretch between barriers: a chain whose every stage reads
+    the last one's output, 0.66 MB per stage, takes the device-counter barrier
+    (2); independent stages of 28.8 MB, one stretch of 115 MB, the L2-flag
+    barrier (1)."""
+    ys = [0x4000000 + 0x1000000 * s for s in range(4)]
+    rc, buf = _encode_ex([_sx(0x100000 if s == 0 else ys[s - 1], 1024, s, 1) for s in range(4)],
+                         [_mx(ys[s], 1024) for s in range(4)])
+    assert rc == q4.Q4_OK
+    assert int.from_bytes(bytes(buf[24:28]), "little") == 2
+    assert [_stage_field(buf, s, NO_BARRIER) for s in range(4)] == [0, 0, 0, 0]

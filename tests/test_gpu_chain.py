@@ -108,6 +108,45 @@ def test_dependent_chain_reads_previous_outputs():
             xr = y_ref[None, :]
 
 
+def test_interleaved_chains_barrier_every_other_stage():
+    """Two dependent chains interleaved: stage s reads the output of stage
+    s - 2, so the encoder puts a grid barrier before every even stage from 2
+    on and none before the odd ones; the outputs stored in a stretch without a
+    barrier (stage s - 2 before stage s - 1) must still be complete when the
+    next barrier opens stage s. Selector matrices make the result bit-exact;
+    outputs start poisoned."""
+    shapes = [(4096, 4096), (11264, 4096), (4096, 4096), (4096, 11264), (1024, 4096), (4096, 4096),
+              (4096, 1024), (4096, 4096), (4096, 4096), (1024, 4096)]
+    r = np.random.default_rng(12)
+    x0 = [workloads.bf16_bits_rne(r.integers(-64, 65, size=shapes[c][1]).astype(np.float32)) for c in range(2)]
+    host, stages = [], []
+    xs = [to_gpu_bf16_bits(x0[0]), to_gpu_bf16_bits(x0[1])]
+    for s, (n, k) in enumerate(shapes):
+        P, S, B = _selector_matrix(n, k, r.integers(0, k, size=n))
+        host.append((P, S, B))
+        y = torch.full((n,), 1.0e4, dtype=torch.bfloat16, device=xs[0].device)  # poison
+        stages.append(Stage(xs[s % 2], [Q4Matrix(*upload_quantized(P, S, B))], [y]))
+        xs[s % 2] = y
+    chain = Chain(stages, torch.bfloat16)
+    chain.run_chain()
+    torch.cuda.synchronize()
+    rec = chain._plan.device_plan.cpu().numpy()
+    no_barrier = [int(rec[64 + 64 * s + 52]) for s in range(len(shapes))]  # the stage records' flag word
+    assert no_barrier == [0, 1] * (len(shapes) // 2)
+    for rep in range(3):
+        for st in stages:
+            st.outs[0].fill_(1.0e4)
+        chain.run_chain()
+        torch.cuda.synchronize()
+        assert chain.chain_status() == 0
+        xr = [x0[0][None, :], x0[1][None, :]]
+        for i, (n, k) in enumerate(shapes):
+            P, S, B = host[i]
+            y_ref = oracle.output_bits_bf16(oracle.matmul(xr[i % 2], P, S, B, k)[0])
+            assert np.array_equal(bf16_bits_np(stages[i].outs[0]), y_ref), (rep, i)
+            xr[i % 2] = y_ref[None, :]
+
+
 def test_chain_matches_per_call_launches():
     """The chain and one q4_gemv launch per matrix compute the same products."""
     specs = [(4096, [4096, 4096]), (11264, [4096]), (4096, [11264])]
