@@ -350,6 +350,10 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--spin-up", type=float, default=0.5, metavar="SECONDS",
+                    help="untimed calls for this long before the warmup steps of each timed workload: the "
+                         "GPU raises its clocks over ~0.1 s of sustained load (steps timed right after the "
+                         "host-side set-up run up to 15%% slower)")
     ap.add_argument("--mode", choices=("chain", "launches"), default="chain")
     ap.add_argument("--workload", choices=("step", "depformer", "gemm", "gemv", "layer", "embed", "attn"),
                     default="step",
@@ -383,6 +387,8 @@ def main(argv=None) -> int:
                          "bitwise_not, MIB MiB read + MIB MiB written each) so that HBM byte "
                          "counters can be scaled against a kernel of known traffic")
     args = ap.parse_args(argv)
+    global SPIN_UP_S
+    SPIN_UP_S = max(0.0, args.spin_up)
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the step "
@@ -434,6 +440,7 @@ def main(argv=None) -> int:
             chain.run_launches()
         run = g.replay
 
+    spin_up(run, args.spin_up)
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
@@ -508,7 +515,7 @@ def main(argv=None) -> int:
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": args.warmup, "spin_up_s": args.spin_up,
         "ms_per_step": round(ms_per_step, 4),
         "us_per_step": round(ms_per_step * 1e3, 1),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
@@ -547,10 +554,28 @@ def main(argv=None) -> int:
     return 0
 
 
-def time_replays(run, steps: int, warmup: int):
-    """HIP events on the launch stream around each of `steps` calls of run()."""
+def spin_up(run, seconds: float) -> None:
+    """Call run() for `seconds` of wall time (untimed; at least once)."""
     import torch
 
+    t_end = time.time() + seconds
+    while True:
+        for _ in range(8):
+            run()
+        torch.cuda.synchronize()
+        if time.time() >= t_end:
+            return
+
+
+SPIN_UP_S = 0.5  # set from --spin-up in main()
+
+
+def time_replays(run, steps: int, warmup: int):
+    """HIP events on the launch stream around each of `steps` calls of run(),
+    after SPIN_UP_S seconds of untimed calls and `warmup` more."""
+    import torch
+
+    spin_up(run, SPIN_UP_S)
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
@@ -613,7 +638,7 @@ def bench_other(args, dev) -> int:
         achieved = (wbytes / copies) / (per_call_us * 1e-6) / 1e9
         result = {
             "metric": "packed-weight GB/s (% HBM peak) + us per 4096x4096 GEMV, M=1",
-            "value": round(achieved, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "value": round(achieved, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "spin_up_s": args.spin_up,
             "us_per_gemv": round(per_call_us, 2), "pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": "gemv_4096x4096_m1", "n": n, "k": k, "m": 1, "group": 32, "copies": copies,
@@ -651,7 +676,7 @@ def bench_other(args, dev) -> int:
         gbs = gathered / (us * 1e-6) / 1e9
         result = {
             "metric": "us per packed-embedding gather + 17-stream sum (GB/s of packed rows read)",
-            "value": round(us, 3), "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "value": round(us, 3), "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "spin_up_s": args.spin_up,
             "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": f"embed_sum_{frames}_frames", "streams": len(shapes), "dim": workloads.HIDDEN,
                        "text_rows": workloads.TEXT_VOCAB, "audio_rows": workloads.AUDIO_CODEBOOK, "frames": frames,
@@ -687,7 +712,7 @@ def bench_other(args, dev) -> int:
         gbs = kv / (us * 1e-6) / 1e9
         result = {
             "metric": "KV-cache GB/s (% HBM peak) + us per layer of decode attention, M=1",
-            "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "spin_up_s": args.spin_up,
             "us_per_layer": round(us, 2), "us_per_step": round(ms * 1e3, 1),
             "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
@@ -719,7 +744,7 @@ def bench_other(args, dev) -> int:
         gbs = wbytes / (ms * 1e-3) / 1e9
         result = {
             "metric": "packed-weight GB/s (% HBM peak) + us per temporal layer (7 GEMVs), M=1",
-            "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "spin_up_s": args.spin_up,
             "us_per_layer": round(per_layer_us, 2), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": "temporal_layer_m1", "hidden": workloads.HIDDEN, "ffn": workloads.FFN, "m": 1,
@@ -800,7 +825,7 @@ def bench_other(args, dev) -> int:
     achieved = (wbytes / launches) / ((ms / launches) * 1e-3) / 1e9
     result = {
         "metric": f"packed-weight GB/s (% HBM peak) + us per {unit_name}",
-        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "spin_up_s": args.spin_up,
         f"ms_per_{unit_name}": round(ms, 4), f"us_per_{unit_name}": round(ms * 1e3, 1),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": config,

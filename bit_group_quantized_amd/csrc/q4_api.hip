@@ -693,6 +693,34 @@ q4_status q4_chain_encode_ex(const q4_chain_stage_ex* stages, int32_t num_stages
       }
     }
   }
+  // One activation row: each stage's activations (and a normalized stage's
+  // norm weights after them) get a region of the kernel's LDS arena, placed
+  // one after another round it; xwait names the last earlier stage whose
+  // region overlaps, which must be finished before these activations are
+  // staged. Several rows share one buffer.
+  {
+    const int32_t arena = q4k::ChainShape<1>::kXBuffers * q4k::ChainShape<1>::kVecWords;
+    int32_t next = 0;
+    for (int32_t t = 0; t < num_stages; ++t) {
+      if (m_rows != 1) {
+        sd[t].xoff = 0;
+        sd[t].xwait = t - 1;
+        continue;
+      }
+      const int32_t size = (stages[t].norm_weight ? 2 : 1) * q4k::kChunkGroups * sd[t].CH * q4k::kXWordsPerGroup;
+      if (next + size > arena) next = 0;
+      sd[t].xoff = next;
+      sd[t].xwait = -1;
+      for (int32_t u = t - 1; u >= 0; --u) {
+        const int32_t us = (stages[u].norm_weight ? 2 : 1) * q4k::kChunkGroups * sd[u].CH * q4k::kXWordsPerGroup;
+        if (sd[u].xoff < next + size && next < sd[u].xoff + us) {
+          sd[t].xwait = u;
+          break;
+        }
+      }
+      next += size;
+    }
+  }
   // Grid barriers only where a dependency needs one. Stage s starts without
   // one when, against every stage u since the last barrier, s reads nothing u
   // writes (its x, its residuals), and writes nothing u reads (x, residuals)

@@ -52,7 +52,7 @@ constexpr int kChainWaves = 1 + kComputeWaves;
 constexpr int kMaxMatsPerStage = 4;
 constexpr int kUnitRows = 4;      // rows per unit
 constexpr int kMaxPieces = 8;     // pieces a unit's chunks may be cut into
-constexpr int kMinPieceChunks = 4;  // chunks a piece keeps at least (shorter pieces cost more to close than they balance)
+constexpr int kMinPieceChunks = 2;  // chunks a piece keeps at least (shorter pieces cost more to close than they balance)
 #ifndef Q4_CHAIN_SPLIT_UNITS
 #define Q4_CHAIN_SPLIT_UNITS 8
 #endif
@@ -81,15 +81,19 @@ struct ChainShape {
   static_assert(MV >= 1 && MV <= kMaxRows, "activation rows");
   static constexpr int kTabStages = MV == 1 ? 384 : 128;  // stages of a chain (the plan is copied into LDS)
   static constexpr int kTabMats = MV == 1 ? 768 : 256;    // matrices of a chain
-  static constexpr int kStageUnits = MV == 1 ? 64 : 32;  // units of one matrix per block and stage
+  static constexpr int kStageUnits = 32;  // units of one matrix per block and stage
   static constexpr int kXBuffers = MV == 1 ? 2 : 1;
-  // With two activation buffers a block's waves may start the next stage
-  // while others finish the current one, so the rows of a stage go to one of
-  // two buffers, by the stage's parity.
-  static constexpr int kRowBufs = kXBuffers;
+  // With one row the activations of successive stages go to regions of an
+  // LDS arena the size of two of the widest, placed one after another round
+  // it by the encoder; the service wave stages a stage's activations as soon
+  // as the stages that used its region are done, up to kRowBufs - 1 stages
+  // ahead of the block's slowest wave, whose rows go to kRowBufs buffers in
+  // turn. With several rows one buffer serves every stage.
+  static constexpr int kRowBufs = MV == 1 ? 4 : 1;
   static constexpr int kMaxGroups = MV == 1 ? 384 : 352;  // k <= 12288 (11264 with several rows)
   static constexpr int kVecWords = kMaxGroups * kXWordsPerGroup + (MV == 1 ? 0 : 4);  // one row (bank shift)
 };
+constexpr int kDoneSlots = 4;  // completion counts, by stage mod 4 (no wave runs more than 3 stages ahead)
 constexpr int kMaxXcc = 16;
 constexpr uint32_t kSpinLimit = 1u << 22;
 
@@ -122,7 +126,8 @@ struct alignas(16) ChainStageDesc {
   double norm_eps;
   int32_t gated;         // outputs silu(matrix 0) * matrix 1, to matrix 0's y
   int32_t no_barrier;    // no grid barrier before this stage (nothing it touches depends on the stages since the last one)
-  int32_t pad[2];
+  int32_t xoff;          // word offset of the stage's activations in the LDS arena (one row)
+  int32_t xwait;         // the last earlier stage whose arena region overlaps this one's, or -1
 };
 struct alignas(16) ChainMatDesc {
   const uint32_t* packed;
@@ -222,7 +227,7 @@ struct StageRec {
   const uint16_t* x;
   const uint16_t* norm;       // RMSNorm weight (flag 8)
   double norm_eps;
-  int32_t pad[2];
+  int32_t xoff, xwait;        // the stage's region of the activation arena (ChainStageDesc)
 };
 struct MatRec {
   const uint32_t* packed;
@@ -241,19 +246,19 @@ constexpr int kStageRagged = 1, kStageXInternal = 2, kStageSyncOut = 4, kStageNo
 template <int MV>
 struct ChainLds {
   using S = ChainShape<MV>;
-  uint32_t x[S::kXBuffers][MV * S::kVecWords];  // activations: per buffer, row v at v * kVecWords
+  uint32_t x[S::kXBuffers * MV * S::kVecWords];  // activations: a stage's at its offset, row v at v * kVecWords
   StageRec st[S::kTabStages];
   MatRec mt[S::kTabMats];
 };
 template <int MV>
 struct ChainFlags {
   using S = ChainShape<MV>;
-  // (per stage parity, kRowBufs == 2)
+  // (buffer s mod kRowBufs for stage s)
   float parts[S::kRowBufs][kSplitItems][kUnitRows][MV];   // partial row sums of the pieces of a stage
   uint32_t pieces_done[S::kRowBufs][kSplitUnits];         // pieces of a unit of the stage finished
   float out[S::kRowBufs][kMaxMatsPerStage][S::kStageUnits][kUnitRows][MV];  // the stage's finished rows
   float res[S::kRowBufs][kMaxMatsPerStage][S::kStageUnits][kUnitRows][MV];  // residuals of those rows, loaded early
-  uint32_t done[2];                  // completions of the even and of the odd stages by the compute waves
+  uint32_t done[kDoneSlots];         // completions of the stages s = j mod kDoneSlots by the compute waves
   int32_t x_stage;                   // last stage whose activations are in LDS
   int32_t x_fill;                    // stage whose activations the compute waves stage together
   uint32_t x_filled;                 // compute-wave shares of such stagings done so far
@@ -458,7 +463,8 @@ __device__ __forceinline__ bool build_stage_rec(StageRec& r, const ChainStageDes
             (sd->no_barrier ? kStageNoBarrier : 0);
   r.norm = sd->norm;
   r.norm_eps = sd->norm_eps;
-  r.pad[0] = r.pad[1] = 0;
+  r.xoff = MV == 1 ? sd->xoff : 0;
+  r.xwait = MV == 1 ? sd->xwait : -1;
   int units = 0;
   bool fits = true;
   for (int mi = 0; mi < kMaxMatsPerStage; ++mi) {
@@ -466,7 +472,6 @@ __device__ __forceinline__ bool build_stage_rec(StageRec& r, const ChainStageDes
     const BlockRange br = block_range(nunits);
     r.U[mi] = br.count;
     r.U0[mi] = br.u0;
-    r.pad[0] = r.pad[1] = 0;
     // (block 0 has the most units; every block takes the same decision)
     fits = fits && (nunits + (int)gridDim.x - 1) / (int)gridDim.x <= ChainShape<MV>::kStageUnits;
     units += r.U[mi];
@@ -484,6 +489,10 @@ template <int MV>
 __device__ __forceinline__ int stage_flags(const ChainLds<MV>& L, int s) { return ufl(L.st[s].flags); }
 template <int MV>
 __device__ __forceinline__ const uint16_t* stage_x(const ChainLds<MV>& L, int s) { return ufl_ptr(L.st[s].x); }
+// the LDS region of stage s's activations (and, after them, a normalized
+// stage's norm weights)
+template <int MV>
+__device__ __forceinline__ uint32_t* stage_xbuf(ChainLds<MV>& L, int s) { return L.x + ufl(L.st[s].xoff); }
 template <int MV>
 __device__ __forceinline__ void stage_info(StageInfo& si, const ChainLds<MV>& L, int s) {
   const StageRec& r = L.st[s];
@@ -722,9 +731,9 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 // (64 cw + lane) & 1 of group (64 cw + lane) >> 1, 16 values; every group of
 // the padded row has its lanes (2 * 16 CH <= 768 < 64 kComputeWaves).
 //  1. The lane loads its 16 values and their 16 norm weights and parks both,
-//     raw, in their slots: the values in the stage's activation buffer, the
-//     weights in the other one (free: every wave of the block has finished the
-//     stage before, and the next prefetch into it waits for this staging).
+//     raw, in their slots: the values in the stage's activation region, the
+//     weights in the same layout right after it (the encoder gives a
+//     normalized stage a region twice the size).
 //     The squares (exact in fp32) are summed in fp64; the wave's sum goes to
 //     LDS and, once all kComputeWaves shares are there, every wave adds them
 //     in wave order, so every block forms the same total.
@@ -867,7 +876,7 @@ __device__ __forceinline__ void compute_body(int num_stages, int cw, ChainLds<MV
         // the service wave asks the compute waves to stage these activations
         compiler_fence();
         const Geo g = geo_of(L.st[si.s]);
-        uint32_t* buf = L.x[S::kXBuffers == 2 ? si.s & 1 : 0];
+        uint32_t* buf = stage_xbuf(L, si.s);
         const int fl = stage_flags(L, si.s);
         if constexpr (MV == 1) {
           // (one activation row: the service wave stages activations no stage
@@ -875,7 +884,7 @@ __device__ __forceinline__ void compute_body(int num_stages, int cw, ChainLds<MV
           // and the ones written in the chain, always with coherent loads)
           if (NORM && (fl & kStageNorm)) {
             if (!fill_x_norm(g, stage_x(L, si.s), ufl_ptr(L.st[si.s].norm), L.st[si.s].norm_eps, buf,
-                             L.x[(si.s & 1) ^ 1], cw, lane, F, nfill))
+                             buf + kChunkGroups * g.CH * kXWordsPerGroup, cw, lane, F, nfill))
               stop = true;
           } else {
             fill_x_share<MV, true>(g, stage_x(L, si.s), buf, cw, lane);
@@ -896,7 +905,7 @@ __device__ __forceinline__ void compute_body(int num_stages, int cw, ChainLds<MV
       stop = lds_get(&F.abort) != 0u || ++spins > kSpinLimit;
     }
     compiler_fence();
-    x0 = L.x[S::kXBuffers == 2 ? si.s & 1 : 0] + vown * S::kVecWords + col * kXWordsPerGroup;
+    x0 = stage_xbuf(L, si.s) + vown * S::kVecWords + col * kXWordsPerGroup;
   };
   // move to the wave's next claimed item, closing the stages it leaves (every
   // stage is counted once, after the wave's rows of it are in LDS) and
@@ -911,7 +920,7 @@ __device__ __forceinline__ void compute_body(int num_stages, int cw, ChainLds<MV
     while (si.s < s_next) {
       if (!left_counted) {
         compiler_fence();
-        if (lane == 0) lds_add(&F.done[si.s & 1], 1u);
+        if (lane == 0) lds_add(&F.done[si.s % kDoneSlots], 1u);
         wake_block();
       }
       left_counted = false;
@@ -935,7 +944,7 @@ __device__ __forceinline__ void compute_body(int num_stages, int cw, ChainLds<MV
     const int s_next = code == kQueueEnd ? num_stages : (int)(code >> 16);
     if (si.s < s_next) {
       compiler_fence();
-      if (lane == 0) lds_add(&F.done[si.s & 1], 1u);
+      if (lane == 0) lds_add(&F.done[si.s % kDoneSlots], 1u);
       wake_block();
     }
     return s_next;
@@ -1014,7 +1023,7 @@ __device__ __forceinline__ void compute_body(int num_stages, int cw, ChainLds<MV
     // (stages before the wave's first item: entered and counted done in turn)
     while (si.s < s_next) {
       compiler_fence();
-      if (lane == 0) lds_add(&F.done[si.s & 1], 1u);
+      if (lane == 0) lds_add(&F.done[si.s % kDoneSlots], 1u);
       wake_block();
       if (si.s + 1 >= num_stages) {
         si.s = num_stages;
@@ -1334,7 +1343,8 @@ __device__ __forceinline__ void service_load_res(const ChainLds<MV>& L, int s, C
 template <int MV, bool OUT_F32, int BAR>
 __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, ChainFlags<MV>& F, uint32_t* ws,
                                             uint32_t nxcc) {
-  constexpr bool kDouble = ChainShape<MV>::kXBuffers == 2;
+  using S = ChainShape<MV>;
+  constexpr bool kAhead = S::kXBuffers == 2;  // activations staged ahead into the arena
   GridSync gs;
   if (!service_start<BAR>(ws, F, gs, nxcc)) return;
   int fills = 0;  // stagings shared with the compute waves so far
@@ -1351,25 +1361,14 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, Cha
     }
     return true;
   };
-  if (stage_flags(L, 0) & kStageNorm) {
-    if ((threadIdx.x & 63) == 0) lds_puti(&F.x_fill, 0);
-    wake_block();
-    ++fills;
-    if (!wait_filled()) return;
-  } else {
-    service_load_x<MV>(geo_of(L.st[0]), stage_x(L, 0), L.x[0]);
-  }
-  compiler_fence();
-  if ((threadIdx.x & 63) == 0) lds_puti(&F.x_stage, 0);
-  wake_block();
-  service_load_res<MV, OUT_F32>(L, 0, F);
-  // Activations no stage writes are staged by this wave into the buffer two
-  // stages back (prefetchable). A stage that needs no grid barrier and whose
-  // activations this wave stages is published as soon as they are in LDS
-  // (early): the block's waves that have finished the stage before it go on
-  // at once, while the others finish.
+  // This wave stages the activations no stage writes (prefetchable), except a
+  // normalized stage's; the compute waves stage the others together when the
+  // stage opens. A prefetchable stage that needs no grid barrier is published
+  // as soon as its activations are in LDS and every stage before it is
+  // published (early): the block's waves that have finished the stages
+  // before it go on at once, while the others finish.
   auto prefetchable = [&](int t) {
-    return kDouble && t < num_stages && !(stage_flags(L, t) & (kStageXInternal | kStageNorm));
+    return kAhead && t < num_stages && !(stage_flags(L, t) & (kStageXInternal | kStageNorm));
   };
   auto early = [&](int t) { return prefetchable(t) && (stage_flags(L, t) & kStageNoBarrier) != 0; };
   auto publish = [&](int t) {
@@ -1378,20 +1377,40 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, Cha
     wake_block();
     service_load_res<MV, OUT_F32>(L, t, F);
   };
-  int published = 0;  // the last stage published
-  if (prefetchable(1)) {
-    service_load_x<MV>(geo_of(L.st[1]), stage_x(L, 1), L.x[kDouble ? 1 : 0]);
-    if (early(1)) publish(published = 1);
+  auto stage = [&](int t) { service_load_x<MV>(geo_of(L.st[t]), stage_x(L, t), stage_xbuf(L, t)); };
+  if (stage_flags(L, 0) & kStageNorm) {
+    if ((threadIdx.x & 63) == 0) lds_puti(&F.x_fill, 0);
+    wake_block();
+    ++fills;
+    if (!wait_filled()) return;
+  } else {
+    stage(0);
   }
+  int published = 0;  // the last stage published
+  int staged = 0;     // the last stage whose activations are in LDS (or staged when it opens)
+  publish(0);
+  // After every compute wave has finished stage done_s and its rows are
+  // stored: publish what is staged and needs no barrier, then stage the next
+  // prefetchable stages whose arena region no unfinished stage uses and whose
+  // row buffer is free (stage t - kRowBufs stored), publishing as it goes.
+  auto run_ahead = [&](int done_s) {
+    while (published < staged && early(published + 1)) publish(++published);
+    while (staged + 1 < num_stages && prefetchable(staged + 1) && ufl(L.st[staged + 1].xwait) <= done_s &&
+           staged + 1 - S::kRowBufs <= done_s) {
+      stage(++staged);
+      if (published == staged - 1 && early(staged)) publish(++published);
+    }
+  };
+  run_ahead(-1);
   // Outputs a later stage reads, stored since the last grid barrier: the next
   // barrier waits for their stores before arriving.
   bool unsynced = false;
   for (int s = 0; s < num_stages; ++s) {
     uint32_t spins = 0;
-    // every compute wave has finished stage s (a wave can be at most one
-    // stage ahead of the block's slowest, so the count of stage s's parity
-    // holds no completions of stage s + 2 yet)
-    while ((int)(lds_get(&F.done[s & 1]) - (uint32_t)(kComputeWaves * (s / 2 + 1))) < 0) {
+    // every compute wave has finished stage s (no wave runs kDoneSlots
+    // stages ahead of the slowest, so the count of stage s's slot holds no
+    // completions of later stages yet)
+    while ((int)(lds_get(&F.done[s % kDoneSlots]) - (uint32_t)(kComputeWaves * (s / kDoneSlots + 1))) < 0) {
       nap();
       if (lds_get(&F.abort) != 0u || ++spins > kSpinLimit) {
         service_fail(ws, F, 1u);
@@ -1426,31 +1445,23 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, Cha
       service_arrive<BAR>(ws, gs);
       service_store<MV, OUT_F32>(L, s, F);
     }
-    // Activations no stage writes, for stage s + 2, go to the buffer stage s
-    // used (every compute wave has finished stage s): the loads of their first
-    // batch are issued now and arrive during the barrier, if any; the batch is
-    // written and the rest fetched once stage s + 1 is published. (Loading
-    // them only after publishing would hold back this wave's next arrival
-    // whenever stage s + 1 is shorter than the load.)
-    const bool prefetch = prefetchable(s + 2);
-    XBatch xb;
-    if (prefetch) xb_issue<MV>(geo_of(L.st[s + 2]), stage_x(L, s + 2), 0, xb);
     if (!ahead) {
       const bool internal = (stage_flags(L, s + 1) & kStageXInternal) != 0;
       const bool norm = (stage_flags(L, s + 1) & kStageNorm) != 0;
-      // (a normalized stage s + 1 parks its norm weights in the buffer stage
-      // s used: the prefetch writes that buffer only after the staging)
       // The compute waves stage the next activations together where they
       // would otherwise wait for this wave to do it alone: with one buffer
-      // (the block's compute waves have all finished stage s, so it is free;
-      // the activations no stage writes are staged during the barrier), and
-      // for activations written in the chain (after the barrier).
-      const bool shared_fill = !kDouble || internal || norm;
+      // (the block's compute waves have all finished stage s, so it is free),
+      // for activations written in the chain (after the barrier), and for a
+      // normalized stage.
+      const bool shared_fill = !kAhead || internal || norm;
       compiler_fence();
       if (shared_fill && !internal) {
         if ((threadIdx.x & 63) == 0) lds_puti(&F.x_fill, s + 1);
         wake_block();
       }
+      // (activations this wave stages, not yet staged because their region
+      // was in use until now: loaded while the barrier completes)
+      if (!shared_fill && staged < s + 1) stage(staged = s + 1);
       if (barrier && !service_wait<BAR>(ws, F, gs)) return;
       if (shared_fill) {
         if (internal) {
@@ -1461,13 +1472,9 @@ __device__ __forceinline__ void service_run(int num_stages, ChainLds<MV>& L, Cha
         if (!wait_filled()) return;
       }
       publish(published = s + 1);
+      if (staged < s + 1) staged = s + 1;
     }
-    if (prefetch) {
-      const Geo g2 = geo_of(L.st[s + 2]);
-      xb_store<MV>(g2, 0, xb, L.x[s & 1]);
-      service_load_x<MV>(g2, stage_x(L, s + 2), L.x[s & 1], 64 * kXBatch);
-      if (early(s + 2)) publish(published = s + 2);
-    }
+    run_ahead(s);
   }
 }
 
@@ -1485,7 +1492,7 @@ chain_kernel(const ChainHeader* __restrict__ plan, uint32_t* __restrict__ ws, ui
   if (threadIdx.x < ChainShape<MV>::kRowBufs * kSplitUnits) (&F.pieces_done[0][0])[threadIdx.x] = 0u;
   for (int e = threadIdx.x; e < S::kTabStages; e += blockDim.x) F.claim[e] = 0u;
   if (threadIdx.x == 0) {
-    F.done[0] = F.done[1] = 0u;
+    for (int j = 0; j < kDoneSlots; ++j) F.done[j] = 0u;
     F.x_stage = -1;
     F.x_fill = -1;
     F.x_filled = 0u;

@@ -227,8 +227,8 @@ q4_status q4_attn_decode(const uint16_t* q, const uint16_t* k_new, const uint16_
  * stage needs >= 1 matrix, all of that stage's k. Limits of the executor
  * (Q4_ERR_UNSUPPORTED from q4_chain_encode otherwise): at most 384 stages and
  * 768 matrices per chain (the block copies the plan into LDS), at most 4
- * matrices per stage, k <= 12288, n < 2^22, at most 64
- * units of 4 rows of one matrix per block (n <= 256 x the number of compute
+ * matrices per stage, k <= 12288, n < 2^22, at most 32
+ * units of 4 rows of one matrix per block (n <= 128 x the number of compute
  * units), scales and biases 16-byte aligned, no stage's output may overlap
  * its own input, and no two outputs of one stage may overlap. Outputs of
  * different stages may overlap: the later stage's values are the ones left
@@ -332,9 +332,8 @@ q4_status q4_chain_run(const void* device_plan, q4_out_dtype y_dtype, void* work
  * contiguous); every row r is the product of that matrix with x row r.
  * m_rows == 1 is q4_chain_encode. With 2..4 rows the executor keeps one
  * activation buffer per block (the next stage's rows are fetched during the
- * stage barrier), which lowers its limits: at most 128 stages, 256 matrices,
- * k <= 11264 and 32 units of 4 rows of one matrix per block
- * (Q4_ERR_UNSUPPORTED otherwise); Q4_ERR_SHAPE if m_rows is out of range. */
+ * stage barrier), which lowers its limits: at most 128 stages, 256 matrices
+ * and k <= 11264 (Q4_ERR_UNSUPPORTED otherwise); Q4_ERR_SHAPE if m_rows is out of range. */
 q4_status q4_chain_encode_rows(const q4_chain_stage* stages, int32_t num_stages,
                                const q4_chain_matrix* matrices, int32_t num_matrices, int32_t m_rows,
                                q4_out_dtype y_dtype, void* host_plan, int64_t plan_bytes);

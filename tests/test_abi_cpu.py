@@ -225,9 +225,10 @@ def test_chain_encode_rows_validation():
     # 32 units of 4 rows per block: n up to 32 * 4 * 256 compute units
     s6, m6 = _chain(n=32 * 4 * 256)
     assert enc(s6, m6, 2) == q4.Q4_OK
+    assert enc(s6, m6, 1) == q4.Q4_OK
     s7, m7 = _chain(n=32 * 4 * 256 + 4)
     assert enc(s7, m7, 2) == q4.Q4_ERR_UNSUPPORTED
-    assert enc(s7, m7, 1) == q4.Q4_OK
+    assert enc(s7, m7, 1) == q4.Q4_ERR_UNSUPPORTED
 
 
 def test_chain_run_rows_validation():
@@ -536,3 +537,35 @@ def test_chain_encoder_barrier_kind_with_dependent_stages():
     assert rc == q4.Q4_OK
     assert int.from_bytes(bytes(buf[24:28]), "little") == 2
     assert [_stage_field(buf, s, NO_BARRIER) for s in range(4)] == [0, 0, 0, 0]
+
+
+XOFF, XWAIT = 56, 60  # byte offsets in a stage record of the plan
+
+
+def test_chain_encoder_places_activations_round_the_arena():
+    """One row: each stage's activations get a region of the LDS arena (two
+    buffers of the widest, 2 x 384 groups x 20 words), one after another round
+    it; a region that does not fit at the end starts again at 0. xwait is the
+    last earlier stage whose region overlaps. A normalized stage takes twice
+    its size (its norm weights follow). Several rows: one buffer, offset 0."""
+    ks = [4096, 4096, 4096, 11264] * 2          # the temporal layer's stages, twice
+    xs = [0x100000 * (i + 1) for i in range(len(ks))]
+    rc, buf = _encode_ex([_sx(x, k, i, 1) for i, (x, k) in enumerate(zip(xs, ks))],
+                         [_mx(0x4000000 + 0x1000000 * i, 64) for i in range(len(ks))])
+    assert rc == q4.Q4_OK
+    size = [16 * (-(-k // 512)) * 20 for k in ks]  # 16 CH groups of 20 words
+    assert size[:4] == [2560, 2560, 2560, 7040]
+    assert [_stage_field(buf, s, XOFF) for s in range(8)] == [0, 2560, 5120, 7680, 0, 2560, 5120, 7680]
+    assert [_stage_field(buf, s, XWAIT) for s in range(8)] == [-1, -1, -1, -1, 0, 1, 2, 3]
+    # a normalized stage of k = 12288 fills the arena: its neighbours wait for it
+    rc, buf = _encode_ex([_sx(0x100000, 4096, 0, 1), _sx(0x200000, 12288, 1, 1, norm=0x300000),
+                          _sx(0x400000, 4096, 2, 1)],
+                         [_mx(0x4000000 + 0x1000000 * i, 64) for i in range(3)])
+    assert rc == q4.Q4_OK
+    assert [_stage_field(buf, s, XOFF) for s in range(3)] == [0, 0, 0]
+    assert [_stage_field(buf, s, XWAIT) for s in range(3)] == [-1, 0, 1]
+    rc, buf = _encode_ex([_sx(x, k, i, 1) for i, (x, k) in enumerate(zip(xs[:3], ks[:3]))],
+                         [_mx(0x4000000 + 0x1000000 * i, 64) for i in range(3)], rows=2)
+    assert rc == q4.Q4_OK
+    assert [_stage_field(buf, s, XOFF) for s in range(3)] == [0, 0, 0]
+    assert [_stage_field(buf, s, XWAIT) for s in range(3)] == [-1, 0, 1]
