@@ -1119,6 +1119,7 @@ __device__ __forceinline__ void xb_issue(const Geo& g, const void* x, int base, 
   const __amdgpu_buffer_rsrc_t rx = byte_range(x, (uint32_t)(MV * g.G * 64));
 #pragma unroll
   for (int b = 0; b < kXBatch; ++b) {
+    if (base + 64 * b >= total) break;  // (no load for a batch past the rows' groups)
     const int e = base + 64 * b + lane;
     const int v = xb_row<MV>(e, gpad);
     const int grp = e - v * gpad;
@@ -1135,6 +1136,7 @@ __device__ __forceinline__ void xb_store(const Geo& g, int base, const XBatch& x
   const int total = MV * gpad;
 #pragma unroll
   for (int b = 0; b < kXBatch; ++b) {
+    if (base + 64 * b >= total) break;
     const int e = base + 64 * b + lane;
     const int v = xb_row<MV>(e, gpad);
     const int grp = e - v * gpad;
@@ -1280,7 +1282,7 @@ __device__ __forceinline__ void service_store(const ChainLds<MV>& L, int s, Chai
   for (int mi = 0; mi < (gated ? 1 : g.num_mats); ++mi) {
     const MatRec& mr = L.mt[g.mat_begin + mi];
     const int n = ufl(mr.n);
-    const BlockRange br = block_range((n + kUnitRows - 1) / kUnitRows);
+    const BlockRange br = {ufl(L.st[s].U0[mi]), ufl(L.st[s].U[mi])};  // (block_range of the unit count)
     void* y = ufl_ptr(mr.y);
     const void* res = ufl_ptr(mr.residual);
     for (int e = lane; e < br.count * kUnitRows; e += 64) {
@@ -1321,7 +1323,7 @@ __device__ __forceinline__ void service_load_res(const ChainLds<MV>& L, int s, C
     const void* res = ufl_ptr(mr.residual);
     if (!res) continue;
     const int n = ufl(mr.n);
-    const BlockRange br = block_range((n + kUnitRows - 1) / kUnitRows);
+    const BlockRange br = {ufl(L.st[s].U0[mi]), ufl(L.st[s].U[mi])};  // (block_range of the unit count)
     for (int e = lane; e < br.count * kUnitRows; e += 64) {
       const int u = e >> 2, r = e & 3;
       const int orow = unit_of(br, u) * kUnitRows + r;
