@@ -45,9 +45,9 @@ HBM_PEAK_GBS = 8000.0
 # whose hash is recorded: any change to them reports traffic as null until the
 # counters are taken again (profiles/chain_kernel_temporal_step_m1_pmc.md).
 CHAIN_TRAFFIC = {
-    "sources_sha256_16": "68b5823c16ca16ad",
-    "fetch_kib": 2014197.9, "fetch_scale": 1048576.0 / 524301.4,
-    "write_kib": 4119.8, "write_scale": 1048576.0 / 1048576.0,
+    "sources_sha256_16": "f10142f9bac93749",
+    "fetch_kib": 2013941.8, "fetch_scale": 1048576.0 / 524301.6,
+    "write_kib": 3072.0, "write_scale": 1048576.0 / 1048576.0,
 }
 KERNEL_SOURCES = ("q4_chain.h", "q4_kernels.h", "q4_api.hip")
 METRIC = "packed-weight GB/s (% HBM peak) + us per 32-layer Q4 temporal step, M=1"
