@@ -165,12 +165,21 @@ q4_status run_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* sc
   return run_gemv_mv<1>(x, packed, scales, biases, n, k, y, dt, st);
 }
 
+uint32_t device_xcc_count();
+
 // ---- small GEMM launch (MFMA): S waves of GS groups each, T row tiles of 16.
+// More than 16 rows: mtiles tiles of 16 rows in the same launch, the tiles of
+// a row block on blocks of one XCD (the grid is a whole number of rounds of
+// nxcc row blocks).
 template <int GS, int T>
 void launch_gemm_gs(int waves, bool f32, const uint16_t* x, int m, const uint32_t* packed,
                     const uint16_t* scales, const uint16_t* biases, int n, int G, void* y,
                     hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(ceil_div(n, 16 * T))), block(64 * waves);
+  const int mtiles = static_cast<int>(ceil_div(m, 16));
+  const int nxcc = mtiles > 1 ? static_cast<int>(device_xcc_count()) : 1;
+  const int64_t nb = ceil_div(n, 16 * T);
+  const int64_t blocks = mtiles > 1 ? ceil_div(nb, nxcc) * nxcc * mtiles : nb;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(64 * waves);
   // the waves' partial tiles, then each wave's code staging (2 batches of
   // KB groups x 16 rows per row tile, rows padded by 16 bytes)
   constexpr int KB = q4k::kGemmKB;
@@ -178,39 +187,34 @@ void launch_gemm_gs(int waves, bool f32, const uint16_t* x, int m, const uint32_
                        static_cast<size_t>(waves) * 2 * T * 16 * (KB * 4 + 4) * sizeof(uint32_t);
   // (16-byte runs of scales per row when every row's run is 16-byte aligned)
   const bool sb16 = G % 8 == 0 && aligned(scales, 16) && aligned(biases, 16);
-  if (f32 && sb16)
-    hipLaunchKernelGGL((q4k::gemm_mfma_kernel<GS, T, true, true>), grid, block, shmem, st, x, m, packed,
-                       scales, biases, n, G, y);
-  else if (f32)
-    hipLaunchKernelGGL((q4k::gemm_mfma_kernel<GS, T, true, false>), grid, block, shmem, st, x, m, packed,
-                       scales, biases, n, G, y);
-  else if (sb16)
-    hipLaunchKernelGGL((q4k::gemm_mfma_kernel<GS, T, false, true>), grid, block, shmem, st, x, m, packed,
-                       scales, biases, n, G, y);
-  else
-    hipLaunchKernelGGL((q4k::gemm_mfma_kernel<GS, T, false, false>), grid, block, shmem, st, x, m, packed,
-                       scales, biases, n, G, y);
+  const int sel = (f32 ? 4 : 0) | (sb16 ? 2 : 0) | (mtiles > 1 ? 1 : 0);
+#define Q4_GEMM_CASE(F, S, TL)                                                                              \
+  case (F ? 4 : 0) | (S ? 2 : 0) | (TL ? 1 : 0):                                                            \
+    hipLaunchKernelGGL((q4k::gemm_mfma_kernel<GS, T, F, S, TL>), grid, block, shmem, st, x, m, packed, scales, \
+                       biases, n, G, y, mtiles, nxcc);                                                      \
+    break;
+  switch (sel) {
+    Q4_GEMM_CASE(true, true, true)
+    Q4_GEMM_CASE(true, true, false)
+    Q4_GEMM_CASE(true, false, true)
+    Q4_GEMM_CASE(true, false, false)
+    Q4_GEMM_CASE(false, true, true)
+    Q4_GEMM_CASE(false, true, false)
+    Q4_GEMM_CASE(false, false, true)
+    Q4_GEMM_CASE(false, false, false)
+  }
+#undef Q4_GEMM_CASE
 }
 
 // Small GEMM: up to 4 activation rows share one pass of the GEMV kernel
 // (each loaded group dequantized once, dotted with every row); 5..16 rows go
 // to the MFMA kernel, one 16-row tile per group. More rows (prefill, up to
-// 64) run the MFMA kernel once per 16-row tile of x: the first pass streams
-// the matrix from HBM, and the later ones find it in the 256 MB last-level
-// cache (a matrix of the model is at most 29 MB).
+// 64) run the MFMA kernel on every 16-row tile of x in one launch, the tiles
+// of a row block on one XCD: the first of them to reach a weight line reads
+// it from HBM, the others from the XCD's L2.
 q4_status run_gemm_small(const uint16_t* x, int64_t m, const uint32_t* packed,
                          const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
                          void* y, q4_out_dtype dt, hipStream_t st) {
-  if (m > 16) {
-    const int64_t ybytes = dt == Q4_OUT_F32 ? 4 : 2;
-    for (int64_t r0 = 0; r0 < m; r0 += 16) {
-      const int64_t mt = m - r0 < 16 ? m - r0 : 16;
-      const q4_status s = run_gemm_small(x + r0 * k, mt, packed, scales, biases, n, k,
-                                         static_cast<unsigned char*>(y) + r0 * n * ybytes, dt, st);
-      if (s != Q4_OK) return s;
-    }
-    return Q4_OK;
-  }
   switch (m) {
     case 1: return run_gemv_mv<1>(x, packed, scales, biases, n, k, y, dt, st);
     case 2: return run_gemv_mv<2>(x, packed, scales, biases, n, k, y, dt, st);

@@ -342,17 +342,31 @@ constexpr int kGemmKB = Q4_GEMM_KB;
 // A block has S waves; wave w owns groups [w*GS, (w+1)*GS) and keeps its
 // activation tile in registers; the block walks T tiles of 16 weight rows and
 // the S waves' tiles are summed in fixed order through LDS.
+// More than 16 activation rows (a prompt's frames, up to 64) run as mtiles
+// tiles of 16 rows in the same launch, one block per (row block, tile). The
+// tiles of a row block go to blocks that the dispatcher deals to the same
+// XCD (it deals blocks to the nxcc XCDs in turn), so that the row block's
+// weights come from HBM once and from that XCD's L2 for the other tiles.
 // SB16: G is a multiple of 8, so a row's scales (and biases) of the wave's GS
 // groups are 16-byte aligned runs, loaded once per row with 16-byte loads
 // (GS / 8 per row) instead of one 2-byte load per group and batch: 16 rows
 // per load either way, so that cuts the cache lines looked up per wave by 8.
-template <int GS, int T, bool OUT_F32, bool SB16>
+template <int GS, int T, bool OUT_F32, bool SB16, bool TILED>
 __global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restrict__ x, int m,
                                                           const uint32_t* __restrict__ packed,
                                                           const uint16_t* __restrict__ scales,
                                                           const uint16_t* __restrict__ biases,
-                                                          int n, int G, void* __restrict__ y) {
+                                                          int n, int G, void* __restrict__ y, int mtiles,
+                                                          int nxcc) {
   extern __shared__ float red_dyn[];  // [nwaves][T][4][64], then each wave's code staging
+  int rblk = blockIdx.x, tile = 0;
+  if constexpr (TILED) {
+    const int b = blockIdx.x, span = nxcc * mtiles;
+    rblk = (b / span) * nxcc + b % nxcc;
+    tile = (b / nxcc) % mtiles;
+    if (rblk * 16 * T >= n) return;  // (past the last row block: the grid is a whole number of XCD rounds)
+  }
+  const int nbase = rblk * 16 * T;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
@@ -361,6 +375,10 @@ __global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restr
   const int g0 = wave * GS;
   const int gcount = max(0, min(G - g0, GS));
   const int64_t K = (int64_t)G * 32;
+  if constexpr (TILED) {
+    x += (int64_t)tile * 16 * K;
+    m = min(16, m - 16 * tile);
+  }
 
   // All loads go through buffer descriptors: lanes past m, G or n get an
   // offset outside the range and read zeros, so the loads carry no branch
@@ -405,7 +423,6 @@ __global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restr
 #pragma unroll
   for (int t = 0; t < T; ++t) acc[t] = zero;
 
-  const int nbase = blockIdx.x * 16 * T;
   const int64_t wpr = (int64_t)G * 4;
   const int tile_rows = max(0, min(16 * T, n - nbase));
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
@@ -560,7 +577,7 @@ __global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restr
     const int t = idx >> 8;
     const int mi = 4 * (l >> 4) + j;
     const int row = nbase + 16 * t + (l & 15);
-    if (mi < m && row < n) store_out<OUT_F32>(y, (int64_t)mi * n + row, s);
+    if (mi < m && row < n) store_out<OUT_F32>(y, (int64_t)(16 * tile + mi) * n + row, s);
   }
 }
 

@@ -171,7 +171,7 @@ def test_gemm_small_sixteen_group_waves(k, m, out_dtype):
     _check(y, oracle.matmul(x, P, S, B, k), out_dtype)
 
 
-@pytest.mark.parametrize("m", [1, 2, 4, 7, 16])
+@pytest.mark.parametrize("m", [1, 2, 4, 7, 16, 50])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_products_on_edge_weights(m, out_dtype):
     """The pack edge cases (degenerate and exact-affine groups, exact code ties,
@@ -191,11 +191,13 @@ def test_products_on_edge_weights(m, out_dtype):
     _check(y, ref[0] if m == 1 else ref, out_dtype)
 
 
-# Prefill (17..64 rows): the MFMA kernel once per 16-row tile of x, ragged
-# last tile included.
+# Prefill (17..64 rows): one pass of the prefill kernel over 2..4 tiles of 16
+# rows of x (ragged last tile included), at 8, 16 and 32 groups per wave
+# (k = 4096, 6400 and 11264 among the shapes).
 @pytest.mark.parametrize("m", [17, 24, 32, 33, 50, 64])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("n,k", [(37, 96), (300, 1056), (4096, 4096), (11264, 4096), (4096, 11264), (100, 16384)])
+@pytest.mark.parametrize("n,k", [(37, 96), (300, 1056), (4096, 4096), (11264, 4096), (4096, 11264), (100, 16384),
+                                 (64, 6400)])
 def test_prefill_matches_oracle(n, k, m, out_dtype):
     P, S, B = oracle.quantize(_w(n, k, seed=n + 5 * k))
     x = _x(m, k, seed=m + 7 * k)
