@@ -118,7 +118,7 @@ def test_gemv_matches_oracle(n, k, out_dtype):
 
 @pytest.mark.parametrize("m", [2, 3, 4, 7, 16])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("n,k", [(37, 96), (300, 1056), (1000, 2048)] + MODEL_SHAPES)
+@pytest.mark.parametrize("n,k", [(37, 96), (300, 1056), (1000, 2048), (8197, 4096)] + MODEL_SHAPES)
 def test_gemm_small_matches_oracle(n, k, m, out_dtype):
     w = _w(n, k, seed=n + 3 * k)
     P, S, B = oracle.quantize(w)
