@@ -350,10 +350,12 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--spin-up", type=float, default=0.5, metavar="SECONDS",
+    ap.add_argument("--spin-up", type=float, default=2.0, metavar="SECONDS",
                     help="untimed calls for this long before the warmup steps of each timed workload: the "
                          "GPU raises its clocks over ~0.1 s of sustained load (steps timed right after the "
-                         "host-side set-up run up to 15%% slower)")
+                         "host-side set-up run up to 15%% slower; once, right after a long test run, a "
+                         "headline timed after 0.5 s ran 13%% slow with a wide spread while the same run's "
+                         "later workloads were normal)")
     ap.add_argument("--mode", choices=("chain", "launches"), default="chain")
     ap.add_argument("--workload", choices=("step", "depformer", "gemm", "gemv", "layer", "embed", "attn"),
                     default="step",
@@ -567,7 +569,7 @@ def spin_up(run, seconds: float) -> None:
             return
 
 
-SPIN_UP_S = 0.5  # set from --spin-up in main()
+SPIN_UP_S = 2.0  # set from --spin-up in main()
 
 
 def time_replays(run, steps: int, warmup: int):
