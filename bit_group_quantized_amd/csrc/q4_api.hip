@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <vector>
@@ -183,7 +184,8 @@ void launch_gemm_gs(int waves, bool f32, bool sb16, const uint16_t* x, int m, co
                     const uint16_t* scales, const uint16_t* biases, int n, int G, void* y,
                     hipStream_t st) {
   const int mtiles = TILED ? static_cast<int>(ceil_div(m, 16)) : 1;
-  const int nxcc = TILED ? static_cast<int>(device_xcc_count()) : 1;
+  // (one XCD if the device cannot be queried: the mapping stays a permutation)
+  const int nxcc = TILED ? std::max(1, static_cast<int>(device_xcc_count())) : 1;
   const int64_t nb = ceil_div(n, 16 * T);
   const int64_t blocks = TILED ? ceil_div(nb, nxcc) * nxcc * mtiles : nb;
   const dim3 grid(static_cast<unsigned>(blocks)), block(64 * waves);
