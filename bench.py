@@ -45,8 +45,8 @@ HBM_PEAK_GBS = 8000.0
 # whose hash is recorded: any change to them reports traffic as null until the
 # counters are taken again (profiles/chain_kernel_temporal_step_m1_pmc.md).
 CHAIN_TRAFFIC = {
-    "sources_sha256_16": "bad4567bd66b2c36",
-    "fetch_kib": 2013915.6, "fetch_scale": 1048576.0 / 524301.6,
+    "sources_sha256_16": "2ffbe8d33da47d13",
+    "fetch_kib": 2013928.4, "fetch_scale": 1048576.0 / 524301.6,
     "write_kib": 3072.0, "write_scale": 1048576.0 / 1048576.0,
 }
 KERNEL_SOURCES = ("q4_chain.h", "q4_kernels.h", "q4_api.hip")
