@@ -383,7 +383,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="step: skip the dependent step, the stream-read ceiling and the pack timing")
+                    help="step: skip the dependent step, the stream-read ceiling and the pack timing; gemv: skip the "
+                         "per-call read floor")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the step, run 5 plain device copies of MIB MiB (int32 "
                          "bitwise_not, MIB MiB read + MIB MiB written each) so that HBM byte "
@@ -592,6 +593,48 @@ def time_replays(run, steps: int, warmup: int):
     return ev[0].elapsed_time(ev[-1]) / steps, per
 
 
+def per_call_read_floor(dev, nbytes: int, copies: int, steps: int, warmup: int):
+    """What one launch that only reads nbytes costs in the per-call GEMV's
+    conditions: the plain read-and-fold kernel (libq4_ceiling.so) over
+    `copies` distinct buffers in turn (past the last-level cache), one launch
+    each, replayed as a graph and timed like the GEMV; the best of a few
+    launch shapes."""
+    import ctypes
+
+    import torch
+
+    from bit_group_quantized_amd import build as q4_build
+
+    lib = ctypes.CDLL(q4_build.CEILING_LIB)
+    lib.q4_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_void_p]
+    nbytes = nbytes // 16 * 16
+    bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(copies)]
+    for b in bufs:
+        b.random_()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(cus * 32, dtype=torch.int32, device=dev)
+    best = None
+    for per_cu in (2, 4, 8):
+        for unroll in (2, 4):
+            for nt in (0, 1):
+                def calls():
+                    st = torch.cuda.current_stream().cuda_stream
+                    for b in bufs:
+                        if lib.q4_stream_read(ctypes.c_void_p(b.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()),
+                                              cus * per_cu, unroll, nt, ctypes.c_void_p(st)) != 0:
+                            raise RuntimeError("q4_stream_read failed")
+                g = graph_of(calls)
+                ms, _ = time_replays(g.replay, steps, warmup)
+                us = ms * 1e3 / copies
+                if best is None or us < best["us_per_launch"]:
+                    best = {"us_per_launch": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                            "blocks_per_cu": per_cu, "loads_in_flight_per_lane": unroll, "nontemporal": bool(nt)}
+    del bufs
+    best.update({"bytes_per_launch": nbytes, "copies": copies, "kernel": "stream_read_kernel"})
+    return best
+
+
 def graph_of(fn):
     """Capture fn (a sequence of launches on the current stream) into a HIP graph."""
     import torch
@@ -649,6 +692,10 @@ def bench_other(args, dev) -> int:
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "traffic_unit": "bytes per launch",
                          "kernel": "gemv_kernel", "bytes_per_launch": wbytes // copies},
         }
+        if not args.no_extras:
+            # (the same bytes per launch, only read: the floor of a per-call kernel)
+            log("[bench] per-call read floor ...")
+            result["read_floor"] = per_call_read_floor(dev, wbytes // copies, copies, args.steps, args.warmup)
         print(json.dumps(result), flush=True)
         return 0
     if args.workload == "embed":
