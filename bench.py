@@ -593,12 +593,12 @@ def time_replays(run, steps: int, warmup: int):
     return ev[0].elapsed_time(ev[-1]) / steps, per
 
 
-def per_call_read_floor(dev, nbytes: int, copies: int, steps: int, warmup: int):
-    """What one launch that only reads nbytes costs in the per-call GEMV's
-    conditions: the plain read-and-fold kernel (libq4_ceiling.so) over
-    `copies` distinct buffers in turn (past the last-level cache), one launch
-    each, replayed as a graph and timed like the GEMV; the best of a few
-    launch shapes."""
+def per_call_read_floor(dev, sizes, steps: int, warmup: int):
+    """What launches that only read the same bytes cost in a per-call
+    workload's conditions: the plain read-and-fold kernel (libq4_ceiling.so)
+    over one distinct buffer per entry of `sizes` (bytes) in turn (past the
+    last-level cache), one launch each, replayed as a graph and timed like the
+    workload; the best of a few launch shapes."""
     import ctypes
 
     import torch
@@ -608,8 +608,8 @@ def per_call_read_floor(dev, nbytes: int, copies: int, steps: int, warmup: int):
     lib = ctypes.CDLL(q4_build.CEILING_LIB)
     lib.q4_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int, ctypes.c_void_p]
-    nbytes = nbytes // 16 * 16
-    bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(copies)]
+    sizes = [int(b) // 16 * 16 for b in sizes]
+    bufs = [torch.empty(b // 4, dtype=torch.int32, device=dev) for b in sizes]
     for b in bufs:
         b.random_()
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
@@ -620,18 +620,19 @@ def per_call_read_floor(dev, nbytes: int, copies: int, steps: int, warmup: int):
             for nt in (0, 1):
                 def calls():
                     st = torch.cuda.current_stream().cuda_stream
-                    for b in bufs:
-                        if lib.q4_stream_read(ctypes.c_void_p(b.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()),
+                    for b, nb in zip(bufs, sizes):
+                        if lib.q4_stream_read(ctypes.c_void_p(b.data_ptr()), nb, ctypes.c_void_p(out.data_ptr()),
                                               cus * per_cu, unroll, nt, ctypes.c_void_p(st)) != 0:
                             raise RuntimeError("q4_stream_read failed")
                 g = graph_of(calls)
                 ms, _ = time_replays(g.replay, steps, warmup)
-                us = ms * 1e3 / copies
-                if best is None or us < best["us_per_launch"]:
-                    best = {"us_per_launch": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                us = ms * 1e3
+                if best is None or us < best["us_total"]:
+                    best = {"us_total": round(us, 1), "us_per_launch": round(us / len(sizes), 2),
+                            "gbs": round(sum(sizes) / (us * 1e-6) / 1e9, 1),
                             "blocks_per_cu": per_cu, "loads_in_flight_per_lane": unroll, "nontemporal": bool(nt)}
     del bufs
-    best.update({"bytes_per_launch": nbytes, "copies": copies, "kernel": "stream_read_kernel"})
+    best.update({"bytes": sum(sizes), "launches": len(sizes), "kernel": "stream_read_kernel"})
     return best
 
 
@@ -695,7 +696,7 @@ def bench_other(args, dev) -> int:
         if not args.no_extras:
             # (the same bytes per launch, only read: the floor of a per-call kernel)
             log("[bench] per-call read floor ...")
-            result["read_floor"] = per_call_read_floor(dev, wbytes // copies, copies, args.steps, args.warmup)
+            result["read_floor"] = per_call_read_floor(dev, [wbytes // copies] * copies, args.steps, args.warmup)
         print(json.dumps(result), flush=True)
         return 0
     if args.workload == "embed":
@@ -878,6 +879,12 @@ def bench_other(args, dev) -> int:
         if use_chain and rows_chain.chain_status() != 0:
             print(f"chain executor reported status {rows_chain.chain_status()}", file=sys.stderr)
             return 1
+        floor = None
+        if not use_chain and not args.no_extras:
+            # (the same matrices' bytes, only read, one launch each: the floor of a per-call step)
+            log("[bench] per-call read floor ...")
+            floor = per_call_read_floor(dev, [m.nbytes() for st in chain.stages for m in st.mats], args.steps,
+                                        args.warmup)
         config = {"workload": f"small_gemm_m{args.m}_temporal_step", "layers": args.layers, "hidden": workloads.HIDDEN,
                   "ffn": workloads.FFN, "m": args.m, "group": 32, "packed_bytes_per_step": wbytes,
                   "executor": "chain" if use_chain else "launches", "launches_per_step": launches}
@@ -895,6 +902,8 @@ def bench_other(args, dev) -> int:
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "traffic_unit": "bytes per launch",
                      "kernel": kernel, "bytes_per_launch": wbytes // launches},
     }
+    if unit_name == "step" and floor is not None:
+        result["read_floor"] = floor
     print(json.dumps(result), flush=True)
     return 0
 
