@@ -246,8 +246,8 @@ void launch_gemm(int waves, bool f32, const uint16_t* x, int m, const uint32_t* 
 // (each loaded group dequantized once, dotted with every row); 5..16 rows go
 // to the MFMA kernel, one 16-row tile per group. More rows (prefill, up to
 // 64) run the MFMA kernel on every 16-row tile of x in one launch, the tiles
-// of a row block on one XCD: the first of them to reach a weight line reads
-// it from HBM, the others from the XCD's L2; a block then holds two tiles of
+// of a row block on one XCD, where a weight line the first of them reads from
+// HBM can serve the others from the XCD's L2; a block then holds two tiles of
 // 16 weight rows, so that each activation load serves twice the weights
 // (M=50 step 6.20 -> 5.19 ms).
 q4_status run_gemm_small(const uint16_t* x, int64_t m, const uint32_t* packed,

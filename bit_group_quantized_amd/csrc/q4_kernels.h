@@ -346,7 +346,9 @@ constexpr int kGemmKB = Q4_GEMM_KB;
 // tiles of 16 rows in the same launch, one block per (row block, tile). The
 // tiles of a row block go to blocks that the dispatcher deals to the same
 // XCD (it deals blocks to the nxcc XCDs in turn), so that the row block's
-// weights come from HBM once and from that XCD's L2 for the other tiles.
+// weights, read from HBM by the first of them, can be served from that XCD's
+// L2 to the others (measured: M=50 step 8.04 -> 6.20 ms against one launch
+// per tile).
 // SB16: G is a multiple of 8, so a row's scales (and biases) of the wave's GS
 // groups are 16-byte aligned runs, loaded once per row with 16-byte loads
 // (GS / 8 per row) instead of one 2-byte load per group and batch: 16 rows
