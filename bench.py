@@ -383,8 +383,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="step: skip the dependent step, the stream-read ceiling and the pack timing; gemv: skip the "
-                         "per-call read floor")
+                    help="step: skip the dependent step, the stream-read ceiling and the pack timing; gemv and "
+                         "gemm by per-call launches: skip the per-call read floor")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the step, run 5 plain device copies of MIB MiB (int32 "
                          "bitwise_not, MIB MiB read + MIB MiB written each) so that HBM byte "
