@@ -262,6 +262,14 @@ q4_status run_gemm_small(const uint16_t* x, int64_t m, const uint32_t* packed,
   }
   const int64_t G = k / 32;
   const bool f32 = dt == Q4_OUT_F32;
+  // 16 groups per wave where that still makes 8..16 waves: two such blocks fit
+  // a compute unit (measured on the step's matrices, k = 4096: M=50 step 5.19
+  // -> 4.76 ms, M=8 0.7% faster, M=16 unchanged)
+  const int64_t w16 = ceil_div(G, 16);
+  if (w16 >= 8 && w16 <= 16) {
+    launch_gemm<16>((int)w16, f32, x, (int)m, packed, scales, biases, (int)n, (int)G, y, st);
+    return launch_status();
+  }
   // (24 groups per wave would spill registers)
   const int gss[3] = {8, 16, 32};
   for (int i = 0; i < 3; ++i) {
