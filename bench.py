@@ -356,7 +356,9 @@ def main(argv=None) -> int:
                          "host-side set-up run up to 15%% slower; once, right after a long test run, a "
                          "headline timed after 0.5 s ran 13%% slow with a wide spread while the same run's "
                          "later workloads were normal)")
-    ap.add_argument("--mode", choices=("chain", "launches"), default="chain")
+    ap.add_argument("--mode", choices=("chain", "launches", "batch"), default="chain",
+                    help="chain: one persistent launch (--workload gemm: m <= 4); launches: one call per matrix; "
+                         "batch (--workload gemm, m = 5..16): q4_gemm_batch_run, one launch per distinct k")
     ap.add_argument("--workload", choices=("step", "depformer", "gemm", "gemv", "layer", "embed", "attn"),
                     default="step",
                     help="step: the 32-layer temporal step at M=1 (the headline); depformer: one "
@@ -867,10 +869,31 @@ def bench_other(args, dev) -> int:
         wbytes = chain.weight_bytes()
         rows_chain = Chain(make_small_gemm(chain, args.m, args.seed, dev))
         use_chain = args.mode == "chain" and args.m <= 4
+        use_batch = args.mode == "batch"
+        if use_batch and not 5 <= args.m <= 16:
+            print("--mode batch needs --m in 5..16", file=sys.stderr)
+            return 2
         if use_chain:
             # the step's weights and the m activation rows through one persistent launch
             rows_chain.prepare_chain()
             run, launches, kernel = rows_chain.run_chain, 1, "chain_kernel"
+        elif use_batch:
+            # every product of one k in one launch (the step: k = 4096 and k = 11264)
+            by_k = {}
+            for st in rows_chain.stages:
+                for mt, y in zip(st.mats, st.outs):
+                    xs, mats, outs = by_k.setdefault(st.x.shape[-1], ([], [], []))
+                    xs.append(st.x)
+                    mats.append((mt.packed, mt.scales, mt.biases))
+                    outs.append(y)
+            plans = [q4.q4_gemm_batch_build(*v) for _, v in sorted(by_k.items())]
+
+            def run_batches():
+                for pl in plans:
+                    q4.q4_gemm_batch_run(pl)
+
+            g = graph_of(run_batches)
+            run, launches, kernel = g.replay, len(plans), "gemm_batch_kernel"
         else:
             g = graph_of(rows_chain.run_launches)
             run, launches = g.replay, chain.num_matrices()
@@ -880,14 +903,15 @@ def bench_other(args, dev) -> int:
             print(f"chain executor reported status {rows_chain.chain_status()}", file=sys.stderr)
             return 1
         floor = None
-        if not use_chain and not args.no_extras:
+        if not use_chain and not use_batch and not args.no_extras:
             # (the same matrices' bytes, only read, one launch each: the floor of a per-call step)
             log("[bench] per-call read floor ...")
             floor = per_call_read_floor(dev, [m.nbytes() for st in chain.stages for m in st.mats], args.steps,
                                         args.warmup)
         config = {"workload": f"small_gemm_m{args.m}_temporal_step", "layers": args.layers, "hidden": workloads.HIDDEN,
                   "ffn": workloads.FFN, "m": args.m, "group": 32, "packed_bytes_per_step": wbytes,
-                  "executor": "chain" if use_chain else "launches", "launches_per_step": launches}
+                  "executor": "chain" if use_chain else ("batch" if use_batch else "launches"),
+                  "launches_per_step": launches}
         unit_name = "step"
     gbs = wbytes / (ms * 1e-3) / 1e9
     achieved = (wbytes / launches) / ((ms / launches) * 1e-3) / 1e9

@@ -38,7 +38,8 @@ _EXPORTS = (
     "q4_layout_version", "q4_status_str", "q4_last_hip_error", "q4_pack", "q4_unpack", "q4_gemv",
     "q4_gemm_small", "q4_multilinear_step", "q4_chain_plan_bytes", "q4_chain_encode", "q4_chain_run",
     "q4_chain_encode_rows", "q4_chain_run_rows", "q4_chain_run_rows_noalloc", "q4_embed_sum",
-    "q4_attn_workspace_bytes", "q4_attn_decode", "q4_chain_encode_ex",
+    "q4_attn_workspace_bytes", "q4_attn_decode", "q4_chain_encode_ex", "q4_gemm_batch_blocks",
+    "q4_gemm_batch_plan_bytes", "q4_gemm_batch_encode", "q4_gemm_batch_run",
 )
 EMBED_MAX_TABLES = 32  # Q4_EMBED_MAX_TABLES
 CHAIN_WORKSPACE_BYTES = 131328
@@ -63,6 +64,11 @@ class _ChainStageEx(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("k", ctypes.c_int64), ("first_matrix", ctypes.c_int32),
                 ("num_matrices", ctypes.c_int32), ("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_double),
                 ("gated", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class _GemmBatchItem(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("biases", ctypes.c_void_p), ("y", ctypes.c_void_p), ("n", ctypes.c_int64)]
 
 
 class _EmbedTable(ctypes.Structure):
@@ -110,6 +116,14 @@ def load():
     lib.q4_attn_workspace_bytes.argtypes = [I, I]
     lib.q4_attn_workspace_bytes.restype = ctypes.c_int64
     lib.q4_attn_decode.argtypes = [P, P, P, P, P, I, I, I, I, ctypes.c_double, P, V, P, I, P]
+    lib.q4_gemm_batch_blocks.argtypes = [P, ctypes.c_int32]
+    lib.q4_gemm_batch_blocks.restype = ctypes.c_int64
+    lib.q4_gemm_batch_plan_bytes.argtypes = [ctypes.c_int32, I]
+    lib.q4_gemm_batch_plan_bytes.restype = ctypes.c_int64
+    lib.q4_gemm_batch_encode.argtypes = [P, ctypes.c_int32, I, I, V, P, I]
+    lib.q4_gemm_batch_run.argtypes = [P, P, P]
+    lib.q4_gemm_batch_encode.restype = V
+    lib.q4_gemm_batch_run.restype = V
     for f in ("q4_pack", "q4_unpack", "q4_gemv", "q4_gemm_small", "q4_multilinear_step", "q4_chain_encode",
               "q4_chain_run", "q4_chain_encode_rows", "q4_chain_run_rows", "q4_chain_run_rows_noalloc", "q4_embed_sum",
               "q4_attn_decode", "q4_chain_encode_ex"):
@@ -266,6 +280,57 @@ def q4_gemm_small(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, b
     _check("q4_gemm_small", load().q4_gemm_small(_ptr(x), m, _ptr(packed), _ptr(scales), _ptr(biases), n, k,
                                                  _ptr(out), code, _ptr_stream(x)))
     return out
+
+
+class GemmBatchPlan:
+    """An encoded product batch: the host and device copies of the plan plus
+    what it references (kept alive here so the device pointers stay valid)."""
+
+    def __init__(self, host_plan, device_plan: torch.Tensor, keep: list):
+        self.host_plan = host_plan
+        self.device_plan = device_plan
+        self._keep = keep
+
+
+def q4_gemm_batch_build(xs, mats, outs) -> GemmBatchPlan:
+    """Encode independent products outs[i] [m, n_i] = xs[i] [m, k] . W_hat_i^T
+    (mats[i] = (packed, scales, biases)) sharing m (5..16) and k, and upload
+    the plan: q4_gemm_batch_run then runs them all in one launch."""
+    if not (len(xs) == len(mats) == len(outs)) or not xs:
+        raise ValueError("xs, mats and outs must be non-empty lists of one length")
+    lib = load()
+    m, k = xs[0].shape
+    code = _out_code(outs[0].dtype)
+    items, keep = [], []
+    for x, (packed, scales, biases), out in zip(xs, mats, outs):
+        n, kk = _check_matrix(packed, scales, biases)
+        _need(x, "x", torch.bfloat16)
+        _need(out, "out", outs[0].dtype)
+        if x.dim() != 2 or tuple(x.shape) != (m, k) or kk != k:
+            raise ValueError(f"every x must be [{m}, {k}] and every weight [n, {k}]")
+        if out.numel() != m * n:
+            raise ValueError("out must hold m*n elements")
+        _same_device(xs[0], x, packed, out)
+        items.append(_GemmBatchItem(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), biases.data_ptr(),
+                                    out.data_ptr(), n))
+        keep += [x, packed, scales, biases, out]
+    arr = (_GemmBatchItem * len(items))(*items)
+    blocks = int(lib.q4_gemm_batch_blocks(ctypes.byref(arr), len(items)))
+    nbytes = int(lib.q4_gemm_batch_plan_bytes(len(items), blocks))
+    if nbytes <= 0:
+        raise ValueError("batch outside the encoder's limits")
+    host = (ctypes.c_uint8 * nbytes)()
+    _check("q4_gemm_batch_encode", lib.q4_gemm_batch_encode(ctypes.byref(arr), len(items), m, k, code,
+                                                            ctypes.byref(host), nbytes))
+    plan = torch.empty(nbytes, dtype=torch.uint8, device=xs[0].device)
+    plan.copy_(torch.frombuffer(bytearray(host), dtype=torch.uint8))
+    return GemmBatchPlan(host, plan, keep)
+
+
+def q4_gemm_batch_run(plan: GemmBatchPlan) -> None:
+    """Run every product of the batch in one launch on the current stream."""
+    _check("q4_gemm_batch_run", load().q4_gemm_batch_run(ctypes.byref(plan.host_plan), _ptr(plan.device_plan),
+                                                         _ptr_stream(plan.device_plan)))
 
 
 def q4_multilinear_step(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor,

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cstring>
 #include <mutex>
 #include <vector>
 
@@ -250,6 +251,28 @@ void launch_gemm(int waves, bool f32, const uint16_t* x, int m, const uint32_t* 
 // HBM can serve the others from the XCD's L2; a block then holds two tiles of
 // 16 weight rows, so that each activation load serves twice the weights
 // (M=50 step 6.20 -> 5.19 ms).
+// Groups per wave of the MFMA kernel for a product with G groups: 16 where
+// that still makes 8..16 waves, since two such blocks fit a compute unit
+// (measured on the step's matrices, k = 4096: M=50 step 5.19 -> 4.76 ms, M=8
+// 0.7% faster, M=16 unchanged); otherwise the first of 8, 16 and 32 that
+// needs at most 16 waves (24 groups per wave would spill registers). False if
+// none does.
+bool gemm_plan(int64_t G, int& gs, int& waves) {
+  const int64_t w16 = ceil_div(G, 16);
+  if (w16 >= 8 && w16 <= 16) {
+    gs = 16, waves = static_cast<int>(w16);
+    return true;
+  }
+  for (const int g : {8, 16, 32}) {
+    const int64_t w = ceil_div(G, g);
+    if (w <= 16) {
+      gs = g, waves = static_cast<int>(w);
+      return true;
+    }
+  }
+  return false;
+}
+
 q4_status run_gemm_small(const uint16_t* x, int64_t m, const uint32_t* packed,
                          const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
                          void* y, q4_out_dtype dt, hipStream_t st) {
@@ -262,27 +285,14 @@ q4_status run_gemm_small(const uint16_t* x, int64_t m, const uint32_t* packed,
   }
   const int64_t G = k / 32;
   const bool f32 = dt == Q4_OUT_F32;
-  // 16 groups per wave where that still makes 8..16 waves: two such blocks fit
-  // a compute unit (measured on the step's matrices, k = 4096: M=50 step 5.19
-  // -> 4.76 ms, M=8 0.7% faster, M=16 unchanged)
-  const int64_t w16 = ceil_div(G, 16);
-  if (w16 >= 8 && w16 <= 16) {
-    launch_gemm<16>((int)w16, f32, x, (int)m, packed, scales, biases, (int)n, (int)G, y, st);
-    return launch_status();
+  int gs = 0, waves = 0;
+  if (!gemm_plan(G, gs, waves)) return Q4_ERR_UNSUPPORTED;
+  switch (gs) {
+    case 8: launch_gemm<8>(waves, f32, x, (int)m, packed, scales, biases, (int)n, (int)G, y, st); break;
+    case 16: launch_gemm<16>(waves, f32, x, (int)m, packed, scales, biases, (int)n, (int)G, y, st); break;
+    default: launch_gemm<32>(waves, f32, x, (int)m, packed, scales, biases, (int)n, (int)G, y, st); break;
   }
-  // (24 groups per wave would spill registers)
-  const int gss[3] = {8, 16, 32};
-  for (int i = 0; i < 3; ++i) {
-    const int64_t waves = ceil_div(G, gss[i]);
-    if (waves > 16) continue;
-    switch (gss[i]) {
-      case 8: launch_gemm<8>((int)waves, f32, x, (int)m, packed, scales, biases, (int)n, (int)G, y, st); break;
-      case 16: launch_gemm<16>((int)waves, f32, x, (int)m, packed, scales, biases, (int)n, (int)G, y, st); break;
-      default: launch_gemm<32>((int)waves, f32, x, (int)m, packed, scales, biases, (int)n, (int)G, y, st); break;
-    }
-    return launch_status();
-  }
-  return Q4_ERR_UNSUPPORTED;
+  return launch_status();
 }
 
 q4_status check_matrix(const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
@@ -310,6 +320,45 @@ q4_status check_product(const uint16_t* x, int64_t m, const uint32_t* packed,
   if (!aligned(x, 16) || !aligned(y, dt == Q4_OUT_F32 ? 4 : 2)) return Q4_ERR_ALIGN;
   if (k > Q4_MAX_K) return Q4_ERR_UNSUPPORTED;
   return Q4_OK;
+}
+
+// Plan of a product batch: this header, the items (q4k::GemmBatchItem), then
+// each block's item index (uint16).
+struct GemmBatchHeader {
+  uint32_t magic;
+  int32_t count, m, G, blocks, dtype, gs, waves, sb16;
+  int32_t reserved[7];
+};
+static_assert(sizeof(GemmBatchHeader) == 64, "the plan's header layout");
+constexpr uint32_t kBatchMagic = 0x51344742u;
+constexpr int32_t kBatchMaxItems = 4096;
+constexpr int64_t kBatchMaxBlocks = int64_t(1) << 24;
+constexpr int64_t batch_owner_offset(int64_t count) {
+  return static_cast<int64_t>(sizeof(GemmBatchHeader)) + count * static_cast<int64_t>(sizeof(q4k::GemmBatchItem));
+}
+
+template <int GS>
+void launch_batch(const GemmBatchHeader& h, const void* device_plan, hipStream_t st) {
+  const char* base = static_cast<const char*>(device_plan);
+  const auto* items = reinterpret_cast<const q4k::GemmBatchItem*>(base + sizeof(GemmBatchHeader));
+  const auto* owner = reinterpret_cast<const uint16_t*>(base + batch_owner_offset(h.count));
+  const dim3 grid(static_cast<unsigned>(h.blocks)), block(64 * h.waves);
+  const size_t shmem = gemm_shmem<1>(h.waves);
+#define Q4_BATCH_LAUNCH(F, S) \
+  hipLaunchKernelGGL((q4k::gemm_batch_kernel<GS, F, S>), grid, block, shmem, st, items, owner, h.m, h.G)
+  const bool f32 = h.dtype == Q4_OUT_F32;
+  if (h.sb16) {
+    if (f32)
+      Q4_BATCH_LAUNCH(true, true);
+    else
+      Q4_BATCH_LAUNCH(false, true);
+  } else {
+    if (f32)
+      Q4_BATCH_LAUNCH(true, false);
+    else
+      Q4_BATCH_LAUNCH(false, false);
+  }
+#undef Q4_BATCH_LAUNCH
 }
 
 }  // namespace
@@ -378,6 +427,77 @@ q4_status q4_gemm_small(const uint16_t* x, int64_t m, const uint32_t* packed,
   if (s != Q4_OK) return s;
   if (n == 0) return Q4_OK;
   return run_gemm_small(x, m, packed, scales, biases, n, k, y, y_dtype, as_stream(stream));
+}
+
+int64_t q4_gemm_batch_blocks(const q4_gemm_batch_item* items, int32_t count) {
+  if (!items || count < 1 || count > kBatchMaxItems) return -1;
+  int64_t blocks = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    if (items[i].n < 1 || items[i].n > (int64_t(1) << 30)) return -1;
+    blocks += ceil_div(items[i].n, 16);
+  }
+  return blocks;
+}
+
+int64_t q4_gemm_batch_plan_bytes(int32_t count, int64_t blocks) {
+  if (count < 1 || count > kBatchMaxItems || blocks < 1 || blocks > kBatchMaxBlocks) return -1;
+  return ceil_div(batch_owner_offset(count) + 2 * blocks, 16) * 16;
+}
+
+q4_status q4_gemm_batch_encode(const q4_gemm_batch_item* items, int32_t count, int64_t m, int64_t k,
+                               q4_out_dtype y_dtype, void* host_plan, int64_t plan_bytes) {
+  if (!items || !host_plan) return Q4_ERR_NULL;
+  if (count < 1 || count > kBatchMaxItems || m < 5 || m > 16) return Q4_ERR_SHAPE;
+  bool sb16 = k % 256 == 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const q4_gemm_batch_item& it = items[i];
+    if (it.n < 1 || it.n > (int64_t(1) << 30)) return Q4_ERR_SHAPE;
+    const q4_status s = check_product(it.x, m, it.packed, it.scales, it.biases, it.n, k, it.y, y_dtype);
+    if (s != Q4_OK) return s;
+    sb16 = sb16 && aligned(it.scales, 16) && aligned(it.biases, 16);
+  }
+  const int64_t blocks = q4_gemm_batch_blocks(items, count);
+  if (blocks > kBatchMaxBlocks) return Q4_ERR_UNSUPPORTED;
+  if (blocks < 1 || plan_bytes < q4_gemm_batch_plan_bytes(count, blocks)) return Q4_ERR_SHAPE;
+  int gs = 0, waves = 0;
+  if (!gemm_plan(k / 32, gs, waves)) return Q4_ERR_UNSUPPORTED;
+
+  char* base = static_cast<char*>(host_plan);
+  GemmBatchHeader h{};
+  h.magic = kBatchMagic;
+  h.count = count, h.m = static_cast<int32_t>(m), h.G = static_cast<int32_t>(k / 32);
+  h.blocks = static_cast<int32_t>(blocks), h.dtype = static_cast<int32_t>(y_dtype);
+  h.gs = gs, h.waves = waves, h.sb16 = sb16 ? 1 : 0;
+  std::memcpy(base, &h, sizeof h);
+  uint16_t* owner = reinterpret_cast<uint16_t*>(base + batch_owner_offset(count));
+  int32_t start = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const q4_gemm_batch_item& it = items[i];
+    q4k::GemmBatchItem d{it.x, it.packed, it.scales, it.biases, it.y, static_cast<int32_t>(it.n), start};
+    std::memcpy(base + sizeof(GemmBatchHeader) + i * sizeof(q4k::GemmBatchItem), &d, sizeof d);
+    const int32_t nb = static_cast<int32_t>(ceil_div(it.n, 16));
+    for (int32_t b = 0; b < nb; ++b) owner[start + b] = static_cast<uint16_t>(i);
+    start += nb;
+  }
+  return Q4_OK;
+}
+
+q4_status q4_gemm_batch_run(const void* host_plan, const void* device_plan, void* stream) {
+  if (!host_plan || !device_plan) return Q4_ERR_NULL;
+  GemmBatchHeader h;
+  std::memcpy(&h, host_plan, sizeof h);
+  if (h.magic != kBatchMagic || h.count < 1 || h.count > kBatchMaxItems || h.blocks < 1 ||
+      h.blocks > kBatchMaxBlocks || h.m < 5 || h.m > 16 || h.waves < 1 || h.waves > 16 ||
+      (h.gs != 8 && h.gs != 16 && h.gs != 32) || (h.dtype != Q4_OUT_BF16 && h.dtype != Q4_OUT_F32))
+    return Q4_ERR_SHAPE;
+  if (!aligned(device_plan, 16)) return Q4_ERR_ALIGN;
+  const hipStream_t st = as_stream(stream);
+  switch (h.gs) {
+    case 8: launch_batch<8>(h, device_plan, st); break;
+    case 16: launch_batch<16>(h, device_plan, st); break;
+    default: launch_batch<32>(h, device_plan, st); break;
+  }
+  return launch_status();
 }
 
 q4_status q4_multilinear_step(const uint16_t* x, int64_t m, const uint32_t* packed,

@@ -353,17 +353,18 @@ constexpr int kGemmKB = Q4_GEMM_KB;
 // groups are 16-byte aligned runs, loaded once per row with 16-byte loads
 // (GS / 8 per row) instead of one 2-byte load per group and batch: 16 rows
 // per load either way, so that cuts the cache lines looked up per wave by 8.
+// The product's body for block `bid` of its grid (the kernels below pass
+// their own block index, or a block's index within one product of a batch).
 template <int GS, int T, bool OUT_F32, bool SB16, bool TILED>
-__global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restrict__ x, int m,
-                                                          const uint32_t* __restrict__ packed,
-                                                          const uint16_t* __restrict__ scales,
-                                                          const uint16_t* __restrict__ biases,
-                                                          int n, int G, void* __restrict__ y, int mtiles,
-                                                          int nxcc) {
+__device__ __forceinline__ void gemm_mfma_body(int bid, const uint16_t* __restrict__ x, int m,
+                                               const uint32_t* __restrict__ packed,
+                                               const uint16_t* __restrict__ scales,
+                                               const uint16_t* __restrict__ biases, int n, int G,
+                                               void* __restrict__ y, int mtiles, int nxcc) {
   extern __shared__ float red_dyn[];  // [nwaves][T][4][64], then each wave's code staging
-  int rblk = blockIdx.x, tile = 0;
+  int rblk = bid, tile = 0;
   if constexpr (TILED) {
-    const int b = blockIdx.x, span = nxcc * mtiles;
+    const int b = bid, span = nxcc * mtiles;
     rblk = (b / span) * nxcc + b % nxcc;
     tile = (b / nxcc) % mtiles;
     if (rblk * 16 * T >= n) return;  // (past the last row block: the grid is a whole number of XCD rounds)
@@ -581,6 +582,38 @@ __global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restr
     const int row = nbase + 16 * t + (l & 15);
     if (mi < m && row < n) store_out<OUT_F32>(y, (int64_t)(16 * tile + mi) * n + row, s);
   }
+}
+
+template <int GS, int T, bool OUT_F32, bool SB16, bool TILED>
+__global__ void __launch_bounds__(1024) gemm_mfma_kernel(const uint16_t* __restrict__ x, int m,
+                                                          const uint32_t* __restrict__ packed,
+                                                          const uint16_t* __restrict__ scales,
+                                                          const uint16_t* __restrict__ biases,
+                                                          int n, int G, void* __restrict__ y, int mtiles,
+                                                          int nxcc) {
+  gemm_mfma_body<GS, T, OUT_F32, SB16, TILED>(blockIdx.x, x, m, packed, scales, biases, n, G, y, mtiles, nxcc);
+}
+
+// A batch of independent products of one shape class (same m <= 16 rows, same
+// k) in one launch: each product's blocks follow the last one's, so the grid
+// has no gap between products. `owner` gives each block its product.
+struct GemmBatchItem {
+  const uint16_t* x;
+  const uint32_t* packed;
+  const uint16_t* scales;
+  const uint16_t* biases;
+  void* y;
+  int32_t n;
+  int32_t block_start;  // its first block in the grid
+};
+static_assert(sizeof(GemmBatchItem) == 48, "the plan's item layout");
+
+template <int GS, bool OUT_F32, bool SB16>
+__global__ void __launch_bounds__(1024) gemm_batch_kernel(const GemmBatchItem* __restrict__ items,
+                                                          const uint16_t* __restrict__ owner, int m, int G) {
+  const GemmBatchItem* it = items + owner[blockIdx.x];
+  gemm_mfma_body<GS, 1, OUT_F32, SB16, false>(static_cast<int>(blockIdx.x) - it->block_start, it->x, m,
+                                              it->packed, it->scales, it->biases, it->n, G, it->y, 1, 1);
 }
 
 // ---------------------------------------------------------------------------

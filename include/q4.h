@@ -130,6 +130,48 @@ q4_status q4_gemm_small(const uint16_t* x, int64_t m, const uint32_t* packed,
                         const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
                         void* y, q4_out_dtype y_dtype, void* stream);
 
+/* A batch of independent q4_gemm_small products that share m (5..16 rows) and
+ * k, run in one launch: the concurrent conversations of q4_gemm_small ("A
+ * smaller voice model", Concurrency section) over many weight matrices, such
+ * as every matrix of a decoder step, without one launch per matrix. Product i
+ * is y_i = x_i w_hat_i^T exactly as q4_gemm_small computes it (same kernel
+ * body and rounding), for item i's x ([m][k] bf16), packed, scales, biases,
+ * y ([m][n] of y_dtype) and n >= 1.
+ *
+ * Use: q4_gemm_batch_encode() the items into a host buffer of
+ * q4_gemm_batch_plan_bytes() (it needs the number of row blocks, sum of
+ * ceil(n_i / 16), as `blocks`; q4_gemm_batch_blocks() returns it), copy the
+ * buffer to device memory (16-byte aligned), then call q4_gemm_batch_run()
+ * with both copies as often as needed. The plan holds the device pointers
+ * given at encode time and stays valid while those buffers live; the two
+ * copies must hold the same bytes. Limits: 1..4096 items (Q4_ERR_SHAPE),
+ * at most 2^24 blocks in total and k <= Q4_MAX_K (Q4_ERR_UNSUPPORTED);
+ * Q4_ERR_SHAPE also for m outside 5..16 or a plan buffer too small. Outputs may not overlap each other or any
+ * input (not checked). Items are not ordered: the products run concurrently. */
+typedef struct q4_gemm_batch_item {
+  const uint16_t* x;      /* bf16 [m][k], 16-byte aligned */
+  const uint32_t* packed; /* [n][k/8]  */
+  const uint16_t* scales; /* [n][k/32] */
+  const uint16_t* biases; /* [n][k/32] */
+  void* y;                /* [m][n] of the batch's output dtype */
+  int64_t n;
+} q4_gemm_batch_item;
+
+/* Blocks of 16 weight rows over the items (< 0 if items is NULL, count is
+ * outside 1..4096 or an n is outside 1..2^30). */
+int64_t q4_gemm_batch_blocks(const q4_gemm_batch_item* items, int32_t count);
+/* Bytes of the plan buffer for `count` items and `blocks` row blocks (< 0
+ * outside the limits above). */
+int64_t q4_gemm_batch_plan_bytes(int32_t count, int64_t blocks);
+/* Validate every item (q4_gemm_small's pointer and shape rules) and write the
+ * plan into host_plan (plan_bytes long). Launches nothing. */
+q4_status q4_gemm_batch_encode(const q4_gemm_batch_item* items, int32_t count, int64_t m, int64_t k,
+                               q4_out_dtype y_dtype, void* host_plan, int64_t plan_bytes);
+/* Run the batch on `stream` (one launch); host_plan is read for the launch
+ * shape, device_plan by the kernel. Q4_ERR_SHAPE if host_plan is not an
+ * encoded plan, Q4_ERR_ALIGN if device_plan is not 16-byte aligned. */
+q4_status q4_gemm_batch_run(const void* host_plan, const void* device_plan, void* stream);
+
 /* Depformer MultiLinear step ("NVIDIA PersonaPlex 7B on Apple Silicon",
  * Depformer section, MultiLinear code figure): the weight holds num_steps
  * blocks of `out` rows ([num_steps*out][k]); step `step` multiplies by rows

@@ -569,3 +569,71 @@ def test_chain_encoder_places_activations_round_the_arena():
     assert rc == q4.Q4_OK
     assert [_stage_field(buf, s, XOFF) for s in range(3)] == [0, 0, 0]
     assert [_stage_field(buf, s, XWAIT) for s in range(3)] == [-1, 0, 1]
+
+
+def _batch(ns, x=None, scales=None, y=None):
+    # fake, aligned device addresses: the encoder only validates and records them
+    items = (q4._GemmBatchItem * len(ns))()
+    for i, n in enumerate(ns):
+        base = 0x100000 * (i + 1)
+        items[i] = q4._GemmBatchItem(x if x is not None else base, base + 0x10000,
+                                     scales if scales is not None else base + 0x20000, base + 0x30000,
+                                     y if y is not None else base + 0x40000, n)
+    return items
+
+
+def test_gemm_batch_encode_validation_and_layout():
+    lib = q4.load()
+    ns = [16, 17, 1, 40]
+    items = _batch(ns)
+    blocks = lib.q4_gemm_batch_blocks(ctypes.byref(items), 4)
+    assert blocks == 1 + 2 + 1 + 3
+    nb = lib.q4_gemm_batch_plan_bytes(4, blocks)
+    assert nb == (64 + 4 * 48 + 2 * blocks + 15) // 16 * 16
+    buf = (ctypes.c_uint8 * nb)()
+    assert lib.q4_gemm_batch_encode(ctypes.byref(items), 4, 8, 4096, 0, ctypes.byref(buf), nb) == q4.Q4_OK
+    raw = bytes(buf)
+    magic, count, m, G, nblocks, dtype, gs, waves, sb16 = struct.unpack_from("<Iiiiiiiii", raw, 0)
+    assert (magic, count, m, G, nblocks, dtype) == (0x51344742, 4, 8, 128, blocks, 0)
+    assert (gs, waves, sb16) == (16, 8, 1)  # k = 4096: 16 groups per wave, 8 waves
+    starts = [struct.unpack_from("<qqqqqii", raw, 64 + 48 * i) for i in range(4)]
+    assert [s[5] for s in starts] == ns and [s[6] for s in starts] == [0, 1, 3, 4]
+    assert starts[2][0] == 0x300000 and starts[2][4] == 0x340000
+    owner = struct.unpack_from("<%dH" % blocks, raw, 64 + 4 * 48)
+    assert owner == (0, 1, 1, 2, 3, 3, 3)
+    # the groups-per-wave rule of q4_gemm_small: k = 11264 -> 32 per wave, 11 waves; k = 1024 -> 8, 4
+    for k, want in ((11264, (32, 11)), (1024, (8, 4))):
+        assert lib.q4_gemm_batch_encode(ctypes.byref(items), 4, 16, k, 1, ctypes.byref(buf), nb) == q4.Q4_OK
+        assert struct.unpack_from("<ii", bytes(buf), 24) == want
+    # scales not 16-byte aligned: one-group scale loads for the whole batch
+    odd = _batch(ns, scales=0x100002)
+    assert lib.q4_gemm_batch_encode(ctypes.byref(odd), 4, 8, 4096, 0, ctypes.byref(buf), nb) == q4.Q4_OK
+    assert struct.unpack_from("<i", bytes(buf), 32)[0] == 0
+    # refusals
+    assert lib.q4_gemm_batch_blocks(None, 4) < 0 and lib.q4_gemm_batch_blocks(ctypes.byref(items), 0) < 0
+    assert lib.q4_gemm_batch_blocks(ctypes.byref(_batch([0])), 1) < 0
+    assert lib.q4_gemm_batch_plan_bytes(4097, 10) < 0 and lib.q4_gemm_batch_plan_bytes(1, (1 << 24) + 1) < 0
+    enc = lambda it, c, m, k, dt=0, n=nb: lib.q4_gemm_batch_encode(ctypes.byref(it), c, m, k, dt, ctypes.byref(buf), n)
+    assert enc(items, 4, 4, 4096) == q4.Q4_ERR_SHAPE  # 1..4 rows are the GEMV kernel's
+    assert enc(items, 4, 17, 4096) == q4.Q4_ERR_SHAPE
+    assert enc(items, 0, 8, 4096) == q4.Q4_ERR_SHAPE
+    assert enc(items, 4, 8, 4096, n=nb - 16) == q4.Q4_ERR_SHAPE
+    assert enc(items, 4, 8, 4096, dt=2) == q4.Q4_ERR_SHAPE
+    assert enc(items, 4, 8, 40) == q4.Q4_ERR_SHAPE
+    assert enc(items, 4, 8, 16384 + 32) == q4.Q4_ERR_UNSUPPORTED
+    assert enc(_batch(ns, x=0x100008), 4, 8, 4096) == q4.Q4_ERR_ALIGN
+    assert enc(_batch(ns, y=0), 4, 8, 4096) == q4.Q4_ERR_NULL
+    assert lib.q4_gemm_batch_encode(None, 4, 8, 4096, 0, ctypes.byref(buf), nb) == q4.Q4_ERR_NULL
+
+
+def test_gemm_batch_run_validation():
+    lib = q4.load()
+    junk = (ctypes.c_uint8 * 64)()
+    assert lib.q4_gemm_batch_run(ctypes.byref(junk), 0x1000, None) == q4.Q4_ERR_SHAPE  # not an encoded plan
+    assert lib.q4_gemm_batch_run(None, 0x1000, None) == q4.Q4_ERR_NULL
+    items = _batch([32])
+    nb = lib.q4_gemm_batch_plan_bytes(1, 2)
+    buf = (ctypes.c_uint8 * nb)()
+    assert lib.q4_gemm_batch_encode(ctypes.byref(items), 1, 5, 256, 0, ctypes.byref(buf), nb) == q4.Q4_OK
+    assert lib.q4_gemm_batch_run(ctypes.byref(buf), 0x1008, None) == q4.Q4_ERR_ALIGN
+    assert lib.q4_gemm_batch_run(ctypes.byref(buf), None, None) == q4.Q4_ERR_NULL

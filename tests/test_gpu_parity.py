@@ -130,9 +130,10 @@ def test_gemm_small_matches_oracle(n, k, m, out_dtype):
 
 
 # The host planner picks the kernel variant from k. The model shapes reach the
-# GEMV with 64/32 lanes per row and the MFMA kernel with 8/32 groups per wave;
-# these k reach the others: 16 lanes per row (G = 16, 48, 80 groups) and 16
-# groups per wave (G = 129, 200, 256; m <= 4 take the GEMV, also 16 lanes).
+# GEMV with 64/32 lanes per row and the MFMA kernel with 8 (k = 1024, 2816),
+# 16 (k = 4096) and 32 (k = 11264) groups per wave; these k reach the others:
+# 16 lanes per row (G = 16, 48, 80 groups) and 16 groups per wave at 9..16
+# waves (G = 129, 200, 256; m <= 4 take the GEMV, also 16 lanes).
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("k", [512, 1536, 2560])
 def test_gemv_sixteen_lane_rows(k, out_dtype):
@@ -291,6 +292,69 @@ def test_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
     assert torch.equal(c.view(torch.int32), d.view(torch.int32))
+
+
+# ------------------------------------------------------------------ product batch
+
+def _batch_case(ns, k, m, out_dtype, seed):
+    mats, xs, outs, refs = [], [], [], []
+    for i, n in enumerate(ns):
+        P, S, B = oracle.quantize(_w(n, k, seed=seed, item=i))
+        x = _x(m, k, seed=seed + 1, item=i)
+        refs.append(oracle.matmul(x, P, S, B, k))
+        mats.append(upload_quantized(P, S, B))
+        xs.append(to_gpu_bf16_bits(x))
+        outs.append(torch.full((m, n), float("nan"), dtype=out_dtype, device=dev()))
+    return mats, xs, outs, refs
+
+
+# ragged row counts (1, 17, 40 rows: partial 16-row blocks), one-group-scale
+# loads (k = 96, 1056: k not a multiple of 256) and the model's widths with 16
+# (k = 4096) and 32 (k = 11264) groups per wave
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("m", [5, 8, 16])
+@pytest.mark.parametrize("ns,k", [([37, 1, 300, 16, 17], 96), ([129, 1000, 64], 1056),
+                                  ([4096, 11264, 40], 4096), ([300, 4096], 11264)])
+def test_gemm_batch_matches_oracle_and_single_calls(ns, k, m, out_dtype):
+    mats, xs, outs, refs = _batch_case(ns, k, m, out_dtype, seed=31 * k + m)
+    plan = q4.q4_gemm_batch_build(xs, mats, outs)
+    q4.q4_gemm_batch_run(plan)
+    torch.cuda.synchronize()
+    first = [o.clone() for o in outs]
+    for o in outs:
+        o.fill_(float("nan"))
+    q4.q4_gemm_batch_run(plan)  # the same plan again: the same bits
+    torch.cuda.synchronize()
+    for i, n in enumerate(ns):
+        _check(outs[i], refs[i], out_dtype)
+        single = q4.q4_gemm_small(xs[i], *mats[i], out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[i].view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32),
+                           single.view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32)), f"item {i}"
+        assert torch.equal(first[i].view(torch.uint8), outs[i].view(torch.uint8))
+
+
+def test_gemm_batch_of_a_full_layer():
+    """One temporal layer's seven matrices (q, k, v, o, gate, up at k = 4096;
+    down at k = 11264) as two batches, against one call per matrix, bit for bit."""
+    m = 16
+    shapes = [(4096, 4096)] * 4 + [(11264, 4096)] * 2
+    outs4, xs4, mats4, singles = [], [], [], []
+    for i, (n, k) in enumerate(shapes):
+        w = _w(n, k, seed=5, item=i)
+        mats4.append(upload_quantized(*oracle.quantize(w)))
+        xs4.append(to_gpu_bf16_bits(_x(m, k, seed=6, item=i)))
+        outs4.append(torch.empty((m, n), dtype=torch.bfloat16, device=dev()))
+    Pd = upload_quantized(*oracle.quantize(_w(4096, 11264, seed=5, item=7)))
+    xd = to_gpu_bf16_bits(_x(m, 11264, seed=6, item=7))
+    yd = torch.empty((m, 4096), dtype=torch.bfloat16, device=dev())
+    q4.q4_gemm_batch_run(q4.q4_gemm_batch_build(xs4, mats4, outs4))
+    q4.q4_gemm_batch_run(q4.q4_gemm_batch_build([xd], [Pd], [yd]))
+    torch.cuda.synchronize()
+    for x, mat, y in zip(xs4 + [xd], mats4 + [Pd], outs4 + [yd]):
+        ref = q4.q4_gemm_small(x, *mat)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
 
 
 # ------------------------------------------------------------------ MultiLinear
