@@ -5,12 +5,13 @@
 // driver and runs it on a machine without a GPU.
 //
 // The driver exercises what runs on the host before any launch: argument
-// validation of every entry point (null pointers, shapes, alignment) and the
-// chain encoders, whose plans are written into host buffers of exactly
-// q4_chain_plan_bytes(). Device pointers are stand-in addresses that the host
-// code must never dereference; a dereference, a write past a plan buffer or an
-// overflow in the encoders' arithmetic ends the run with the sanitizer's
-// report. Expected status codes are checked as well.
+// validation of every entry point (null pointers, shapes, alignment), the
+// chain encoders and the product-batch encoder, whose plans are written into
+// host buffers of exactly q4_chain_plan_bytes() or q4_gemm_batch_plan_bytes().
+// Device pointers are stand-in addresses that the host code must never
+// dereference; a dereference, a write past a plan buffer or an overflow in the
+// encoders' arithmetic ends the run with the sanitizer's report. Expected
+// status codes are checked as well.
 #include <stdint.h>
 #include <stdio.h>
 
@@ -220,9 +221,57 @@ void check_chains() {
 
 }  // namespace
 
+// the product batch: plans written into buffers of exactly
+// q4_gemm_batch_plan_bytes(), up to the item and block limits
+q4_status encode_batch(const std::vector<q4_gemm_batch_item>& it, int64_t m, int64_t k, int64_t short_by = 0) {
+  const int64_t blocks = q4_gemm_batch_blocks(it.data(), (int32_t)it.size());
+  const int64_t bytes = q4_gemm_batch_plan_bytes((int32_t)it.size(), blocks);
+  if (bytes <= 0) return Q4_ERR_SHAPE;
+  std::vector<unsigned char> plan((size_t)(bytes - short_by));
+  return q4_gemm_batch_encode(it.data(), (int32_t)it.size(), m, k, Q4_OUT_BF16, plan.data(), bytes - short_by);
+}
+
+q4_gemm_batch_item batch_item(int64_t n, int64_t k, int64_t m) {
+  const Mat w = make_mat(n, k, (int)m);
+  return {fake<uint16_t>(2 * m * k), w.packed, w.scales, w.biases, w.y, n};
+}
+
+void check_batches() {
+  std::vector<q4_gemm_batch_item> step;  // the temporal step's 192 products with k = 4096
+  for (int l = 0; l < 32; ++l)
+    for (int64_t n : {4096, 4096, 4096, 4096, 11264, 11264}) step.push_back(batch_item(n, 4096, 16));
+  expect(encode_batch(step, 16, 4096) == Q4_OK, "batch of the step's k = 4096 products");
+  expect(encode_batch(step, 16, 4096, 16) == Q4_ERR_SHAPE, "batch plan buffer too small");
+  expect(encode_batch(step, 4, 4096) == Q4_ERR_SHAPE, "batch of 4 rows");
+  std::vector<q4_gemm_batch_item> ragged;
+  for (int64_t n : {1, 15, 16, 17, 33, 1000}) ragged.push_back(batch_item(n, 96, 5));
+  expect(encode_batch(ragged, 5, 96) == Q4_OK, "ragged batch");
+  // 4096 items of 4096 blocks each: the 2^24-block limit exactly, then one block more
+  std::vector<q4_gemm_batch_item> big;
+  for (int i = 0; i < 4096; ++i) big.push_back(batch_item(65536, 256, 8));
+  expect(encode_batch(big, 8, 256) == Q4_OK, "2^24 blocks");
+  big.back().n += 1;
+  const int64_t max_bytes = q4_gemm_batch_plan_bytes(4096, (int64_t)1 << 24);
+  std::vector<unsigned char> plan((size_t)max_bytes);
+  expect(q4_gemm_batch_encode(big.data(), 4096, 8, 256, Q4_OUT_BF16, plan.data(), max_bytes) == Q4_ERR_UNSUPPORTED,
+         "2^24 + 1 blocks");
+  big.back().n -= 1;
+  big.push_back(batch_item(16, 256, 8));
+  expect(q4_gemm_batch_blocks(big.data(), 4097) < 0, "4097 items");
+  // run: refusals only (nothing is launched)
+  std::vector<unsigned char> junk(64, 0);
+  expect(q4_gemm_batch_run(junk.data(), fake<void>(64), nullptr) == Q4_ERR_SHAPE, "run of a non-plan");
+  const int64_t bytes = q4_gemm_batch_plan_bytes(6, q4_gemm_batch_blocks(ragged.data(), 6));
+  std::vector<unsigned char> rp((size_t)bytes);
+  expect(q4_gemm_batch_encode(ragged.data(), 6, 5, 96, Q4_OUT_F32, rp.data(), bytes) == Q4_OK, "ragged plan");
+  expect(q4_gemm_batch_run(rp.data(), reinterpret_cast<const char*>(fake<void>(64)) + 8, nullptr) == Q4_ERR_ALIGN,
+         "run with a misaligned device plan");
+}
+
 int main() {
   check_validation();
   check_chains();
+  check_batches();
   if (failures) {
     fprintf(stderr, "%d check(s) failed\n", failures);
     return 1;
