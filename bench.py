@@ -879,21 +879,9 @@ def bench_other(args, dev) -> int:
             run, launches, kernel = rows_chain.run_chain, 1, "chain_kernel"
         elif use_batch:
             # every product of one k in one launch (the step: k = 4096 and k = 11264)
-            by_k = {}
-            for st in rows_chain.stages:
-                for mt, y in zip(st.mats, st.outs):
-                    xs, mats, outs = by_k.setdefault(st.x.shape[-1], ([], [], []))
-                    xs.append(st.x)
-                    mats.append((mt.packed, mt.scales, mt.biases))
-                    outs.append(y)
-            plans = [q4.q4_gemm_batch_build(*v) for _, v in sorted(by_k.items())]
-
-            def run_batches():
-                for pl in plans:
-                    q4.q4_gemm_batch_run(pl)
-
-            g = graph_of(run_batches)
-            run, launches, kernel = g.replay, len(plans), "gemm_batch_kernel"
+            rows_chain.prepare_batches()
+            g = graph_of(rows_chain.run_batches)
+            run, launches, kernel = g.replay, len(rows_chain._batches), "gemm_batch_kernel"
         else:
             g = graph_of(rows_chain.run_launches)
             run, launches = g.replay, chain.num_matrices()

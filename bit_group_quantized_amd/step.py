@@ -8,11 +8,14 @@ This is the per-frame temporal step's weight stream (blog translation,
 pipeline diagram: 32 layers of width 4096) and the Depformer's per-codebook
 step (same page, MultiLinear figure).
 
-Two executors:
+Three executors:
 * ``launches``: one q4_gemv (or, for several activation rows, q4_gemm_small)
   call per matrix, in order, on the current stream
   (capturable into a HIP graph with ``torch.cuda.graph``);
-* ``chain``: the whole chain in one persistent launch (q4_chain_run).
+* ``chain``: the whole chain in one persistent launch (q4_chain_run);
+* ``batches``: for 5..16 activation rows and stages that read no output of
+  the chain, every product at once, one q4_gemm_batch_run launch per distinct
+  k (the products are unordered, so a stage may not consume another's output).
 """
 from __future__ import annotations
 
@@ -21,7 +24,8 @@ from typing import List, Optional
 
 import torch
 
-from . import q4_chain_build, q4_chain_run, q4_chain_workspace_bytes, q4_gemm_small, q4_gemv
+from . import (q4_chain_build, q4_chain_run, q4_chain_workspace_bytes, q4_gemm_batch_build, q4_gemm_batch_run,
+               q4_gemm_small, q4_gemv)
 
 
 @dataclass
@@ -75,6 +79,7 @@ class Chain:
                            for i, m in enumerate(st.mats)]
         self._plan = None
         self._ws: Optional[torch.Tensor] = None
+        self._batches = None
         self.device = dev
 
     def weight_bytes(self) -> int:
@@ -103,6 +108,36 @@ class Chain:
     def run_chain(self) -> None:
         self.prepare_chain()
         q4_chain_run(self._plan, self._ws)
+
+    # ---- executor 3: all products at once, one launch per distinct k
+    def prepare_batches(self) -> None:
+        if self._batches is not None:
+            return
+        if any(st.fused() for st in self.stages):
+            raise ValueError("norm, gate and residual are fused in the persistent executor only")
+
+        def span(t: torch.Tensor):
+            return t.data_ptr(), t.data_ptr() + t.numel() * t.element_size()
+
+        outs = [span(y) for st in self.stages for y in st.outs if y is not None]
+        by_k = {}
+        for st in self.stages:
+            if st.x.dim() != 2 or not 5 <= st.x.shape[0] <= 16:
+                raise ValueError("the product batch takes x of 5..16 activation rows")
+            lo, hi = span(st.x)
+            if any(lo < b and a < hi for a, b in outs):
+                raise ValueError("a stage reads an output of the chain: the batch runs every product at once")
+            xs, mats, ys = by_k.setdefault(st.x.shape[-1], ([], [], []))
+            for m, y in zip(st.mats, st.outs):
+                xs.append(st.x)
+                mats.append((m.packed, m.scales, m.biases))
+                ys.append(y)
+        self._batches = [q4_gemm_batch_build(*v) for _, v in sorted(by_k.items())]
+
+    def run_batches(self) -> None:
+        self.prepare_batches()
+        for plan in self._batches:
+            q4_gemm_batch_run(plan)
 
     def chain_status(self) -> int:
         """Device-side status word of the persistent executor (0 = ok)."""

@@ -637,3 +637,18 @@ def test_gemm_batch_run_validation():
     assert lib.q4_gemm_batch_encode(ctypes.byref(items), 1, 5, 256, 0, ctypes.byref(buf), nb) == q4.Q4_OK
     assert lib.q4_gemm_batch_run(ctypes.byref(buf), 0x1008, None) == q4.Q4_ERR_ALIGN
     assert lib.q4_gemm_batch_run(ctypes.byref(buf), None, None) == q4.Q4_ERR_NULL
+
+
+def test_step_batches_refuse_dependent_stages_and_row_counts():
+    import torch
+    from bit_group_quantized_amd.step import Chain, Q4Matrix, Stage
+    mat = Q4Matrix(torch.zeros(16, 8, dtype=torch.int32), torch.zeros(16, 2, dtype=torch.bfloat16),
+                   torch.zeros(16, 2, dtype=torch.bfloat16))
+    y0 = torch.zeros(8, 64, dtype=torch.bfloat16)
+    first = Stage(torch.zeros(8, 64, dtype=torch.bfloat16), [mat], [y0[:, :16]])
+    reads_y0 = Stage(y0, [mat], [torch.zeros(8, 16, dtype=torch.bfloat16)])
+    with pytest.raises(ValueError, match="reads an output"):
+        Chain([first, reads_y0]).prepare_batches()
+    four_rows = Stage(torch.zeros(4, 64, dtype=torch.bfloat16), [mat], [torch.zeros(4, 16, dtype=torch.bfloat16)])
+    with pytest.raises(ValueError, match="5..16 activation rows"):
+        Chain([four_rows]).prepare_batches()

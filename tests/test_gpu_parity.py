@@ -357,6 +357,29 @@ def test_gemm_batch_of_a_full_layer():
         assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
 
 
+def test_step_batches_equal_launches():
+    """The step module's batch executor (one launch per k) against its
+    one-launch-per-matrix executor on a chain of two widths, bit for bit."""
+    from bit_group_quantized_amd.step import Chain, Q4Matrix, Stage
+    m = 8
+    stages = []
+    for si, (ns, k) in enumerate([((300, 17), 1024), ((129,), 2816), ((64, 1000), 1024)]):
+        mats = [Q4Matrix(*upload_quantized(*oracle.quantize(_w(n, k, seed=40 + si, item=j)))) for j, n in enumerate(ns)]
+        stages.append(Stage(to_gpu_bf16_bits(_x(m, k, seed=50 + si)), mats))
+    chain = Chain(stages)
+    chain.run_launches()
+    torch.cuda.synchronize()
+    want = [y.clone() for st in stages for y in st.outs]
+    for st in stages:
+        for y in st.outs:
+            y.fill_(float("nan"))
+    chain.run_batches()
+    torch.cuda.synchronize()
+    assert len(chain._batches) == 2
+    for got, ref in zip([y for st in stages for y in st.outs], want):
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
 # ------------------------------------------------------------------ MultiLinear
 
 @pytest.mark.parametrize("m", [1, 4])
