@@ -652,3 +652,26 @@ def test_step_batches_refuse_dependent_stages_and_row_counts():
     four_rows = Stage(torch.zeros(4, 64, dtype=torch.bfloat16), [mat], [torch.zeros(4, 16, dtype=torch.bfloat16)])
     with pytest.raises(ValueError, match="5..16 activation rows"):
         Chain([four_rows]).prepare_batches()
+
+
+def _no_gpu() -> bool:
+    import torch
+    return torch.cuda.device_count() == 0  # (counts devices without initialising HIP)
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="only where no GPU exists: the calls below pass validation and launch")
+def test_launch_failure_reports_hip_error():
+    """With no device, a call that passes every host check fails at its launch:
+    Q4_ERR_HIP, with the runtime's error kept for q4_last_hip_error()."""
+    lib = q4.load()
+    a = 0x10000000  # aligned stand-in addresses, never dereferenced: the launch fails first
+    assert lib.q4_gemv(a, a + 0x100000, a + 0x200000, a + 0x300000, 64, 256, a + 0x400000, 0, None) == q4.Q4_ERR_HIP
+    assert lib.q4_last_hip_error() != 0
+    assert lib.q4_gemm_small(a, 8, a + 0x100000, a + 0x200000, a + 0x300000, 64, 256, a + 0x400000, 1,
+                             None) == q4.Q4_ERR_HIP
+    items = (q4._GemmBatchItem * 1)(q4._GemmBatchItem(a, a + 0x100000, a + 0x200000, a + 0x300000, a + 0x400000, 64))
+    nb = lib.q4_gemm_batch_plan_bytes(1, 4)
+    buf = (ctypes.c_uint8 * nb)()
+    assert lib.q4_gemm_batch_encode(ctypes.byref(items), 1, 8, 256, 0, ctypes.byref(buf), nb) == q4.Q4_OK
+    assert lib.q4_gemm_batch_run(ctypes.byref(buf), a + 0x500000, None) == q4.Q4_ERR_HIP
+    assert q4.q4_status_str(q4.Q4_ERR_HIP)
