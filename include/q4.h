@@ -138,15 +138,16 @@ q4_status q4_gemm_small(const uint16_t* x, int64_t m, const uint32_t* packed,
  * body and rounding), for item i's x ([m][k] bf16), packed, scales, biases,
  * y ([m][n] of y_dtype) and n >= 1.
  *
- * Use: q4_gemm_batch_encode() the items into a host buffer of
- * q4_gemm_batch_plan_bytes() (it needs the number of row blocks, sum of
- * ceil(n_i / 16), as `blocks`; q4_gemm_batch_blocks() returns it), copy the
- * buffer to device memory (16-byte aligned), then call q4_gemm_batch_run()
- * with both copies as often as needed. The plan holds the device pointers
- * given at encode time and stays valid while those buffers live; the two
- * copies must hold the same bytes. Limits: 1..4096 items (Q4_ERR_SHAPE),
- * at most 2^24 blocks in total and k <= Q4_MAX_K (Q4_ERR_UNSUPPORTED);
- * Q4_ERR_SHAPE also for m outside 5..16 or a plan buffer too small. Outputs may not overlap each other or any
+ * Use: q4_gemm_batch_encode() the items into a host buffer (2-byte aligned,
+ * as any allocated or array buffer is) of q4_gemm_batch_plan_bytes() (it
+ * needs the number of row blocks, sum of ceil(n_i / 16), as `blocks`;
+ * q4_gemm_batch_blocks() returns it), copy the buffer to device memory
+ * (16-byte aligned), then call q4_gemm_batch_run() with both copies as often
+ * as needed. The plan holds the device pointers given at encode time and
+ * stays valid while those buffers live; the two copies must hold the same
+ * bytes. Limits: 1..4096 items (Q4_ERR_SHAPE), at most 2^24 blocks in total
+ * and k <= Q4_MAX_K (Q4_ERR_UNSUPPORTED); Q4_ERR_SHAPE also for m outside
+ * 5..16 or a plan buffer too small. Outputs may not overlap each other or any
  * input (not checked). Items are not ordered: the products run concurrently. */
 typedef struct q4_gemm_batch_item {
   const uint16_t* x;      /* bf16 [m][k], 16-byte aligned */
