@@ -602,7 +602,10 @@ def test_gemm_batch_encode_validation_and_layout():
     owner = struct.unpack_from("<%dH" % blocks, raw, 64 + 4 * 48)
     assert owner == (0, 1, 1, 2, 3, 3, 3)
     # the groups-per-wave rule of q4_gemm_small: k = 11264 -> 32 per wave, 11 waves; k = 1024 -> 8, 4
-    for k, want in ((11264, (32, 11)), (1024, (8, 4))):
+    # and its edges: 16 per wave only while that gives 8..16 waves (k = 3584: 7 -> 8 per wave;
+    # k = 8192: 16 waves; k = 8224: 17 -> 32 per wave)
+    for k, want in ((11264, (32, 11)), (1024, (8, 4)), (3584, (8, 14)), (3840, (16, 8)), (8192, (16, 16)),
+                    (8224, (32, 9)), (16384, (32, 16))):
         assert lib.q4_gemm_batch_encode(ctypes.byref(items), 4, 16, k, 1, ctypes.byref(buf), nb) == q4.Q4_OK
         assert struct.unpack_from("<ii", bytes(buf), 24) == want
     # scales not 16-byte aligned: one-group scale loads for the whole batch
